@@ -1,0 +1,142 @@
+"""Seeded input generators (no attention arithmetic here).
+
+Recipe (the same for every consumer):
+
+* ``numpy.random.default_rng(seed)``.
+* Varlen configs draw the sequence lengths first (``draw_varlen_lengths``).
+* Then q, k, v and dO are drawn, in that order, as float32 standard normals of
+  shape ``[B, S, H, D]`` (``[T, H, D]`` for packed batches) and each is
+  rounded once to bfloat16 with round-to-nearest-even.  Both sides consume
+  those exact bfloat16 values.
+* Then the T5 bias table is drawn as float32 ``normal(0, 0.5)`` of shape
+  ``[num_buckets, H]``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns as ``uint16``.  Inputs here are finite
+    normal draws, so no NaN handling is needed; infinities pass through.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    rounded = (bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to the float32 values they encode (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def draw_varlen_lengths(rng: np.random.Generator, total: int, mu: float = 6.0,
+                        sigma: float = 1.0, lo: int = 16, hi: int = 4096) -> np.ndarray:
+    """Packed-batch sequence lengths that sum exactly to ``total``.
+
+    Lengths are ``rint(lognormal(mu, sigma))`` clipped to ``[lo, hi]``, drawn
+    one at a time until the running sum reaches ``total``; the last length is
+    the remainder.  A remainder below ``lo`` is merged into the previous
+    sequence, or, if that would exceed ``hi``, the previous sequence gives
+    ``lo - r`` tokens to a last sequence of length ``lo``.
+    """
+    lens: list[int] = []
+    acc = 0
+    while acc < total:
+        L = int(np.clip(np.rint(rng.lognormal(mu, sigma)), lo, hi))
+        if acc + L >= total:
+            r = total - acc
+            if r < lo and lens:
+                if lens[-1] + r <= hi:
+                    lens[-1] += r
+                else:
+                    lens[-1] -= lo - r
+                    lens.append(lo)
+            else:
+                lens.append(r)
+            acc = total
+        else:
+            lens.append(L)
+            acc += L
+    out = np.asarray(lens, dtype=np.int64)
+    assert out.sum() == total and out.min() >= min(lo, total) and out.max() <= hi
+    return out
+
+
+def alibi_slope_values(heads: int) -> np.ndarray:
+    """The per-head ALiBi slope inputs the long-context config prescribes:
+    ``2**(-8*h/heads)`` for ``h = 1..heads``, as float32."""
+    h = np.arange(1, heads + 1, dtype=np.float64)
+    return np.exp2(-8.0 * h / heads).astype(np.float32)
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    return bf16_round(rng.standard_normal(size=shape, dtype=np.float32))
+
+
+@dataclass
+class DenseInputs:
+    q: np.ndarray      # uint16 bf16 bits [B,S,H,D]
+    k: np.ndarray
+    v: np.ndarray
+    do: Optional[np.ndarray]
+    table: Optional[np.ndarray]  # float32 [nb, H]
+
+    def f64(self, name: str) -> np.ndarray:
+        return bf16_bits_to_f32(getattr(self, name)).astype(np.float64)
+
+
+@dataclass
+class VarlenInputs:
+    lengths: np.ndarray      # int64 [nseq]
+    cu_seqlens: np.ndarray   # int32 [nseq+1]
+    q: np.ndarray            # uint16 bf16 bits [T,H,D]
+    k: np.ndarray
+    v: np.ndarray
+    do: Optional[np.ndarray]
+    table: Optional[np.ndarray]
+
+    def f64(self, name: str) -> np.ndarray:
+        return bf16_bits_to_f32(getattr(self, name)).astype(np.float64)
+
+
+def draw_dense(seed: int, B: int, S: int, H: int, D: int, *, num_buckets: int = 32,
+               with_dout: bool = True, with_table: bool = True) -> DenseInputs:
+    rng = np.random.default_rng(seed)
+    shape = (B, S, H, D)
+    q = _normal_bf16(rng, shape)
+    k = _normal_bf16(rng, shape)
+    v = _normal_bf16(rng, shape)
+    do = _normal_bf16(rng, shape) if with_dout else None
+    table = (rng.normal(0.0, 0.5, size=(num_buckets, H)).astype(np.float32)
+             if with_table else None)
+    return DenseInputs(q, k, v, do, table)
+
+
+def draw_varlen(seed: int, total: int, H: int, D: int, *, num_buckets: int = 32,
+                lengths: Optional[np.ndarray] = None, with_dout: bool = True,
+                with_table: bool = True, mu: float = 6.0, sigma: float = 1.0,
+                lo: int = 16, hi: int = 4096) -> VarlenInputs:
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        lengths = draw_varlen_lengths(rng, total, mu, sigma, lo, hi)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    assert lengths.sum() == total
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    shape = (total, H, D)
+    q = _normal_bf16(rng, shape)
+    k = _normal_bf16(rng, shape)
+    v = _normal_bf16(rng, shape)
+    do = _normal_bf16(rng, shape) if with_dout else None
+    table = (rng.normal(0.0, 0.5, size=(num_buckets, H)).astype(np.float32)
+             if with_table else None)
+    return VarlenInputs(lengths, cu, q, k, v, do, table)
