@@ -31,6 +31,7 @@ from .attention import (  # noqa: F401
     alibi_slopes,
     rope_rotate,
     rope_unrotate,
+    bf16_round_exact,
     bias_matrix,
     attention_fwd,
     attention_bwd,

@@ -29,6 +29,11 @@ Readings taken where the pages are silent:
   (geometric sequence of the ALiBi paper, which the report links).
 * RoPE: interleaved pairs (2p, 2p+1) rotated by angle t * base^(-2p/D), t the
   0-based position (local to each packed sequence); applied to q and k only.
+  The report trains in full bf16 and its kernels take bf16 q and k from the
+  positional-encoding classes, so the rotated q and k are bf16 tensors: the
+  exact rotation is rounded once to bf16 (nearest, ties to even) before the
+  scores.  Gradients flow through the rotation as if the rounding were the
+  identity.
 * Causal: key j is visible to query i iff j <= i.
 * Packed batches: a query attends only keys of its own sequence; positions are
   local to the sequence.
@@ -102,6 +107,16 @@ def rope_rotate(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarray
     return out
 
 
+def bf16_round_exact(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (8 significant bits),
+    ties to even, in one rounding step: x = m * 2^e with 0.5 <= |m| < 1, so
+    m * 2^8 rounded half-to-even by numpy gives the kept significand exactly.
+    (Normal range only; the inputs here are O(1).)"""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(m * 256.0), e - 8)
+
+
 def rope_unrotate(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarray:
     """Inverse of :func:`rope_rotate` (rotation by the opposite angle); maps a
     gradient with respect to rotated rows back to the unrotated rows."""
@@ -137,12 +152,14 @@ def bias_matrix(seqlen: int, head: int, *, bias: str, table=None, num_buckets: i
 
 
 def _scores(qh, kh, head, *, scale, causal, bias, table, num_buckets, max_distance,
-            bidirectional, slopes, rope_base):
+            bidirectional, slopes, rope_base, rope_round=True):
     S = qh.shape[0]
     pos = np.arange(S)
     if rope_base is not None:
         qh = rope_rotate(qh, pos, rope_base)
         kh = rope_rotate(kh, pos, rope_base)
+        if rope_round:
+            qh, kh = bf16_round_exact(qh), bf16_round_exact(kh)
     s = scale * (qh @ kh.T)
     bm = bias_matrix(S, head, bias=bias, table=table, num_buckets=num_buckets,
                      max_distance=max_distance, bidirectional=bidirectional, slopes=slopes)
@@ -167,23 +184,28 @@ def _softmax_rows(s):
 
 def head_fwd(qh, kh, vh, head, *, scale=1.0, causal=False, bias="none", table=None,
              num_buckets=32, max_distance=128, bidirectional=True, slopes=None,
-             rope_base=None):
-    """Forward for one head: qh, kh, vh float64 [S, D] -> (O [S, D], LSE [S])."""
+             rope_base=None, rope_round=True):
+    """Forward for one head: qh, kh, vh float64 [S, D] -> (O [S, D], LSE [S]).
+
+    ``rope_round=False`` skips the bf16 rounding of the rotated q, k (only the
+    finite-difference pin uses it: a rounding step has no derivative)."""
     s, _, _ = _scores(qh, kh, head, scale=scale, causal=causal, bias=bias, table=table,
                       num_buckets=num_buckets, max_distance=max_distance,
-                      bidirectional=bidirectional, slopes=slopes, rope_base=rope_base)
+                      bidirectional=bidirectional, slopes=slopes, rope_base=rope_base,
+                      rope_round=rope_round)
     P, lse = _softmax_rows(s)
     return P @ vh, lse
 
 
 def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", table=None,
              num_buckets=32, max_distance=128, bidirectional=True, slopes=None,
-             rope_base=None):
+             rope_base=None, rope_round=True):
     """Backward for one head -> (dq, dk, dv [S, D], dtable_h [num_buckets] or None)."""
     S = qh.shape[0]
     s, qr, kr = _scores(qh, kh, head, scale=scale, causal=causal, bias=bias, table=table,
                         num_buckets=num_buckets, max_distance=max_distance,
-                        bidirectional=bidirectional, slopes=slopes, rope_base=rope_base)
+                        bidirectional=bidirectional, slopes=slopes, rope_base=rope_base,
+                        rope_round=rope_round)
     P, _ = _softmax_rows(s)
     dP = doh @ vh.T
     Drow = (P * dP).sum(axis=1)

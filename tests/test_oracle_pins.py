@@ -94,8 +94,44 @@ def test_t5_bucket_closed_form_tables_32_128():
 
 
 # ---------------------------------------------------------------------------
-# ALiBi, RoPE
+# ALiBi, RoPE, bf16 rounding
 # ---------------------------------------------------------------------------
+
+
+def nearest_bf16(x: float) -> float:
+    """Nearest bfloat16 value by brute force over the two candidates that
+    bracket x (8 significant bits), ties to the even significand."""
+    if x == 0.0:
+        return 0.0
+    e = math.floor(math.log2(abs(x)))
+    # make sure 2^e <= |x| < 2^(e+1) despite log2 rounding
+    while 2.0 ** e > abs(x):
+        e -= 1
+    while 2.0 ** (e + 1) <= abs(x):
+        e += 1
+    ulp = 2.0 ** (e - 7)
+    lo = math.floor(abs(x) / ulp) * ulp
+    hi = lo + ulp
+    dlo, dhi = abs(x) - lo, hi - abs(x)
+    if dlo < dhi or (dlo == dhi and int(round(lo / ulp)) % 2 == 0):
+        r = lo
+    else:
+        r = hi
+    return math.copysign(r, x)
+
+
+def test_bf16_round_exact_matches_brute_force():
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(20000) * 3.0,
+                        # exact ties between neighbours: odd multiples of half an ulp
+                        (np.arange(1, 2001) * 2 + 1) * 2.0 ** -9 + 1.0,
+                        -(np.arange(1, 2001) * 2 + 1) * 2.0 ** -9 - 2.0])
+    got = oracle.bf16_round_exact(x)
+    want = np.array([nearest_bf16(float(v)) for v in x])
+    np.testing.assert_array_equal(got, want)
+    # fp32 inputs that are already bf16 values are unchanged
+    b = synth.bf16_bits_to_f32(synth.bf16_round(rng.standard_normal(1000).astype(np.float32)))
+    np.testing.assert_array_equal(oracle.bf16_round_exact(b.astype(np.float64)), b)
 
 
 def test_alibi_slopes_closed_form():
@@ -156,7 +192,7 @@ def brute_force_head(q, k, v, head, *, scale, causal, bias, table, nb, md, bidir
         out = []
         for p in range(D // 2):
             z = complex(x[2 * p], x[2 * p + 1]) * cmath.exp(1j * t * rope_base ** (-2 * p / D))
-            out += [z.real, z.imag]
+            out += [nearest_bf16(z.real), nearest_bf16(z.imag)]
         return out
 
     qr = [rot(q[i], i) for i in range(S)]
@@ -266,9 +302,10 @@ def test_backward_matches_finite_differences(case):
     q, k, v, do = (rng.standard_normal((S, D)) for _ in range(4))
     table = rng.normal(0, 0.5, (nb, 2))
     slopes = oracle.alibi_slopes(2)
+    # a rounding step has no derivative: check the calculus with it switched off
     kw = dict(scale=case["scale"], causal=case["causal"], bias=case["bias"], table=table,
               num_buckets=nb, max_distance=md, bidirectional=case["bidirectional"],
-              slopes=slopes, rope_base=case["rope_base"])
+              slopes=slopes, rope_base=case["rope_base"], rope_round=False)
     dq, dk, dv, dtab = head_bwd(q, k, v, do, head, **kw)
 
     def loss(q_, k_, v_, table_):
