@@ -1,0 +1,286 @@
+"""Python binding of libfat5attn with the C entry points' names.
+
+Torch is plumbing here: it owns device memory and supplies the current HIP
+stream.  Each function checks dtypes/shapes, fills the C params struct with
+``data_ptr()`` values and calls the library; every step of the attention path
+runs in the HIP kernels.  ``attention`` / ``varlen_attention`` wrap the pair
+of calls in a ``torch.autograd.Function``.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Union
+
+import torch
+
+from . import _lib
+from ._lib import (FaBias, FaBwdParams, FaFwdParams, FaVarlenBwdParams, FaVarlenFwdParams,
+                   check)
+
+
+@dataclass
+class T5Bias:
+    """T5 bucketed relative-position bias: table fp32 [num_buckets, H]."""
+    table: torch.Tensor
+    num_buckets: int = 32
+    max_distance: int = 128
+    bidirectional: bool = True
+
+
+@dataclass
+class ALiBi:
+    """ALiBi bias -slopes[h] * |i - j|: slopes fp32 [H]."""
+    slopes: torch.Tensor
+
+
+BiasSpec = Optional[Union[T5Bias, ALiBi]]
+
+
+def alibi_slopes(heads: int, device=None) -> torch.Tensor:
+    """ALiBi's geometric head slopes 2^(-8h/H), h = 1..H, as fp32."""
+    h = torch.arange(1, heads + 1, dtype=torch.float64)
+    return torch.exp2(-8.0 * h / heads).to(torch.float32).to(device)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _bias_struct(bias: BiasSpec, heads: int, device) -> FaBias:
+    b = FaBias()
+    if bias is None:
+        b.mode = _lib.FA_BIAS_NONE
+    elif isinstance(bias, T5Bias):
+        _need(bias.table, "bias.table", torch.float32, (bias.num_buckets, heads), device)
+        b.mode = _lib.FA_BIAS_T5
+        b.num_buckets = bias.num_buckets
+        b.max_distance = bias.max_distance
+        b.bidirectional = int(bool(bias.bidirectional))
+        b.table = bias.table.data_ptr()
+    elif isinstance(bias, ALiBi):
+        _need(bias.slopes, "bias.slopes", torch.float32, (heads,), device)
+        b.mode = _lib.FA_BIAS_ALIBI
+        b.slopes = bias.slopes.data_ptr()
+    else:
+        raise TypeError("bias must be None, T5Bias or ALiBi")
+    return b
+
+
+def _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base) -> FaFwdParams:
+    if q.dim() != 4:
+        raise ValueError("dense q must be [B, S, H, D]")
+    B, S, H, D = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, name, torch.bfloat16, (B, S, H, D), dev)
+    _need(lse, "lse", torch.float32, (B, H, S), dev)
+    p = FaFwdParams()
+    p.batch, p.seqlen, p.heads, p.head_dim = B, S, H, D
+    p.causal = int(bool(causal))
+    p.scale = float(scale)
+    p.rope_base = float(rope_base or 0.0)
+    p.q, p.k, p.v, p.o, p.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr()
+    p.bias = _bias_struct(bias, H, dev)
+    return p
+
+
+def _varlen_params(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, bias,
+                   rope_base) -> FaVarlenFwdParams:
+    if q.dim() != 3:
+        raise ValueError("packed q must be [T, H, D]")
+    T, H, D = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, name, torch.bfloat16, (T, H, D), dev)
+    _need(lse, "lse", torch.float32, (H, T), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    p = FaVarlenFwdParams()
+    p.nseq = cu_seqlens.numel() - 1
+    p.total, p.max_seqlen, p.heads, p.head_dim = T, int(max_seqlen), H, D
+    p.causal = int(bool(causal))
+    p.scale = float(scale)
+    p.rope_base = float(rope_base or 0.0)
+    p.cu_seqlens = cu_seqlens.data_ptr()
+    p.q, p.k, p.v, p.o, p.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr()
+    p.bias = _bias_struct(bias, H, dev)
+    return p
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == ctypes.c_size_t(-1).value:
+        raise _lib.FaError(_lib.FA_ERR_INVALID, "workspace size")
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+
+def fa_fwd(q, k, v, o, lse, *, scale=1.0, causal=False, bias: BiasSpec = None, rope_base=0.0,
+           workspace=None, stream=None) -> None:
+    """Dense forward into o [B,S,H,D] bf16 and lse [B,H,S] fp32."""
+    lib = _lib.load()
+    p = _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base)
+    ws, wsb = _workspace(lib.fa_fwd_workspace_size(ctypes.byref(p)), q.device, workspace)
+    check(lib.fa_fwd(ctypes.byref(p), _ptr(ws), wsb, _stream(q.device, stream)), "fa_fwd")
+
+
+def fa_varlen_fwd(q, k, v, o, lse, cu_seqlens, max_seqlen, *, scale=1.0, causal=False,
+                  bias: BiasSpec = None, rope_base=0.0, workspace=None, stream=None) -> None:
+    """Packed forward into o [T,H,D] bf16 and lse [H,T] fp32."""
+    lib = _lib.load()
+    p = _varlen_params(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, bias, rope_base)
+    ws, wsb = _workspace(lib.fa_varlen_fwd_workspace_size(ctypes.byref(p)), q.device, workspace)
+    check(lib.fa_varlen_fwd(ctypes.byref(p), _ptr(ws), wsb, _stream(q.device, stream)),
+          "fa_varlen_fwd")
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, scale=1.0, causal=False,
+           bias: BiasSpec = None, rope_base=0.0, workspace=None, stream=None) -> None:
+    """Dense backward into dq, dk, dv [B,S,H,D] bf16 and dtable [nb,H] fp32."""
+    lib = _lib.load()
+    p = FaBwdParams()
+    p.f = _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base)
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, torch.bfloat16, q.shape, q.device)
+    if dtable is not None:
+        _need(dtable, "dtable", torch.float32, (p.f.bias.num_buckets, q.shape[2]), q.device)
+    p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    p.dtable = _ptr(dtable)
+    ws, wsb = _workspace(lib.fa_bwd_workspace_size(ctypes.byref(p)), q.device, workspace)
+    check(lib.fa_bwd(ctypes.byref(p), _ptr(ws), wsb, _stream(q.device, stream)), "fa_bwd")
+
+
+def fa_varlen_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, max_seqlen, dtable=None, *,
+                  scale=1.0, causal=False, bias: BiasSpec = None, rope_base=0.0, workspace=None,
+                  stream=None) -> None:
+    """Packed backward into dq, dk, dv [T,H,D] bf16 and dtable [nb,H] fp32."""
+    lib = _lib.load()
+    p = FaVarlenBwdParams()
+    p.f = _varlen_params(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, bias, rope_base)
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, torch.bfloat16, q.shape, q.device)
+    if dtable is not None:
+        _need(dtable, "dtable", torch.float32, (p.f.bias.num_buckets, q.shape[1]), q.device)
+    p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    p.dtable = _ptr(dtable)
+    ws, wsb = _workspace(lib.fa_varlen_bwd_workspace_size(ctypes.byref(p)), q.device, workspace)
+    check(lib.fa_varlen_bwd(ctypes.byref(p), _ptr(ws), wsb, _stream(q.device, stream)),
+          "fa_varlen_bwd")
+
+
+def fa_t5_buckets(qlen: int, klen: int, num_buckets: int, max_distance: int,
+                  bidirectional: bool, out: torch.Tensor, stream=None) -> None:
+    """Bucket index of every (query, key) pair into out int32 [qlen, klen]."""
+    lib = _lib.load()
+    _need(out, "out", torch.int32, (qlen, klen))
+    check(lib.fa_t5_buckets(qlen, klen, num_buckets, max_distance, int(bool(bidirectional)),
+                            out.data_ptr(), _stream(out.device, stream)), "fa_t5_buckets")
+
+
+def fa_fwd_workspace_size(q, *, causal=False, scale=1.0, bias: BiasSpec = None,
+                          rope_base=0.0) -> int:
+    lib = _lib.load()
+    B, S, H, D = q.shape
+    o = q
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    p = _fwd_params(q, q, q, o, lse, scale, causal, bias, rope_base)
+    return lib.fa_fwd_workspace_size(ctypes.byref(p))
+
+
+# ---------------------------------------------------------------------------
+# Autograd wrappers
+# ---------------------------------------------------------------------------
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, table, slopes, bias, scale, causal, rope_base):
+        B, S, H, D = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+        fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, bias=bias, rope_base=rope_base)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.bias, ctx.scale, ctx.causal, ctx.rope_base = bias, scale, causal, rope_base
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dtable = None
+        if isinstance(ctx.bias, T5Bias) and ctx.bias.table.requires_grad:
+            dtable = torch.empty_like(ctx.bias.table)
+        fa_bwd(q, k, v, o, lse, do.contiguous(), dq, dk, dv, dtable, scale=ctx.scale,
+               causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
+        return dq, dk, dv, dtable, None, None, None, None, None
+
+
+def attention(q, k, v, *, bias: BiasSpec = None, causal=False, scale=1.0, rope_base=0.0,
+              return_lse=False):
+    """Exact attention with optional T5/ALiBi bias and RoPE; q, k, v [B,S,H,D] bf16."""
+    table = bias.table if isinstance(bias, T5Bias) else None
+    slopes = bias.slopes if isinstance(bias, ALiBi) else None
+    o, lse = _Attention.apply(q, k, v, table, slopes, bias, scale, causal, rope_base)
+    return (o, lse) if return_lse else o
+
+
+class _VarlenAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, table, cu_seqlens, max_seqlen, bias, scale, causal, rope_base):
+        T, H, D = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+        fa_varlen_fwd(q, k, v, o, lse, cu_seqlens, max_seqlen, scale=scale, causal=causal,
+                      bias=bias, rope_base=rope_base)
+        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
+        ctx.max_seqlen, ctx.bias, ctx.scale = max_seqlen, bias, scale
+        ctx.causal, ctx.rope_base = causal, rope_base
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, dlse):
+        q, k, v, o, lse, cu = ctx.saved_tensors
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dtable = None
+        if isinstance(ctx.bias, T5Bias) and ctx.bias.table.requires_grad:
+            dtable = torch.empty_like(ctx.bias.table)
+        fa_varlen_bwd(q, k, v, o, lse, do.contiguous(), dq, dk, dv, cu, ctx.max_seqlen, dtable,
+                      scale=ctx.scale, causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
+        return dq, dk, dv, dtable, None, None, None, None, None, None
+
+
+def varlen_attention(q, k, v, cu_seqlens, max_seqlen, *, bias: BiasSpec = None, causal=False,
+                     scale=1.0, rope_base=0.0, return_lse=False):
+    """Packed attention; q, k, v [T,H,D] bf16, cu_seqlens int32 [nseq+1]."""
+    table = bias.table if isinstance(bias, T5Bias) else None
+    o, lse = _VarlenAttention.apply(q, k, v, table, cu_seqlens, max_seqlen, bias, scale, causal,
+                                    rope_base)
+    return (o, lse) if return_lse else o

@@ -1,0 +1,399 @@
+// C ABI of libfat5attn: argument checks, workspace layout, T5 bucket
+// thresholds and dispatch to the kernel launchers.  The declarations and the
+// contract of every entry point are in include/fat5attn.h.
+#include "fat5attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fa_status hip_fail(hipError_t e, const char *where) {
+  return fail(FA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// T5 thresholds by exact integer comparison.  For n >= me the T5 bucket is
+// me + floor(ln(n/me) / ln(md/me) * L) (L = nb' - me) capped at nb' - 1, and
+// floor(...) >= k  <=>  n^L * me^k >= md^k * me^L.  thr[k-1] is the smallest
+// such n (k = 1 .. L-1), found by binary search on n in [me, md].
+// ---------------------------------------------------------------------------
+using Big = std::vector<uint32_t>;
+
+void mul_small(Big &a, uint32_t m) {
+  uint64_t carry = 0;
+  for (auto &x : a) {
+    const uint64_t t = (uint64_t)x * m + carry;
+    x = (uint32_t)t;
+    carry = t >> 32;
+  }
+  if (carry) a.push_back((uint32_t)carry);
+}
+
+int cmp_big(Big a, Big b) {
+  while (a.size() > 1 && a.back() == 0) a.pop_back();
+  while (b.size() > 1 && b.back() == 0) b.pop_back();
+  if (a.size() != b.size()) return a.size() < b.size() ? -1 : 1;
+  for (size_t i = a.size(); i-- > 0;)
+    if (a[i] != b[i]) return a[i] < b[i] ? -1 : 1;
+  return 0;
+}
+
+bool reaches(int n, int k, int L, int me, int md) {
+  Big lhs{1}, rhs{1};
+  for (int i = 0; i < L; ++i) mul_small(lhs, (uint32_t)n);
+  for (int i = 0; i < k; ++i) mul_small(lhs, (uint32_t)me);
+  for (int i = 0; i < k; ++i) mul_small(rhs, (uint32_t)md);
+  for (int i = 0; i < L; ++i) mul_small(rhs, (uint32_t)me);
+  return cmp_big(lhs, rhs) >= 0;
+}
+
+fa::T5Geometry make_geometry(int nb, int md, int bidir) {
+  fa::T5Geometry g{};
+  g.bidir = bidir;
+  g.nbp = bidir ? nb / 2 : nb;
+  g.me = g.nbp / 2;
+  const int L = g.nbp - g.me;
+  g.nthr = L - 1;
+  for (int k = 1; k < L; ++k) {
+    int lo = g.me, hi = md;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (reaches(mid, k, L, g.me, md)) hi = mid; else lo = mid + 1;
+    }
+    g.thr[k - 1] = lo;
+  }
+  g.sat = g.nthr > 0 ? g.thr[g.nthr - 1] : g.me;
+  return g;
+}
+
+const fa::T5Geometry &geometry(int nb, int md, int bidir) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int>, fa::T5Geometry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(nb, md, bidir);
+  auto it = cache.find(key);
+  if (it == cache.end()) it = cache.emplace(key, make_geometry(nb, md, bidir)).first;
+  return it->second;
+}
+
+// ---------------------------------------------------------------------------
+// Checks
+// ---------------------------------------------------------------------------
+fa_status check_t5_shape(int nb, int md, int bidir) {
+  if (bidir != 0 && bidir != 1) return fail(FA_ERR_INVALID, "bias.bidirectional must be 0 or 1");
+  if (nb < 2 || nb > 256)
+    return fail(FA_ERR_UNSUPPORTED, "bias.num_buckets=%d outside [2, 256]", nb);
+  if (bidir && (nb % 2 != 0 || nb < 4))
+    return fail(FA_ERR_UNSUPPORTED, "bidirectional T5 needs an even num_buckets >= 4 (got %d)",
+                nb);
+  const int nbp = bidir ? nb / 2 : nb, me = nbp / 2;
+  if (md <= me || md > fa::kMaxDistance)
+    return fail(FA_ERR_UNSUPPORTED, "bias.max_distance=%d must be in (%d, %d]", md, me,
+                fa::kMaxDistance);
+  return FA_OK;
+}
+
+fa_status check_common(int heads, int head_dim, int causal, float scale, float rope_base,
+                       const fa_bias &bias, long long maxlen) {
+  if (heads < 1) return fail(FA_ERR_INVALID, "heads=%d must be >= 1", heads);
+  if (head_dim <= 0) return fail(FA_ERR_INVALID, "head_dim=%d must be > 0", head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim=%d: only 64 and 128 are built", head_dim);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale is not finite");
+  if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale must be > 0");
+  if (!std::isfinite(rope_base) || rope_base < 0.f)
+    return fail(FA_ERR_INVALID, "rope_base must be 0 (off) or a finite positive base");
+  if (maxlen > fa::kMaxSeqlen)
+    return fail(FA_ERR_UNSUPPORTED, "sequence length %lld exceeds %d", maxlen, fa::kMaxSeqlen);
+  if (maxlen * heads * head_dim * 2 >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "one sequence spans >= 2^31 bytes per tensor");
+  switch (bias.mode) {
+    case FA_BIAS_NONE: break;
+    case FA_BIAS_T5: {
+      if (!bias.table) return fail(FA_ERR_INVALID, "bias.table is NULL");
+      const fa_status st = check_t5_shape(bias.num_buckets, bias.max_distance,
+                                          bias.bidirectional);
+      if (st != FA_OK) return st;
+      break;
+    }
+    case FA_BIAS_ALIBI:
+      if (!bias.slopes) return fail(FA_ERR_INVALID, "bias.slopes is NULL");
+      break;
+    default: return fail(FA_ERR_INVALID, "bias.mode=%d is not a fa_bias_mode", bias.mode);
+  }
+  return FA_OK;
+}
+
+fa_status check_fwd_impl(const fa_fwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID, "params is NULL");
+  if (p->batch < 0 || p->seqlen < 0) return fail(FA_ERR_INVALID, "negative batch or seqlen");
+  if (p->reserved != 0) return fail(FA_ERR_INVALID, "reserved must be 0");
+  const bool empty = (long long)p->batch * p->seqlen == 0;
+  if ((long long)p->batch * p->seqlen * (p->heads > 0 ? p->heads : 1) >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "batch * seqlen * heads must stay below 2^31");
+  if (!empty && (!p->q || !p->k || !p->v || !p->o || !p->lse))
+    return fail(FA_ERR_INVALID, "q, k, v, o and lse must be non-NULL");
+  return check_common(p->heads, p->head_dim, p->causal, p->scale, p->rope_base, p->bias,
+                      p->seqlen);
+}
+
+fa_status check_varlen_fwd_impl(const fa_varlen_fwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID, "params is NULL");
+  if (p->nseq < 0 || p->total < 0 || p->max_seqlen < 0)
+    return fail(FA_ERR_INVALID, "negative nseq, total or max_seqlen");
+  if (!p->cu_seqlens) return fail(FA_ERR_INVALID, "cu_seqlens is NULL");
+  if (p->total > 0 && (!p->q || !p->k || !p->v || !p->o || !p->lse))
+    return fail(FA_ERR_INVALID, "q, k, v, o and lse must be non-NULL");
+  if ((long long)p->total * p->heads >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "total * heads must stay below 2^31");
+  return check_common(p->heads, p->head_dim, p->causal, p->scale, p->rope_base, p->bias,
+                      p->max_seqlen);
+}
+
+fa_status check_bwd_ptrs(bool empty, const void *dout, const void *dq, const void *dk,
+                         const void *dv) {
+  if (!empty && (!dout || !dq || !dk || !dv))
+    return fail(FA_ERR_INVALID, "dout, dq, dk, dv must be non-NULL");
+  return FA_OK;
+}
+
+fa::Problem make_problem(const fa_fwd_params &f) {
+  fa::Problem p{};
+  p.varlen = 0;
+  p.nbatch = f.batch;
+  p.seqlen = f.seqlen;
+  p.total = f.batch * f.seqlen;
+  p.heads = f.heads;
+  p.head_dim = f.head_dim;
+  p.causal = f.causal;
+  p.scale = f.scale;
+  p.rope_base = f.rope_base;
+  p.bias = f.bias.mode;
+  p.cu_seqlens = nullptr;
+  p.table = f.bias.table;
+  p.slopes = f.bias.slopes;
+  if (p.bias == FA_BIAS_T5)
+    p.t5 = geometry(f.bias.num_buckets, f.bias.max_distance, f.bias.bidirectional);
+  return p;
+}
+
+fa::Problem make_problem(const fa_varlen_fwd_params &f) {
+  fa::Problem p{};
+  p.varlen = 1;
+  p.nbatch = f.nseq;
+  p.seqlen = f.max_seqlen;
+  p.total = f.total;
+  p.heads = f.heads;
+  p.head_dim = f.head_dim;
+  p.causal = f.causal;
+  p.scale = f.scale;
+  p.rope_base = f.rope_base;
+  p.bias = f.bias.mode;
+  p.cu_seqlens = f.cu_seqlens;
+  p.table = f.bias.table;
+  p.slopes = f.bias.slopes;
+  if (p.bias == FA_BIAS_T5)
+    p.t5 = geometry(f.bias.num_buckets, f.bias.max_distance, f.bias.bidirectional);
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout (every region 256-byte aligned).
+// ---------------------------------------------------------------------------
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  }
+};
+
+struct FwdLayout {
+  size_t qrot = 0, krot = 0, prefix = 0, sched = 0, total = 0;
+  int nsched = 0;
+};
+
+FwdLayout fwd_layout(const fa::Problem &p) {
+  FwdLayout L;
+  Carve c;
+  const size_t tokens = (size_t)p.total;
+  if (p.rope_base > 0.f) {
+    L.qrot = c.take(tokens * p.heads * p.head_dim * 2);
+    L.krot = c.take(tokens * p.heads * p.head_dim * 2);
+  }
+  if (p.varlen) {
+    const int br = fa::fwd_tile_rows();
+    L.nsched = p.heads * ((p.total + br - 1) / br + p.nbatch);
+    L.prefix = c.take((size_t)(p.nbatch + 1) * 4);
+    L.sched = c.take((size_t)L.nsched * 16);
+  }
+  L.total = c.off;
+  return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void *v, void *o,
+                  float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
+  const FwdLayout L = fwd_layout(p);
+  if (L.total > 0 && (ws == nullptr || ws_bytes < L.total))
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  if (p.total == 0 || (!p.varlen && (p.nbatch == 0 || p.seqlen == 0))) return FA_OK;
+  fa::FwdBuffers b{q, k, v, o, lse};
+  hipError_t e;
+  if (p.rope_base > 0.f) {
+    e = fa::launch_rope_pair(p, q, k, at<void>(ws, L.qrot), at<void>(ws, L.krot), s);
+    if (e != hipSuccess) return hip_fail(e, "rope");
+    b.q = at<void>(ws, L.qrot);
+    b.k = at<void>(ws, L.krot);
+  }
+  const int4 *sched = nullptr;
+  if (p.varlen) {
+    e = fa::launch_sched(p.cu_seqlens, p.nbatch, p.heads, fa::fwd_tile_rows(), L.nsched,
+                         at<int32_t>(ws, L.prefix), at<int4>(ws, L.sched), s);
+    if (e != hipSuccess) return hip_fail(e, "schedule");
+    sched = at<int4>(ws, L.sched);
+  }
+  e = fa::launch_fwd_impl(p, b, sched, L.nsched, s);
+  if (e != hipSuccess) return hip_fail(e, "forward");
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *fa_status_str(fa_status st) {
+  switch (st) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *fa_last_error(void) { return g_last_error.c_str(); }
+
+const char *fa_version(void) { return "0.1.0"; }
+
+fa_status fa_check_fwd(const fa_fwd_params *p) {
+  g_last_error.clear();
+  return check_fwd_impl(p);
+}
+
+fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p) {
+  g_last_error.clear();
+  return check_varlen_fwd_impl(p);
+}
+
+fa_status fa_check_bwd(const fa_bwd_params *p) {
+  g_last_error.clear();
+  if (!p) return fail(FA_ERR_INVALID, "params is NULL");
+  const fa_status st = check_fwd_impl(&p->f);
+  if (st != FA_OK) return st;
+  return check_bwd_ptrs((long long)p->f.batch * p->f.seqlen == 0, p->dout, p->dq, p->dk, p->dv);
+}
+
+fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p) {
+  g_last_error.clear();
+  if (!p) return fail(FA_ERR_INVALID, "params is NULL");
+  const fa_status st = check_varlen_fwd_impl(&p->f);
+  if (st != FA_OK) return st;
+  return check_bwd_ptrs(p->f.total == 0, p->dout, p->dq, p->dk, p->dv);
+}
+
+size_t fa_fwd_workspace_size(const fa_fwd_params *p) {
+  if (fa_check_fwd(p) != FA_OK) return (size_t)-1;
+  return fwd_layout(make_problem(*p)).total;
+}
+
+size_t fa_varlen_fwd_workspace_size(const fa_varlen_fwd_params *p) {
+  if (fa_check_varlen_fwd(p) != FA_OK) return (size_t)-1;
+  return fwd_layout(make_problem(*p)).total;
+}
+
+size_t fa_bwd_workspace_size(const fa_bwd_params *p) {
+  if (fa_check_bwd(p) != FA_OK) return (size_t)-1;
+  return 0;
+}
+
+size_t fa_varlen_bwd_workspace_size(const fa_varlen_bwd_params *p) {
+  if (fa_check_varlen_bwd(p) != FA_OK) return (size_t)-1;
+  return 0;
+}
+
+fa_status fa_fwd(const fa_fwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
+  const fa_status st = fa_check_fwd(p);
+  if (st != FA_OK) return st;
+  return run_fwd(make_problem(*p), p->q, p->k, p->v, p->o, p->lse, ws, ws_bytes, stream);
+}
+
+fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  const fa_status st = fa_check_varlen_fwd(p);
+  if (st != FA_OK) return st;
+  return run_fwd(make_problem(*p), p->q, p->k, p->v, p->o, p->lse, ws, ws_bytes, stream);
+}
+
+fa_status fa_bwd(const fa_bwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws; (void)ws_bytes; (void)stream;
+  const fa_status st = fa_check_bwd(p);
+  if (st != FA_OK) return st;
+  return fail(FA_ERR_UNSUPPORTED, "backward is not built yet");
+}
+
+fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  (void)ws; (void)ws_bytes; (void)stream;
+  const fa_status st = fa_check_varlen_bwd(p);
+  if (st != FA_OK) return st;
+  return fail(FA_ERR_UNSUPPORTED, "backward is not built yet");
+}
+
+fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t max_distance,
+                        int32_t bidirectional, int32_t *out, hipStream_t stream) {
+  g_last_error.clear();
+  if (qlen < 0 || klen < 0) return fail(FA_ERR_INVALID, "negative qlen or klen");
+  if (!out && (long long)qlen * klen > 0) return fail(FA_ERR_INVALID, "out is NULL");
+  const fa_status st = check_t5_shape(num_buckets, max_distance, bidirectional);
+  if (st != FA_OK) return st;
+  const hipError_t e = fa::launch_t5_buckets(geometry(num_buckets, max_distance, bidirectional),
+                                             qlen, klen, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "t5_buckets");
+  return FA_OK;
+}
+
+}  // extern "C"

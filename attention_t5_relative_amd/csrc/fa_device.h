@@ -1,0 +1,99 @@
+// Device helpers for the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Buffer resource over `bytes` bytes at `p`.  Loads past the end return 0 and
+// stores past the end are dropped by the hardware range check, which handles
+// ragged tiles without branches.  0x00020000 is the gfx9 dword-3 word (32-bit
+// data format, no swizzle).
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ i32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, i32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, i32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)off, 0, 0);
+}
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.  Lane l holds
+// row (l % 32) of A and column (l % 32) of B, each with 8 consecutive k values
+// for half-wave (l / 32); the accumulator holds, in register r, the element
+// (row 8*(r/4) + 4*(l/32) + r%4, column l % 32).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8),
+// each XCD with its own L2.  This remap gives every XCD a contiguous range of
+// logical ids, so the query tiles of one (sequence, head) - which stream the
+// same K and V - share one L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int per = n >> 3;
+  if (b >= (per << 3)) return b;
+  return (b & 7) * per + (b >> 3);
+}
+
+// T5 bucket of relative position r (key - query) from the integer thresholds.
+__device__ __forceinline__ int t5_bucket_dev(int r, const T5Geometry &g) {
+  int off = 0, n;
+  if (g.bidir) {
+    off = r > 0 ? g.nbp : 0;
+    n = r > 0 ? r : -r;
+  } else {
+    n = r < 0 ? -r : 0;
+  }
+  if (n < g.me) return off + n;
+  int b = g.me;
+  for (int k = 0; k < g.nthr; ++k) b += (n >= g.thr[k]) ? 1 : 0;
+  return off + b;
+}
+
+// Bijective key reordering inside each group of 16 keys used for the
+// transposed V tile: swaps bits 2 and 3 of the key offset, so that the eight
+// keys one MFMA B-operand lane supplies (see the forward kernel) are
+// contiguous.
+__device__ __forceinline__ int key_perm16(int j) {
+  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+}
+
+}  // namespace fa

@@ -1,0 +1,70 @@
+// Internal launch descriptors shared by the C-ABI glue (api.cpp) and the
+// kernel translation units.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+constexpr int kMaxThresholds = 128;   // (buckets per side) - (exact buckets) - 1 <= 127
+constexpr int kMaxDistance = 1024;    // bounds the per-distance bias table in LDS
+constexpr int kMaxSeqlen = 65536;
+
+// T5 bucket boundaries for one (num_buckets, max_distance, bidirectional).
+// For n >= me, bucket(n) = me + #{k : thr[k] <= n}; `sat` is the first n of
+// the last bucket of a side (every n >= sat shares that bucket).
+struct T5Geometry {
+  int32_t nbp;        // buckets per side
+  int32_t me;         // exact buckets per side (nbp / 2)
+  int32_t sat;        // first saturated distance
+  int32_t nthr;       // number of thresholds (nbp - me - 1)
+  int32_t bidir;
+  int32_t thr[kMaxThresholds];
+};
+
+enum BiasKind : int32_t { kBiasNone = 0, kBiasT5 = 1, kBiasAlibi = 2 };
+
+// One attention problem, dense or packed, as the kernels see it.
+struct Problem {
+  int32_t varlen;       // 0 dense [B,S,H,D], 1 packed [T,H,D]
+  int32_t nbatch;       // dense B, packed nseq
+  int32_t seqlen;       // dense S, packed max_seqlen
+  int32_t total;        // packed T (dense: B*S)
+  int32_t heads;
+  int32_t head_dim;
+  int32_t causal;
+  float scale;
+  float rope_base;      // 0: none
+  int32_t bias;         // BiasKind
+  const int32_t *cu_seqlens;
+  const float *table;
+  const float *slopes;
+  T5Geometry t5;
+};
+
+struct FwdBuffers {
+  const void *q, *k, *v;   // bf16 (already rotated when RoPE is on)
+  void *o;
+  float *lse;
+};
+
+// Launchers (return the first HIP error, hipSuccess otherwise).
+int fwd_tile_rows();
+hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sched, int nsched,
+                           hipStream_t s);
+hipError_t launch_sched(const int32_t *cu, int nseq, int heads, int tile, int nentries,
+                        int32_t *prefix, int4 *sched, hipStream_t s);
+// Rotates q and k (bf16 [tokens, H, D]) into qo and ko.
+hipError_t launch_rope_pair(const Problem &p, const void *q, const void *k, void *qo, void *ko,
+                            hipStream_t s);
+// Un-rotates an fp32 gradient [tokens, H, D] into bf16 g_out.
+hipError_t launch_rope_grad(const Problem &p, const float *g_rot, void *g_out, hipStream_t s);
+hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
+                             hipStream_t s);
+hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
+
+
+}  // namespace fa

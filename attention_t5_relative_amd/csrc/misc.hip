@@ -1,0 +1,217 @@
+// Small kernels around the attention kernels: the packed-batch tile schedule,
+// RoPE rotation of q/k and un-rotation of their gradients, the T5 bucket test
+// hook and a fill kernel.
+#include "fa_device.h"
+
+namespace fa {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Packed batches: map every workgroup id to {token0, length, head, tile} so
+// the attention kernels need a single load to find their work.  One
+// workgroup: an exclusive scan of (tiles per sequence * heads) into `prefix`,
+// then a binary search per entry.  Entries past the real work get length -1.
+// ---------------------------------------------------------------------------
+constexpr int SCHED_NT = 256;
+
+__global__ __launch_bounds__(SCHED_NT) void sched_kernel(const int32_t *cu, int nseq, int heads,
+                                                          int tile, int nentries, int32_t *prefix,
+                                                          int4 *sched) {
+  __shared__ int scan[SCHED_NT];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int c0 = 0; c0 < nseq; c0 += SCHED_NT) {
+    const int s = c0 + tid;
+    int cnt = 0;
+    if (s < nseq) {
+      const int len = cu[s + 1] - cu[s];
+      cnt = ((len + tile - 1) / tile) * heads;
+    }
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < SCHED_NT; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    if (s < nseq) prefix[s] = carry + scan[tid] - cnt;
+    carry += scan[SCHED_NT - 1];
+    __syncthreads();
+  }
+  if (tid == 0) prefix[nseq] = carry;
+  __syncthreads();
+  __threadfence_block();
+  for (int gidx = tid; gidx < nentries; gidx += SCHED_NT) {
+    int4 e = {0, -1, 0, 0};
+    if (gidx < carry) {
+      int lo = 0, hi = nseq - 1;   // last s with prefix[s] <= gidx
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= gidx) lo = mid; else hi = mid - 1;
+      }
+      const int s = lo;
+      const int t0 = cu[s], len = cu[s + 1] - t0;
+      const int nt = (len + tile - 1) / tile;
+      const int rem = gidx - prefix[s];
+      const int hh = rem / nt;
+      const int t = nt - 1 - (rem - hh * nt);   // longest causal rows first
+      e = int4{t0, len, hh, t};
+    }
+    sched[gidx] = e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RoPE.  Thread (token, pair p) computes the angle pos * base^(-2p/D) and its
+// cosine and sine in fp64 (positions reach 65535, where an fp32 angle would
+// already be off by ~4e-3 rad), rotates that pair of every head in fp64 and
+// rounds the result once to bf16.  The attention kernels then run on these
+// bf16 rotated q and k, as a full-bf16 pipeline feeds them.
+// ---------------------------------------------------------------------------
+constexpr int ROPE_NT = 256;
+
+__device__ __forceinline__ int token_position(int token, int seqlen, const int32_t *cu, int nseq) {
+  if (cu == nullptr) return token % seqlen;
+  int lo = 0, hi = nseq - 1;   // last s with cu[s] <= token
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= token) lo = mid; else hi = mid - 1;
+  }
+  return token - cu[lo];
+}
+
+__device__ __forceinline__ void rope_cs(int pos, int p, int D, double log2base, double &c,
+                                        double &s) {
+  const double theta = exp2(-(2.0 * p / D) * log2base);
+  sincos((double)pos * theta, &s, &c);
+}
+
+// fp64 -> bf16 with one rounding to nearest, ties to even: round to fp32 with
+// round-to-odd (truncate, then set the last bit if anything was dropped),
+// which keeps enough information for the final fp32 -> bf16 rounding to be
+// the correctly rounded result.
+__device__ __forceinline__ uint32_t bf16_bits_rne(double x) {
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != x) {
+    if (fabs(back) > fabs(x)) u -= 1;   // step back toward zero
+    u |= 1u;
+  }
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t rot_pack(uint32_t w, double c, double s) {
+  const double x0 = (double)bf16_lo(w), x1 = (double)bf16_hi(w);
+  return bf16_bits_rne(fma(x0, c, -x1 * s)) | (bf16_bits_rne(fma(x0, s, x1 * c)) << 16);
+}
+
+__global__ __launch_bounds__(ROPE_NT) void rope_fwd_kernel(const uint32_t *q, const uint32_t *k,
+                                                            uint32_t *qo, uint32_t *ko,
+                                                            int tokens, int heads, int D,
+                                                            int seqlen, const int32_t *cu,
+                                                            int nseq, double log2base) {
+  const int half = D / 2;
+  const long long idx = (long long)blockIdx.x * ROPE_NT + threadIdx.x;
+  if (idx >= (long long)tokens * half) return;
+  const int token = (int)(idx / half), p = (int)(idx - (long long)token * half);
+  double c, s;
+  rope_cs(token_position(token, seqlen, cu, nseq), p, D, log2base, c, s);
+  for (int hh = 0; hh < heads; ++hh) {
+    const size_t w = ((size_t)token * heads + hh) * half + p;
+    qo[w] = rot_pack(q[w], c, s);
+    ko[w] = rot_pack(k[w], c, s);
+  }
+}
+
+// Gradients come back w.r.t. the rotated rows (fp32); rotating by the
+// opposite angle maps them to the unrotated q / k, rounded once to bf16.
+__global__ __launch_bounds__(ROPE_NT) void rope_grad_kernel(const float2 *g, uint32_t *out,
+                                                             int tokens, int heads, int D,
+                                                             int seqlen, const int32_t *cu,
+                                                             int nseq, double log2base) {
+  const int half = D / 2;
+  const long long idx = (long long)blockIdx.x * ROPE_NT + threadIdx.x;
+  if (idx >= (long long)tokens * half) return;
+  const int token = (int)(idx / half), p = (int)(idx - (long long)token * half);
+  double cd, sd;
+  rope_cs(token_position(token, seqlen, cu, nseq), p, D, log2base, cd, sd);
+  const float c = (float)cd, s = (float)sd;
+  for (int hh = 0; hh < heads; ++hh) {
+    const size_t w = ((size_t)token * heads + hh) * half + p;
+    const float2 x = g[w];
+    out[w] = pack_bf16x2(fmaf(x.x, c, x.y * s), fmaf(-x.x, s, x.y * c));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// T5 bucket test hook: the same clamp-then-threshold path the attention
+// kernels use to fill their per-distance bias table.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void t5_buckets_kernel(const T5Geometry g, int qlen, int klen,
+                                                          int32_t *out) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)qlen * klen) return;
+  const int i = (int)(idx / klen), j = (int)(idx - (long long)i * klen);
+  const int r = min(max(j - i, -g.sat), g.sat);
+  out[idx] = t5_bucket_dev(r, g);
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float *p, size_t n, float v) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx < n) p[idx] = v;
+}
+
+}  // namespace
+
+hipError_t launch_sched(const int32_t *cu, int nseq, int heads, int tile, int nentries,
+                        int32_t *prefix, int4 *sched, hipStream_t s) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(SCHED_NT), 0, s, cu, nseq, heads, tile,
+                     nentries, prefix, sched);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_pair(const Problem &p, const void *q, const void *k, void *qo, void *ko,
+                            hipStream_t s) {
+  const int tokens = p.varlen ? p.total : p.nbatch * p.seqlen;
+  const long long n = (long long)tokens * (p.head_dim / 2);
+  if (n == 0) return hipSuccess;
+  const int grid = (int)((n + ROPE_NT - 1) / ROPE_NT);
+  hipLaunchKernelGGL(rope_fwd_kernel, dim3(grid), dim3(ROPE_NT), 0, s,
+                     static_cast<const uint32_t *>(q), static_cast<const uint32_t *>(k),
+                     static_cast<uint32_t *>(qo), static_cast<uint32_t *>(ko), tokens, p.heads,
+                     p.head_dim, p.seqlen, p.varlen ? p.cu_seqlens : nullptr, p.nbatch,
+                     log2((double)p.rope_base));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_grad(const Problem &p, const float *g_rot, void *g_out, hipStream_t s) {
+  const int tokens = p.varlen ? p.total : p.nbatch * p.seqlen;
+  const long long n = (long long)tokens * (p.head_dim / 2);
+  if (n == 0) return hipSuccess;
+  const int grid = (int)((n + ROPE_NT - 1) / ROPE_NT);
+  hipLaunchKernelGGL(rope_grad_kernel, dim3(grid), dim3(ROPE_NT), 0, s,
+                     reinterpret_cast<const float2 *>(g_rot), static_cast<uint32_t *>(g_out),
+                     tokens, p.heads, p.head_dim, p.seqlen, p.varlen ? p.cu_seqlens : nullptr,
+                     p.nbatch, log2((double)p.rope_base));
+  return hipGetLastError();
+}
+
+hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
+                             hipStream_t s) {
+  const long long n = (long long)qlen * klen;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(t5_buckets_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g,
+                     qlen, klen, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,196 @@
+/*
+ * libfat5attn: exact softmax attention with the T5 relative-position bias,
+ * ALiBi and RoPE, dense or packed (cu_seqlens), forward and backward, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (FAT5 report, section "Noyau CUDA", second kernel): for
+ * every (sequence, head) the scores S = scale * Q K^T, then S' = S plus a bias
+ * filled on the fly from a small per-head table T indexed by the bucket of the
+ * relative position, then P = softmax(S') row by row with a running
+ * ("cumulative") softmax, then O = P V.  The N x N matrices S, S', P are never
+ * written to memory: memory stays linear in the sequence length, which the
+ * report credits for inference on tens of thousands of tokens.  The same
+ * kernel serves ALiBi and RoPE (listed beside the T5 encoding in the note
+ * under that section).  Packed batches follow the flash_attn_varlen_func
+ * convention of the packing blog (DataCollatorWithFlattening): tokens of
+ * several examples are concatenated and attention never crosses an example
+ * boundary.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers; the caller owns every buffer.  They
+ *   may be NULL only when the problem is empty (B*S == 0, or total == 0).
+ *   Dense tensors are [B, S, H, D] and packed tensors [T, H, D], bfloat16,
+ *   contiguous (D innermost).  LSE is fp32 [B, H, S] (packed: [H, T]).  The
+ *   T5 table and its gradient are fp32 [num_buckets, H] row-major; ALiBi
+ *   slopes are fp32 [H].  cu_seqlens is int32 [nseq + 1] on the device.
+ * - Everything is enqueued on `stream` and returns without synchronising.
+ *   The library allocates no device memory: scratch space is the caller's
+ *   workspace, sized by the matching *_workspace_size call (0 means none is
+ *   needed and `ws` may be NULL).
+ * - The params struct is only read during the call.  Outputs (O, LSE, dQ,
+ *   dK, dV, dtable) are fully overwritten, never accumulated into.
+ * - A validation failure returns a negative status before anything is
+ *   enqueued; fa_last_error() then names the offending field.  A failed
+ *   launch returns FA_ERR_HIP with the HIP error text in fa_last_error().
+ *   Device faults surface at the caller's next synchronisation.
+ * - head_dim must be 64 or 128; scale must be finite and > 0; the sequence
+ *   length (dense S, packed max_seqlen) is at most 65536 and a single
+ *   sequence times H*D*2 bytes must stay below 2^31.
+ * - cu_seqlens is trusted: it must start at 0, be non-decreasing, end at
+ *   `total`, and no sequence may be longer than max_seqlen.  It is not read
+ *   on the host (no device-to-host copy).
+ * - Buckets (FA_BIAS_T5): relative position r = key index - query index.
+ *   Bidirectional: num_buckets/2 buckets per side, keys after the query use
+ *   the upper half, n = |r|.  Unidirectional: n = max(-r, 0).  With nb' the
+ *   buckets per side and me = nb'/2, n < me maps to bucket n, larger n to
+ *   me + floor(ln(n/me)/ln(max_distance/me) * (nb'-me)), capped at nb'-1 (the
+ *   T5 scheme, cited by the report; it prints no formula).  The kernels decide
+ *   each boundary exactly with integer thresholds.  Requires num_buckets in
+ *   [2, 256] (even when bidirectional), me < max_distance <= 1024.
+ * - ALiBi (FA_BIAS_ALIBI): bias = -slope[h] * |i - j|.
+ * - RoPE (rope_base > 0): interleaved pairs (2p, 2p+1) of q and k at
+ *   position t (0-based, local to each packed sequence) are rotated by the
+ *   angle t * rope_base^(-2p/D) before the scores; gradients are returned
+ *   with respect to the unrotated q and k.  RoPE combines with any bias mode.
+ * - Causal: key j is visible to query i iff j <= i (self-attention only:
+ *   queries and keys share one length).
+ */
+#ifndef FAT5ATTN_H
+#define FAT5ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = -1,     /* a NULL pointer, a negative size, a bad enum value */
+  FA_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement   */
+  FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+  FA_ERR_HIP = -4          /* a HIP launch failed                            */
+} fa_status;
+
+typedef enum { FA_BIAS_NONE = 0, FA_BIAS_T5 = 1, FA_BIAS_ALIBI = 2 } fa_bias_mode;
+
+/* Additive score bias.  FAT5 report, "Noyau CUDA": the second kernel is
+ * handed the compact bucket tensor T instead of a dense bias matrix. */
+typedef struct {
+  int32_t mode;            /* fa_bias_mode                                     */
+  int32_t num_buckets;     /* T5 only                                          */
+  int32_t max_distance;    /* T5 only                                          */
+  int32_t bidirectional;   /* T5 only: 1 encoder style, 0 decoder style        */
+  const float *table;      /* T5: device fp32 [num_buckets, H]                 */
+  const float *slopes;     /* ALiBi: device fp32 [H]                           */
+} fa_bias;
+
+/* Dense forward: q, k, v [B, S, H, D] bf16 in; o [B, S, H, D] bf16 and
+ * lse [B, H, S] fp32 out (lse_i = log sum_j exp(S'_ij), natural log). */
+typedef struct {
+  int32_t batch;
+  int32_t seqlen;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t causal;
+  float scale;             /* multiplies Q K^T; the bias is added unscaled     */
+  float rope_base;         /* > 0 enables RoPE, 0 disables it                  */
+  int32_t reserved;        /* must be 0                                        */
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;
+  float *lse;
+  fa_bias bias;
+} fa_fwd_params;
+
+/* Dense backward.  `f` describes the forward; f.o and f.lse are READ here (the
+ * forward's outputs for the same inputs).  dout [B, S, H, D] bf16 in; dq, dk,
+ * dv [B, S, H, D] bf16 out; dtable fp32 [num_buckets, H] out (T5 only, may be
+ * NULL to skip the bias gradient): the sum over the batch and over every
+ * visible (query, key) pair in bucket b of dL/dS'. */
+typedef struct {
+  fa_fwd_params f;
+  const void *dout;
+  void *dq;
+  void *dk;
+  void *dv;
+  float *dtable;
+} fa_bwd_params;
+
+/* Packed forward: q, k, v, o [total, H, D] bf16; lse [H, total] fp32;
+ * sequence s holds tokens cu_seqlens[s] .. cu_seqlens[s+1]-1.  max_seqlen is
+ * a host-side upper bound on every sequence length. */
+typedef struct {
+  int32_t nseq;
+  int32_t total;
+  int32_t max_seqlen;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t causal;
+  float scale;
+  float rope_base;
+  const int32_t *cu_seqlens;
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;
+  float *lse;
+  fa_bias bias;
+} fa_varlen_fwd_params;
+
+typedef struct {
+  fa_varlen_fwd_params f;
+  const void *dout;
+  void *dq;
+  void *dk;
+  void *dv;
+  float *dtable;
+} fa_varlen_bwd_params;
+
+/* Host-only argument checks (no HIP call, nothing enqueued). */
+fa_status fa_check_fwd(const fa_fwd_params *p);
+fa_status fa_check_bwd(const fa_bwd_params *p);
+fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p);
+fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p);
+
+/* Workspace bytes the matching call needs (0 when none); (size_t)-1 when the
+ * params fail the checks above. */
+size_t fa_fwd_workspace_size(const fa_fwd_params *p);
+size_t fa_bwd_workspace_size(const fa_bwd_params *p);
+size_t fa_varlen_fwd_workspace_size(const fa_varlen_fwd_params *p);
+size_t fa_varlen_bwd_workspace_size(const fa_varlen_bwd_params *p);
+
+/* Forward attention (FAT5 report, "Noyau CUDA", kernel v2 forward steps). */
+fa_status fa_fwd(const fa_fwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream);
+/* Backward: dQ, dK, dV and the table gradient (the report trains T, so its
+ * gradient is implied; it prints no backward). */
+fa_status fa_bwd(const fa_bwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream);
+/* Packed variants (packing blog: flash_attn_varlen_func semantics). */
+fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Test hook: out[i * klen + j] = T5 bucket of (query i, key j), computed on
+ * the device by the same threshold code the attention kernels use.  out is a
+ * device int32 [qlen, klen]. */
+fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t max_distance,
+                        int32_t bidirectional, int32_t *out, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *fa_status_str(fa_status st);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *fa_last_error(void);
+/* Library version, "major.minor.patch". */
+const char *fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAT5ATTN_H */

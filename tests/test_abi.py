@@ -1,0 +1,183 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fat5attn.h declares, the ctypes structs match the C layout, and the
+host-side argument checks return the documented status codes.  Nothing here
+launches a kernel."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from attention_t5_relative_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fat5attn.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version(lib):
+    assert lib.fa_status_str(0) == b"ok"
+    assert lib.fa_status_str(-3) == b"workspace missing or too small"
+    assert re.match(rb"^\d+\.\d+\.\d+$", lib.fa_version())
+
+
+STRUCTS = {
+    "fa_bias": (_lib.FaBias, ["mode", "num_buckets", "max_distance", "bidirectional", "table",
+                              "slopes"]),
+    "fa_fwd_params": (_lib.FaFwdParams, ["batch", "seqlen", "heads", "head_dim", "causal",
+                                         "scale", "rope_base", "reserved", "q", "k", "v", "o",
+                                         "lse", "bias"]),
+    "fa_bwd_params": (_lib.FaBwdParams, ["f", "dout", "dq", "dk", "dv", "dtable"]),
+    "fa_varlen_fwd_params": (_lib.FaVarlenFwdParams, ["nseq", "total", "max_seqlen", "heads",
+                                                      "head_dim", "causal", "scale", "rope_base",
+                                                      "cu_seqlens", "q", "k", "v", "o", "lse",
+                                                      "bias"]),
+    "fa_varlen_bwd_params": (_lib.FaVarlenBwdParams, ["f", "dout", "dq", "dk", "dv", "dtable"]),
+}
+
+
+def test_ctypes_layout_matches_c_compiler(tmp_path):
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fat5attn.h"',
+             "int main(void) {"]
+    for s, (_, fields) in STRUCTS.items():
+        lines.append(f'printf("{s} %zu\\n", sizeof({s}));')
+        for f in fields:
+            lines.append(f'printf("{s}.{f} %zu\\n", offsetof({s}, {f}));')
+    lines.append("return 0; }")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(c), "-o", str(exe)], check=True)
+    got = dict(line.rsplit(" ", 1) for line in subprocess.run(
+        [str(exe)], capture_output=True, text=True, check=True).stdout.split("\n") if line)
+    for s, (cls, fields) in STRUCTS.items():
+        assert int(got[s]) == ctypes.sizeof(cls), s
+        for f in fields:
+            assert int(got[f"{s}.{f}"]) == getattr(cls, f).offset, f"{s}.{f}"
+
+
+def _dense(**kw):
+    p = _lib.FaFwdParams()
+    p.batch, p.seqlen, p.heads, p.head_dim = 2, 100, 3, 64
+    p.causal, p.scale, p.rope_base = 0, 1.0, 0.0
+    p.q = p.k = p.v = p.o = p.lse = 0x1000
+    p.bias.mode = _lib.FA_BIAS_T5
+    p.bias.num_buckets, p.bias.max_distance, p.bias.bidirectional = 32, 128, 1
+    p.bias.table = 0x2000
+    for k, v in kw.items():
+        if k.startswith("bias_"):
+            setattr(p.bias, k[5:], v)
+        else:
+            setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("change,status", [
+    ({}, _lib.FA_OK),
+    ({"q": None}, _lib.FA_ERR_INVALID),
+    ({"lse": None}, _lib.FA_ERR_INVALID),
+    ({"batch": -1}, _lib.FA_ERR_INVALID),
+    ({"heads": 0}, _lib.FA_ERR_INVALID),
+    ({"head_dim": 96}, _lib.FA_ERR_UNSUPPORTED),
+    ({"head_dim": 0}, _lib.FA_ERR_INVALID),
+    ({"causal": 2}, _lib.FA_ERR_INVALID),
+    ({"scale": float("nan")}, _lib.FA_ERR_INVALID),
+    ({"scale": -1.0}, _lib.FA_ERR_UNSUPPORTED),
+    ({"rope_base": -2.0}, _lib.FA_ERR_INVALID),
+    ({"reserved": 1}, _lib.FA_ERR_INVALID),
+    ({"seqlen": 70000}, _lib.FA_ERR_UNSUPPORTED),
+    ({"bias_mode": 7}, _lib.FA_ERR_INVALID),
+    ({"bias_table": None}, _lib.FA_ERR_INVALID),
+    ({"bias_num_buckets": 31}, _lib.FA_ERR_UNSUPPORTED),
+    ({"bias_num_buckets": 300}, _lib.FA_ERR_UNSUPPORTED),
+    ({"bias_max_distance": 8}, _lib.FA_ERR_UNSUPPORTED),
+    ({"bias_max_distance": 2048}, _lib.FA_ERR_UNSUPPORTED),
+    ({"bias_bidirectional": 3}, _lib.FA_ERR_INVALID),
+    ({"bias_mode": _lib.FA_BIAS_ALIBI}, _lib.FA_ERR_INVALID),   # slopes NULL
+    ({"bias_mode": _lib.FA_BIAS_ALIBI, "bias_slopes": 0x3000}, _lib.FA_OK),
+    ({"bias_mode": _lib.FA_BIAS_NONE, "bias_table": None}, _lib.FA_OK),
+    ({"bias_bidirectional": 0, "bias_num_buckets": 31}, _lib.FA_OK),
+])
+def test_dense_checks(lib, change, status):
+    p = _dense(**change)
+    assert lib.fa_check_fwd(ctypes.byref(p)) == status, lib.fa_last_error()
+    if status != _lib.FA_OK:
+        assert lib.fa_last_error() != b""
+        assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == ctypes.c_size_t(-1).value
+        # the entry point refuses before touching the device
+        assert lib.fa_fwd(ctypes.byref(p), None, 0, None) == status
+
+
+def test_bwd_checks(lib):
+    b = _lib.FaBwdParams()
+    b.f = _dense()
+    b.dout = b.dq = b.dk = b.dv = 0x4000
+    assert lib.fa_check_bwd(ctypes.byref(b)) == _lib.FA_OK
+    b.dk = None
+    assert lib.fa_check_bwd(ctypes.byref(b)) == _lib.FA_ERR_INVALID
+    assert lib.fa_bwd(ctypes.byref(b), None, 0, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_check_bwd(None) == _lib.FA_ERR_INVALID
+
+
+def test_varlen_checks(lib):
+    p = _lib.FaVarlenFwdParams()
+    p.nseq, p.total, p.max_seqlen, p.heads, p.head_dim = 3, 300, 200, 4, 128
+    p.scale = 0.1
+    p.cu_seqlens = 0x5000
+    p.q = p.k = p.v = p.o = p.lse = 0x1000
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == _lib.FA_OK
+    p.cu_seqlens = None
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == _lib.FA_ERR_INVALID
+    p.cu_seqlens = 0x5000
+    p.nseq = -1
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == _lib.FA_ERR_INVALID
+    p.nseq = 3
+    p.max_seqlen = 100000
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == _lib.FA_ERR_UNSUPPORTED
+    b = _lib.FaVarlenBwdParams()
+    p.max_seqlen = 200
+    b.f = p
+    b.dout = b.dq = b.dk = b.dv = 0x4000
+    assert lib.fa_check_varlen_bwd(ctypes.byref(b)) == _lib.FA_OK
+
+
+def test_workspace_sizes(lib):
+    p = _dense()
+    assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == 0
+    p.rope_base = 10000.0
+    # rotated copies of q and k, each 256-byte aligned
+    one = 2 * 100 * 3 * 64 * 2
+    assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == 2 * ((one + 255) // 256 * 256)
+    # a call that needs a workspace refuses without one
+    assert lib.fa_fwd(ctypes.byref(p), None, 0, None) == _lib.FA_ERR_WORKSPACE
+
+
+def test_t5_buckets_checks(lib):
+    assert lib.fa_t5_buckets(4, 4, 33, 128, 1, 0x1000, None) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_t5_buckets(-1, 4, 32, 128, 1, 0x1000, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_t5_buckets(4, 4, 32, 128, 1, None, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_t5_buckets(0, 0, 32, 128, 1, None, None) == _lib.FA_OK
