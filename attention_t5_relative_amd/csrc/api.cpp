@@ -258,6 +258,40 @@ FwdLayout fwd_layout(const fa::Problem &p) {
   return L;
 }
 
+struct BwdLayout {
+  size_t qrot = 0, krot = 0, dk_acc = 0, dq_acc = 0, delta = 0, part = 0, prefix = 0,
+         sched = 0, total = 0;
+  int nsched = 0;
+  bool has_part = false;
+};
+
+BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
+  BwdLayout L;
+  Carve c;
+  const size_t tokens = (size_t)p.total;
+  const size_t elems = tokens * p.heads * p.head_dim;
+  if (p.rope_base > 0.f) {
+    L.qrot = c.take(elems * 2);
+    L.krot = c.take(elems * 2);
+    L.dk_acc = c.take(elems * 4);
+  }
+  L.dq_acc = c.take(elems * 4);
+  L.delta = c.take(tokens * p.heads * 4);
+  if (p.varlen) {
+    const int bt = fa::bwd_tile();
+    L.nsched = p.heads * ((p.total + bt - 1) / bt + p.nbatch);
+    L.prefix = c.take((size_t)(p.nbatch + 1) * 4);
+    L.sched = c.take((size_t)L.nsched * 16);
+  }
+  L.has_part = want_dtable && p.bias == FA_BIAS_T5;
+  if (L.has_part) {
+    const int nb = p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp;
+    L.part = c.take((size_t)fa::bwd_num_parts(p, L.nsched) * nb * 4);
+  }
+  L.total = c.off;
+  return L;
+}
+
 template <typename T>
 T *at(void *ws, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
@@ -287,6 +321,63 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
   }
   e = fa::launch_fwd_impl(p, b, sched, L.nsched, s);
   if (e != hipSuccess) return hip_fail(e, "forward");
+  return FA_OK;
+}
+
+fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void *v,
+                  const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                  float *dtable, void *ws, size_t ws_bytes, hipStream_t s) {
+  const BwdLayout L = bwd_layout(p, dtable != nullptr);
+  if (L.total > 0 && (ws == nullptr || ws_bytes < L.total))
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  hipError_t e;
+  const bool t5grad = dtable != nullptr && p.bias == FA_BIAS_T5;
+  const int nb = p.bias == FA_BIAS_T5 ? (p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp) : 0;
+  if (p.total == 0 || (!p.varlen && (p.nbatch == 0 || p.seqlen == 0))) {
+    if (t5grad) {
+      e = fa::launch_fill_f32(dtable, (size_t)nb * p.heads, 0.f, s);
+      if (e != hipSuccess) return hip_fail(e, "fill");
+    }
+    return FA_OK;
+  }
+  fa::BwdBuffers b{};
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.dout = dout;
+  b.lse = lse;
+  b.dk = dk;
+  b.dv = dv;
+  b.dq_acc = at<float>(ws, L.dq_acc);
+  b.delta = at<float>(ws, L.delta);
+  b.part = L.has_part ? at<float>(ws, L.part) : nullptr;
+  b.dtable = t5grad ? dtable : nullptr;
+  const bool rope = p.rope_base > 0.f;
+  if (rope) {
+    e = fa::launch_rope_pair(p, q, k, at<void>(ws, L.qrot), at<void>(ws, L.krot), s);
+    if (e != hipSuccess) return hip_fail(e, "rope");
+    b.q = at<void>(ws, L.qrot);
+    b.k = at<void>(ws, L.krot);
+    b.dk_acc = at<float>(ws, L.dk_acc);
+  }
+  const int4 *sched = nullptr;
+  if (p.varlen) {
+    e = fa::launch_sched(p.cu_seqlens, p.nbatch, p.heads, fa::bwd_tile(), L.nsched,
+                         at<int32_t>(ws, L.prefix), at<int4>(ws, L.sched), s);
+    if (e != hipSuccess) return hip_fail(e, "schedule");
+    sched = at<int4>(ws, L.sched);
+  }
+  e = fa::launch_bwd_impl(p, b, sched, L.nsched, s);
+  if (e != hipSuccess) return hip_fail(e, "backward");
+  const size_t elems = (size_t)p.total * p.heads * p.head_dim;
+  if (rope) {
+    e = fa::launch_rope_grad(p, b.dq_acc, dq, s);
+    if (e == hipSuccess) e = fa::launch_rope_grad(p, b.dk_acc, dk, s);
+  } else {
+    e = fa::launch_f32_to_bf16(b.dq_acc, dq, elems, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "dq/dk epilogue");
   return FA_OK;
 }
 
@@ -347,12 +438,12 @@ size_t fa_varlen_fwd_workspace_size(const fa_varlen_fwd_params *p) {
 
 size_t fa_bwd_workspace_size(const fa_bwd_params *p) {
   if (fa_check_bwd(p) != FA_OK) return (size_t)-1;
-  return 0;
+  return bwd_layout(make_problem(p->f), p->dtable != nullptr).total;
 }
 
 size_t fa_varlen_bwd_workspace_size(const fa_varlen_bwd_params *p) {
   if (fa_check_varlen_bwd(p) != FA_OK) return (size_t)-1;
-  return 0;
+  return bwd_layout(make_problem(p->f), p->dtable != nullptr).total;
 }
 
 fa_status fa_fwd(const fa_fwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
@@ -369,18 +460,18 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *ws, size_t ws_bytes
 }
 
 fa_status fa_bwd(const fa_bwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws; (void)ws_bytes; (void)stream;
   const fa_status st = fa_check_bwd(p);
   if (st != FA_OK) return st;
-  return fail(FA_ERR_UNSUPPORTED, "backward is not built yet");
+  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.lse, p->dout, p->dq, p->dk,
+                 p->dv, p->dtable, ws, ws_bytes, stream);
 }
 
 fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes,
                         hipStream_t stream) {
-  (void)ws; (void)ws_bytes; (void)stream;
   const fa_status st = fa_check_varlen_bwd(p);
   if (st != FA_OK) return st;
-  return fail(FA_ERR_UNSUPPORTED, "backward is not built yet");
+  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.lse, p->dout, p->dq, p->dk,
+                 p->dv, p->dtable, ws, ws_bytes, stream);
 }
 
 fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t max_distance,

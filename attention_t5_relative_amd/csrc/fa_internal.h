@@ -51,6 +51,18 @@ struct FwdBuffers {
   float *lse;
 };
 
+struct BwdBuffers {
+  const void *q, *k, *v;   // bf16 (rotated when RoPE is on)
+  const void *dout;
+  const float *lse;
+  void *dk, *dv;           // bf16 outputs
+  float *dk_acc;           // fp32 dK in the rotated space (RoPE only)
+  float *dq_acc;           // fp32 [tokens, H, D]
+  float *delta;            // fp32, lse layout
+  float *part;             // fp32 [parts, num_buckets] (T5 table gradient) or nullptr
+  float *dtable;           // [num_buckets, H] or nullptr
+};
+
 // Launchers (return the first HIP error, hipSuccess otherwise).
 int fwd_tile_rows();
 hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sched, int nsched,
@@ -62,6 +74,11 @@ hipError_t launch_rope_pair(const Problem &p, const void *q, const void *k, void
                             hipStream_t s);
 // Un-rotates an fp32 gradient [tokens, H, D] into bf16 g_out.
 hipError_t launch_rope_grad(const Problem &p, const float *g_rot, void *g_out, hipStream_t s);
+int bwd_tile();
+int64_t bwd_num_parts(const Problem &p, int nsched);
+hipError_t launch_bwd_impl(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
+                           hipStream_t s);
+hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t s);
 hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
                              hipStream_t s);
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);

@@ -1,0 +1,214 @@
+"""Backward parity on the GPU: dQ, dK, dV and the T5 table gradient from the
+HIP path (through the C ABI) against the fp64 oracle on identical seeded
+inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import (assert_dtable, assert_grad, assert_o, bf16_tensor, oracle_kwargs, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+fa = pytest.importorskip("attention_t5_relative_amd")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _bias(kind, H, table, nb, md, bidirectional):
+    if kind == "t5":
+        return fa.T5Bias(torch.from_numpy(table).cuda(), nb, md, bidirectional), None
+    if kind == "alibi":
+        s = synth.alibi_slope_values(H)
+        return fa.ALiBi(torch.from_numpy(s).cuda()), s.astype(np.float64)
+    return None, None
+
+
+def run_dense_bwd(inp, *, causal, kind, scale, bidirectional=True, rope_base=None, nb=32,
+                  md=128, want_dtable=True):
+    q, k, v, do = (bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    B, S, H, D = q.shape
+    bias, slopes = _bias(kind, H, inp.table, nb, md, bidirectional)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    fa.fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, bias=bias, rope_base=rope_base or 0.0)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dtable = (torch.full((nb, H), float("nan"), device="cuda")
+              if (kind == "t5" and want_dtable) else None)
+    fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, scale=scale, causal=causal, bias=bias,
+              rope_base=rope_base or 0.0)
+    torch.cuda.synchronize()
+    kw = oracle_kwargs(kind, causal, scale, inp.table, slopes, nb, md, bidirectional, rope_base)
+    out = dict(o=to_f64(o), dq=to_f64(dq), dk=to_f64(dk), dv=to_f64(dv),
+               dtable=None if dtable is None else dtable.cpu().numpy().astype(np.float64))
+    return out, kw
+
+
+SMALL = [
+    # B, S, H, D, causal, bias, bidirectional, scale, rope
+    (1, 1, 1, 64, False, "t5", True, 1.0, None),
+    (2, 37, 3, 64, False, "t5", True, 1.0, None),
+    (1, 200, 2, 64, True, "t5", False, 1.0, None),
+    (2, 333, 2, 64, False, "t5", False, 0.5, None),
+    (1, 300, 3, 128, True, "alibi", False, 0.125, None),
+    (1, 257, 2, 128, False, "alibi", False, 0.125, None),
+    (1, 300, 2, 128, True, "none", False, 0.088, 10000.0),
+    (2, 190, 2, 64, False, "none", False, 0.3, None),
+    (1, 260, 2, 64, True, "t5", False, 1.0, 500.0),
+    (1, 129, 4, 128, False, "t5", True, 0.2, None),
+    (1, 700, 1, 64, False, "t5", True, 1.0, None),
+    (1, 520, 2, 128, True, "t5", False, 0.2, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "b{}s{}h{}d{}-c{}-{}-bi{}-r{}".format(
+    c[0], c[1], c[2], c[3], int(c[4]), c[5], int(c[6]), int(c[8] is not None)))
+def test_backward_small(case):
+    B, S, H, D, causal, kind, bidi, scale, rope = case
+    inp = synth.draw_dense(300 + S, B, S, H, D)
+    out, kw = run_dense_bwd(inp, causal=causal, kind=kind, scale=scale, bidirectional=bidi,
+                            rope_base=rope)
+    dq, dk, dv, dtab = oracle.attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                            inp.f64("do"), **kw)
+    assert_grad(out["dq"], dq, "dQ")
+    assert_grad(out["dk"], dk, "dK")
+    assert_grad(out["dv"], dv, "dV")
+    if dtab is not None:
+        assert_dtable(out["dtable"], dtab)
+        # sum over buckets of a head's gradient is zero (rows of dS sum to zero)
+        assert np.abs(out["dtable"].sum(axis=0)).max() <= 1e-3 * np.abs(dtab).max() + 1e-4
+
+
+@pytest.mark.parametrize("name,heads", [("c2", [0, 11]), ("c3", [3])])
+def test_backward_full_size_sampled_heads(name, heads):
+    """Full-size launch; the oracle computes every batch of the sampled heads
+    (the table gradient of a head sums over the batch)."""
+    c = synth.config_by_name(name)
+    inp = synth.draw_dense(c.seed, c.batch, c.seqlen, c.heads, c.head_dim)
+    out, kw = run_dense_bwd(inp, causal=c.causal, kind=c.bias, scale=c.scale,
+                            bidirectional=c.bidirectional)
+    pairs = [(b, h) for h in heads for b in range(c.batch)]
+    dq, dk, dv, dtab = oracle.attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                            inp.f64("do"), pairs=pairs, **kw)
+    for h in heads:
+        assert_grad(out["dq"][:, :, h], dq[:, :, h], f"dQ[:,:,{h}]")
+        assert_grad(out["dk"][:, :, h], dk[:, :, h], f"dK[:,:,{h}]")
+        assert_grad(out["dv"][:, :, h], dv[:, :, h], f"dV[:,:,{h}]")
+        assert_dtable(out["dtable"][:, h], dtab[:, h], f"dtable[:,{h}]")
+
+
+@pytest.mark.parametrize("name", ["c5a", "c5b"])
+def test_backward_long_context_sampled_head(name):
+    c = synth.config_by_name(name)
+    inp = synth.draw_dense(c.seed, c.batch, c.seqlen, c.heads, c.head_dim, with_table=False)
+    out, kw = run_dense_bwd(inp, causal=True, kind=c.bias, scale=c.scale,
+                            rope_base=c.rope_base)
+    pairs = [(0, 2)]
+    dq, dk, dv, _ = oracle.attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                         inp.f64("do"), pairs=pairs, **kw)
+    for b, h in pairs:
+        assert_grad(out["dq"][b, :, h], dq[b, :, h], "dQ")
+        assert_grad(out["dk"][b, :, h], dk[b, :, h], "dK")
+        assert_grad(out["dv"][b, :, h], dv[b, :, h], "dV")
+
+
+def run_varlen_bwd(inp, H, *, causal, scale, kind="t5", bidirectional=True, rope_base=None):
+    q, k, v, do = (bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    T = q.shape[0]
+    cu = torch.from_numpy(inp.cu_seqlens).cuda()
+    bias, slopes = _bias(kind, H, inp.table, 32, 128, bidirectional)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    mx = int(inp.lengths.max())
+    fa.fa_varlen_fwd(q, k, v, o, lse, cu, mx, scale=scale, causal=causal, bias=bias,
+                     rope_base=rope_base or 0.0)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dtable = torch.full((32, H), float("nan"), device="cuda") if kind == "t5" else None
+    fa.fa_varlen_bwd(q, k, v, o, lse, do, dq, dk, dv, cu, mx, dtable, scale=scale,
+                     causal=causal, bias=bias, rope_base=rope_base or 0.0)
+    torch.cuda.synchronize()
+    kw = oracle_kwargs(kind, causal, scale, inp.table, slopes, 32, 128, bidirectional, rope_base)
+    return dict(dq=to_f64(dq), dk=to_f64(dk), dv=to_f64(dv),
+                dtable=None if dtable is None else dtable.cpu().numpy().astype(np.float64)), kw
+
+
+@pytest.mark.parametrize("causal,kind,rope", [(False, "t5", None), (True, "t5", None),
+                                              (True, "alibi", None), (False, "none", 1000.0)])
+def test_varlen_backward_small(causal, kind, rope):
+    lengths = np.array([1, 130, 17, 256, 64, 300, 5])
+    inp = synth.draw_varlen(31, int(lengths.sum()), 3, 64, lengths=lengths)
+    out, kw = run_varlen_bwd(inp, 3, causal=causal, scale=1.0 if kind == "t5" else 0.25,
+                             kind=kind, bidirectional=not causal, rope_base=rope)
+    dq, dk, dv, dtab = oracle.varlen_attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                                   inp.f64("do"), inp.cu_seqlens, **kw)
+    assert_grad(out["dq"], dq, "dQ")
+    assert_grad(out["dk"], dk, "dK")
+    assert_grad(out["dv"], dv, "dV")
+    if dtab is not None:
+        assert_dtable(out["dtable"], dtab)
+
+
+def test_varlen_c4_full_size_two_heads():
+    c = synth.config_by_name("c4")
+    inp = synth.draw_varlen(c.seed, c.varlen_total, c.heads, c.head_dim)
+    out, kw = run_varlen_bwd(inp, c.heads, causal=False, scale=1.0)
+    heads = [1, 10]
+    dq, dk, dv, dtab = oracle.varlen_attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                                   inp.f64("do"), inp.cu_seqlens, heads=heads,
+                                                   **kw)
+    for h in heads:
+        assert_grad(out["dq"][:, h], dq[:, h], f"dQ[:,{h}]")
+        assert_grad(out["dk"][:, h], dk[:, h], f"dK[:,{h}]")
+        assert_grad(out["dv"][:, h], dv[:, h], f"dV[:,{h}]")
+        assert_dtable(out["dtable"][:, h], dtab[:, h], f"dtable[:,{h}]")
+
+
+def test_backward_deterministic_dk_dv_dtable():
+    inp = synth.draw_dense(77, 2, 300, 2, 64)
+    a, _ = run_dense_bwd(inp, causal=True, kind="t5", scale=1.0, bidirectional=False)
+    b, _ = run_dense_bwd(inp, causal=True, kind="t5", scale=1.0, bidirectional=False)
+    for name in ("dk", "dv", "dtable"):
+        np.testing.assert_array_equal(a[name], b[name])
+
+
+def test_dtable_optional_and_empty_problem():
+    inp = synth.draw_dense(78, 1, 150, 2, 64)
+    a, kw = run_dense_bwd(inp, causal=False, kind="t5", scale=1.0, want_dtable=False)
+    assert a["dtable"] is None
+    dq, dk, dv, _ = oracle.attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                         inp.f64("do"), **kw)
+    assert_grad(a["dk"], dk, "dK")
+    # an empty batch still overwrites the table gradient (with zeros)
+    q = torch.empty((0, 16, 2, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((0, 2, 16), device="cuda")
+    dtable = torch.full((32, 2), 5.0, device="cuda")
+    bias = fa.T5Bias(torch.zeros(32, 2, device="cuda"), 32, 128, True)
+    fa.fa_bwd(q, q, q, q, lse, q, q, q, q, dtable, bias=bias)
+    torch.cuda.synchronize()
+    assert float(dtable.abs().max()) == 0.0
+
+
+def test_autograd_wrapper_matches_oracle():
+    inp = synth.draw_dense(79, 1, 170, 2, 64)
+    q, k, v, do = (bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    q.requires_grad_(True)
+    k.requires_grad_(True)
+    v.requires_grad_(True)
+    table = torch.from_numpy(inp.table).cuda().requires_grad_(True)
+    o = fa.attention(q, k, v, bias=fa.T5Bias(table, 32, 128, False), causal=True, scale=1.0)
+    o.backward(do)
+    torch.cuda.synchronize()
+    kw = oracle_kwargs("t5", True, 1.0, inp.table, None, 32, 128, False, None)
+    O, _ = oracle.attention_fwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), **kw)
+    dq, dk, dv, dtab = oracle.attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                            inp.f64("do"), **kw)
+    assert_o(to_f64(o), O)
+    assert_grad(to_f64(q.grad), dq, "dQ")
+    assert_grad(to_f64(k.grad), dk, "dK")
+    assert_grad(to_f64(v.grad), dv, "dV")
+    assert_dtable(table.grad.cpu().numpy().astype(np.float64), dtab)
