@@ -17,6 +17,10 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_HIP = -4
 
+FA_KERNEL_FWD = 0
+FA_KERNEL_BWD_PRE = 1
+FA_KERNEL_BWD_MAIN = 2
+
 FA_BIAS_NONE = 0
 FA_BIAS_T5 = 1
 FA_BIAS_ALIBI = 2
@@ -70,6 +74,7 @@ SIGNATURES = {
     "fa_varlen_fwd": (c_i32, [ctypes.POINTER(FaVarlenFwdParams), c_ptr, ctypes.c_size_t, c_ptr]),
     "fa_varlen_bwd": (c_i32, [ctypes.POINTER(FaVarlenBwdParams), c_ptr, ctypes.c_size_t, c_ptr]),
     "fa_t5_buckets": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr, c_ptr]),
+    "fa_set_kernel_timer": (c_i32, [c_i32, c_ptr, c_ptr]),
     "fa_status_str": (ctypes.c_char_p, [c_i32]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_version": (ctypes.c_char_p, []),

@@ -35,6 +35,34 @@ fa_status hip_fail(hipError_t e, const char *where) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernel timers (benchmark hook)
+// ---------------------------------------------------------------------------
+struct Timer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+std::mutex g_timer_mu;
+Timer g_timers[FA_KERNEL_COUNT];
+
+Timer timer_of(int id) {
+  std::lock_guard<std::mutex> lock(g_timer_mu);
+  return g_timers[id];
+}
+
+// Runs `launch` bracketed by the events registered for kernel `id`, if any.
+template <typename F>
+hipError_t timed(int id, hipStream_t s, F &&launch) {
+  const Timer t = timer_of(id);
+  if (t.start) {
+    const hipError_t e = hipEventRecord(t.start, s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = launch();
+  if (e != hipSuccess) return e;
+  if (t.stop) return hipEventRecord(t.stop, s);
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
 // T5 thresholds by exact integer comparison.  For n >= me the T5 bucket is
 // me + floor(ln(n/me) / ln(md/me) * L) (L = nb' - me) capped at nb' - 1, and
 // floor(...) >= k  <=>  n^L * me^k >= md^k * me^L.  thr[k-1] is the smallest
@@ -319,7 +347,7 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
     if (e != hipSuccess) return hip_fail(e, "schedule");
     sched = at<int4>(ws, L.sched);
   }
-  e = fa::launch_fwd_impl(p, b, sched, L.nsched, s);
+  e = timed(FA_KERNEL_FWD, s, [&] { return fa::launch_fwd_impl(p, b, sched, L.nsched, s); });
   if (e != hipSuccess) return hip_fail(e, "forward");
   return FA_OK;
 }
@@ -368,8 +396,14 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
     if (e != hipSuccess) return hip_fail(e, "schedule");
     sched = at<int4>(ws, L.sched);
   }
-  e = fa::launch_bwd_impl(p, b, sched, L.nsched, s);
-  if (e != hipSuccess) return hip_fail(e, "backward");
+  e = timed(FA_KERNEL_BWD_PRE, s,
+            [&] { return fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdPre, s); });
+  if (e != hipSuccess) return hip_fail(e, "backward pre-pass");
+  e = timed(FA_KERNEL_BWD_MAIN, s,
+            [&] { return fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdMain, s); });
+  if (e != hipSuccess) return hip_fail(e, "backward main");
+  e = fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdReduce, s);
+  if (e != hipSuccess) return hip_fail(e, "table-gradient reduction");
   const size_t elems = (size_t)p.total * p.heads * p.head_dim;
   if (rope) {
     e = fa::launch_rope_grad(p, b.dq_acc, dq, s);
@@ -399,6 +433,16 @@ const char *fa_status_str(fa_status st) {
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
 const char *fa_version(void) { return "0.1.0"; }
+
+fa_status fa_set_kernel_timer(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
+  g_last_error.clear();
+  if (kernel < 0 || kernel >= FA_KERNEL_COUNT)
+    return fail(FA_ERR_INVALID, "kernel id %d is not a fa_kernel", kernel);
+  std::lock_guard<std::mutex> lock(g_timer_mu);
+  g_timers[kernel].start = start;
+  g_timers[kernel].stop = stop;
+  return FA_OK;
+}
 
 fa_status fa_check_fwd(const fa_fwd_params *p) {
   g_last_error.clear();

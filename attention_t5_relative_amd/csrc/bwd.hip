@@ -37,7 +37,7 @@ struct BwdArgs {
   float *dk_acc;           // fp32 dK in the rotated space (RoPE), else unused
   float *dq_acc;           // fp32 [tokens, H, D]
   float *delta;            // same layout as lse
-  float *part;             // [nwg, nb] bias-gradient partials
+  float *part;             // [nb, nwg] bias-gradient partials
   const int4 *sched;       // packed batches: {token0, length, head, tile}
   const float *table, *slopes;
   int32_t nbatch, seqlen, heads, total;
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(const BwdArgs a) {
       float t = 0.f;
       for (int x = 0; x <= 2 * sat; ++x)
         if (bkt[x] == b) t += bins[0][x];
-      a.part[(size_t)g * a.nb + b] = t;
+      a.part[(size_t)b * a.nwg + g] = t;
     }
   }
 }
@@ -602,25 +602,36 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4 *x, uint2
   y[i] = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
 }
 
-// dtable[b, h] = sum of the partial rows of head h, in a fixed order.
+// dtable[b, h] = sum of the partials of head h, one workgroup per (b, h):
+// strided per-thread sums, then a tree in LDS, both in a fixed order.
+// Partials are stored bucket-major, part[b * nwg + g].
 __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *part, const int4 *sched,
                                                             int nwg, int nbatch, int heads,
-                                                            int ntile, int nb, float *dtable) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= nb * heads) return;
+                                                            int ntile, float *dtable) {
+  __shared__ float red[256];
+  const int idx = blockIdx.x, tid = threadIdx.x;
   const int b = idx / heads, h = idx - b * heads;
+  const float *pb = part + (size_t)b * nwg;
   float t = 0.f;
   if (sched != nullptr) {
-    for (int gg = 0; gg < nwg; ++gg) {
+    for (int gg = tid; gg < nwg; gg += 256) {
       const int4 e = sched[gg];
-      if (e.y > 0 && e.z == h) t += part[(size_t)gg * nb + b];
+      if (e.y > 0 && e.z == h) t += pb[gg];
     }
   } else {
-    for (int bb = 0; bb < nbatch; ++bb)
-      for (int tt = 0; tt < ntile; ++tt)
-        t += part[((size_t)(bb * heads + h) * ntile + tt) * nb + b];
+    const int n = nbatch * ntile;
+    for (int i = tid; i < n; i += 256) {
+      const int bb = i / ntile, tt = i - bb * ntile;
+      t += pb[(bb * heads + h) * ntile + tt];
+    }
   }
-  dtable[idx] = t;
+  red[tid] = t;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  if (tid == 0) dtable[idx] = red[0];
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
@@ -637,9 +648,8 @@ hipError_t launch_main_t(const BwdArgs &a, hipStream_t s) {
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
-hipError_t launch_pair(const BwdArgs &a, bool rope, bool dbias, hipStream_t s) {
-  hipError_t e = launch_pre_t<D, BIAS, CAUSAL, VARLEN>(a, s);
-  if (e != hipSuccess) return e;
+hipError_t launch_pair(const BwdArgs &a, int phase, bool rope, bool dbias, hipStream_t s) {
+  if (phase == kBwdPre) return launch_pre_t<D, BIAS, CAUSAL, VARLEN>(a, s);
   if constexpr (BIAS == kBiasT5) {
     if (dbias)
       return rope ? launch_main_t<D, BIAS, CAUSAL, VARLEN, true, true>(a, s)
@@ -650,22 +660,22 @@ hipError_t launch_pair(const BwdArgs &a, bool rope, bool dbias, hipStream_t s) {
 }
 
 template <int D, int BIAS>
-hipError_t launch_b(const BwdArgs &a, bool causal, bool varlen, bool rope, bool dbias,
+hipError_t launch_b(const BwdArgs &a, int phase, bool causal, bool varlen, bool rope, bool dbias,
                     hipStream_t s) {
   if (causal)
-    return varlen ? launch_pair<D, BIAS, true, true>(a, rope, dbias, s)
-                  : launch_pair<D, BIAS, true, false>(a, rope, dbias, s);
-  return varlen ? launch_pair<D, BIAS, false, true>(a, rope, dbias, s)
-                : launch_pair<D, BIAS, false, false>(a, rope, dbias, s);
+    return varlen ? launch_pair<D, BIAS, true, true>(a, phase, rope, dbias, s)
+                  : launch_pair<D, BIAS, true, false>(a, phase, rope, dbias, s);
+  return varlen ? launch_pair<D, BIAS, false, true>(a, phase, rope, dbias, s)
+                : launch_pair<D, BIAS, false, false>(a, phase, rope, dbias, s);
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs &a, int bias, bool causal, bool varlen, bool rope, bool dbias,
-                    hipStream_t s) {
+hipError_t launch_d(const BwdArgs &a, int phase, int bias, bool causal, bool varlen, bool rope,
+                    bool dbias, hipStream_t s) {
   switch (bias) {
-    case kBiasT5: return launch_b<D, kBiasT5>(a, causal, varlen, rope, dbias, s);
-    case kBiasAlibi: return launch_b<D, kBiasAlibi>(a, causal, varlen, rope, dbias, s);
-    default: return launch_b<D, kBiasNone>(a, causal, varlen, rope, dbias, s);
+    case kBiasT5: return launch_b<D, kBiasT5>(a, phase, causal, varlen, rope, dbias, s);
+    case kBiasAlibi: return launch_b<D, kBiasAlibi>(a, phase, causal, varlen, rope, dbias, s);
+    default: return launch_b<D, kBiasNone>(a, phase, causal, varlen, rope, dbias, s);
   }
 }
 
@@ -678,8 +688,8 @@ int64_t bwd_num_parts(const Problem &p, int nsched) {
   return (int64_t)p.nbatch * p.heads * ((p.seqlen + BKV - 1) / BKV);
 }
 
-hipError_t launch_bwd_impl(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
-                           hipStream_t s) {
+hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
+                            int phase, hipStream_t s) {
   static_assert(BR == BKV, "pre-pass and main kernel share the packed-batch schedule");
   BwdArgs a;
   a.q = static_cast<const uint16_t *>(b.q);
@@ -714,17 +724,14 @@ hipError_t launch_bwd_impl(const Problem &p, const BwdBuffers &b, const int4 *sc
   if (a.nwg <= 0) return hipSuccess;
   const bool rope = p.rope_base > 0.f;
   const bool dbias = b.part != nullptr;
-  hipError_t e = p.head_dim == 64
-                     ? launch_d<64>(a, p.bias, p.causal, p.varlen, rope, dbias, s)
-                     : launch_d<128>(a, p.bias, p.causal, p.varlen, rope, dbias, s);
-  if (e != hipSuccess) return e;
-  if (dbias) {
-    const int n = a.nb * p.heads;
-    hipLaunchKernelGGL(dbias_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a.part,
-                       sched, a.nwg, p.nbatch, p.heads, a.ntile, a.nb, b.dtable);
-    e = hipGetLastError();
+  if (phase == kBwdReduce) {
+    if (!dbias) return hipSuccess;
+    hipLaunchKernelGGL(dbias_reduce_kernel, dim3(a.nb * p.heads), dim3(256), 0, s, a.part,
+                       sched, a.nwg, p.nbatch, p.heads, a.ntile, b.dtable);
+    return hipGetLastError();
   }
-  return e;
+  return p.head_dim == 64 ? launch_d<64>(a, phase, p.bias, p.causal, p.varlen, rope, dbias, s)
+                          : launch_d<128>(a, phase, p.bias, p.causal, p.varlen, rope, dbias, s);
 }
 
 hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t s) {

@@ -59,7 +59,7 @@ struct BwdBuffers {
   float *dk_acc;           // fp32 dK in the rotated space (RoPE only)
   float *dq_acc;           // fp32 [tokens, H, D]
   float *delta;            // fp32, lse layout
-  float *part;             // fp32 [parts, num_buckets] (T5 table gradient) or nullptr
+  float *part;             // fp32 [num_buckets, parts] (T5 table gradient) or nullptr
   float *dtable;           // [num_buckets, H] or nullptr
 };
 
@@ -76,8 +76,9 @@ hipError_t launch_rope_pair(const Problem &p, const void *q, const void *k, void
 hipError_t launch_rope_grad(const Problem &p, const float *g_rot, void *g_out, hipStream_t s);
 int bwd_tile();
 int64_t bwd_num_parts(const Problem &p, int nsched);
-hipError_t launch_bwd_impl(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
-                           hipStream_t s);
+enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2 };
+hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
+                            int phase, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t s);
 hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
                              hipStream_t s);

@@ -1,0 +1,247 @@
+#!/usr/bin/env python
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = forward + backward (dQ, dK, dV, table gradient) of causal decoder
+self-attention with the unidirectional T5 bias: B8 H12 S4096 D64, 32 buckets,
+max distance 128, scale 1.  Inputs are seeded synthetic bf16 N(0,1) tensors
+resident in HBM before the timed region.
+
+Prints ONE JSON line.  value = algorithmic TFLOP/s of the whole step with the
+FlashAttention convention: forward 4*B*H*S^2*D/2 (causal), backward 2.5x the
+forward (5 GEMMs); the backward pre-pass and the hi/lo splits are extra work
+that is not counted.  "roofline" reports the dominant kernel (timed alone with
+HIP events through the library's fa_set_kernel_timer hook, on the stream it
+runs on) against the 2.5 PFLOP/s dense bf16 MFMA peak.  "cpu_baseline" times
+the fp64 NumPy oracle on a bounded sample of the same workload on the host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s (fraction of bf16 MFMA peak), T5-bias, seq 4096 d64"
+PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+B, S, H, D = 8, 4096, 12, 64
+NB, MD = 32, 128
+SEED = 3
+
+
+def _hip():
+    # the HIP runtime torch (and through it libfat5attn) already loaded: its
+    # SONAME, so no second runtime copy enters the process
+    lib = ctypes.CDLL("libamdhip64.so.7")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _event(hip):
+    ev = ctypes.c_void_p()
+    assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+    return ev
+
+
+def _elapsed(hip, a, b) -> float:
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    return ms.value
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_c3_b8h12s4096d64_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = fields.get("source_sha256")
+    cur = hashlib.sha256()
+    for f in ("attention_t5_relative_amd/csrc/bwd.hip", "attention_t5_relative_amd/csrc/fwd.hip",
+              "attention_t5_relative_amd/csrc/fa_device.h"):
+        cur.update(open(os.path.join(ROOT, f), "rb").read())
+    if src != cur.hexdigest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, pairs):
+    """The fp64 oracle, as it stands, on `pairs` (batch, head) of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0])
+    except Exception:  # noqa: BLE001
+        threads = 0
+    threads = threads or (os.cpu_count() or 1)
+    q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    kw = dict(scale=1.0, causal=True, bias="t5", table=inp.table, num_buckets=NB,
+              max_distance=MD, bidirectional=False)
+    t0 = time.perf_counter()
+    oracle.attention_fwd(q, k, v, pairs=pairs, **kw)
+    oracle.attention_bwd(q, k, v, do, pairs=pairs, **kw)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * 4.0 * S * S * D / 2.0 * len(pairs)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {B * H} (batch, head) pairs of the same workload, "
+                      f"fwd+bwd in fp64 NumPy on the host ({dt:.1f} s); same algorithmic "
+                      f"flop count per pair as the GPU value"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=12)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB before the "
+                         "timed steps (a known-size kernel to calibrate HBM byte counters)")
+    a = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
+              "this library has no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import attention_t5_relative_amd as fa
+    import synth
+    from attention_t5_relative_amd import _lib
+
+    dev = torch.device("cuda:0")
+    inp = synth.draw_dense(SEED, B, S, H, D)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    q, k, v, do = (up(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    table = torch.from_numpy(inp.table).to(dev)
+    bias = fa.T5Bias(table, NB, MD, bidirectional=False)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dtable = torch.empty_like(table)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, scale=1.0, causal=True, bias=bias)
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, scale=1.0, causal=True, bias=bias,
+                  workspace=wsb)
+
+    # workspace sized once, outside the timed region
+    lib = _lib.load()
+    p = _lib.FaBwdParams()
+    p.f = fa.api._fwd_params(q, k, v, o, lse, 1.0, True, bias, 0.0)
+    p.dout, p.dq, p.dk, p.dv, p.dtable = (do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                          dv.data_ptr(), dtable.data_ptr())
+    wsb = torch.empty(lib.fa_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=dev)
+    del ws
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    if a.copy_mib > 0:
+        src = torch.ones(a.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    hip = _hip()
+    kernels = {"fwd": _lib.FA_KERNEL_FWD, "bwd_pre": _lib.FA_KERNEL_BWD_PRE,
+               "bwd_main": _lib.FA_KERNEL_BWD_MAIN}
+    evs = {n: [(_event(hip), _event(hip)) for _ in range(a.steps)] for n in kernels}
+    t_start, t_stop = _event(hip), _event(hip)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    torch.cuda.synchronize()
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventRecord(t_start, ctypes.c_void_p(stream))
+    wall0 = time.perf_counter()
+    for i in range(a.steps):
+        for n, kid in kernels.items():
+            lib.fa_set_kernel_timer(kid, evs[n][i][0], evs[n][i][1])
+        step()
+    hip.hipEventRecord(t_stop, ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for kid in kernels.values():
+        lib.fa_set_kernel_timer(kid, None, None)
+
+    ms_step = _elapsed(hip, t_start, t_stop) / a.steps
+    kernel_ms = {n: sum(_elapsed(hip, s0, s1) for s0, s1 in evs[n]) / a.steps for n in kernels}
+    fwd_flops = 4.0 * B * H * S * S * D / 2.0
+    step_flops = 3.5 * fwd_flops
+    algo = {"fwd": fwd_flops, "bwd_pre": 0.0, "bwd_main": 2.5 * fwd_flops}
+    dom = max(kernel_ms, key=kernel_ms.get)
+    achieved = algo[dom] / (kernel_ms[dom] * 1e-3) / 1e12
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal decoder self-attention fwd+bwd with unidirectional T5 bias "
+                        "(32 buckets, max distance 128), B8 H12 S4096 D64, scale 1",
+            "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
+            "parallelism": "none (one GPU)",
+            "frac_of_peak": round(value / PEAK_TFLOPS, 4),
+            "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
+            "fwd_tflops": round(fwd_flops / (kernel_ms["fwd"] * 1e-3) / 1e12, 2),
+            "host_wall_ms_per_step": round(wall / a.steps * 1e3, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": dom,
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": _traffic(dom),
+        },
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        pairs = [(i % B, (5 * i + 1) % H) for i in range(min(a.cpu_pairs, B * H))]
+        line["cpu_baseline"] = cpu_baseline(inp, pairs)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -108,8 +108,10 @@ typedef struct {
   fa_bias bias;
 } fa_fwd_params;
 
-/* Dense backward.  `f` describes the forward; f.o and f.lse are READ here (the
- * forward's outputs for the same inputs).  dout [B, S, H, D] bf16 in; dq, dk,
+/* Dense backward.  `f` describes the forward; f.lse is READ here (the
+ * forward's output for the same inputs).  f.o is checked like in the forward
+ * but not read: D_i = sum_j P_ij dP_ij is recomputed from fp32 P instead of
+ * taken from the bf16 O.  dout [B, S, H, D] bf16 in; dq, dk,
  * dv [B, S, H, D] bf16 out; dtable fp32 [num_buckets, H] out (T5 only, may be
  * NULL to skip the bias gradient): the sum over the batch and over every
  * visible (query, key) pair in bucket b of dL/dS'. */
@@ -181,6 +183,21 @@ fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes
  * device int32 [qlen, klen]. */
 fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t max_distance,
                         int32_t bidirectional, int32_t *out, hipStream_t stream);
+
+/* Kernels that fa_set_kernel_timer can bracket. */
+typedef enum {
+  FA_KERNEL_FWD = 0,       /* the attention forward kernel                   */
+  FA_KERNEL_BWD_PRE = 1,   /* backward pre-pass (D_i, dQ accumulator zeroing) */
+  FA_KERNEL_BWD_MAIN = 2,  /* backward main kernel (dK, dV, dQ, table grad)  */
+  FA_KERNEL_COUNT = 3
+} fa_kernel;
+
+/* Benchmark hook.  While set, every launch of `kernel` is bracketed by
+ * hipEventRecord(start) and hipEventRecord(stop) on the stream it is launched
+ * on, so a caller can time that kernel alone.  NULL events clear the hook.
+ * The setting is process-wide: change it only while no other thread is inside
+ * the library.  Returns FA_ERR_INVALID for an unknown kernel id. */
+fa_status fa_set_kernel_timer(int32_t kernel, hipEvent_t start, hipEvent_t stop);
 
 /* Static text for a status code. */
 const char *fa_status_str(fa_status st);

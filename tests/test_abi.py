@@ -38,6 +38,13 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
     assert set(names) <= exported
 
 
+def test_kernel_timer_ids(lib):
+    assert lib.fa_set_kernel_timer(3, None, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_set_kernel_timer(-1, None, None) == _lib.FA_ERR_INVALID
+    for k in range(3):
+        assert lib.fa_set_kernel_timer(k, None, None) == _lib.FA_OK
+
+
 def test_status_strings_and_version(lib):
     assert lib.fa_status_str(0) == b"ok"
     assert lib.fa_status_str(-3) == b"workspace missing or too small"
