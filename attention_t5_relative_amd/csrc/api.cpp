@@ -277,7 +277,7 @@ FwdLayout fwd_layout(const fa::Problem &p) {
     L.krot = c.take(tokens * p.heads * p.head_dim * 2);
   }
   if (p.varlen) {
-    const int br = fa::fwd_tile_rows();
+    const int br = fa::fwd_tile_rows(p.head_dim);
     L.nsched = p.heads * ((p.total + br - 1) / br + p.nbatch);
     L.prefix = c.take((size_t)(p.nbatch + 1) * 4);
     L.sched = c.take((size_t)L.nsched * 16);
@@ -342,7 +342,7 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
   }
   const int4 *sched = nullptr;
   if (p.varlen) {
-    e = fa::launch_sched(p.cu_seqlens, p.nbatch, p.heads, fa::fwd_tile_rows(), L.nsched,
+    e = fa::launch_sched(p.cu_seqlens, p.nbatch, p.heads, fa::fwd_tile_rows(p.head_dim), L.nsched,
                          at<int32_t>(ws, L.prefix), at<int4>(ws, L.sched), s);
     if (e != hipSuccess) return hip_fail(e, "schedule");
     sched = at<int4>(ws, L.sched);

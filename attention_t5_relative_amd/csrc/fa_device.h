@@ -88,6 +88,27 @@ __device__ __forceinline__ int t5_bucket_dev(int r, const T5Geometry &g) {
   return off + b;
 }
 
+// Row sum of a packed pair of bf16 values added to acc (v_dot2c_f32_bf16
+// with the pair (1, 1)).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// source lane s reads 4 consecutive bf16 values at its own address; lane i
+// of the group receives element (i % 4) of the values read by source lanes
+// 4m + i/4, m = 0..3, in that order.  So if source lane s = 4m + c points at
+// row r_m, columns c0 + 4c .. c0 + 4c + 3 of a row-major tile, lane i gets
+// column c0 + i of rows r_0..r_3.
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(__attribute__((address_space(3))) void *)(p));
+}
+
 // Bijective key reordering inside each group of 16 keys used for the
 // transposed V tile: swaps bits 2 and 3 of the key offset, so that the eight
 // keys one MFMA B-operand lane supplies (see the forward kernel) are

@@ -64,7 +64,7 @@ struct BwdBuffers {
 };
 
 // Launchers (return the first HIP error, hipSuccess otherwise).
-int fwd_tile_rows();
+int fwd_tile_rows(int head_dim);
 hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sched, int nsched,
                            hipStream_t s);
 hipError_t launch_sched(const int32_t *cu, int nseq, int heads, int tile, int nentries,

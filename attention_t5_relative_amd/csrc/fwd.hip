@@ -10,16 +10,25 @@
 //   query row and 32 of the tile's keys: the row max and row sum are in-lane
 //   reductions plus one exchange between the two half-waves.
 //   O^T (dims x queries) = V^T P^T reuses P straight from the score
-//   accumulators as the MFMA B operand; V is stored transposed in LDS with a
-//   key order (key_perm16) that makes each lane's 8 keys contiguous.
+//   accumulators as the MFMA B operand; its A operand (each lane: one dim,
+//   the 8 keys matching its P values) comes from the row-major V tile through
+//   the transposing LDS read, so K and V are staged the same way.
 #include "fa_device.h"
 
 namespace fa {
 namespace {
 
-constexpr int BR = 128;   // query rows per workgroup
 constexpr int BC = 64;    // keys per tile
-constexpr int NT = 256;   // threads per workgroup
+constexpr int NT = 256;   // threads per workgroup (4 waves)
+// Query rows per wave, in blocks of 32.  Two blocks per wave would let every
+// K and V operand read from LDS feed two MFMAs, but at ~240 registers it drops
+// occupancy to 2 waves per SIMD and measured slower at head_dim 64 (and does
+// not fit at 128), so each wave owns one block.
+template <int D>
+struct FwdTile {
+  static constexpr int RB = 1;                   // 32-row blocks per wave
+  static constexpr int BR = 4 * 32 * RB;         // query rows per workgroup
+};
 // A row's running max is only raised when a tile's max exceeds it by more
 // than 2^8; until then exp2 values stay <= 256, exact enough in fp32 and bf16,
 // and the O accumulator rescale is skipped.
@@ -39,17 +48,26 @@ struct FwdArgs {
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
+  constexpr int RB = FwdTile<D>::RB;
+  constexpr int BR = FwdTile<D>::BR;
+  constexpr int WR = 32 * RB;                 // rows per wave
   constexpr int NCH = D / 8;                  // 16-byte chunks per row
-  constexpr int KLOADS = BC * NCH / NT;       // K chunks per thread per tile
-  constexpr int VUNITS = (BC / 2) * NCH / NT; // (key pair, chunk) units per thread
-  static_assert(KLOADS * NT == BC * NCH && VUNITS * NT == (BC / 2) * NCH, "tile split");
+  constexpr int LOADS = BC * NCH / NT;        // K (and V) chunks per thread per tile
+  // Row pitches (elements).  K rows are read 16 B per lane by 8 consecutive
+  // rows at once: a pitch of an odd number of 16-byte slots keeps those reads
+  // on distinct banks.  V is read with the transposing read, 4 rows x 32 B per
+  // 16 lanes: a pitch of 2 (mod 8) slots keeps those on distinct banks.
+  constexpr int KP = D + 8;
+  constexpr int VP = D + 16;
+  static_assert(LOADS * NT == BC * NCH, "tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][D * BC];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BC * VP];
   __shared__ float lut[BIAS == kBiasT5 ? 2 * kMaxDistance + 1 : 1];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, il = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, il = lane & 31;
   const int g = xcd_remap(blockIdx.x, a.nwg);
 
   int h, qt, tok0, L, bidx = 0;
@@ -78,16 +96,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   const rsrc_t ro = make_rsrc(a.o + base, nrec);
 
   const int q0 = qt * BR;
-  const int wrow0 = q0 + 32 * wave;
-  const int myrow = wrow0 + il;
+  const int wrow0 = q0 + WR * wave;           // first row of this wave
+  const bool wave_live = wrow0 < L;           // rows past the end do nothing
 
-  // Q as the B operand of S^T = K Q^T: lane (hl, il) holds row myrow,
-  // dims 16s + 8hl .. +7 for k-step s.
-  bf16x8 qf[D / 16];
+  // Q as the B operand of S^T = K Q^T: lane (hl, il) holds row
+  // wrow0 + 32rb + il, dims 16s + 8hl .. +7 for k-step s.
+  bf16x8 qf[RB][D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    qf[s] = __builtin_bit_cast(
-        bf16x8, buf_load16(rq, ((uint32_t)myrow * (uint32_t)HD + 16 * s + 8 * hl) * 2u));
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qf[rb][s] = __builtin_bit_cast(
+          bf16x8, buf_load16(rq, ((uint32_t)(wrow0 + 32 * rb + il) * (uint32_t)HD + 16 * s +
+                                  8 * hl) * 2u));
 
   int sat = 0;
   if constexpr (BIAS == kBiasT5) {
@@ -102,194 +123,220 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
   const int nkt = (kend + BC - 1) / BC;
 
-  i32x4 kreg[KLOADS];
-  i32x4 vreg[VUNITS][2];
-
-  auto gload = [&](int j0) {
+  // staging: chunk c = tid + NT*u is row c / NCH, 16-byte column c % NCH.
+  // K and V of the next tile are staged separately (K after this tile's QK
+  // products, V after its PV products) so fewer staging registers are live at
+  // the softmax.
+  i32x4 sreg[LOADS];
+  auto gload = [&](rsrc_t r, int j0) {
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
+    for (int u = 0; u < LOADS; ++u) {
       const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      kreg[u] = buf_load16(rk, ((uint32_t)(j0 + row) * (uint32_t)HD + col * 8) * 2u);
-    }
-#pragma unroll
-    for (int u = 0; u < VUNITS; ++u) {
-      const int unit = tid + NT * u, col = unit % NCH, kp = unit / NCH;
-      vreg[u][0] = buf_load16(rv, ((uint32_t)(j0 + 2 * kp) * (uint32_t)HD + col * 8) * 2u);
-      vreg[u][1] = buf_load16(rv, ((uint32_t)(j0 + 2 * kp + 1) * (uint32_t)HD + col * 8) * 2u);
+      sreg[u] = buf_load16(r, ((uint32_t)(j0 + row) * (uint32_t)HD + col * 8) * 2u);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](uint16_t *dst, int pitch) {
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
+    for (int u = 0; u < LOADS; ++u) {
       const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      *reinterpret_cast<i32x4 *>(&ks[buf][row * D + ((col ^ (row & 7)) * 8)]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VUNITS; ++u) {
-      const int unit = tid + NT * u, col = unit % NCH, kp = unit / NCH;
-      const int kpr = key_perm16(2 * kp);
-      const int kch = kpr >> 3, within = kpr & 7;
-      const i32x4 x0 = vreg[u][0], x1 = vreg[u][1];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = (uint32_t)x0[e >> 1], w1 = (uint32_t)x1[e >> 1];
-        const uint32_t w = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                   : ((w0 & 0xffffu) | (w1 << 16));
-        const int d = 8 * col + e;
-        const int sw = kch ^ ((d ^ (d >> 3)) & 7);
-        *reinterpret_cast<uint32_t *>(&vt[buf][d * BC + sw * 8 + within]) = w;
-      }
+      *reinterpret_cast<i32x4 *>(&dst[row * pitch + col * 8]) = sreg[u];
     }
   };
 
-  f32x16 oacc[D / 32];
+  // per-lane LDS offsets (elements); the rest of each address is a constant
+  const int koff = il * KP + 8 * hl;                       // + 32kb*KP + 16s
+  const int i16 = lane & 15;
+  const int voff = (4 * hl + (i16 >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  //              + (32kb + 16u + 8 half) * VP + 32db
+
+  f32x16 oacc[RB][D / 32];
+  float m_run[RB], lsum[RB][4];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[rb][db] = f32x16{};
+    m_run[rb] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lsum[rb][e] = 0.f;
+  }
   const float c = a.scale_log2;
 
   if (nkt > 0) {
-    gload(0);
-    lstore(0);
+    gload(rk, 0);
+    lstore(ks[0], KP);
+    gload(rv, 0);
+    lstore(vs[0], VP);
   }
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int j0 = kt * BC;
     const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(j0 + BC);
-    const bool active = !CAUSAL || (j0 <= wrow0 + 31);
+    const bool more = kt + 1 < nkt;
+    if (more) gload(rk, j0 + BC);
+    // a causal wave starts work once the tile reaches its last row
+    const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + WR - 1));
+    f32x16 sacc[RB][2];
     if (active) {
-      const uint16_t *kb_s = ks[buf];
-      const uint16_t *vt_s = vt[buf];
-      f32x16 sacc[2];
+      const uint16_t *kb_s = ks[buf] + koff;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        const int row = 32 * kb + il;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = f32x16{};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
-              &kb_s[row * D + (((2 * s + hl) ^ (row & 7)) * 8)]);
-          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb_s + 32 * kb * KP + 16 * s);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32(kf, qf[rb][s], sacc[rb][kb]);
         }
       }
+    }
+    if (more) {
+      lstore(ks[buf ^ 1], KP);
+      gload(rv, j0 + BC);
+    }
+    if (active) {
+      const uint16_t *vt_s = vs[buf] + voff;
 
-      // Element (kb, r) of this lane: key j0 + 32kb + 8(r/4) + 4hl + r%4, query myrow.
-      const int rmin = j0 - (wrow0 + 31), rmax = j0 + BC - 1 - wrow0;
-      const bool mask_c = CAUSAL && rmax > 0;
-      const bool mask_l = (j0 + BC > L);
-      bool uniform = (BIAS == kBiasNone);
-      float bconst = 0.f;
-      if constexpr (BIAS == kBiasT5) {
-        const int lo = min(max(rmin, -sat), sat), hi = min(max(rmax, -sat), sat);
-        uniform = (lo == hi);
-        bconst = lut[lo + sat];
-      }
+      bf16x8 pb[RB][2][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        // Element (kb, r) of block rb: key j0 + 32kb + 8(r/4) + 4hl + r%4,
+        // query row0 + il.
+        const int row0 = wrow0 + 32 * rb;
+        const int myrow = row0 + il;
+        const int rmin = j0 - (row0 + 31), rmax = j0 + BC - 1 - row0;
+        const bool mask_c = CAUSAL && rmax > 0;
+        const bool mask_l = (j0 + BC > L);
+        bool uniform = (BIAS == kBiasNone);
+        float bconst = 0.f;
+        if constexpr (BIAS == kBiasT5) {
+          const int lo = min(max(rmin, -sat), sat), hi = min(max(rmax, -sat), sat);
+          uniform = (lo == hi);
+          bconst = lut[lo + sat];
+        }
+        const bool fast = uniform && !mask_c && !mask_l;
 
-      float tmax;
-      float nbias;   // added to fma(s, c, .) before exp2 on the uniform path
-      if (uniform && !mask_c && !mask_l) {
-        float mx = -INFINITY;
+        float tmax;
+        if (fast) {
+          float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        mx = fmaxf(mx, xor32(mx));
-        tmax = fmaf(mx, c, bconst);
-        nbias = bconst;
-      } else {
-        const int rb = j0 - myrow + 4 * hl;
-        const int jb = j0 + 4 * hl;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-            const int rr = rb + off;
-            float t = sacc[kb][r] * c;
-            if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
-            if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
-            if (mask_c && rr > 0) t = -INFINITY;
-            if (mask_l && jb + off >= L) t = -INFINITY;
-            sacc[kb][r] = t;
-            mx = fmaxf(mx, t);
+          for (int r = 0; r < 16; r += 2) {
+            m0 = fmaxf(m0, fmaxf(sacc[rb][0][r], sacc[rb][0][r + 1]));
+            m1 = fmaxf(m1, fmaxf(sacc[rb][1][r], sacc[rb][1][r + 1]));
           }
-        mx = fmaxf(mx, xor32(mx));
-        tmax = mx;
-        nbias = 0.f;
-        // from here on sacc holds finished log2-domain scores: exp2(s*1 + 0 - m)
-      }
-      const float cc = (uniform && !mask_c && !mask_l) ? c : 1.f;
-
-      const bool need = tmax > m_run + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? exp2f(m_run - tmax) : 1.f;
-        if (need) m_run = tmax;
-        l_run *= alpha;
+          float mx = fmaxf(m0, m1);
+          mx = fmaxf(mx, xor32(mx));
+          tmax = fmaf(mx, c, bconst);
+        } else {
+          const int rbase = j0 - myrow + 4 * hl;
+          const int jb = j0 + 4 * hl;
+          float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      const float sub = nbias - m_use;
-
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * u + 2 * e], cc, sub));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * u + 2 * e + 1], cc, sub));
-            l_run += p0 + p1;
-            w[e] = pack_bf16x2(p0, p1);
-          }
-          i32x4 wv = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-          pb[kb][u] = __builtin_bit_cast(bf16x8, wv);
+            for (int r = 0; r < 16; ++r) {
+              const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+              const int rr = rbase + off;
+              float t = sacc[rb][kb][r] * c;
+              if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
+              if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+              if (mask_c && rr > 0) t = -INFINITY;
+              if (mask_l && jb + off >= L) t = -INFINITY;
+              sacc[rb][kb][r] = t;
+              if (kb == 0) m0 = fmaxf(m0, t); else m1 = fmaxf(m1, t);
+              // keep the bias-table reads from being hoisted all at once
+              // (their results would pin 32 registers)
+              if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+            }
+          float mx = fmaxf(m0, m1);
+          mx = fmaxf(mx, xor32(mx));
+          tmax = mx;
+          // sacc now holds finished log2-domain scores: exp2(s * 1 + 0 - m)
         }
 
+        const bool need = tmax > m_run[rb] + kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[rb] - tmax) : 1.f;
+          if (need) m_run[rb] = tmax;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = 32 * db + il;
-        const int swz = (d ^ (d >> 3)) & 7;
+          for (int e = 0; e < 4; ++e) lsum[rb][e] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+        }
+        const float m_use = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
+        const float cc = fast ? c : 1.f;
+        const float sub = (fast ? bconst : 0.f) - m_use;
+
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int ch = 4 * kb + 2 * u + hl;
-            const bf16x8 vf =
-                *reinterpret_cast<const bf16x8 *>(&vt_s[d * BC + ((ch ^ swz) * 8)]);
-            oacc[db] = mfma32(vf, pb[kb][u], oacc[db]);
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 =
+                  __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][8 * u + 2 * e], cc, sub));
+              const float p1 =
+                  __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][8 * u + 2 * e + 1], cc, sub));
+              w[e] = pack_bf16x2(p0, p1);
+              // fp32 row sums (not of the bf16-rounded values): LSE stays exact
+              // to fp32, which the backward's recomputed P relies on
+              lsum[rb][e] += p0 + p1;
+            }
+            pb[rb][kb][u] =
+                __builtin_bit_cast(bf16x8, i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
           }
       }
+
+      // O^T += V^T P^T: the A operand (dims x keys) comes straight from the
+      // row-major V tile through two transposing reads per MFMA, shared by the
+      // wave's row blocks.
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint16_t *pv = vt_s + (32 * kb + 16 * u) * VP + 32 * db;
+            const s16x4 lo = lds_read_tr(pv);
+            const s16x4 hi = lds_read_tr(pv + 8 * VP);
+            const bf16x8 vf = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32(vf, pb[rb][kb][u], oacc[rb][db]);
+          }
     }
-    if (kt + 1 < nkt) lstore(buf ^ 1);
+    if (more) lstore(vs[buf ^ 1], VP);
     __syncthreads();
   }
 
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int myrow = wrow0 + 32 * rb + il;
+    const float l_run = (lsum[rb][0] + lsum[rb][1]) + (lsum[rb][2] + lsum[rb][3]);
+    const float l_tot = l_run + xor32(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      i32x2 w = {(int)pack_bf16x2(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv),
-                 (int)pack_bf16x2(oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv)};
-      buf_store8(ro, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 2u, w);
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        i32x2 w = {(int)pack_bf16x2(oacc[rb][db][4 * rq] * inv, oacc[rb][db][4 * rq + 1] * inv),
+                   (int)pack_bf16x2(oacc[rb][db][4 * rq + 2] * inv,
+                                    oacc[rb][db][4 * rq + 3] * inv)};
+        buf_store8(ro, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 2u, w);
+      }
+    if (hl == 0 && myrow < L) {
+      const float lse = l_tot > 0.f ? (m_run[rb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      size_t idx;
+      if constexpr (VARLEN)
+        idx = (size_t)h * a.total + tok0 + myrow;
+      else
+        idx = ((size_t)bidx * a.heads + h) * a.seqlen + myrow;
+      a.lse[idx] = lse;
     }
-  if (hl == 0 && myrow < L) {
-    const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    size_t idx;
-    if constexpr (VARLEN)
-      idx = (size_t)h * a.total + tok0 + myrow;
-    else
-      idx = ((size_t)bidx * a.heads + h) * a.seqlen + myrow;
-    a.lse[idx] = lse;
   }
 }
 
@@ -320,7 +367,7 @@ hipError_t launch_d(const FwdArgs &a, int grid, int bias, bool causal, bool varl
 
 }  // namespace
 
-int fwd_tile_rows() { return BR; }
+int fwd_tile_rows(int head_dim) { return head_dim == 64 ? FwdTile<64>::BR : FwdTile<128>::BR; }
 
 hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sched, int nsched,
                            hipStream_t s) {
@@ -344,7 +391,8 @@ hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sc
     a.nq = 0;
     grid = nsched;
   } else {
-    a.nq = (p.seqlen + BR - 1) / BR;
+    const int br = fwd_tile_rows(p.head_dim);
+    a.nq = (p.seqlen + br - 1) / br;
     grid = p.nbatch * p.heads * a.nq;
   }
   a.nwg = grid;
