@@ -18,8 +18,8 @@ FA_ERR_WORKSPACE = -3
 FA_ERR_HIP = -4
 
 FA_KERNEL_FWD = 0
-FA_KERNEL_BWD_PRE = 1
-FA_KERNEL_BWD_MAIN = 2
+FA_KERNEL_BWD_DQ = 1
+FA_KERNEL_BWD_DKV = 2
 
 FA_BIAS_NONE = 0
 FA_BIAS_T5 = 1

@@ -287,8 +287,8 @@ FwdLayout fwd_layout(const fa::Problem &p) {
 }
 
 struct BwdLayout {
-  size_t qrot = 0, krot = 0, dk_acc = 0, dq_acc = 0, delta = 0, part = 0, prefix = 0,
-         sched = 0, total = 0;
+  size_t qrot = 0, krot = 0, dq_f32 = 0, dk_f32 = 0, delta = 0, part = 0, prefix = 0, sched = 0,
+         total = 0;
   int nsched = 0;
   bool has_part = false;
 };
@@ -301,9 +301,9 @@ BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
   if (p.rope_base > 0.f) {
     L.qrot = c.take(elems * 2);
     L.krot = c.take(elems * 2);
-    L.dk_acc = c.take(elems * 4);
+    L.dq_f32 = c.take(elems * 4);
+    L.dk_f32 = c.take(elems * 4);
   }
-  L.dq_acc = c.take(elems * 4);
   L.delta = c.take(tokens * p.heads * 4);
   if (p.varlen) {
     const int bt = fa::bwd_tile();
@@ -375,9 +375,9 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   b.v = v;
   b.dout = dout;
   b.lse = lse;
+  b.dq = dq;
   b.dk = dk;
   b.dv = dv;
-  b.dq_acc = at<float>(ws, L.dq_acc);
   b.delta = at<float>(ws, L.delta);
   b.part = L.has_part ? at<float>(ws, L.part) : nullptr;
   b.dtable = t5grad ? dtable : nullptr;
@@ -387,7 +387,8 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
     if (e != hipSuccess) return hip_fail(e, "rope");
     b.q = at<void>(ws, L.qrot);
     b.k = at<void>(ws, L.krot);
-    b.dk_acc = at<float>(ws, L.dk_acc);
+    b.dq_f32 = at<float>(ws, L.dq_f32);
+    b.dk_f32 = at<float>(ws, L.dk_f32);
   }
   const int4 *sched = nullptr;
   if (p.varlen) {
@@ -396,22 +397,19 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
     if (e != hipSuccess) return hip_fail(e, "schedule");
     sched = at<int4>(ws, L.sched);
   }
-  e = timed(FA_KERNEL_BWD_PRE, s,
+  e = timed(FA_KERNEL_BWD_DQ, s,
             [&] { return fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdPre, s); });
-  if (e != hipSuccess) return hip_fail(e, "backward pre-pass");
-  e = timed(FA_KERNEL_BWD_MAIN, s,
+  if (e != hipSuccess) return hip_fail(e, "backward dq kernel");
+  e = timed(FA_KERNEL_BWD_DKV, s,
             [&] { return fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdMain, s); });
-  if (e != hipSuccess) return hip_fail(e, "backward main");
+  if (e != hipSuccess) return hip_fail(e, "backward dkv kernel");
   e = fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdReduce, s);
   if (e != hipSuccess) return hip_fail(e, "table-gradient reduction");
-  const size_t elems = (size_t)p.total * p.heads * p.head_dim;
   if (rope) {
-    e = fa::launch_rope_grad(p, b.dq_acc, dq, s);
-    if (e == hipSuccess) e = fa::launch_rope_grad(p, b.dk_acc, dk, s);
-  } else {
-    e = fa::launch_f32_to_bf16(b.dq_acc, dq, elems, s);
+    e = fa::launch_rope_grad(p, b.dq_f32, dq, s);
+    if (e == hipSuccess) e = fa::launch_rope_grad(p, b.dk_f32, dk, s);
+    if (e != hipSuccess) return hip_fail(e, "rope gradient");
   }
-  if (e != hipSuccess) return hip_fail(e, "dq/dk epilogue");
   return FA_OK;
 }
 

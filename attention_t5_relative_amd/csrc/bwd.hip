@@ -6,38 +6,42 @@
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K,
 //   dTable[b, h] = sum over (i, j) with bucket b of dS_ij.
 //
-// Three kernels per call:
-//   pre   row-parallel (128 queries per workgroup, forward-shaped): recomputes
-//         P in fp32 and dP, writes D_i = sum_j P_ij dP_ij (consistent with the
-//         P the main kernel recomputes, which D = rowsum(dO * O) from a bf16 O
-//         is not), and zeroes the fp32 dQ accumulator rows it owns.
-//   main  column-parallel (128 keys per workgroup, 32 per wave): loops over
-//         query blocks; S = Q K^T puts each lane on one key, so P and dS feed
-//         the dV and dK products straight from the accumulators; dS goes to
-//         LDS transposed for dQ, which is added to the fp32 accumulator with
-//         coalesced atomics; dS enters the dK and dQ products as a bf16 hi/lo
-//         pair (16 significant bits); the table gradient is binned by relative
-//         distance in per-wave LDS bins and reduced in a fixed order.
-//   reduce (elsewhere) dQ fp32 -> bf16, bias partials -> dTable.
+// Two kernels per call, each owning its outputs (no atomics):
+//   dq   query-parallel, forward-shaped (128 queries per workgroup, 32 per
+//        wave, 64-key tiles of K and V in LDS).  A first sweep over the keys
+//        recomputes P in fp32 with dP and forms D_i = sum_j P_ij dP_ij; the
+//        second sweep forms dS and accumulates dQ^T = K^T dS^T, reading K's
+//        operand with the transposing LDS read.  D is written for the dkv
+//        kernel.  D is taken from the recomputed P rather than from
+//        rowsum(dO * O) with a bf16 O, whose rounding would dominate the dQ
+//        and dK errors.
+//   dkv  key-parallel (128 keys per workgroup, 32 per wave): query blocks of
+//        Q, dO (row-major) and their LSE and D go through double-buffered LDS;
+//        S = Q K^T puts each lane on one key, so P and dS serve as MFMA B
+//        operands from registers for dV^T = dO^T P and dK^T = Q^T dS, whose
+//        A operands come from the same row-major tiles through the
+//        transposing read.  The table gradient is binned by relative
+//        distance in per-half-wave LDS bins (whole saturated blocks in
+//        registers) and reduced in a fixed order.
+// In both, dS enters the dQ and dK products as a bf16 hi + lo pair (16
+// significant bits); with bf16 alone the gradients miss the accuracy gate.
 #include "fa_device.h"
 
 namespace fa {
 namespace {
 
 constexpr int NT = 256;
-constexpr int BR = 128;    // pre-pass: query rows per workgroup
-constexpr int BC = 64;     // pre-pass: keys per tile
-constexpr int BKV = 128;   // main: keys per workgroup
-constexpr int NBINS = 2 * kMaxDistance + 1;
+constexpr int BR = 128;    // dq: query rows per workgroup
+constexpr int BC = 64;     // dq: keys per tile
+constexpr int BKV = 128;   // dkv: keys per workgroup
 
 struct BwdArgs {
   const uint16_t *q, *k, *v, *dout;
   const float *lse;
-  uint16_t *dk, *dv;
-  float *dk_acc;           // fp32 dK in the rotated space (RoPE), else unused
-  float *dq_acc;           // fp32 [tokens, H, D]
+  uint16_t *dq, *dk, *dv;  // bf16 outputs
+  float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
   float *delta;            // same layout as lse
-  float *part;             // [nb, nwg] bias-gradient partials
+  float *part;             // [nb, nwg] table-gradient partials
   const int4 *sched;       // packed batches: {token0, length, head, tile}
   const float *table, *slopes;
   int32_t nbatch, seqlen, heads, total;
@@ -77,19 +81,33 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int g, Work &w) {
   return true;
 }
 
+__device__ __forceinline__ void split_hi_lo(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
+}
+
+__device__ __forceinline__ bf16x8 frag(const uint32_t (&w)[4]) {
+  return __builtin_bit_cast(bf16x8, i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
+}
+
 // ---------------------------------------------------------------------------
-// Pre-pass
+// dq kernel
 // ---------------------------------------------------------------------------
-template <int D, int BIAS, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NT, 2) void bwd_pre_kernel(const BwdArgs a) {
+template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE>
+__global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdArgs a) {
   constexpr int NCH = D / 8;
-  constexpr int KLOADS = BC * NCH / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BC * D];
-  __shared__ float lut[BIAS == kBiasT5 ? NBINS : 1];
+  constexpr int LOADS = BC * NCH / NT;
+  // K is read both row-wise (S^T = K Q^T) and transposed (dQ^T = K^T dS^T):
+  // its pitch suits the transposing read; V is only read row-wise.
+  constexpr int KP = D + 16;
+  constexpr int VP = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BC * VP];
+  __shared__ float lut[BIAS == kBiasT5 ? 2 * kMaxDistance + 1 : 1];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, il = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, il = lane & 31;
   const int g = xcd_remap(blockIdx.x, a.nwg);
   Work w;
   if (!locate<VARLEN>(a, g, w)) return;
@@ -104,22 +122,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_pre_kernel(const BwdArgs a) {
   const rsrc_t rk = make_rsrc(a.k + base, nrec);
   const rsrc_t rv = make_rsrc(a.v + base, nrec);
   const rsrc_t rdo = make_rsrc(a.dout + base, nrec);
-  const rsrc_t rdq = make_rsrc(a.dq_acc + base, nrec * 2u);
 
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * wave;
   const int myrow = wrow0 + il;
-
-  // zero the fp32 dQ rows of this tile (the main kernel adds into them)
-  {
-    constexpr int CH = BR * D / 4;   // 16-byte chunks
-    const i32x4 z = {0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < CH / NT; ++u) {
-      const int c = tid + NT * u, row = c / (D / 4), col = c % (D / 4);
-      buf_store16(rdq, ((uint32_t)(q0 + row) * (uint32_t)HD + col * 4) * 4u, z);
-    }
-  }
+  const bool wave_live = wrow0 < L;
 
   bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
@@ -141,133 +148,177 @@ __global__ __launch_bounds__(NT, 2) void bwd_pre_kernel(const BwdArgs a) {
 
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
   const int nkt = (kend + BC - 1) / BC;
-  i32x4 kreg[KLOADS], vreg[KLOADS];
-  auto gload = [&](int j0) {
+  i32x4 sreg[LOADS];
+  auto gload = [&](rsrc_t r, int j0) {
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
+    for (int u = 0; u < LOADS; ++u) {
       const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      const uint32_t off = ((uint32_t)(j0 + row) * (uint32_t)HD + col * 8) * 2u;
-      kreg[u] = buf_load16(rk, off);
-      vreg[u] = buf_load16(rv, off);
+      sreg[u] = buf_load16(r, ((uint32_t)(j0 + row) * (uint32_t)HD + col * 8) * 2u);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](uint16_t *dst, int pitch) {
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
+    for (int u = 0; u < LOADS; ++u) {
       const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      const int at = row * D + ((col ^ (row & 7)) * 8);
-      *reinterpret_cast<i32x4 *>(&ks[buf][at]) = kreg[u];
-      *reinterpret_cast<i32x4 *>(&vs[buf][at]) = vreg[u];
+      *reinterpret_cast<i32x4 *>(&dst[row * pitch + col * 8]) = sreg[u];
     }
   };
 
+  const int koff = il * KP + 8 * hl;
+  const int voff = il * VP + 8 * hl;
+  const int ktro = tr_lane_offset(lane, KP);
   const float c = a.scale_log2;
-  float acc = 0.f;
-  if (nkt > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int j0 = kt * BC;
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(j0 + BC);
-    const bool active = !CAUSAL || (j0 <= wrow0 + 31);
-    if (active) {
+  const float dscale = a.scale;
+
+  float dsum = 0.f;   // first sweep: sum_j P_ij dP_ij (this lane's keys)
+  float Di = 0.f;     // second sweep: the full D_i
+  f32x16 qacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) qacc[db] = f32x16{};
+
+#pragma unroll 1
+  for (int sweep = 0; sweep < 2; ++sweep) {
+    if (nkt > 0) {
+      gload(rk, 0);
+      lstore(ks[0], KP);
+      gload(rv, 0);
+      lstore(vs[0], VP);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int j0 = kt * BC;
+      const int buf = kt & 1;
+      const bool more = kt + 1 < nkt;
+      if (more) gload(rk, j0 + BC);
+      const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + 31));
       f32x16 sacc[2], pacc[2];
+      if (active) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        pacc[kb] = f32x16{};
-        const int row = 32 * kb + il;
+        for (int kb = 0; kb < 2; ++kb) {
+          sacc[kb] = f32x16{};
+          pacc[kb] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const int at = row * D + (((2 * s + hl) ^ (row & 7)) * 8);
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&ks[buf][at]);
-          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&vs[buf][at]);
-          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
-          pacc[kb] = mfma32(vf, df[s], pacc[kb]);
+          for (int s = 0; s < D / 16; ++s) {
+            const bf16x8 kf =
+                *reinterpret_cast<const bf16x8 *>(&ks[buf][koff + 32 * kb * KP + 16 * s]);
+            const bf16x8 vf =
+                *reinterpret_cast<const bf16x8 *>(&vs[buf][voff + 32 * kb * VP + 16 * s]);
+            sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+            pacc[kb] = mfma32(vf, df[s], pacc[kb]);
+          }
         }
       }
-      const int rmin = j0 - (wrow0 + 31), rmax = j0 + BC - 1 - wrow0;
-      const bool mask_c = CAUSAL && rmax > 0;
-      const bool mask_l = (j0 + BC > L);
-      bool uniform = (BIAS == kBiasNone);
-      float bconst = 0.f;
-      if constexpr (BIAS == kBiasT5) {
-        const int lo = min(max(rmin, -sat), sat), hi = min(max(rmax, -sat), sat);
-        uniform = (lo == hi);
-        bconst = lut[lo + sat];
+      if (more) {
+        lstore(ks[buf ^ 1], KP);
+        gload(rv, j0 + BC);
       }
-      if (uniform && !mask_c && !mask_l) {
+      if (active) {
+        float bconst;
+        const bool fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut,
+                                                    slope_l2, bconst);
+        const float cc = fast ? c : 1.f;
         const float sub = bconst - lse2;
+        if (sweep == 0) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc = fmaf(__builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c, sub)), pacc[kb][r], acc);
-      } else {
-        const int rb = j0 - myrow + 4 * hl;
-        const int jb = j0 + 4 * hl;
+            for (int r = 0; r < 16; ++r)
+              dsum = fmaf(__builtin_amdgcn_exp2f(fmaf(sacc[kb][r], cc, sub)), pacc[kb][r], dsum);
+        } else {
+          // per 16-key group: dS (scaled) as hi + lo fragments, consumed at
+          // once by dQ^T += K^T dS^T, K's operand by transposing reads
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-            const int rr = rb + off;
-            float t = sacc[kb][r] * c;
-            if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
-            if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
-            const bool dead = (mask_c && rr > 0) || (mask_l && jb + off >= L);
-            const float p = dead ? 0.f : __builtin_amdgcn_exp2f(t - lse2);
-            acc = fmaf(p, pacc[kb][r], acc);
-          }
+            for (int u = 0; u < 2; ++u) {
+              uint32_t hw[4], lw[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 8 * u + 2 * e;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], cc, sub));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], cc, sub));
+                split_hi_lo(p0 * (pacc[kb][r] - Di) * dscale,
+                            p1 * (pacc[kb][r + 1] - Di) * dscale, hw[e], lw[e]);
+              }
+              const bf16x8 hb = frag(hw), lb = frag(lw);
+#pragma unroll
+              for (int db = 0; db < D / 32; ++db) {
+                const bf16x8 kt8 =
+                    lds_read_tr8(&ks[buf][ktro + (32 * kb + 16 * u) * KP + 32 * db], KP);
+                qacc[db] = mfma32(kt8, hb, qacc[db]);
+                qacc[db] = mfma32(kt8, lb, qacc[db]);
+              }
+            }
+        }
       }
+      if (more) lstore(vs[buf ^ 1], VP);
+      __syncthreads();
     }
-    if (kt + 1 < nkt) lstore(buf ^ 1);
-    __syncthreads();
+    if (sweep == 0) {
+      Di = dsum + xor32(dsum);
+      if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = Di;
+    }
   }
-  const float dsum = acc + xor32(acc);
-  if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = dsum;
+
+  // dQ row myrow: lane holds dims 32db + 8(r/4) + 4hl + r%4
+  if constexpr (ROPE) {
+    const rsrc_t rdq = make_rsrc(a.dq_f32 + base, nrec * 2u);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x4 v4 = {qacc[db][4 * rq], qacc[db][4 * rq + 1], qacc[db][4 * rq + 2],
+                          qacc[db][4 * rq + 3]};
+        buf_store16(rdq, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 4u,
+                    __builtin_bit_cast(i32x4, v4));
+      }
+  } else {
+    const rsrc_t rdq = make_rsrc(a.dq + base, nrec);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        i32x2 w2 = {(int)pack_bf16x2(qacc[db][4 * rq], qacc[db][4 * rq + 1]),
+                    (int)pack_bf16x2(qacc[db][4 * rq + 2], qacc[db][4 * rq + 3])};
+        buf_store8(rdq, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 2u, w2);
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel
+// dkv kernel
 // ---------------------------------------------------------------------------
 template <int D>
-struct MainCfg {
-  static constexpr int QB = (D == 64) ? 64 : 32;   // query rows per iteration
-  static constexpr int PN = D + 8;                 // padded pitch, natural rows
-  static constexpr int PQ = QB + 8;                // padded pitch, transposed rows
-  static constexpr int PK = BKV + 8;               // padded pitch, K^T and dS rows
+struct DkvTile {
+  static constexpr int QB = (D == 64) ? 64 : 32;   // query rows per block
+  static constexpr int QP = D + 16;                // pitch of the Q / dO rows
 };
 
-template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
-__global__ __launch_bounds__(NT, 1) void bwd_main_kernel(const BwdArgs a) {
-  using C = MainCfg<D>;
-  constexpr int QB = C::QB, PN = C::PN, PQ = C::PQ, PK = C::PK;
-  constexpr int NCH = D / 8;
-  constexpr int QUNITS = (QB / 2) * NCH / NT;     // (row pair, chunk) units per thread
-  constexpr int KUNITS = (BKV / 2) * NCH / NT;
-  static_assert(QUNITS == 1, "one q staging unit per thread");
-  static_assert((QB / 32) * (D / 32) == 4, "one dQ block per wave");
+// Dynamic LDS of the dkv kernel: the T5 bias table by distance, then
+// (with the table gradient) the bucket of each distance and 8 bin arrays.
+__host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
+  if (!t5) return 0;
+  const size_t n = (size_t)(2 * sat + 1);
+  return n * 4 + (dbias ? n * 4 + 8 * n * 4 : 0);
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t qs[QB * PN];
-  __shared__ __attribute__((aligned(16))) uint16_t dos[QB * PN];
-  __shared__ __attribute__((aligned(16))) uint16_t qtr[D * PQ];
-  __shared__ __attribute__((aligned(16))) uint16_t dotr[D * PQ];
-  __shared__ __attribute__((aligned(16))) float lse2s[QB];
-  __shared__ __attribute__((aligned(16))) float dls[QB];
-  __shared__ __attribute__((aligned(16))) uint16_t dsh[QB * PK];
-  __shared__ __attribute__((aligned(16))) uint16_t dsl[QB * PK];
-  __shared__ __attribute__((aligned(16))) uint16_t ktr[D * PK];
-  __shared__ float lut[BIAS == kBiasT5 ? NBINS : 1];
-  __shared__ float bins[DBIAS ? 4 : 1][DBIAS ? NBINS : 1];
-  __shared__ int16_t bkt[DBIAS ? NBINS : 1];
+template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
+__global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdArgs a) {
+  constexpr int QB = DkvTile<D>::QB, QP = DkvTile<D>::QP;
+  constexpr int NCH = D / 8;
+  constexpr int LOADS = QB * NCH / NT;     // Q (and dO) chunks per thread per block
+  static_assert(LOADS * NT == QB * NCH, "block split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][QB * QP];
+  __shared__ __attribute__((aligned(16))) uint16_t dos[2][QB * QP];
+  __shared__ __attribute__((aligned(16))) float lse2s[2][QB];
+  __shared__ __attribute__((aligned(16))) float dls[2][QB];
   __shared__ float ubin[4][2];
+  extern __shared__ float dyn[];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, il = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, il = lane & 31;
   const int g = xcd_remap(blockIdx.x, a.nwg);
   Work w;
   if (!locate<VARLEN>(a, g, w)) return;
@@ -278,6 +329,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(const BwdArgs a) {
   const int kt0 = ktile * BKV;
   const int kw0 = kt0 + 32 * wave;
   const int myk = kw0 + il;
+  const bool wave_live = kw0 < L;
 
   const int HD = a.heads * D;
   const size_t base = ((size_t)w.tok0 * a.heads + h) * D;
@@ -286,10 +338,6 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(const BwdArgs a) {
   const rsrc_t rk = make_rsrc(a.k + base, nrec);
   const rsrc_t rv = make_rsrc(a.v + base, nrec);
   const rsrc_t rdo = make_rsrc(a.dout + base, nrec);
-  const rsrc_t rdk = make_rsrc(ROPE ? (const void *)(a.dk_acc + base) : (const void *)(a.dk + base),
-                               ROPE ? nrec * 2u : nrec);
-  const rsrc_t rdv = make_rsrc(a.dv + base, nrec);
-  float *const dq_base = a.dq_acc + base;
 
   // this wave's 32 keys as the B operand of S = Q K^T and dP = dO V^T
   bf16x8 kf[D / 16], vf[D / 16];
@@ -299,36 +347,27 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(const BwdArgs a) {
     kf[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
     vf[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
   }
-  // K^T of the workgroup's 128 keys (natural key order) for dQ = dS K
-#pragma unroll
-  for (int u = 0; u < KUNITS; ++u) {
-    const int unit = tid + NT * u, col = unit % NCH, kp = unit / NCH;
-    const i32x4 x0 = buf_load16(rk, ((uint32_t)(kt0 + 2 * kp) * (uint32_t)HD + col * 8) * 2u);
-    const i32x4 x1 = buf_load16(rk, ((uint32_t)(kt0 + 2 * kp + 1) * (uint32_t)HD + col * 8) * 2u);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w0 = (uint32_t)x0[e >> 1], w1 = (uint32_t)x1[e >> 1];
-      const uint32_t wd = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                  : ((w0 & 0xffffu) | (w1 << 16));
-      *reinterpret_cast<uint32_t *>(&ktr[(8 * col + e) * PK + 2 * kp]) = wd;
-    }
-  }
 
   int sat = 0;
+  float *lut = dyn;
+  int *bkt = reinterpret_cast<int *>(dyn + (2 * a.t5.sat + 1));
+  float *bins = dyn + 2 * (2 * a.t5.sat + 1);
+  const int nbin = 2 * a.t5.sat + 1;
   if constexpr (BIAS == kBiasT5) {
     sat = a.t5.sat;
-    for (int x = tid; x <= 2 * sat; x += NT) {
+    for (int x = tid; x < nbin; x += NT) {
       const int b = t5_bucket_dev(x - sat, a.t5);
       lut[x] = a.table[b * a.heads + h] * kLog2e;
       if constexpr (DBIAS) {
-        bkt[x] = (int16_t)b;
+        bkt[x] = b;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) bins[ww][x] = 0.f;
+        for (int hw = 0; hw < 8; ++hw) bins[hw * nbin + x] = 0.f;
       }
     }
   }
   float slope_l2 = 0.f;
   if constexpr (BIAS == kBiasAlibi) slope_l2 = -a.slopes[h] * kLog2e;
+  float *const mybins = bins + (2 * wave + hl) * nbin;
 
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -336,102 +375,69 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(const BwdArgs a) {
     dkacc[db] = f32x16{};
     dvacc[db] = f32x16{};
   }
-  float ub0 = 0.f, ub1 = 0.f;   // table-gradient sums of saturated tiles (low / high side)
+  float ub0 = 0.f, ub1 = 0.f;   // table-gradient sums of saturated blocks (low / high side)
 
   const float c = a.scale_log2;
-  const float scale = a.scale;
+  const float dscale = a.scale;
   const int nqb = (L + QB - 1) / QB;
   const int qb_first = CAUSAL ? (kt0 / QB) : 0;
 
-  // staging registers for one query block
-  i32x4 qr0, qr1, dr0, dr1;
+  i32x4 qreg[LOADS], dreg[LOADS];
   float lsev = 0.f, dlv = 0.f;
-  const int s_col = tid % NCH, s_ip = tid / NCH;
   auto gload = [&](int q0) {
-    const uint32_t o0 = ((uint32_t)(q0 + 2 * s_ip) * (uint32_t)HD + s_col * 8) * 2u;
-    const uint32_t o1 = o0 + (uint32_t)HD * 2u;
-    qr0 = buf_load16(rq, o0);
-    qr1 = buf_load16(rq, o1);
-    dr0 = buf_load16(rdo, o0);
-    dr1 = buf_load16(rdo, o1);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cc = tid + NT * u, row = cc / NCH, col = cc % NCH;
+      const uint32_t off = ((uint32_t)(q0 + row) * (uint32_t)HD + col * 8) * 2u;
+      qreg[u] = buf_load16(rq, off);
+      dreg[u] = buf_load16(rdo, off);
+    }
     if (tid < QB) {
       const int row = q0 + tid;
       lsev = row < L ? a.lse[w.lse_base + row] * kLog2e : 0.f;
       dlv = row < L ? a.delta[w.lse_base + row] : 0.f;
     }
   };
-  auto lstore = [&]() {
-    const int r0 = 2 * s_ip;
-    *reinterpret_cast<i32x4 *>(&qs[r0 * PN + s_col * 8]) = qr0;
-    *reinterpret_cast<i32x4 *>(&qs[(r0 + 1) * PN + s_col * 8]) = qr1;
-    *reinterpret_cast<i32x4 *>(&dos[r0 * PN + s_col * 8]) = dr0;
-    *reinterpret_cast<i32x4 *>(&dos[(r0 + 1) * PN + s_col * 8]) = dr1;
-    const int ip = key_perm16(r0);
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * s_col + e;
-      {
-        const uint32_t w0 = (uint32_t)qr0[e >> 1], w1 = (uint32_t)qr1[e >> 1];
-        const uint32_t wd = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                    : ((w0 & 0xffffu) | (w1 << 16));
-        *reinterpret_cast<uint32_t *>(&qtr[d * PQ + ip]) = wd;
-      }
-      {
-        const uint32_t w0 = (uint32_t)dr0[e >> 1], w1 = (uint32_t)dr1[e >> 1];
-        const uint32_t wd = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                    : ((w0 & 0xffffu) | (w1 << 16));
-        *reinterpret_cast<uint32_t *>(&dotr[d * PQ + ip]) = wd;
-      }
+    for (int u = 0; u < LOADS; ++u) {
+      const int cc = tid + NT * u, row = cc / NCH, col = cc % NCH;
+      *reinterpret_cast<i32x4 *>(&qs[buf][row * QP + col * 8]) = qreg[u];
+      *reinterpret_cast<i32x4 *>(&dos[buf][row * QP + col * 8]) = dreg[u];
     }
     if (tid < QB) {
-      lse2s[tid] = lsev;
-      dls[tid] = dlv;
+      lse2s[buf][tid] = lsev;
+      dls[buf][tid] = dlv;
     }
   };
 
-  if (qb_first < nqb) gload(qb_first * QB);
+  const int aoff = il * QP + 8 * hl;            // row-wise A operand
+  const int troff = tr_lane_offset(lane, QP);   // transposed A operand
+
+  if (qb_first < nqb) {
+    gload(qb_first * QB);
+    lstore(0);
+  }
+  __syncthreads();
   for (int qb = qb_first; qb < nqb; ++qb) {
     const int q0 = qb * QB;
-    lstore();
-    __syncthreads();
-    if (qb + 1 < nqb) gload(q0 + QB);
+    const int buf = (qb - qb_first) & 1;
+    const bool more = qb + 1 < nqb;
+    if (more) gload(q0 + QB);
 
 #pragma unroll
     for (int rb = 0; rb < QB / 32; ++rb) {
       const int irow0 = q0 + 32 * rb;
-      const bool active = !CAUSAL || (kw0 <= irow0 + 31);
-      uint16_t *const dsh_blk = &dsh[(32 * rb + 4 * hl) * PK + 32 * wave + il];
-      uint16_t *const dsl_blk = &dsl[(32 * rb + 4 * hl) * PK + 32 * wave + il];
-      if (!active) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int roff = 8 * (r >> 2) + (r & 3);
-          dsh_blk[roff * PK] = 0;
-          dsl_blk[roff * PK] = 0;
-        }
-        continue;
-      }
+      const bool active = wave_live && irow0 < L && (!CAUSAL || kw0 <= irow0 + 31);
+      if (!active) continue;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const int at = (32 * rb + il) * PN + 16 * s + 8 * hl;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&qs[at]);
-        const bf16x8 da = *reinterpret_cast<const bf16x8 *>(&dos[at]);
-        sacc = mfma32(qa, kf[s], sacc);
-        pacc = mfma32(da, vf[s], pacc);
+        const int at = aoff + 32 * rb * QP + 16 * s;
+        sacc = mfma32(*reinterpret_cast<const bf16x8 *>(&qs[buf][at]), kf[s], sacc);
+        pacc = mfma32(*reinterpret_cast<const bf16x8 *>(&dos[buf][at]), vf[s], pacc);
       }
       // element r: row irow0 + 8(r/4) + 4hl + r%4, key myk
-      float lv[16], dv[16];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse2s[32 * rb + 8 * qq + 4 * hl]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dls[32 * rb + 8 * qq + 4 * hl]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lv[4 * qq + e] = l4[e];
-          dv[4 * qq + e] = d4[e];
-        }
-      }
       const int rmin = kw0 - (irow0 + 31), rmax = kw0 + 31 - irow0;
       const bool mask_c = CAUSAL && rmax > 0;
       const bool mask_r = irow0 + 32 > L;
@@ -445,126 +451,100 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(const BwdArgs a) {
         uniform = (ulo == uhi);
         bconst = lut[ulo + sat];
       }
-      float p[16], ds[16];
-      if (uniform && !mask_c && !mask_r && !mask_k) {
-        float tsum = 0.f;
+      const bool fast = uniform && !mask_c && !mask_r && !mask_k;
+      float ds[16];
+      uint32_t pw[2][4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, bconst - lv[r]));
-          ds[r] = p[r] * (pacc[r] - dv[r]);
-          tsum += ds[r];
-        }
-        if constexpr (DBIAS) {
-          if (ulo <= 0) ub0 += tsum; else ub1 += tsum;
-        }
-      } else {
-        const int rbase = myk - irow0 - 4 * hl;
-        const int rowb = irow0 + 4 * hl;
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse2s[buf][32 * rb + 8 * qq + 4 * hl]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dls[buf][32 * rb + 8 * qq + 4 * hl]);
+        float p[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int roff = 8 * (r >> 2) + (r & 3);
-          const int rr = rbase - roff;
-          float t = sacc[r] * c;
-          int x = 0;
-          if constexpr (BIAS == kBiasT5) {
-            x = min(max(rr, -sat), sat) + sat;
-            t += lut[x];
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * qq + e;
+          if (fast) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, bconst - l4[e]));
+          } else {
+            const int roff = 8 * qq + e;
+            const int rr = myk - (irow0 + 4 * hl + roff);
+            float t = sacc[r] * c;
+            int x = 0;
+            if constexpr (BIAS == kBiasT5) {
+              x = min(max(rr, -sat), sat) + sat;
+              t += lut[x];
+            }
+            if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+            const bool dead = (mask_c && rr > 0) || (mask_r && irow0 + 4 * hl + roff >= L) ||
+                              (mask_k && myk >= L);
+            p[e] = dead ? 0.f : __builtin_amdgcn_exp2f(t - l4[e]);
+            if constexpr (DBIAS) {
+              if (!dead) atomicAdd(&mybins[x], p[e] * (pacc[r] - d4[e]));
+            }
           }
-          if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
-          const bool dead = (mask_c && rr > 0) || (mask_r && rowb + roff >= L) ||
-                            (mask_k && myk >= L);
-          p[r] = dead ? 0.f : __builtin_amdgcn_exp2f(t - lv[r]);
-          ds[r] = p[r] * (pacc[r] - dv[r]);
-          if constexpr (DBIAS) {
-            if (!dead) atomicAdd(&bins[wave][x], ds[r]);
-          }
+          ds[r] = p[e] * (pacc[r] - d4[e]);
+        }
+        pw[qq >> 1][2 * (qq & 1)] = pack_bf16x2(p[0], p[1]);
+        pw[qq >> 1][2 * (qq & 1) + 1] = pack_bf16x2(p[2], p[3]);
+      }
+      if constexpr (DBIAS) {
+        if (fast) {
+          float t = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t += ds[r];
+          if (ulo <= 0) ub0 += t; else ub1 += t;
         }
       }
 
-      // dV += P^T dO and dK += scale dS^T Q; rows enter as the k dimension
-      // in key_perm16 order, matching the transposed LDS tiles.
+      // dV^T += dO^T P and dK^T += Q^T dS (scaled): P / dS from registers as
+      // the B operand (k = the block's rows), dO^T / Q^T through transposing
+      // reads of the row-major tiles.
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        uint32_t pw[4], hw[4], lw[4];
+        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r0 = 8 * u + 2 * e;
-          pw[e] = pack_bf16x2(p[r0], p[r0 + 1]);
-          const float s0 = ds[r0] * scale, s1 = ds[r0 + 1] * scale;
-          hw[e] = pack_bf16x2(s0, s1);
-          lw[e] = pack_bf16x2(s0 - bf16_lo(hw[e]), s1 - bf16_hi(hw[e]));
-        }
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
-        const bf16x8 ha = __builtin_bit_cast(bf16x8, i32x4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]});
-        const bf16x8 la = __builtin_bit_cast(bf16x8, i32x4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]});
+        for (int e = 0; e < 4; ++e)
+          split_hi_lo(ds[8 * u + 2 * e] * dscale, ds[8 * u + 2 * e + 1] * dscale, hw[e], lw[e]);
+        const bf16x8 pb = frag(pw[u]), hb = frag(hw), lb = frag(lw);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int at = (32 * db + il) * PQ + 32 * rb + 16 * u + 8 * hl;
-          const bf16x8 dob = *reinterpret_cast<const bf16x8 *>(&dotr[at]);
-          const bf16x8 qb8 = *reinterpret_cast<const bf16x8 *>(&qtr[at]);
-          dvacc[db] = mfma32(pa, dob, dvacc[db]);
-          dkacc[db] = mfma32(ha, qb8, dkacc[db]);
-          dkacc[db] = mfma32(la, qb8, dkacc[db]);
-        }
-        // dS (scaled, hi and lo) to LDS as [row][key] for dQ
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r0 = 8 * u + 2 * e;
-          const int ro0 = 8 * (r0 >> 2) + (r0 & 3), ro1 = 8 * ((r0 + 1) >> 2) + ((r0 + 1) & 3);
-          dsh_blk[ro0 * PK] = (uint16_t)(hw[e] & 0xffffu);
-          dsh_blk[ro1 * PK] = (uint16_t)(hw[e] >> 16);
-          dsl_blk[ro0 * PK] = (uint16_t)(lw[e] & 0xffffu);
-          dsl_blk[ro1 * PK] = (uint16_t)(lw[e] >> 16);
+          const int at = troff + (32 * rb + 16 * u) * QP + 32 * db;
+          const bf16x8 dot8 = lds_read_tr8(&dos[buf][at], QP);
+          const bf16x8 qt8 = lds_read_tr8(&qs[buf][at], QP);
+          dvacc[db] = mfma32(dot8, pb, dvacc[db]);
+          dkacc[db] = mfma32(qt8, hb, dkacc[db]);
+          dkacc[db] = mfma32(qt8, lb, dkacc[db]);
         }
       }
     }
+    if (more) lstore(buf ^ 1);
     __syncthreads();
-
-    // dQ block of this wave: rows 32*rbq.., dims 32*dbq..; contraction over
-    // the workgroup's 128 keys with dS as hi + lo.
-    {
-      const int rbq = wave / (D / 32), dbq = wave % (D / 32);
-      f32x16 qacc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < BKV / 16; ++s) {
-        const int aa = (32 * rbq + il) * PK + 16 * s + 8 * hl;
-        const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(&dsh[aa]);
-        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(&dsl[aa]);
-        const bf16x8 kb8 =
-            *reinterpret_cast<const bf16x8 *>(&ktr[(32 * dbq + il) * PK + 16 * s + 8 * hl]);
-        qacc = mfma32(ah, kb8, qacc);
-        qacc = mfma32(al, kb8, qacc);
-      }
-      const int rowq = q0 + 32 * rbq + 4 * hl;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rowq + 8 * (r >> 2) + (r & 3);
-        if (row < L)
-          __builtin_amdgcn_global_atomic_fadd_f32(
-              dq_base + (size_t)row * HD + 32 * dbq + il, qacc[r]);
-      }
-    }
   }
 
-  // dK, dV: lane holds dims 32*db + il of keys kw0 + 8(r/4) + 4hl + r%4
+  // dK, dV of key myk: lane holds dims 32db + 8(r/4) + 4hl + r%4
+  const rsrc_t rdv = make_rsrc(a.dv + base, nrec);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-      const uint32_t el = (uint32_t)key * (uint32_t)HD + 32 * db + il;
-      const uint32_t vb = pack_bf16x2(dvacc[db][r], 0.f);
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vb & 0xffffu), rdv, (int)(el * 2u), 0, 0);
+    for (int rq = 0; rq < 4; ++rq) {
+      const uint32_t el = (uint32_t)myk * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl;
+      i32x2 v2 = {(int)pack_bf16x2(dvacc[db][4 * rq], dvacc[db][4 * rq + 1]),
+                  (int)pack_bf16x2(dvacc[db][4 * rq + 2], dvacc[db][4 * rq + 3])};
+      buf_store8(rdv, el * 2u, v2);
       if constexpr (ROPE) {
-        buf_store_f32(rdk, el * 4u, dkacc[db][r]);
+        const rsrc_t rdk = make_rsrc(a.dk_f32 + base, nrec * 2u);
+        const f32x4 k4 = {dkacc[db][4 * rq], dkacc[db][4 * rq + 1], dkacc[db][4 * rq + 2],
+                          dkacc[db][4 * rq + 3]};
+        buf_store16(rdk, el * 4u, __builtin_bit_cast(i32x4, k4));
       } else {
-        const uint32_t kb = pack_bf16x2(dkacc[db][r], 0.f);
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(kb & 0xffffu), rdk, (int)(el * 2u), 0, 0);
+        const rsrc_t rdk = make_rsrc(a.dk + base, nrec);
+        i32x2 k2 = {(int)pack_bf16x2(dkacc[db][4 * rq], dkacc[db][4 * rq + 1]),
+                    (int)pack_bf16x2(dkacc[db][4 * rq + 2], dkacc[db][4 * rq + 3])};
+        buf_store8(rdk, el * 2u, k2);
       }
     }
 
   if constexpr (DBIAS) {
-    // saturated-tile sums: reduce over the wave, then fold into the end bins
+    // saturated-block sums: reduce over the wave, then fold into the end bins
     float s0 = ub0, s1 = ub1;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -576,32 +556,27 @@ __global__ __launch_bounds__(NT, 1) void bwd_main_kernel(const BwdArgs a) {
       ubin[wave][1] = s1;
     }
     __syncthreads();
-    for (int x = tid; x <= 2 * sat; x += NT) {
-      float t = bins[0][x] + bins[1][x] + bins[2][x] + bins[3][x];
+    for (int x = tid; x < nbin; x += NT) {
+      float t = 0.f;
+#pragma unroll
+      for (int hw = 0; hw < 8; ++hw) t += bins[hw * nbin + x];
       if (x == 0) t += ubin[0][0] + ubin[1][0] + ubin[2][0] + ubin[3][0];
-      if (x == 2 * sat) t += ubin[0][1] + ubin[1][1] + ubin[2][1] + ubin[3][1];
-      bins[0][x] = t;
+      if (x == nbin - 1) t += ubin[0][1] + ubin[1][1] + ubin[2][1] + ubin[3][1];
+      bins[x] = t;
     }
     __syncthreads();
     for (int b = tid; b < a.nb; b += NT) {
       float t = 0.f;
-      for (int x = 0; x <= 2 * sat; ++x)
-        if (bkt[x] == b) t += bins[0][x];
+      for (int x = 0; x < nbin; ++x)
+        if (bkt[x] == b) t += bins[x];
       a.part[(size_t)b * a.nwg + g] = t;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// dQ conversion and table-gradient reduction
+// Table-gradient reduction
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4 *x, uint2 *y, size_t n4) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const float4 v = x[i];
-  y[i] = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
-}
-
 // dtable[b, h] = sum of the partials of head h, one workgroup per (b, h):
 // strided per-thread sums, then a tree in LDS, both in a fixed order.
 // Partials are stored bucket-major, part[b * nwg + g].
@@ -635,28 +610,40 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *part, co
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
-hipError_t launch_pre_t(const BwdArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_pre_kernel<D, BIAS, CAUSAL, VARLEN>), dim3(a.nwg), dim3(NT), 0, s, a);
+hipError_t launch_dq_t(const BwdArgs &a, bool rope, hipStream_t s) {
+  if (rope)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BIAS, CAUSAL, VARLEN, true>), dim3(a.nwg), dim3(NT), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BIAS, CAUSAL, VARLEN, false>), dim3(a.nwg), dim3(NT), 0,
+                       s, a);
   return hipGetLastError();
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
-hipError_t launch_main_t(const BwdArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_main_kernel<D, BIAS, CAUSAL, VARLEN, ROPE, DBIAS>), dim3(a.nwg),
-                     dim3(NT), 0, s, a);
+hipError_t launch_dkv_t(const BwdArgs &a, hipStream_t s) {
+  const size_t dyn = dkv_dyn_bytes(a.t5.sat, BIAS == kBiasT5, DBIAS);
+  auto kern = bwd_dkv_kernel<D, BIAS, CAUSAL, VARLEN, ROPE, DBIAS>;
+  if (dyn > 16384) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)dyn);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(NT), dyn, s, a);
   return hipGetLastError();
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 hipError_t launch_pair(const BwdArgs &a, int phase, bool rope, bool dbias, hipStream_t s) {
-  if (phase == kBwdPre) return launch_pre_t<D, BIAS, CAUSAL, VARLEN>(a, s);
+  if (phase == kBwdPre) return launch_dq_t<D, BIAS, CAUSAL, VARLEN>(a, rope, s);
   if constexpr (BIAS == kBiasT5) {
     if (dbias)
-      return rope ? launch_main_t<D, BIAS, CAUSAL, VARLEN, true, true>(a, s)
-                  : launch_main_t<D, BIAS, CAUSAL, VARLEN, false, true>(a, s);
+      return rope ? launch_dkv_t<D, BIAS, CAUSAL, VARLEN, true, true>(a, s)
+                  : launch_dkv_t<D, BIAS, CAUSAL, VARLEN, false, true>(a, s);
   }
-  return rope ? launch_main_t<D, BIAS, CAUSAL, VARLEN, true, false>(a, s)
-              : launch_main_t<D, BIAS, CAUSAL, VARLEN, false, false>(a, s);
+  return rope ? launch_dkv_t<D, BIAS, CAUSAL, VARLEN, true, false>(a, s)
+              : launch_dkv_t<D, BIAS, CAUSAL, VARLEN, false, false>(a, s);
 }
 
 template <int D, int BIAS>
@@ -690,17 +677,18 @@ int64_t bwd_num_parts(const Problem &p, int nsched) {
 
 hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
                             int phase, hipStream_t s) {
-  static_assert(BR == BKV, "pre-pass and main kernel share the packed-batch schedule");
+  static_assert(BR == BKV, "dq and dkv kernels share the packed-batch schedule");
   BwdArgs a;
   a.q = static_cast<const uint16_t *>(b.q);
   a.k = static_cast<const uint16_t *>(b.k);
   a.v = static_cast<const uint16_t *>(b.v);
   a.dout = static_cast<const uint16_t *>(b.dout);
   a.lse = b.lse;
+  a.dq = static_cast<uint16_t *>(b.dq);
   a.dk = static_cast<uint16_t *>(b.dk);
   a.dv = static_cast<uint16_t *>(b.dv);
-  a.dk_acc = b.dk_acc;
-  a.dq_acc = b.dq_acc;
+  a.dq_f32 = b.dq_f32;
+  a.dk_f32 = b.dk_f32;
   a.delta = b.delta;
   a.part = b.part;
   a.sched = sched;
@@ -714,6 +702,7 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
   a.t5 = p.t5;
+  if (p.bias != kBiasT5) a.t5.sat = 0;
   if (p.varlen) {
     a.ntile = 0;
     a.nwg = nsched;
@@ -732,14 +721,6 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   }
   return p.head_dim == 64 ? launch_d<64>(a, phase, p.bias, p.causal, p.varlen, rope, dbias, s)
                           : launch_d<128>(a, phase, p.bias, p.causal, p.varlen, rope, dbias, s);
-}
-
-hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t s) {
-  const size_t n4 = n / 4;   // n is a multiple of head_dim, hence of 4
-  if (n4 == 0) return hipSuccess;
-  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<const float4 *>(x), static_cast<uint2 *>(y), n4);
-  return hipGetLastError();
 }
 
 }  // namespace fa

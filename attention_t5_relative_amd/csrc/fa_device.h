@@ -109,6 +109,70 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
       (lds_s16x4 *)(__attribute__((address_space(3))) void *)(p));
 }
 
+// Scores of one 64-key x 32-query tile in the transposed layout used by the
+// query-parallel kernels: sacc[kb][r] holds q.k (unscaled) for query
+// row0 + il and key j0 + 32kb + 8(r/4) + 4hl + r%4.
+//
+// Returns true when the tile needs no per-element work: no mask applies and
+// the bias is one value for the whole tile (no bias, or every pair saturated
+// to the same T5 bucket); the log2-domain score is then fma(s, c, bconst).
+// Otherwise the scores are finished in place in log2 units (scaled, biased,
+// masked to -inf) and bconst is 0, so fma(s, 1, 0) gives them.
+// The causal mask hides keys after the query; keys at or past L are masked.
+template <int BIAS, bool CAUSAL>
+__device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0, int il, int hl,
+                                             int L, float c, int sat, const float *lut,
+                                             float slope_l2, float &bconst) {
+  const int rmin = j0 - (row0 + 31), rmax = j0 + 63 - row0;
+  const bool mask_c = CAUSAL && rmax > 0;
+  const bool mask_l = j0 + 64 > L;
+  bool uniform = (BIAS == kBiasNone);
+  bconst = 0.f;
+  if constexpr (BIAS == kBiasT5) {
+    const int lo = min(max(rmin, -sat), sat), hi = min(max(rmax, -sat), sat);
+    uniform = (lo == hi);
+    bconst = lut[lo + sat];
+  }
+  if (uniform && !mask_c && !mask_l) return true;
+  bconst = 0.f;
+  const int rbase = j0 - (row0 + il) + 4 * hl;
+  const int jb = j0 + 4 * hl;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+      const int rr = rbase + off;
+      float t = sacc[kb][r] * c;
+      if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
+      if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+      if (mask_c && rr > 0) t = -INFINITY;
+      if (mask_l && jb + off >= L) t = -INFINITY;
+      sacc[kb][r] = t;
+      // keep the bias-table reads from being hoisted all at once
+      if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+  return false;
+}
+
+// Per-lane LDS element offset for the transposing read that assembles an
+// MFMA operand of 8 rows x 1 column from a row-major tile with row pitch
+// `pitch`: the lane's own column is (lane % 32) and the 8 rows are, for
+// k-slot v of half-wave hl, 4hl + v (v < 4) and 8 + 4hl + (v - 4), relative
+// to a 16-row group.  Add (16-row group start) * pitch + 32 * column block
+// for the first four rows, and 8 * pitch more for the last four.
+__device__ __forceinline__ int tr_lane_offset(int lane, int pitch) {
+  const int i16 = lane & 15, hl = lane >> 5;
+  return (4 * hl + (i16 >> 2)) * pitch + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+}
+
+// The 8-row operand for one MFMA k-step, read as two transposing reads.
+__device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t *p, int pitch) {
+  const s16x4 lo = lds_read_tr(p);
+  const s16x4 hi = lds_read_tr(p + 8 * pitch);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Bijective key reordering inside each group of 16 keys used for the
 // transposed V tile: swaps bits 2 and 3 of the key offset, so that the eight
 // keys one MFMA B-operand lane supplies (see the forward kernel) are

@@ -55,9 +55,8 @@ struct BwdBuffers {
   const void *q, *k, *v;   // bf16 (rotated when RoPE is on)
   const void *dout;
   const float *lse;
-  void *dk, *dv;           // bf16 outputs
-  float *dk_acc;           // fp32 dK in the rotated space (RoPE only)
-  float *dq_acc;           // fp32 [tokens, H, D]
+  void *dq, *dk, *dv;      // bf16 outputs
+  float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
   float *delta;            // fp32, lse layout
   float *part;             // fp32 [num_buckets, parts] (T5 table gradient) or nullptr
   float *dtable;           // [num_buckets, H] or nullptr
@@ -76,10 +75,9 @@ hipError_t launch_rope_pair(const Problem &p, const void *q, const void *k, void
 hipError_t launch_rope_grad(const Problem &p, const float *g_rot, void *g_out, hipStream_t s);
 int bwd_tile();
 int64_t bwd_num_parts(const Problem &p, int nsched);
-enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2 };
+enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2 };   // dq, dkv, table reduce
 hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
                             int phase, hipStream_t s);
-hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t s);
 hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
                              hipStream_t s);
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);

@@ -145,9 +145,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
 
   // per-lane LDS offsets (elements); the rest of each address is a constant
   const int koff = il * KP + 8 * hl;                       // + 32kb*KP + 16s
-  const int i16 = lane & 15;
-  const int voff = (4 * hl + (i16 >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-  //              + (32kb + 16u + 8 half) * VP + 32db
+  const int voff = tr_lane_offset(lane, VP);               // + (32kb + 16u) * VP + 32db
 
   f32x16 oacc[RB][D / 32];
   float m_run[RB], lsum[RB][4];
@@ -204,56 +202,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
         // Element (kb, r) of block rb: key j0 + 32kb + 8(r/4) + 4hl + r%4,
         // query row0 + il.
         const int row0 = wrow0 + 32 * rb;
-        const int myrow = row0 + il;
-        const int rmin = j0 - (row0 + 31), rmax = j0 + BC - 1 - row0;
-        const bool mask_c = CAUSAL && rmax > 0;
-        const bool mask_l = (j0 + BC > L);
-        bool uniform = (BIAS == kBiasNone);
-        float bconst = 0.f;
-        if constexpr (BIAS == kBiasT5) {
-          const int lo = min(max(rmin, -sat), sat), hi = min(max(rmax, -sat), sat);
-          uniform = (lo == hi);
-          bconst = lut[lo + sat];
+        float bconst;
+        const bool fast = score_tile_T<BIAS, CAUSAL>(sacc[rb], j0, row0, il, hl, L, c, sat, lut,
+                                                    slope_l2, bconst);
+        float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          m0 = fmaxf(m0, fmaxf(sacc[rb][0][r], sacc[rb][0][r + 1]));
+          m1 = fmaxf(m1, fmaxf(sacc[rb][1][r], sacc[rb][1][r + 1]));
         }
-        const bool fast = uniform && !mask_c && !mask_l;
-
-        float tmax;
-        if (fast) {
-          float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            m0 = fmaxf(m0, fmaxf(sacc[rb][0][r], sacc[rb][0][r + 1]));
-            m1 = fmaxf(m1, fmaxf(sacc[rb][1][r], sacc[rb][1][r + 1]));
-          }
-          float mx = fmaxf(m0, m1);
-          mx = fmaxf(mx, xor32(mx));
-          tmax = fmaf(mx, c, bconst);
-        } else {
-          const int rbase = j0 - myrow + 4 * hl;
-          const int jb = j0 + 4 * hl;
-          float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-              const int rr = rbase + off;
-              float t = sacc[rb][kb][r] * c;
-              if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
-              if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
-              if (mask_c && rr > 0) t = -INFINITY;
-              if (mask_l && jb + off >= L) t = -INFINITY;
-              sacc[rb][kb][r] = t;
-              if (kb == 0) m0 = fmaxf(m0, t); else m1 = fmaxf(m1, t);
-              // keep the bias-table reads from being hoisted all at once
-              // (their results would pin 32 registers)
-              if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-            }
-          float mx = fmaxf(m0, m1);
-          mx = fmaxf(mx, xor32(mx));
-          tmax = mx;
-          // sacc now holds finished log2-domain scores: exp2(s * 1 + 0 - m)
-        }
+        float mx = fmaxf(m0, m1);
+        mx = fmaxf(mx, xor32(mx));
+        // c > 0, so the scaled max is the max of the scaled scores
+        const float tmax = fast ? fmaf(mx, c, bconst) : mx;
 
         const bool need = tmax > m_run[rb] + kRescaleLog2;
         if (__builtin_amdgcn_ballot_w64(need)) {
@@ -268,7 +229,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
         }
         const float m_use = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
         const float cc = fast ? c : 1.f;
-        const float sub = (fast ? bconst : 0.f) - m_use;
+        const float sub = bconst - m_use;
 
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -300,11 +261,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const uint16_t *pv = vt_s + (32 * kb + 16 * u) * VP + 32 * db;
-            const s16x4 lo = lds_read_tr(pv);
-            const s16x4 hi = lds_read_tr(pv + 8 * VP);
-            const bf16x8 vf = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 vf = lds_read_tr8(vt_s + (32 * kb + 16 * u) * VP + 32 * db, VP);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32(vf, pb[rb][kb][u], oacc[rb][db]);
           }

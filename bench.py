@@ -173,8 +173,8 @@ def main(argv=None):
         del src, dst
 
     hip = _hip()
-    kernels = {"fwd": _lib.FA_KERNEL_FWD, "bwd_pre": _lib.FA_KERNEL_BWD_PRE,
-               "bwd_main": _lib.FA_KERNEL_BWD_MAIN}
+    kernels = {"fwd": _lib.FA_KERNEL_FWD, "bwd_dq": _lib.FA_KERNEL_BWD_DQ,
+               "bwd_dkv": _lib.FA_KERNEL_BWD_DKV}
     evs = {n: [(_event(hip), _event(hip)) for _ in range(a.steps)] for n in kernels}
     t_start, t_stop = _event(hip), _event(hip)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -197,7 +197,9 @@ def main(argv=None):
     kernel_ms = {n: sum(_elapsed(hip, s0, s1) for s0, s1 in evs[n]) / a.steps for n in kernels}
     fwd_flops = 4.0 * B * H * S * S * D / 2.0
     step_flops = 3.5 * fwd_flops
-    algo = {"fwd": fwd_flops, "bwd_pre": 0.0, "bwd_main": 2.5 * fwd_flops}
+    # per kernel, the products its own outputs need (each backward kernel
+    # recomputes S and dP): dq kernel S, dP, dQ; dkv kernel S, dP, dV, dK
+    algo = {"fwd": fwd_flops, "bwd_dq": 1.5 * fwd_flops, "bwd_dkv": 2.0 * fwd_flops}
     dom = max(kernel_ms, key=kernel_ms.get)
     achieved = algo[dom] / (kernel_ms[dom] * 1e-3) / 1e12
     value = step_flops / (ms_step * 1e-3) / 1e12

@@ -186,9 +186,9 @@ fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t
 
 /* Kernels that fa_set_kernel_timer can bracket. */
 typedef enum {
-  FA_KERNEL_FWD = 0,       /* the attention forward kernel                   */
-  FA_KERNEL_BWD_PRE = 1,   /* backward pre-pass (D_i, dQ accumulator zeroing) */
-  FA_KERNEL_BWD_MAIN = 2,  /* backward main kernel (dK, dV, dQ, table grad)  */
+  FA_KERNEL_FWD = 0,       /* the attention forward kernel                       */
+  FA_KERNEL_BWD_DQ = 1,    /* backward, query-parallel: D_i and dQ               */
+  FA_KERNEL_BWD_DKV = 2,   /* backward, key-parallel: dK, dV and table gradient  */
   FA_KERNEL_COUNT = 3
 } fa_kernel;
 
