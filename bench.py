@@ -8,7 +8,7 @@ resident in HBM before the timed region.
 
 Prints ONE JSON line.  value = algorithmic TFLOP/s of the whole step with the
 FlashAttention convention: forward 4*B*H*S^2*D/2 (causal), backward 2.5x the
-forward (5 GEMMs); the backward pre-pass and the hi/lo splits are extra work
+forward (5 GEMMs); the backward's D sweep and the hi/lo splits are extra work
 that is not counted.  "roofline" reports the dominant kernel (timed alone with
 HIP events through the library's fa_set_kernel_timer hook, on the stream it
 runs on) against the 2.5 PFLOP/s dense bf16 MFMA peak.  "cpu_baseline" times
