@@ -23,8 +23,13 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfat5attn.so")
 ARCH = "gfx950"
 
-# Packed fp32 VALU forms are kept out of the device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are kept out of the device code.  Device code is
+# also built without NaN semantics: the kernels never produce or consume NaN
+# (masked scores are -inf, which keeps its meaning), and IEEE NaN handling
+# would put a canonicalising max in front of every fmaxf of the softmax.
+# Host code (the argument checks in api.cpp) keeps full IEEE semantics.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-Xarch_device", "-fno-honor-nans"]
 
 
 def hipcc() -> str:

@@ -176,6 +176,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) qacc[db] = f32x16{};
 
+  wait_vmem_loads();
 #pragma unroll 1
   for (int sweep = 0; sweep < 2; ++sweep) {
     if (nkt > 0) {
@@ -418,6 +419,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
     gload(qb_first * QB);
     lstore(0);
   }
+  wait_vmem_loads();
   __syncthreads();
   for (int qb = qb_first; qb < nqb; ++qb) {
     const int q0 = qb * QB;

@@ -44,6 +44,13 @@ __device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)off, 0, 0);
 }
 
+// Waits until every vector memory load issued so far has returned (vmcnt(0),
+// other counters untouched).  Registers loaded before a loop must be waited
+// for once before it: otherwise the compiler's wait insertion, which cannot
+// tell across iterations that they have arrived, waits for all outstanding
+// loads - including prefetches issued in the loop - at their first use.
+__device__ __forceinline__ void wait_vmem_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.  Lane l holds
 // row (l % 32) of A and column (l % 32) of B, each with 8 consecutive k values
 // for half-wave (l / 32); the accumulator holds, in register r, the element
@@ -62,6 +69,20 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
 }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Max / sum of a value over the two half-waves (lanes l and l ^ 32), with
+// v_permlane32_swap (a VALU lane exchange, no LDS round trip).  Both lanes of
+// a pair get the same result, bit for bit.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8),
 // each XCD with its own L2.  This remap gives every XCD a contiguous range of

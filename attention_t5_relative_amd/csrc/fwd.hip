@@ -13,6 +13,13 @@
 //   accumulators as the MFMA B operand; its A operand (each lane: one dim,
 //   the 8 keys matching its P values) comes from the row-major V tile through
 //   the transposing LDS read, so K and V are staged the same way.
+//
+// Latency.  With operands read from LDS right before each MFMA, every MFMA
+// waits out an LDS round trip; measured per 64-key tile that cost more than
+// the softmax itself.  So the K operands of a tile are read in one batch
+// before its QK^T products, and the V operands are read before the softmax,
+// whose VALU work covers their latency.  K and V tiles are fetched from
+// global memory one full iteration before they are written to LDS.
 #include "fa_device.h"
 
 namespace fa {
@@ -20,15 +27,7 @@ namespace {
 
 constexpr int BC = 64;    // keys per tile
 constexpr int NT = 256;   // threads per workgroup (4 waves)
-// Query rows per wave, in blocks of 32.  Two blocks per wave would let every
-// K and V operand read from LDS feed two MFMAs, but at ~240 registers it drops
-// occupancy to 2 waves per SIMD and measured slower at head_dim 64 (and does
-// not fit at 128), so each wave owns one block.
-template <int D>
-struct FwdTile {
-  static constexpr int RB = 1;                   // 32-row blocks per wave
-  static constexpr int BR = 4 * 32 * RB;         // query rows per workgroup
-};
+constexpr int BR = 128;   // query rows per workgroup (32 per wave)
 // A row's running max is only raised when a tile's max exceeds it by more
 // than 2^8; until then exp2 values stay <= 256, exact enough in fp32 and bf16,
 // and the O accumulator rescale is skipped.
@@ -48,11 +47,15 @@ struct FwdArgs {
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
-  constexpr int RB = FwdTile<D>::RB;
-  constexpr int BR = FwdTile<D>::BR;
-  constexpr int WR = 32 * RB;                 // rows per wave
   constexpr int NCH = D / 8;                  // 16-byte chunks per row
   constexpr int LOADS = BC * NCH / NT;        // K (and V) chunks per thread per tile
+  constexpr int NVF = D / 8;                  // V operand fragments per tile
+  // Register budget: at head_dim 64 the K operands of both 32-key blocks are
+  // read in one batch and every V operand before the softmax; at 128 the K
+  // operands go one key block at a time and a quarter of V before the softmax.
+  constexpr int KBATCH = D == 64 ? 2 : 1;     // key blocks per K read batch
+  constexpr int NKF = KBATCH * (D / 16);      // K fragments per batch
+  constexpr int VPRE = D == 64 ? NVF : NVF / 4;
   // Row pitches (elements).  K rows are read 16 B per lane by 8 consecutive
   // rows at once: a pitch of an odd number of 16-byte slots keeps those reads
   // on distinct banks.  V is read with the transposing read, 4 rows x 32 B per
@@ -96,19 +99,16 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   const rsrc_t ro = make_rsrc(a.o + base, nrec);
 
   const int q0 = qt * BR;
-  const int wrow0 = q0 + WR * wave;           // first row of this wave
+  const int wrow0 = q0 + 32 * wave;           // first row of this wave
   const bool wave_live = wrow0 < L;           // rows past the end do nothing
 
-  // Q as the B operand of S^T = K Q^T: lane (hl, il) holds row
-  // wrow0 + 32rb + il, dims 16s + 8hl .. +7 for k-step s.
-  bf16x8 qf[RB][D / 16];
+  // Q as the B operand of S^T = K Q^T: lane (hl, il) holds row wrow0 + il,
+  // dims 16s + 8hl .. +7 for k-step s.
+  bf16x8 qf[D / 16];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qf[rb][s] = __builtin_bit_cast(
-          bf16x8, buf_load16(rq, ((uint32_t)(wrow0 + 32 * rb + il) * (uint32_t)HD + 16 * s +
-                                  8 * hl) * 2u));
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = __builtin_bit_cast(
+        bf16x8, buf_load16(rq, ((uint32_t)(wrow0 + il) * (uint32_t)HD + 16 * s + 8 * hl) * 2u));
 
   int sat = 0;
   if constexpr (BIAS == kBiasT5) {
@@ -123,23 +123,20 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
   const int nkt = (kend + BC - 1) / BC;
 
-  // staging: chunk c = tid + NT*u is row c / NCH, 16-byte column c % NCH.
-  // K and V of the next tile are staged separately (K after this tile's QK
-  // products, V after its PV products) so fewer staging registers are live at
-  // the softmax.
-  i32x4 sreg[LOADS];
-  auto gload = [&](rsrc_t r, int j0) {
+  // staging: chunk c = tid + NT*u is row c / NCH, 16-byte column c % NCH
+  i32x4 kreg[LOADS], vreg[LOADS];
+  auto gload = [&](i32x4 (&r)[LOADS], rsrc_t src, int j0) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      sreg[u] = buf_load16(r, ((uint32_t)(j0 + row) * (uint32_t)HD + col * 8) * 2u);
+      r[u] = buf_load16(src, ((uint32_t)(j0 + row) * (uint32_t)HD + col * 8) * 2u);
     }
   };
-  auto lstore = [&](uint16_t *dst, int pitch) {
+  auto lstore = [&](const i32x4 (&r)[LOADS], uint16_t *dst, int pitch) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      *reinterpret_cast<i32x4 *>(&dst[row * pitch + col * 8]) = sreg[u];
+      *reinterpret_cast<i32x4 *>(&dst[row * pitch + col * 8]) = r[u];
     }
   };
 
@@ -147,153 +144,156 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   const int koff = il * KP + 8 * hl;                       // + 32kb*KP + 16s
   const int voff = tr_lane_offset(lane, VP);               // + (32kb + 16u) * VP + 32db
 
-  f32x16 oacc[RB][D / 32];
-  float m_run[RB], lsum[RB][4];
+  f32x16 oacc[D / 32];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[rb][db] = f32x16{};
-    m_run[rb] = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lsum[rb][e] = 0.f;
-  }
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
   const float c = a.scale_log2;
 
+  // Tile 0 goes to LDS now; tile 1 waits in registers.  From then on,
+  // iteration kt writes tile kt + 1 to the other buffer (last read in
+  // iteration kt - 1, before the barrier that ended it) and fetches tile
+  // kt + 2, so each global load has a whole iteration to arrive.
   if (nkt > 0) {
-    gload(rk, 0);
-    lstore(ks[0], KP);
-    gload(rv, 0);
-    lstore(vs[0], VP);
+    gload(kreg, rk, 0);
+    gload(vreg, rv, 0);
+    lstore(kreg, ks[0], KP);
+    lstore(vreg, vs[0], VP);
+  }
+  wait_vmem_loads();
+  if (nkt > 1) {
+    gload(kreg, rk, BC);
+    gload(vreg, rv, BC);
   }
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int j0 = kt * BC;
     const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) gload(rk, j0 + BC);
     // a causal wave starts work once the tile reaches its last row
-    const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + WR - 1));
-    f32x16 sacc[RB][2];
+    const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + 31));
+
+    // K operands in batches of KBATCH key blocks
+    const uint16_t *kb_s = ks[buf] + koff;
+    auto kread = [&](bf16x8 (&kf)[NKF], int kb0) {
+#pragma unroll
+      for (int i = 0; i < NKF; ++i) {
+        const int kb = kb0 + i / (D / 16), s = i % (D / 16);
+        kf[i] = *reinterpret_cast<const bf16x8 *>(kb_s + 32 * kb * KP + 16 * s);
+      }
+    };
+    bf16x8 kf[NKF];
+    if (active) kread(kf, 0);
+    if (kt + 1 < nkt) {
+      lstore(kreg, ks[buf ^ 1], KP);
+      lstore(vreg, vs[buf ^ 1], VP);
+    }
+    if (kt + 2 < nkt) {
+      gload(kreg, rk, j0 + 2 * BC);
+      gload(vreg, rv, j0 + 2 * BC);
+    }
+
     if (active) {
-      const uint16_t *kb_s = ks[buf] + koff;
+      f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        if (kb % KBATCH == 0 && kb > 0) kread(kf, kb);
+        f32x16 acc = f32x16{};
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb_s + 32 * kb * KP + 16 * s);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32(kf, qf[rb][s], sacc[rb][kb]);
-        }
+        for (int s = 0; s < D / 16; ++s) acc = mfma32(kf[(kb % KBATCH) * (D / 16) + s], qf[s], acc);
+        sacc[kb] = acc;
       }
-    }
-    if (more) {
-      lstore(ks[buf ^ 1], KP);
-      gload(rv, j0 + BC);
-    }
-    if (active) {
+
+      // V operands (fragment i: dims 32db, keys 32kb + 16u), read now so the
+      // softmax below covers their latency
       const uint16_t *vt_s = vs[buf] + voff;
+      auto vread = [&](int i) {
+        const int db = i >> 2, kb = (i >> 1) & 1, u = i & 1;
+        return lds_read_tr8(vt_s + (32 * kb + 16 * u) * VP + 32 * db, VP);
+      };
+      bf16x8 vf[NVF];
+#pragma unroll
+      for (int i = 0; i < VPRE; ++i) vf[i] = vread(i);
 
-      bf16x8 pb[RB][2][2];
+      // Element (kb, r): key j0 + 32kb + 8(r/4) + 4hl + r%4, query wrow0 + il.
+      float bconst;
+      const bool fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut,
+                                                  slope_l2, bconst);
+      float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        // Element (kb, r) of block rb: key j0 + 32kb + 8(r/4) + 4hl + r%4,
-        // query row0 + il.
-        const int row0 = wrow0 + 32 * rb;
-        float bconst;
-        const bool fast = score_tile_T<BIAS, CAUSAL>(sacc[rb], j0, row0, il, hl, L, c, sat, lut,
-                                                    slope_l2, bconst);
-        float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          m0 = fmaxf(m0, fmaxf(sacc[rb][0][r], sacc[rb][0][r + 1]));
-          m1 = fmaxf(m1, fmaxf(sacc[rb][1][r], sacc[rb][1][r + 1]));
-        }
-        float mx = fmaxf(m0, m1);
-        mx = fmaxf(mx, xor32(mx));
-        // c > 0, so the scaled max is the max of the scaled scores
-        const float tmax = fast ? fmaf(mx, c, bconst) : mx;
-
-        const bool need = tmax > m_run[rb] + kRescaleLog2;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[rb] - tmax) : 1.f;
-          if (need) m_run[rb] = tmax;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lsum[rb][e] *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-        }
-        const float m_use = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
-        const float cc = fast ? c : 1.f;
-        const float sub = bconst - m_use;
-
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0 =
-                  __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][8 * u + 2 * e], cc, sub));
-              const float p1 =
-                  __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][8 * u + 2 * e + 1], cc, sub));
-              w[e] = pack_bf16x2(p0, p1);
-              // fp32 row sums (not of the bf16-rounded values): LSE stays exact
-              // to fp32, which the backward's recomputed P relies on
-              lsum[rb][e] += p0 + p1;
-            }
-            pb[rb][kb][u] =
-                __builtin_bit_cast(bf16x8, i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
-          }
+      for (int r = 0; r < 16; r += 2) {
+        m0 = fmaxf(m0, fmaxf(sacc[0][r], sacc[0][r + 1]));
+        m1 = fmaxf(m1, fmaxf(sacc[1][r], sacc[1][r + 1]));
       }
+      const float mx = half_max(fmaxf(m0, m1));
+      // c > 0, so the scaled max is the max of the scaled scores
+      const float tmax = fast ? fmaf(mx, c, bconst) : mx;
 
-      // O^T += V^T P^T: the A operand (dims x keys) comes straight from the
-      // row-major V tile through two transposing reads per MFMA, shared by the
-      // wave's row blocks.
+      const bool need = tmax > m_run + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.f;
+        if (need) m_run = tmax;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int e = 0; e < 4; ++e) lsum[e] *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 vf = lds_read_tr8(vt_s + (32 * kb + 16 * u) * VP + 32 * db, VP);
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      const float cc = fast ? c : 1.f;
+      const float sub = bconst - m_use;
+
+      bf16x8 pb[2][2];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32(vf, pb[rb][kb][u], oacc[rb][db]);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * u + 2 * e], cc, sub));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * u + 2 * e + 1], cc, sub));
+            w[e] = pack_bf16x2(p0, p1);
+            // fp32 row sums (not of the bf16-rounded values): LSE stays exact
+            // to fp32, which the backward's recomputed P relies on
+            lsum[e] += p0 + p1;
           }
+          pb[kb][u] = __builtin_bit_cast(bf16x8, i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
+        }
+
+#pragma unroll
+      for (int i = VPRE; i < NVF; ++i) vf[i] = vread(i);
+      // O^T += V^T P^T
+#pragma unroll
+      for (int i = 0; i < NVF; ++i) {
+        const int db = i >> 2, kb = (i >> 1) & 1, u = i & 1;
+        oacc[db] = mfma32(vf[i], pb[kb][u], oacc[db]);
+      }
     }
-    if (more) lstore(vs[buf ^ 1], VP);
     __syncthreads();
   }
 
+  const int myrow = wrow0 + il;
+  const float l_tot = half_sum((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int myrow = wrow0 + 32 * rb + il;
-    const float l_run = (lsum[rb][0] + lsum[rb][1]) + (lsum[rb][2] + lsum[rb][3]);
-    const float l_tot = l_run + xor32(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        i32x2 w = {(int)pack_bf16x2(oacc[rb][db][4 * rq] * inv, oacc[rb][db][4 * rq + 1] * inv),
-                   (int)pack_bf16x2(oacc[rb][db][4 * rq + 2] * inv,
-                                    oacc[rb][db][4 * rq + 3] * inv)};
-        buf_store8(ro, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 2u, w);
-      }
-    if (hl == 0 && myrow < L) {
-      const float lse = l_tot > 0.f ? (m_run[rb] + __log2f(l_tot)) * kLn2 : -INFINITY;
-      size_t idx;
-      if constexpr (VARLEN)
-        idx = (size_t)h * a.total + tok0 + myrow;
-      else
-        idx = ((size_t)bidx * a.heads + h) * a.seqlen + myrow;
-      a.lse[idx] = lse;
+    for (int rq = 0; rq < 4; ++rq) {
+      i32x2 w = {(int)pack_bf16x2(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv),
+                 (int)pack_bf16x2(oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv)};
+      buf_store8(ro, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 2u, w);
     }
+  if (hl == 0 && myrow < L) {
+    const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    size_t idx;
+    if constexpr (VARLEN)
+      idx = (size_t)h * a.total + tok0 + myrow;
+    else
+      idx = ((size_t)bidx * a.heads + h) * a.seqlen + myrow;
+    a.lse[idx] = lse;
   }
 }
 
@@ -324,7 +324,7 @@ hipError_t launch_d(const FwdArgs &a, int grid, int bias, bool causal, bool varl
 
 }  // namespace
 
-int fwd_tile_rows(int head_dim) { return head_dim == 64 ? FwdTile<64>::BR : FwdTile<128>::BR; }
+int fwd_tile_rows(int) { return BR; }
 
 hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sched, int nsched,
                            hipStream_t s) {
@@ -348,8 +348,7 @@ hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sc
     a.nq = 0;
     grid = nsched;
   } else {
-    const int br = fwd_tile_rows(p.head_dim);
-    a.nq = (p.seqlen + br - 1) / br;
+    a.nq = (p.seqlen + BR - 1) / BR;
     grid = p.nbatch * p.heads * a.nq;
   }
   a.nwg = grid;
