@@ -54,6 +54,7 @@ struct BwdArgs {
 
 struct Work {
   int h, tile, tok0, L;
+  int part;                // table-gradient partial slot (reduction order)
   size_t lse_base;         // index of row 0 in lse / delta
 };
 
@@ -68,10 +69,12 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int g, Work &w) {
     w.L = e.y;
     w.h = e.z;
     w.tile = e.w;
+    w.part = g;
     w.lse_base = (size_t)w.h * a.total + w.tok0;
   } else {
-    const int pair = g / a.ntile;
-    w.tile = g - pair * a.ntile;
+    int pair;
+    tile_order(g, a.nbatch * a.heads, a.ntile, pair, w.tile);
+    w.part = pair * a.ntile + w.tile;
     const int b = pair / a.heads;
     w.h = pair - b * a.heads;
     w.tok0 = b * a.seqlen;
@@ -571,7 +574,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       float t = 0.f;
       for (int x = 0; x < nbin; ++x)
         if (bkt[x] == b) t += bins[x];
-      a.part[(size_t)b * a.nwg + g] = t;
+      a.part[(size_t)b * a.nwg + w.part] = t;
     }
   }
 }
@@ -581,7 +584,9 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
 // ---------------------------------------------------------------------------
 // dtable[b, h] = sum of the partials of head h, one workgroup per (b, h):
 // strided per-thread sums, then a tree in LDS, both in a fixed order.
-// Partials are stored bucket-major, part[b * nwg + g].
+// Partials are stored bucket-major, part[b * nwg + slot]: the schedule
+// entry for packed batches, (batch * heads + head) * ntile + key tile for
+// dense ones.
 __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *part, const int4 *sched,
                                                             int nwg, int nbatch, int heads,
                                                             int ntile, float *dtable) {

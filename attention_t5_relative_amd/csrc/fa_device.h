@@ -94,6 +94,25 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return (b & 7) * per + (b >> 3);
 }
 
+// Dense grids: logical id g -> (pair, rank), pair = (batch, head) and rank 0
+// the heaviest tile of a pair (most key or query tiles to visit).  When the
+// pairs split evenly over the 8 XCDs, the ids an XCD receives (a contiguous
+// range, see xcd_remap) cover its own pairs rank-major, so each XCD
+// dispatches all its heaviest tiles first (longest-processing-time order);
+// with pair-major order the heaviest tiles of the last pairs would start last
+// and run nearly alone at the end.  Otherwise the order is pair-major.
+__device__ __forceinline__ void tile_order(int g, int npairs, int ntile, int &pair, int &rank) {
+  if ((npairs & 7) == 0) {
+    const int pp = npairs >> 3, per = pp * ntile;
+    const int x = g / per, r = g - x * per;
+    rank = r / pp;
+    pair = x * pp + (r - rank * pp);
+  } else {
+    pair = g / ntile;
+    rank = g - pair * ntile;
+  }
+}
+
 // T5 bucket of relative position r (key - query) from the integer thresholds.
 __device__ __forceinline__ int t5_bucket_dev(int r, const T5Geometry &g) {
   int off = 0, n;

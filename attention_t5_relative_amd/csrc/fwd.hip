@@ -82,8 +82,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
     qt = e.w;
     if (L <= 0) return;
   } else {
-    const int pair = g / a.nq;
-    qt = a.nq - 1 - (g - pair * a.nq);        // longest causal rows first
+    int pair, rank;
+    tile_order(g, a.nbatch * a.heads, a.nq, pair, rank);
+    qt = a.nq - 1 - rank;                     // longest causal rows first
     bidx = pair / a.heads;
     h = pair - bidx * a.heads;
     tok0 = bidx * a.seqlen;
