@@ -299,11 +299,14 @@ struct DkvTile {
 };
 
 // Dynamic LDS of the dkv kernel: the T5 bias table by distance, then
-// (with the table gradient) the bucket of each distance and 8 bin arrays.
+// (with the table gradient) the bucket of each distance, one array of
+// 2 * sat + 1 distance bins per wave, and one 32 x 33 fp32 scratch tile per
+// wave for the diagonal sums.
+constexpr int kTilePitch = 33;
 __host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
   if (!t5) return 0;
   const size_t n = (size_t)(2 * sat + 1);
-  return n * 4 + (dbias ? n * 4 + 8 * n * 4 : 0);
+  return n * 4 + (dbias ? n * 4 + 4 * n * 4 + 4 * 32 * kTilePitch * 4 : 0);
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
@@ -357,6 +360,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   int *bkt = reinterpret_cast<int *>(dyn + (2 * a.t5.sat + 1));
   float *bins = dyn + 2 * (2 * a.t5.sat + 1);
   const int nbin = 2 * a.t5.sat + 1;
+  float *const tiles = bins + 4 * nbin;
   if constexpr (BIAS == kBiasT5) {
     sat = a.t5.sat;
     for (int x = tid; x < nbin; x += NT) {
@@ -365,13 +369,14 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       if constexpr (DBIAS) {
         bkt[x] = b;
 #pragma unroll
-        for (int hw = 0; hw < 8; ++hw) bins[hw * nbin + x] = 0.f;
+        for (int w4 = 0; w4 < 4; ++w4) bins[w4 * nbin + x] = 0.f;
       }
     }
   }
   float slope_l2 = 0.f;
   if constexpr (BIAS == kBiasAlibi) slope_l2 = -a.slopes[h] * kLog2e;
-  float *const mybins = bins + (2 * wave + hl) * nbin;
+  float *const mybins = bins + wave * nbin;
+  float *const mytile = tiles + wave * (32 * kTilePitch);
 
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -482,9 +487,6 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
             const bool dead = (mask_c && rr > 0) || (mask_r && irow0 + 4 * hl + roff >= L) ||
                               (mask_k && myk >= L);
             p[e] = dead ? 0.f : __builtin_amdgcn_exp2f(t - l4[e]);
-            if constexpr (DBIAS) {
-              if (!dead) atomicAdd(&mybins[x], p[e] * (pacc[r] - d4[e]));
-            }
           }
           ds[r] = p[e] * (pacc[r] - d4[e]);
         }
@@ -497,6 +499,31 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
 #pragma unroll
           for (int r = 0; r < 16; ++r) t += ds[r];
           if (ulo <= 0) ub0 += t; else ub1 += t;
+        } else {
+          // Near the diagonal the bucket varies within the block, but it is
+          // constant along each diagonal (fixed key - query).  The block's
+          // dS goes to this wave's scratch tile rotated so that diagonal
+          // c (>= 0) and c - 32 share column c; lane (hl, c) then sums
+          // diagonal c (hl = 0) or c - 32 (hl = 1) - 64 distinct distances,
+          // so each lane owns one bin and no LDS atomics are needed.  Masked
+          // pairs carry dS = 0.  LDS operations of one wave complete in
+          // order, so no barrier separates the writes from the reads.
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
+            mytile[row * kTilePitch + ((il - row) & 31)] = ds[r];
+          }
+          const int lim = 32 - il;   // rows of diagonal il above the wrap
+          float gsum = 0.f;
+#pragma unroll
+          for (int row = 0; row < 32; ++row) {
+            const float val = mytile[row * kTilePitch + il];
+            gsum += ((row < lim) == (hl == 0)) ? val : 0.f;
+          }
+          const int dd = kw0 - irow0 + (hl ? il - 32 : il);   // key - query
+          if (dd <= -sat) ub0 += gsum;
+          else if (dd >= sat) ub1 += gsum;
+          else mybins[dd + sat] += gsum;
         }
       }
 
@@ -564,7 +591,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
     for (int x = tid; x < nbin; x += NT) {
       float t = 0.f;
 #pragma unroll
-      for (int hw = 0; hw < 8; ++hw) t += bins[hw * nbin + x];
+      for (int w4 = 0; w4 < 4; ++w4) t += bins[w4 * nbin + x];
       if (x == 0) t += ubin[0][0] + ubin[1][0] + ubin[2][0] + ubin[3][0];
       if (x == nbin - 1) t += ubin[0][1] + ubin[1][1] + ubin[2][1] + ubin[3][1];
       bins[x] = t;
