@@ -8,11 +8,11 @@
 //
 // Two kernels per call, each owning its outputs (no atomics):
 //   dq   query-parallel, forward-shaped (128 queries per workgroup, 32 per
-//        wave, 64-key tiles of K and V in LDS).  A first sweep over the keys
-//        recomputes P in fp32 with dP and forms D_i = sum_j P_ij dP_ij; the
-//        second sweep forms dS and accumulates dQ^T = K^T dS^T, reading K's
-//        operand with the transposing LDS read.  D is written for the dkv
-//        kernel.  D is taken from the recomputed P rather than from
+//        wave, 64-key tiles of K and V in LDS).  One sweep over the keys
+//        recomputes P in fp32 with dP, accumulates D_i = sum_j P_ij dP_ij,
+//        A = K^T (P o dP)^T and B = K^T P^T (K's operand by the transposing
+//        LDS read), and ends with dQ = scale (A - D B).  D is written for
+//        the dkv kernel.  D is taken from the recomputed P rather than from
 //        rowsum(dO * O) with a bf16 O, whose rounding would dominate the dQ
 //        and dK errors.
 //   dkv  key-parallel (128 keys per workgroup, 32 per wave): query blocks of
@@ -23,8 +23,9 @@
 //        transposing read.  The table gradient is binned by relative
 //        distance in per-half-wave LDS bins (whole saturated blocks in
 //        registers) and reduced in a fixed order.
-// In both, dS enters the dQ and dK products as a bf16 hi + lo pair (16
-// significant bits); with bf16 alone the gradients miss the accuracy gate.
+// The operands of the dQ and dK products (P o dP and P, or dS) enter the
+// MFMAs as bf16 hi + lo pairs (16 significant bits); with bf16 alone the
+// gradients miss the accuracy gate.
 #include "fa_device.h"
 
 namespace fa {
@@ -173,96 +174,101 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   const float c = a.scale_log2;
   const float dscale = a.scale;
 
-  float dsum = 0.f;   // first sweep: sum_j P_ij dP_ij (this lane's keys)
-  float Di = 0.f;     // second sweep: the full D_i
-  f32x16 qacc[D / 32];
+  // One sweep over the keys.  dQ_i = scale * sum_j P_ij (dP_ij - D_i) k_j
+  // needs D_i = sum_j P_ij dP_ij, known only after the last key, so it is
+  // accumulated as scale * (A_i - D_i B_i) with A_i = sum_j (P o dP)_ij k_j
+  // and B_i = sum_j P_ij k_j.  P o dP and P enter the MFMAs as bf16 hi + lo
+  // pairs (16 significant bits), which keeps A and B, and so their fp32
+  // difference, well inside the gradient's accuracy.
+  float dsum = 0.f;   // sum_j P_ij dP_ij over this lane's keys
+  f32x16 aacc[D / 32], bacc[D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) qacc[db] = f32x16{};
+  for (int db = 0; db < D / 32; ++db) {
+    aacc[db] = f32x16{};
+    bacc[db] = f32x16{};
+  }
 
   wait_vmem_loads();
-#pragma unroll 1
-  for (int sweep = 0; sweep < 2; ++sweep) {
-    if (nkt > 0) {
-      gload(rk, 0);
-      lstore(ks[0], KP);
-      gload(rv, 0);
-      lstore(vs[0], VP);
+  if (nkt > 0) {
+    gload(rk, 0);
+    lstore(ks[0], KP);
+    gload(rv, 0);
+    lstore(vs[0], VP);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int j0 = kt * BC;
+    const int buf = kt & 1;
+    const bool more = kt + 1 < nkt;
+    if (more) gload(rk, j0 + BC);
+    const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + 31));
+    f32x16 sacc[2], pacc[2];
+    if (active) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+        pacc[kb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8 *>(&ks[buf][koff + 32 * kb * KP + 16 * s]);
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8 *>(&vs[buf][voff + 32 * kb * VP + 16 * s]);
+          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+          pacc[kb] = mfma32(vf, df[s], pacc[kb]);
+        }
+      }
     }
-    __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int j0 = kt * BC;
-      const int buf = kt & 1;
-      const bool more = kt + 1 < nkt;
-      if (more) gload(rk, j0 + BC);
-      const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + 31));
-      f32x16 sacc[2], pacc[2];
-      if (active) {
+    if (more) {
+      lstore(ks[buf ^ 1], KP);
+      gload(rv, j0 + BC);
+    }
+    if (active) {
+      float bconst;
+      const bool fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut,
+                                                  slope_l2, bconst);
+      const float cc = fast ? c : 1.f;
+      const float sub = bconst - lse2;
+      // per 16-key group: P o dP and P as hi + lo fragments, consumed at once
+      // by A^T += K^T (P o dP)^T and B^T += K^T P^T, K's operand by
+      // transposing reads
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          sacc[kb] = f32x16{};
-          pacc[kb] = f32x16{};
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 kf =
-                *reinterpret_cast<const bf16x8 *>(&ks[buf][koff + 32 * kb * KP + 16 * s]);
-            const bf16x8 vf =
-                *reinterpret_cast<const bf16x8 *>(&vs[buf][voff + 32 * kb * VP + 16 * s]);
-            sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
-            pacc[kb] = mfma32(vf, df[s], pacc[kb]);
+        for (int u = 0; u < 2; ++u) {
+          uint32_t xh[4], xl[4], ph[4], pl[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * u + 2 * e;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], cc, sub));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], cc, sub));
+            const float x0 = p0 * pacc[kb][r], x1 = p1 * pacc[kb][r + 1];
+            dsum += x0 + x1;
+            split_hi_lo(x0, x1, xh[e], xl[e]);
+            split_hi_lo(p0, p1, ph[e], pl[e]);
+          }
+          const bf16x8 xhb = frag(xh), xlb = frag(xl), phb = frag(ph), plb = frag(pl);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16x8 kt8 =
+                lds_read_tr8(&ks[buf][ktro + (32 * kb + 16 * u) * KP + 32 * db], KP);
+            aacc[db] = mfma32(kt8, xhb, aacc[db]);
+            aacc[db] = mfma32(kt8, xlb, aacc[db]);
+            bacc[db] = mfma32(kt8, phb, bacc[db]);
+            bacc[db] = mfma32(kt8, plb, bacc[db]);
           }
         }
-      }
-      if (more) {
-        lstore(ks[buf ^ 1], KP);
-        gload(rv, j0 + BC);
-      }
-      if (active) {
-        float bconst;
-        const bool fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut,
-                                                    slope_l2, bconst);
-        const float cc = fast ? c : 1.f;
-        const float sub = bconst - lse2;
-        if (sweep == 0) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              dsum = fmaf(__builtin_amdgcn_exp2f(fmaf(sacc[kb][r], cc, sub)), pacc[kb][r], dsum);
-        } else {
-          // per 16-key group: dS (scaled) as hi + lo fragments, consumed at
-          // once by dQ^T += K^T dS^T, K's operand by transposing reads
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              uint32_t hw[4], lw[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 8 * u + 2 * e;
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], cc, sub));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], cc, sub));
-                split_hi_lo(p0 * (pacc[kb][r] - Di) * dscale,
-                            p1 * (pacc[kb][r + 1] - Di) * dscale, hw[e], lw[e]);
-              }
-              const bf16x8 hb = frag(hw), lb = frag(lw);
-#pragma unroll
-              for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 kt8 =
-                    lds_read_tr8(&ks[buf][ktro + (32 * kb + 16 * u) * KP + 32 * db], KP);
-                qacc[db] = mfma32(kt8, hb, qacc[db]);
-                qacc[db] = mfma32(kt8, lb, qacc[db]);
-              }
-            }
-        }
-      }
-      if (more) lstore(vs[buf ^ 1], VP);
-      __syncthreads();
     }
-    if (sweep == 0) {
-      Di = dsum + xor32(dsum);
-      if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = Di;
-    }
+    if (more) lstore(vs[buf ^ 1], VP);
+    __syncthreads();
   }
+  const float Di = half_sum(dsum);
+  if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = Di;
+  f32x16 qacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) qacc[db][r] = dscale * fmaf(-Di, bacc[db][r], aacc[db][r]);
 
   // dQ row myrow: lane holds dims 32db + 8(r/4) + 4hl + r%4
   if constexpr (ROPE) {
