@@ -468,36 +468,46 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
         bconst = lut[ulo + sat];
       }
       const bool fast = uniform && !mask_c && !mask_r && !mask_k;
-      float ds[16];
-      uint32_t pw[2][4];
+      // Element r: row irow0 + 8(r/4) + 4hl + r%4, key myk.  The fast/slow
+      // choice is made once per block, outside the element loops.
+      float lr[16], dr[16], p[16], ds[16];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse2s[buf][32 * rb + 8 * qq + 4 * hl]);
         const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dls[buf][32 * rb + 8 * qq + 4 * hl]);
-        float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * qq + e;
-          if (fast) {
-            p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, bconst - l4[e]));
-          } else {
-            const int roff = 8 * qq + e;
-            const int rr = myk - (irow0 + 4 * hl + roff);
-            float t = sacc[r] * c;
-            int x = 0;
-            if constexpr (BIAS == kBiasT5) {
-              x = min(max(rr, -sat), sat) + sat;
-              t += lut[x];
-            }
-            if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
-            const bool dead = (mask_c && rr > 0) || (mask_r && irow0 + 4 * hl + roff >= L) ||
-                              (mask_k && myk >= L);
-            p[e] = dead ? 0.f : __builtin_amdgcn_exp2f(t - l4[e]);
-          }
-          ds[r] = p[e] * (pacc[r] - d4[e]);
+          lr[4 * qq + e] = l4[e];
+          dr[4 * qq + e] = d4[e];
         }
-        pw[qq >> 1][2 * (qq & 1)] = pack_bf16x2(p[0], p[1]);
-        pw[qq >> 1][2 * (qq & 1) + 1] = pack_bf16x2(p[2], p[3]);
+      }
+      if (fast) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, bconst - lr[r]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int roff = 8 * (r >> 2) + (r & 3);
+          const int rr = myk - (irow0 + 4 * hl + roff);
+          float t = sacc[r] * c;
+          if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
+          if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+          // non-short-circuit operators keep this straight-line code
+          const bool dead = (mask_c & (rr > 0)) | (mask_r & (irow0 + 4 * hl + roff >= L)) |
+                            (mask_k & (myk >= L));
+          // the mask as an additive -inf (exp2(-inf) = 0): a select between
+          // the whole argument and -inf would be turned into a branch around
+          // the table read
+          p[r] = __builtin_amdgcn_exp2f((t - lr[r]) + (dead ? -INFINITY : 0.f));
+        }
+      }
+      uint32_t pw[2][4];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = p[r] * (pacc[r] - dr[r]);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        pw[qq >> 1][2 * (qq & 1)] = pack_bf16x2(p[4 * qq], p[4 * qq + 1]);
+        pw[qq >> 1][2 * (qq & 1) + 1] = pack_bf16x2(p[4 * qq + 2], p[4 * qq + 3]);
       }
       if constexpr (DBIAS) {
         if (fast) {
@@ -533,7 +543,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
         }
       }
 
-      // dV^T += dO^T P and dK^T += Q^T dS (scaled): P / dS from registers as
+      // dV^T += dO^T P and dK^T += Q^T dS (unscaled): P / dS from registers as
       // the B operand (k = the block's rows), dO^T / Q^T through transposing
       // reads of the row-major tiles.
 #pragma unroll
@@ -541,7 +551,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          split_hi_lo(ds[8 * u + 2 * e] * dscale, ds[8 * u + 2 * e + 1] * dscale, hw[e], lw[e]);
+          split_hi_lo(ds[8 * u + 2 * e], ds[8 * u + 2 * e + 1], hw[e], lw[e]);
         const bf16x8 pb = frag(pw[u]), hb = frag(hw), lb = frag(lw);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -558,6 +568,11 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
     __syncthreads();
   }
 
+  // dK = scale dS^T Q: the scale is applied once here
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkacc[db][r] *= dscale;
   // dK, dV of key myk: lane holds dims 32db + 8(r/4) + 4hl + r%4
   const rsrc_t rdv = make_rsrc(a.dv + base, nrec);
 #pragma unroll
