@@ -97,16 +97,21 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 // Dense grids: logical id g -> (pair, rank), pair = (batch, head) and rank 0
 // the heaviest tile of a pair (most key or query tiles to visit).  When the
 // pairs split evenly over the 8 XCDs, the ids an XCD receives (a contiguous
-// range, see xcd_remap) cover its own pairs rank-major, so each XCD
-// dispatches all its heaviest tiles first (longest-processing-time order);
-// with pair-major order the heaviest tiles of the last pairs would start last
-// and run nearly alone at the end.  Otherwise the order is pair-major.
+// range, see xcd_remap) cover its own pairs in groups of kPairGroup, each
+// group rank-major: heavy tiles start early (longest-processing-time order;
+// with plain pair-major order the heaviest tiles of the last pairs start last
+// and run nearly alone at the end), while the tiles running at any time
+// belong to few pairs, whose K and V stay in the XCD's L2.  Otherwise the
+// order is pair-major.
+constexpr int kPairGroup = 4;
 __device__ __forceinline__ void tile_order(int g, int npairs, int ntile, int &pair, int &rank) {
-  if ((npairs & 7) == 0) {
-    const int pp = npairs >> 3, per = pp * ntile;
+  const int pp = npairs >> 3;
+  if ((npairs & 7) == 0 && pp % kPairGroup == 0) {
+    const int per = pp * ntile, gsz = kPairGroup * ntile;
     const int x = g / per, r = g - x * per;
-    rank = r / pp;
-    pair = x * pp + (r - rank * pp);
+    const int gi = r / gsz, rg = r - gi * gsz;
+    rank = rg / kPairGroup;
+    pair = x * pp + gi * kPairGroup + (rg - rank * kPairGroup);
   } else {
     pair = g / ntile;
     rank = g - pair * ntile;
