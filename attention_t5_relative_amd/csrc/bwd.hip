@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   __shared__ __attribute__((aligned(16))) float lse2s[2][QB];
   __shared__ __attribute__((aligned(16))) float dls[2][QB];
   __shared__ float ubin[4][2];
-  extern __shared__ float dyn[];
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -511,35 +511,26 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       }
       if constexpr (DBIAS) {
         if (fast) {
-          float t = 0.f;
+          float t4[4];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t += ds[r];
+          for (int k = 0; k < 4; ++k) t4[k] = (ds[k] + ds[k + 4]) + (ds[k + 8] + ds[k + 12]);
+          const float t = (t4[0] + t4[1]) + (t4[2] + t4[3]);
           if (ulo <= 0) ub0 += t; else ub1 += t;
         } else {
           // Near the diagonal the bucket varies within the block, but it is
           // constant along each diagonal (fixed key - query).  The block's
           // dS goes to this wave's scratch tile rotated so that diagonal
-          // c (>= 0) and c - 32 share column c; lane (hl, c) then sums
-          // diagonal c (hl = 0) or c - 32 (hl = 1) - 64 distinct distances,
-          // so each lane owns one bin and no LDS atomics are needed.  Masked
-          // pairs carry dS = 0.  LDS operations of one wave complete in
-          // order, so no barrier separates the writes from the reads.
+          // c (>= 0) and c - 32 share column c; after the block's products,
+          // lane (hl, c) sums diagonal c (hl = 0) or c - 32 (hl = 1) - 64
+          // distinct distances, so each lane owns one bin and no LDS atomics
+          // are needed.  Masked pairs carry dS = 0.  LDS operations of one
+          // wave complete in order, so no barrier separates the writes from
+          // the reads.
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
             mytile[row * kTilePitch + ((il - row) & 31)] = ds[r];
           }
-          const int lim = 32 - il;   // rows of diagonal il above the wrap
-          float gsum = 0.f;
-#pragma unroll
-          for (int row = 0; row < 32; ++row) {
-            const float val = mytile[row * kTilePitch + il];
-            gsum += ((row < lim) == (hl == 0)) ? val : 0.f;
-          }
-          const int dd = kw0 - irow0 + (hl ? il - 32 : il);   // key - query
-          if (dd <= -sat) ub0 += gsum;
-          else if (dd >= sat) ub1 += gsum;
-          else mybins[dd + sat] += gsum;
         }
       }
 
@@ -561,6 +552,29 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
           dvacc[db] = mfma32(dot8, pb, dvacc[db]);
           dkacc[db] = mfma32(qt8, hb, dkacc[db]);
           dkacc[db] = mfma32(qt8, lb, dkacc[db]);
+        }
+      }
+      if constexpr (DBIAS) {
+        if (!fast) {
+          // column il of the rotated tile: rows below 32 - il belong to
+          // diagonal il, the others to il - 32; all 32 reads issue before the
+          // masked tree sum
+          float col[32];
+#pragma unroll
+          for (int row = 0; row < 32; ++row) col[row] = mytile[row * kTilePitch + il];
+          const int lim = 32 - il;
+#pragma unroll
+          for (int row = 0; row < 32; ++row)
+            col[row] = ((row < lim) == (hl == 0)) ? col[row] : 0.f;
+#pragma unroll
+          for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+            for (int k = 0; k < w; ++k) col[k] += col[k + w];
+          const float gsum = col[0];
+          const int dd = kw0 - irow0 + (hl ? il - 32 : il);   // key - query
+          if (dd <= -sat) ub0 += gsum;
+          else if (dd >= sat) ub1 += gsum;
+          else mybins[dd + sat] += gsum;
         }
       }
     }
@@ -618,10 +632,34 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       bins[x] = t;
     }
     __syncthreads();
+    // Bin x holds relative distance r = x - sat.  On each side of r = 0 the
+    // bucket is monotone in n = |r|, so bucket b covers one run of bins,
+    // found from the thresholds (bucket me + j covers thr[j-1] <= n <
+    // thr[j]); the bkt test keeps the sum exact whatever the run's ends.
     for (int b = tid; b < a.nb; b += NT) {
+      const T5Geometry &ge = a.t5;
+      const bool upper = ge.bidir && b >= ge.nbp;   // keys after the query
+      const int bl = upper ? b - ge.nbp : b;
+      int n0, n1;
+      if (bl < ge.me) {
+        n0 = n1 = bl;
+      } else {
+        const int j = bl - ge.me;
+        n0 = j == 0 ? ge.me : ge.thr[j - 1];
+        n1 = j < ge.nthr ? ge.thr[j] - 1 : sat;
+      }
+      n1 = min(n1, sat);
+      int x0, x1;   // inclusive bin range
+      if (upper) {
+        x0 = sat + max(n0, 1);
+        x1 = sat + n1;
+      } else {
+        x0 = sat - n1;
+        x1 = sat - n0;
+        if (!ge.bidir && b == 0) x1 = 2 * sat;   // unidirectional: r > 0 is bucket 0
+      }
       float t = 0.f;
-      for (int x = 0; x < nbin; ++x)
-        if (bkt[x] == b) t += bins[x];
+      for (int x = x0; x <= x1; ++x) t += bkt[x] == b ? bins[x] : 0.f;
       a.part[(size_t)b * a.nwg + w.part] = t;
     }
   }
