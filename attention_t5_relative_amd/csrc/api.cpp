@@ -353,7 +353,7 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
 }
 
 fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void *v,
-                  const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                  const void *o, const float *lse, const void *dout, void *dq, void *dk, void *dv,
                   float *dtable, void *ws, size_t ws_bytes, hipStream_t s) {
   const BwdLayout L = bwd_layout(p, dtable != nullptr);
   if (L.total > 0 && (ws == nullptr || ws_bytes < L.total))
@@ -373,6 +373,7 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   b.q = q;
   b.k = k;
   b.v = v;
+  b.o = o;
   b.dout = dout;
   b.lse = lse;
   b.dq = dq;
@@ -504,16 +505,16 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *ws, size_t ws_bytes
 fa_status fa_bwd(const fa_bwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
   const fa_status st = fa_check_bwd(p);
   if (st != FA_OK) return st;
-  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.lse, p->dout, p->dq, p->dk,
-                 p->dv, p->dtable, ws, ws_bytes, stream);
+  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dout, p->dq,
+                 p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
 }
 
 fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes,
                         hipStream_t stream) {
   const fa_status st = fa_check_varlen_bwd(p);
   if (st != FA_OK) return st;
-  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.lse, p->dout, p->dq, p->dk,
-                 p->dv, p->dtable, ws, ws_bytes, stream);
+  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dout, p->dq,
+                 p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
 }
 
 fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t max_distance,

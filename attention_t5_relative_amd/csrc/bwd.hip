@@ -9,12 +9,13 @@
 // Two kernels per call, each owning its outputs (no atomics):
 //   dq   query-parallel, forward-shaped (128 queries per workgroup, 32 per
 //        wave, 64-key tiles of K and V in LDS).  One sweep over the keys
-//        recomputes P in fp32 with dP, accumulates D_i = sum_j P_ij dP_ij,
-//        A = K^T (P o dP)^T and B = K^T P^T (K's operand by the transposing
-//        LDS read), and ends with dQ = scale (A - D B).  D is written for
-//        the dkv kernel.  D is taken from the recomputed P rather than from
-//        rowsum(dO * O) with a bf16 O, whose rounding would dominate the dQ
-//        and dK errors.
+//        recomputes P in fp32 with dP.  About a centre Dc_i = dO_i . O_i
+//        (bf16 O) it accumulates D_i - Dc_i = sum_j P_ij (dP_ij - Dc_i),
+//        A = K^T (P o (dP - Dc))^T and B = K^T P^T (K's operand by the
+//        transposing LDS read), and ends with dQ = scale (A - (D - Dc) B).
+//        D = Dc + (D - Dc) is written for the dkv kernel: it comes from the
+//        recomputed P, so O's bf16 rounding, which would dominate the dQ and
+//        dK errors if D were rowsum(dO * O), cancels.
 //   dkv  key-parallel (128 keys per workgroup, 32 per wave): query blocks of
 //        Q, dO (row-major) and their LSE and D go through double-buffered LDS;
 //        S = Q K^T puts each lane on one key, so P and dS serve as MFMA B
@@ -23,8 +24,8 @@
 //        transposing read.  The table gradient is binned by relative
 //        distance in per-half-wave LDS bins (whole saturated blocks in
 //        registers) and reduced in a fixed order.
-// The operands of the dQ and dK products (P o dP and P, or dS) enter the
-// MFMAs as bf16 hi + lo pairs (16 significant bits); with bf16 alone the
+// The large operands of the dQ and dK products (P o (dP - Dc), or dS) enter
+// the MFMAs as bf16 hi + lo pairs (16 significant bits); with bf16 alone the
 // gradients miss the accuracy gate.
 #include "fa_device.h"
 
@@ -37,7 +38,7 @@ constexpr int BC = 64;     // dq: keys per tile
 constexpr int BKV = 128;   // dkv: keys per workgroup
 
 struct BwdArgs {
-  const uint16_t *q, *k, *v, *dout;
+  const uint16_t *q, *k, *v, *o, *dout;
   const float *lse;
   uint16_t *dq, *dk, *dv;  // bf16 outputs
   float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
@@ -126,6 +127,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   const rsrc_t rk = make_rsrc(a.k + base, nrec);
   const rsrc_t rv = make_rsrc(a.v + base, nrec);
   const rsrc_t rdo = make_rsrc(a.dout + base, nrec);
+  const rsrc_t ro = make_rsrc(a.o + base, nrec);
 
   const int q0 = qt * BR;
   const int wrow0 = q0 + 32 * wave;
@@ -133,11 +135,13 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   const bool wave_live = wrow0 < L;
 
   bf16x8 qf[D / 16], df[D / 16];
+  i32x4 of[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const uint32_t off = ((uint32_t)myrow * (uint32_t)HD + 16 * s + 8 * hl) * 2u;
     qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
     df[s] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+    of[s] = buf_load16(ro, off);
   }
   const float lse2 = myrow < L ? a.lse[w.lse_base + myrow] * kLog2e : 0.f;
 
@@ -176,11 +180,13 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
 
   // One sweep over the keys.  dQ_i = scale * sum_j P_ij (dP_ij - D_i) k_j
   // needs D_i = sum_j P_ij dP_ij, known only after the last key, so it is
-  // accumulated as scale * (A_i - D_i B_i) with A_i = sum_j (P o dP)_ij k_j
-  // and B_i = sum_j P_ij k_j.  P o dP and P enter the MFMAs as bf16 hi + lo
-  // pairs (16 significant bits), which keeps A and B, and so their fp32
-  // difference, well inside the gradient's accuracy.
-  float dsum = 0.f;   // sum_j P_ij dP_ij over this lane's keys
+  // accumulated about a per-row centre Dc_i known up front:
+  //   dQ_i = scale * (A_i - (D_i - Dc_i) B_i),
+  //   A_i = sum_j P_ij (dP_ij - Dc_i) k_j,  B_i = sum_j P_ij k_j,
+  // with D_i - Dc_i = sum_j P_ij (dP_ij - Dc_i) (rows of P sum to one).
+  // A's operand enters the MFMAs as a bf16 hi + lo pair (16 significant
+  // bits); B's as bf16 alone, as its factor D_i - Dc_i is tiny.
+  float dsum = 0.f;   // sum_j P_ij (dP_ij - Dc_i) over this lane's keys
   f32x16 aacc[D / 32], bacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -189,6 +195,22 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   }
 
   wait_vmem_loads();
+  // Centre Dc_i = dO_i . O_i from the bf16 O: it differs from D_i by O's
+  // rounding only, so P o (dP - Dc) and the D_i - Dc_i that multiplies B are
+  // both small.  Any finite Dc gives the same result up to rounding; a
+  // non-finite one (O not the forward's output) falls back to 0.
+  float dc = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const i32x4 d4 = __builtin_bit_cast(i32x4, df[s]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dc = fmaf(bf16_lo((uint32_t)of[s][e]), bf16_lo((uint32_t)d4[e]), dc);
+      dc = fmaf(bf16_hi((uint32_t)of[s][e]), bf16_hi((uint32_t)d4[e]), dc);
+    }
+  }
+  dc = half_sum(dc);
+  if ((__builtin_bit_cast(uint32_t, dc) & 0x7f800000u) == 0x7f800000u) dc = 0.f;
   if (nkt > 0) {
     gload(rk, 0);
     lstore(ks[0], KP);
@@ -229,25 +251,25 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
                                                   slope_l2, bconst);
       const float cc = fast ? c : 1.f;
       const float sub = bconst - lse2;
-      // per 16-key group: P o dP and P as hi + lo fragments, consumed at once
-      // by A^T += K^T (P o dP)^T and B^T += K^T P^T, K's operand by
-      // transposing reads
+      // per 16-key group: P o (dP - Dc) as hi + lo fragments and P as bf16,
+      // consumed at once by A^T += K^T (P o (dP - Dc))^T and B^T += K^T P^T,
+      // K's operand by transposing reads
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          uint32_t xh[4], xl[4], ph[4], pl[4];
+          uint32_t xh[4], xl[4], ph[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 8 * u + 2 * e;
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], cc, sub));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], cc, sub));
-            const float x0 = p0 * pacc[kb][r], x1 = p1 * pacc[kb][r + 1];
+            const float x0 = p0 * (pacc[kb][r] - dc), x1 = p1 * (pacc[kb][r + 1] - dc);
             dsum += x0 + x1;
             split_hi_lo(x0, x1, xh[e], xl[e]);
-            split_hi_lo(p0, p1, ph[e], pl[e]);
+            ph[e] = pack_bf16x2(p0, p1);
           }
-          const bf16x8 xhb = frag(xh), xlb = frag(xl), phb = frag(ph), plb = frag(pl);
+          const bf16x8 xhb = frag(xh), xlb = frag(xl), phb = frag(ph);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             const bf16x8 kt8 =
@@ -255,20 +277,19 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
             aacc[db] = mfma32(kt8, xhb, aacc[db]);
             aacc[db] = mfma32(kt8, xlb, aacc[db]);
             bacc[db] = mfma32(kt8, phb, bacc[db]);
-            bacc[db] = mfma32(kt8, plb, bacc[db]);
           }
         }
     }
     if (more) lstore(vs[buf ^ 1], VP);
     __syncthreads();
   }
-  const float Di = half_sum(dsum);
-  if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = Di;
+  const float dd = half_sum(dsum);   // D_i - Dc_i
+  if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = dc + dd;
   f32x16 qacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) qacc[db][r] = dscale * fmaf(-Di, bacc[db][r], aacc[db][r]);
+    for (int r = 0; r < 16; ++r) qacc[db][r] = dscale * fmaf(-dd, bacc[db][r], aacc[db][r]);
 
   // dQ row myrow: lane holds dims 32db + 8(r/4) + 4hl + r%4
   if constexpr (ROPE) {
@@ -775,6 +796,7 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.q = static_cast<const uint16_t *>(b.q);
   a.k = static_cast<const uint16_t *>(b.k);
   a.v = static_cast<const uint16_t *>(b.v);
+  a.o = static_cast<const uint16_t *>(b.o);
   a.dout = static_cast<const uint16_t *>(b.dout);
   a.lse = b.lse;
   a.dq = static_cast<uint16_t *>(b.dq);

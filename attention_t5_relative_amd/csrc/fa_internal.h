@@ -53,6 +53,7 @@ struct FwdBuffers {
 
 struct BwdBuffers {
   const void *q, *k, *v;   // bf16 (rotated when RoPE is on)
+  const void *o;           // bf16 forward output (centres the dq accumulation)
   const void *dout;
   const float *lse;
   void *dq, *dk, *dv;      // bf16 outputs

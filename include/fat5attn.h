@@ -108,10 +108,11 @@ typedef struct {
   fa_bias bias;
 } fa_fwd_params;
 
-/* Dense backward.  `f` describes the forward; f.lse is READ here (the
- * forward's output for the same inputs).  f.o is checked like in the forward
- * but not read: D_i = sum_j P_ij dP_ij is recomputed from fp32 P instead of
- * taken from the bf16 O.  dout [B, S, H, D] bf16 in; dq, dk,
+/* Dense backward.  `f` describes the forward; f.lse and f.o are READ here
+ * (the forward's outputs for the same inputs).  D_i = sum_j P_ij dP_ij is
+ * recomputed from fp32 P; dO_i . O_i only centres that sum, so an O other than
+ * the forward's costs accuracy, not correctness (a non-finite centre is
+ * dropped).  dout [B, S, H, D] bf16 in; dq, dk,
  * dv [B, S, H, D] bf16 out; dtable fp32 [num_buckets, H] out (T5 only, may be
  * NULL to skip the bias gradient): the sum over the batch and over every
  * visible (query, key) pair in bucket b of dL/dS'. */

@@ -7,7 +7,8 @@ import torch
 
 import oracle
 import synth
-from helpers import (assert_dtable, assert_grad, assert_o, bf16_tensor, oracle_kwargs, to_f64)
+from helpers import (assert_dtable, assert_grad, assert_o, bf16_tensor, norm_err, oracle_kwargs,
+                     to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +31,7 @@ def _bias(kind, H, table, nb, md, bidirectional):
 
 
 def run_dense_bwd(inp, *, causal, kind, scale, bidirectional=True, rope_base=None, nb=32,
-                  md=128, want_dtable=True):
+                  md=128, want_dtable=True, o_for_bwd=None):
     q, k, v, do = (bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do"))
     B, S, H, D = q.shape
     bias, slopes = _bias(kind, H, inp.table, nb, md, bidirectional)
@@ -40,7 +41,8 @@ def run_dense_bwd(inp, *, causal, kind, scale, bidirectional=True, rope_base=Non
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     dtable = (torch.full((nb, H), float("nan"), device="cuda")
               if (kind == "t5" and want_dtable) else None)
-    fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, scale=scale, causal=causal, bias=bias,
+    o_in = o if o_for_bwd is None else o_for_bwd(o)
+    fa.fa_bwd(q, k, v, o_in, lse, do, dq, dk, dv, dtable, scale=scale, causal=causal, bias=bias,
               rope_base=rope_base or 0.0)
     torch.cuda.synchronize()
     kw = oracle_kwargs(kind, causal, scale, inp.table, slopes, nb, md, bidirectional, rope_base)
@@ -82,6 +84,32 @@ def test_backward_small(case):
         assert_dtable(out["dtable"], dtab)
         # sum over buckets of a head's gradient is zero (rows of dS sum to zero)
         assert np.abs(out["dtable"].sum(axis=0)).max() <= 1e-3 * np.abs(dtab).max() + 1e-4
+
+
+def test_backward_o_only_centres():
+    """The backward reads O only as the centre dO.O of its D accumulation.
+    With another O, dK, dV and the table gradient still meet the gate (D
+    itself is summed in fp32 from the recomputed P); dQ keeps a bounded
+    error (its B = sum P k enters as bf16 and is multiplied by D - dO.O, no
+    longer small); a non-finite centre is replaced by 0, bit for bit."""
+    inp = synth.draw_dense(77, 1, 300, 2, 64)
+    ref = oracle.attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do"),
+                               **oracle_kwargs("t5", True, 1.0, inp.table, None, 32, 128, False))
+    runs = {}
+    for kind, alter in (("zero", torch.zeros_like),
+                        ("nan", lambda o: torch.full_like(o, float("nan"))),
+                        ("scaled", lambda o: (o.float() * 1.25).to(o.dtype))):
+        out, _ = run_dense_bwd(inp, causal=True, kind="t5", scale=1.0, bidirectional=False,
+                               o_for_bwd=alter)
+        runs[kind] = out
+        dq, dk, dv, dtab = ref
+        assert_grad(out["dk"], dk, f"dK ({kind} O)")
+        assert_grad(out["dv"], dv, f"dV ({kind} O)")
+        assert_dtable(out["dtable"], dtab, f"dtable ({kind} O)")
+        assert np.isfinite(out["dq"]).all()
+        assert norm_err(out["dq"], dq)[0] <= 0.25, f"dQ ({kind} O)"
+    for name in ("dq", "dk", "dv", "dtable"):
+        assert np.array_equal(runs["nan"][name], runs["zero"][name]), name
 
 
 @pytest.mark.parametrize("name,heads", [("c2", [0, 11]), ("c3", [3])])
