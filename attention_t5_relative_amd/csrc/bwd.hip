@@ -42,7 +42,7 @@ struct BwdArgs {
   const float *lse;
   uint16_t *dq, *dk, *dv;  // bf16 outputs
   float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
-  float *delta;            // same layout as lse
+  float *delta;            // -D_i, same layout as lse
   float *part;             // [nb, nwg] table-gradient partials
   const int4 *sched;       // packed batches: {token0, length, head, tile}
   const float *table, *slopes;
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
     __syncthreads();
   }
   const float dd = half_sum(dsum);   // D_i - Dc_i
-  if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = dc + dd;
+  if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = -(dc + dd);
   f32x16 qacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -322,31 +322,31 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
 template <int D>
 struct DkvTile {
   static constexpr int QB = (D == 64) ? 64 : 32;   // query rows per block
-  static constexpr int QP = D + 16;                // pitch of the Q / dO rows
 };
 
 // Dynamic LDS of the dkv kernel: the T5 bias table by distance, then
 // (with the table gradient) the bucket of each distance, one array of
-// 2 * sat + 1 distance bins per wave, and one 32 x 33 fp32 scratch tile per
-// wave for the diagonal sums.
-constexpr int kTilePitch = 33;
+// 2 * sat + 1 distance bins per wave, and one 32 x 40 fp32 scratch tile per
+// wave for the diagonal sums, with kTileGuard floats on either side of the
+// tiles (the diagonal reads of masked-out rows reach up to 32 floats past a
+// tile; their values are discarded).
+constexpr int kTilePitch = 40;
+constexpr int kTileGuard = 32;
 __host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
   if (!t5) return 0;
   const size_t n = (size_t)(2 * sat + 1);
-  return n * 4 + (dbias ? n * 4 + 4 * n * 4 + 4 * 32 * kTilePitch * 4 : 0);
+  return n * 4 + (dbias ? n * 4 + 4 * n * 4 + (4 * 32 * kTilePitch + 2 * kTileGuard) * 4 : 0);
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
 __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdArgs a) {
-  constexpr int QB = DkvTile<D>::QB, QP = DkvTile<D>::QP;
-  constexpr int NCH = D / 8;
-  constexpr int LOADS = QB * NCH / NT;     // Q (and dO) chunks per thread per block
-  static_assert(LOADS * NT == QB * NCH, "block split");
-
-  __shared__ __attribute__((aligned(16))) uint16_t qs[2][QB * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t dos[2][QB * QP];
-  __shared__ __attribute__((aligned(16))) float lse2s[2][QB];
-  __shared__ __attribute__((aligned(16))) float dls[2][QB];
+  constexpr int QB = DkvTile<D>::QB;
+  // Q and dO blocks as swizzled tiles (see swz), with the rows' LSE and -D
+  // (64 entries: the 4-byte copy fills one per lane)
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][QB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dos[2][QB * D];
+  __shared__ __attribute__((aligned(16))) float lses[2][64];
+  __shared__ __attribute__((aligned(16))) float ndls[2][64];
   __shared__ float ubin[4][2];
   extern __shared__ __attribute__((aligned(16))) float dyn[];
 
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   int *bkt = reinterpret_cast<int *>(dyn + (2 * a.t5.sat + 1));
   float *bins = dyn + 2 * (2 * a.t5.sat + 1);
   const int nbin = 2 * a.t5.sat + 1;
-  float *const tiles = bins + 4 * nbin;
+  float *const tiles = bins + 4 * nbin + kTileGuard;
   if constexpr (BIAS == kBiasT5) {
     sat = a.t5.sat;
     for (int x = tid; x < nbin; x += NT) {
@@ -418,188 +418,250 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   const int nqb = (L + QB - 1) / QB;
   const int qb_first = CAUSAL ? (kt0 / QB) : 0;
 
-  i32x4 qreg[LOADS], dreg[LOADS];
-  float lsev = 0.f, dlv = 0.f;
-  auto gload = [&](int q0) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int cc = tid + NT * u, row = cc / NCH, col = cc % NCH;
-      const uint32_t off = ((uint32_t)(q0 + row) * (uint32_t)HD + col * 8) * 2u;
-      qreg[u] = buf_load16(rq, off);
-      dreg[u] = buf_load16(rdo, off);
-    }
-    if (tid < QB) {
-      const int row = q0 + tid;
-      lsev = row < L ? a.lse[w.lse_base + row] * kLog2e : 0.f;
-      dlv = row < L ? a.delta[w.lse_base + row] : 0.f;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int cc = tid + NT * u, row = cc / NCH, col = cc % NCH;
-      *reinterpret_cast<i32x4 *>(&qs[buf][row * QP + col * 8]) = qreg[u];
-      *reinterpret_cast<i32x4 *>(&dos[buf][row * QP + col * 8]) = dreg[u];
-    }
-    if (tid < QB) {
-      lse2s[buf][tid] = lsev;
-      dls[buf][tid] = dlv;
-    }
+  // one query block to LDS by buffer-to-LDS copies: Q and dO tiles split
+  // over the four waves, LSE and -D one 4-byte copy each
+  const i32x4 dq_src = dma_desc(a.q + base, nrec), ddo_src = dma_desc(a.dout + base, nrec);
+  const i32x4 dlse_src = dma_desc(a.lse + w.lse_base, (uint32_t)L * 4u);
+  const i32x4 dnd_src = dma_desc(a.delta + w.lse_base, (uint32_t)L * 4u);
+  auto fill = [&](int q0, int buf) {
+    dma_tile<D, QB, 4>(dq_src, HD, q0, qs[buf], wave, lane);
+    dma_tile<D, QB, 4>(ddo_src, HD, q0, dos[buf], wave, lane);
+    if (wave == 0) dma4(dlse_src, (uint32_t)(q0 + lane) * 4u, lses[buf]);
+    if (wave == 1) dma4(dnd_src, (uint32_t)(q0 + lane) * 4u, ndls[buf]);
   };
 
-  const int aoff = il * QP + 8 * hl;            // row-wise A operand
-  const int troff = tr_lane_offset(lane, QP);   // transposed A operand
-
-  if (qb_first < nqb) {
-    gload(qb_first * QB);
-    lstore(0);
+  // row-wise A operand: row il, chunk 2s + hl; transposed A operand: the
+  // two halves of each 16-row group, per 32-column block
+  int aof[D / 16], tro[D / 32][2];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) aof[s] = swz_off<D>(il, 2 * s + hl);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    tro[db][0] = swz_tr_off<D>(lane, 0, db);
+    tro[db][1] = swz_tr_off<D>(lane, 1, db);
   }
+
+  if (qb_first < nqb) fill(qb_first * QB, 0);
   wait_vmem_loads();
   __syncthreads();
+  // S and dP - D of one 32-row block: each lane holds key myk and rows
+  // irow0 + 8(r/4) + 4hl + r%4.  The dP accumulator starts at -D_i, read
+  // from LDS straight into the MFMA's C operand.
+  auto block_sdp = [&](int buf, int rb, f32x16 &sacc, f32x16 &pacc) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&ndls[buf][32 * rb + 8 * qq + 4 * hl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pacc[4 * qq + e] = d4[e];
+    }
+    sacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const int at = aof[s] + 32 * rb * D;
+      sacc = mfma32(*reinterpret_cast<const bf16x8 *>(&qs[buf][at]), kf[s], sacc);
+      pacc = mfma32(*reinterpret_cast<const bf16x8 *>(&dos[buf][at]), vf[s], pacc);
+    }
+  };
+  // P of a block whose bias is the constant bconst and that has no mask
+  auto block_p_fast = [&](int buf, int rb, const f32x16 &sacc, float bconst, float (&p)[16]) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lses[buf][32 * rb + 8 * qq + 4 * hl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p[4 * qq + e] =
+            __builtin_amdgcn_exp2f(fmaf(sacc[4 * qq + e], c, fmaf(-l4[e], kLog2e, bconst)));
+    }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS (unscaled): P / dS from registers as
+  // the B operand (k = the block's rows), dO^T / Q^T through transposing
+  // reads of the row-major tiles.
+  auto block_dvdk = [&](int buf, int rb, const float (&p)[16], const float (&ds)[16]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t pw[4], hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pw[e] = pack_bf16x2(p[8 * u + 2 * e], p[8 * u + 2 * e + 1]);
+        split_hi_lo(ds[8 * u + 2 * e], ds[8 * u + 2 * e + 1], hw[e], lw[e]);
+      }
+      const bf16x8 pb = frag(pw), hb = frag(hw), lb = frag(lw);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int at = (32 * rb + 16 * u) * D;
+        const bf16x8 dot8 = lds_read_tr8_at(&dos[buf][at], tro[db][0], tro[db][1]);
+        const bf16x8 qt8 = lds_read_tr8_at(&qs[buf][at], tro[db][0], tro[db][1]);
+        dvacc[db] = mfma32(dot8, pb, dvacc[db]);
+        dkacc[db] = mfma32(qt8, hb, dkacc[db]);
+        dkacc[db] = mfma32(qt8, lb, dkacc[db]);
+      }
+    }
+  };
+
   for (int qb = qb_first; qb < nqb; ++qb) {
     const int q0 = qb * QB;
     const int buf = (qb - qb_first) & 1;
     const bool more = qb + 1 < nqb;
-    if (more) gload(q0 + QB);
+    if (more) fill(q0 + QB, buf ^ 1);
 
+    // Whole query block unmasked with one bias value: straight-line code
+    // over its row blocks, so that one block's softmax can issue while the
+    // other's products run.
+    // (head_dim 128 has one row block per query block: no gain there)
+    bool qfast = QB / 32 >= 2 && wave_live && q0 + QB <= L && kw0 + 32 <= L &&
+                 (!CAUSAL || kw0 + 31 <= q0);
+    float qconst = 0.f;
+    int qlo = 0;
+    if constexpr (BIAS == kBiasT5) {
+      qlo = min(max(kw0 - (q0 + QB - 1), -sat), sat);
+      const int qhi = min(max(kw0 + 31 - q0, -sat), sat);
+      qfast = qfast && qlo == qhi;
+      qconst = lut[qlo + sat];
+    } else if constexpr (BIAS == kBiasAlibi) {
+      qfast = false;
+    }
+    if (qfast) {
+      // order: S/dP(0), softmax(0), S/dP(1), dV/dK(0), softmax(1), dV/dK(1)
+      float tsum = 0.f;
+      float p[QB / 32][16], ds[QB / 32][16];
+      auto soft = [&](int rb, const f32x16 &sacc, const f32x16 &pacc) {
+        block_p_fast(buf, rb, sacc, qconst, p[rb]);
 #pragma unroll
-    for (int rb = 0; rb < QB / 32; ++rb) {
-      const int irow0 = q0 + 32 * rb;
-      const bool active = wave_live && irow0 < L && (!CAUSAL || kw0 <= irow0 + 31);
-      if (!active) continue;
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int at = aoff + 32 * rb * QP + 16 * s;
-        sacc = mfma32(*reinterpret_cast<const bf16x8 *>(&qs[buf][at]), kf[s], sacc);
-        pacc = mfma32(*reinterpret_cast<const bf16x8 *>(&dos[buf][at]), vf[s], pacc);
-      }
-      // element r: row irow0 + 8(r/4) + 4hl + r%4, key myk
-      const int rmin = kw0 - (irow0 + 31), rmax = kw0 + 31 - irow0;
-      const bool mask_c = CAUSAL && rmax > 0;
-      const bool mask_r = irow0 + 32 > L;
-      const bool mask_k = kw0 + 32 > L;
-      bool uniform = (BIAS == kBiasNone);
-      float bconst = 0.f;
-      int ulo = 0;
-      if constexpr (BIAS == kBiasT5) {
-        ulo = min(max(rmin, -sat), sat);
-        const int uhi = min(max(rmax, -sat), sat);
-        uniform = (ulo == uhi);
-        bconst = lut[ulo + sat];
-      }
-      const bool fast = uniform && !mask_c && !mask_r && !mask_k;
-      // Element r: row irow0 + 8(r/4) + 4hl + r%4, key myk.  The fast/slow
-      // choice is made once per block, outside the element loops.
-      float lr[16], dr[16], p[16], ds[16];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse2s[buf][32 * rb + 8 * qq + 4 * hl]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dls[buf][32 * rb + 8 * qq + 4 * hl]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lr[4 * qq + e] = l4[e];
-          dr[4 * qq + e] = d4[e];
-        }
-      }
-      if (fast) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, bconst - lr[r]));
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int roff = 8 * (r >> 2) + (r & 3);
-          const int rr = myk - (irow0 + 4 * hl + roff);
-          float t = sacc[r] * c;
-          if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
-          if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
-          // non-short-circuit operators keep this straight-line code
-          const bool dead = (mask_c & (rr > 0)) | (mask_r & (irow0 + 4 * hl + roff >= L)) |
-                            (mask_k & (myk >= L));
-          // the mask as an additive -inf (exp2(-inf) = 0): a select between
-          // the whole argument and -inf would be turned into a branch around
-          // the table read
-          p[r] = __builtin_amdgcn_exp2f((t - lr[r]) + (dead ? -INFINITY : 0.f));
-        }
-      }
-      uint32_t pw[2][4];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] = p[r] * (pacc[r] - dr[r]);
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        pw[qq >> 1][2 * (qq & 1)] = pack_bf16x2(p[4 * qq], p[4 * qq + 1]);
-        pw[qq >> 1][2 * (qq & 1) + 1] = pack_bf16x2(p[4 * qq + 2], p[4 * qq + 3]);
-      }
-      if constexpr (DBIAS) {
-        if (fast) {
+        for (int r = 0; r < 16; ++r) ds[rb][r] = p[rb][r] * pacc[r];
+        if constexpr (DBIAS) {
           float t4[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) t4[k] = (ds[k] + ds[k + 4]) + (ds[k + 8] + ds[k + 12]);
-          const float t = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-          if (ulo <= 0) ub0 += t; else ub1 += t;
-        } else {
-          // Near the diagonal the bucket varies within the block, but it is
-          // constant along each diagonal (fixed key - query).  The block's
-          // dS goes to this wave's scratch tile rotated so that diagonal
-          // c (>= 0) and c - 32 share column c; after the block's products,
-          // lane (hl, c) sums diagonal c (hl = 0) or c - 32 (hl = 1) - 64
-          // distinct distances, so each lane owns one bin and no LDS atomics
-          // are needed.  Masked pairs carry dS = 0.  LDS operations of one
-          // wave complete in order, so no barrier separates the writes from
-          // the reads.
+          for (int k = 0; k < 4; ++k)
+            t4[k] = (ds[rb][k] + ds[rb][k + 4]) + (ds[rb][k + 8] + ds[rb][k + 12]);
+          tsum += (t4[0] + t4[1]) + (t4[2] + t4[3]);
+        }
+      };
+      {
+        f32x16 sacc, pacc;
+        block_sdp(buf, 0, sacc, pacc);
+        soft(0, sacc, pacc);
+      }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
-            mytile[row * kTilePitch + ((il - row) & 31)] = ds[r];
+      for (int rb = 1; rb < QB / 32; ++rb) {
+        f32x16 sacc, pacc;
+        block_sdp(buf, rb, sacc, pacc);
+        block_dvdk(buf, rb - 1, p[rb - 1], ds[rb - 1]);
+        soft(rb, sacc, pacc);
+      }
+      block_dvdk(buf, QB / 32 - 1, p[QB / 32 - 1], ds[QB / 32 - 1]);
+      if constexpr (DBIAS) {
+        if (qlo <= 0) ub0 += tsum; else ub1 += tsum;
+      }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < QB / 32; ++rb) {
+        const int irow0 = q0 + 32 * rb;
+        const bool active = wave_live && irow0 < L && (!CAUSAL || kw0 <= irow0 + 31);
+        if (!active) continue;
+        f32x16 sacc, pacc;
+        block_sdp(buf, rb, sacc, pacc);
+        const int rmin = kw0 - (irow0 + 31), rmax = kw0 + 31 - irow0;
+        const bool mask_c = CAUSAL && rmax > 0;
+        const bool mask_r = irow0 + 32 > L;
+        const bool mask_k = kw0 + 32 > L;
+        bool uniform = (BIAS == kBiasNone);
+        float bconst = 0.f;
+        int ulo = 0;
+        if constexpr (BIAS == kBiasT5) {
+          ulo = min(max(rmin, -sat), sat);
+          const int uhi = min(max(rmax, -sat), sat);
+          uniform = (ulo == uhi);
+          bconst = lut[ulo + sat];
+        }
+        const bool fast = uniform && !mask_c && !mask_r && !mask_k;
+        // The fast/slow choice is made once per block, outside the element
+        // loops.
+        float p[16], ds[16];
+        if (fast) {
+          block_p_fast(buf, rb, sacc, bconst, p);
+        } else {
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 l4 =
+                *reinterpret_cast<const f32x4 *>(&lses[buf][32 * rb + 8 * qq + 4 * hl]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * qq + e;
+              const int roff = 8 * qq + e;
+              const int rr = myk - (irow0 + 4 * hl + roff);
+              float t = sacc[r] * c;
+              if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
+              if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+              // non-short-circuit operators keep this straight-line code
+              const bool dead = (mask_c & (rr > 0)) | (mask_r & (irow0 + 4 * hl + roff >= L)) |
+                                (mask_k & (myk >= L));
+              // the mask as an additive -inf (exp2(-inf) = 0): a select
+              // between the whole argument and -inf would be turned into a
+              // branch around the table read
+              p[r] = __builtin_amdgcn_exp2f(fmaf(-l4[e], kLog2e, t) + (dead ? -INFINITY : 0.f));
+            }
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = p[r] * pacc[r];
+        if constexpr (DBIAS) {
+          if (fast) {
+            float t4[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) t4[k] = (ds[k] + ds[k + 4]) + (ds[k + 8] + ds[k + 12]);
+            const float t = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+            if (ulo <= 0) ub0 += t; else ub1 += t;
+          } else {
+            // Near the diagonal the bucket varies within the block, but it
+            // is constant along each diagonal (fixed key - query).  The
+            // block's dS goes to this wave's scratch tile, row = query,
+            // column = key; after the block's products, lane (hl, c) sums
+            // diagonal c (hl = 0: entries (row, row + c)) or c - 32 (hl = 1:
+            // entries (row, row + c - 32)), reading with pitch kTilePitch + 1
+            // - 64 distinct distances, so each lane owns one bin and no LDS
+            // atomics are needed.  Masked pairs carry dS = 0.  LDS
+            // operations of one wave complete in order, so no barrier
+            // separates the writes from the reads.
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
+              mytile[row * kTilePitch + il] = ds[r];
+            }
+          }
+        }
+        block_dvdk(buf, rb, p, ds);
+        if constexpr (DBIAS) {
+          if (!fast) {
+            // diagonal il (hl = 0) covers rows below 32 - il, diagonal il - 32
+            // (hl = 1) the others; a lane reads all 32 rows of its line (the
+            // entries of the other rows lie outside the tile's row or in the
+            // guard and are discarded), all reads before the masked tree sum
+            float col[32];
+#pragma unroll
+            for (int row = 0; row < 32; ++row)
+              col[row] = mytile[row * (kTilePitch + 1) + il - 32 * hl];
+            // (opaque to the compiler: 32 masks hoisted out of the loop
+            // would hold 64 scalar registers for the whole kernel)
+            int lim = 32 - il;
+            asm volatile("" : "+v"(lim));
+#pragma unroll
+            for (int row = 0; row < 32; ++row)
+              col[row] = ((row < lim) == (hl == 0)) ? col[row] : 0.f;
+#pragma unroll
+            for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+              for (int k = 0; k < w; ++k) col[k] += col[k + w];
+            const float gsum = col[0];
+            const int dd = kw0 - irow0 + (hl ? il - 32 : il);   // key - query
+            if (dd <= -sat) ub0 += gsum;
+            else if (dd >= sat) ub1 += gsum;
+            else mybins[dd + sat] += gsum;
           }
         }
       }
-
-      // dV^T += dO^T P and dK^T += Q^T dS (unscaled): P / dS from registers as
-      // the B operand (k = the block's rows), dO^T / Q^T through transposing
-      // reads of the row-major tiles.
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          split_hi_lo(ds[8 * u + 2 * e], ds[8 * u + 2 * e + 1], hw[e], lw[e]);
-        const bf16x8 pb = frag(pw[u]), hb = frag(hw), lb = frag(lw);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int at = troff + (32 * rb + 16 * u) * QP + 32 * db;
-          const bf16x8 dot8 = lds_read_tr8(&dos[buf][at], QP);
-          const bf16x8 qt8 = lds_read_tr8(&qs[buf][at], QP);
-          dvacc[db] = mfma32(dot8, pb, dvacc[db]);
-          dkacc[db] = mfma32(qt8, hb, dkacc[db]);
-          dkacc[db] = mfma32(qt8, lb, dkacc[db]);
-        }
-      }
-      if constexpr (DBIAS) {
-        if (!fast) {
-          // column il of the rotated tile: rows below 32 - il belong to
-          // diagonal il, the others to il - 32; all 32 reads issue before the
-          // masked tree sum
-          float col[32];
-#pragma unroll
-          for (int row = 0; row < 32; ++row) col[row] = mytile[row * kTilePitch + il];
-          const int lim = 32 - il;
-#pragma unroll
-          for (int row = 0; row < 32; ++row)
-            col[row] = ((row < lim) == (hl == 0)) ? col[row] : 0.f;
-#pragma unroll
-          for (int w = 16; w >= 1; w >>= 1)
-#pragma unroll
-            for (int k = 0; k < w; ++k) col[k] += col[k + w];
-          const float gsum = col[0];
-          const int dd = kw0 - irow0 + (hl ? il - 32 : il);   // key - query
-          if (dd <= -sat) ub0 += gsum;
-          else if (dd >= sat) ub1 += gsum;
-          else mybins[dd + sat] += gsum;
-        }
-      }
     }
-    if (more) lstore(buf ^ 1);
+    // the next block's copies have landed (each wave waits for its own)
+    wait_vmem_loads();
     __syncthreads();
   }
 

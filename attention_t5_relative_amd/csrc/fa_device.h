@@ -218,6 +218,107 @@ __device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t *p, int pitch) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// ---------------------------------------------------------------------------
+// Unpadded bf16 tiles in LDS, swizzled by 16-byte chunk, filled straight from
+// global memory by buffer-to-LDS copies.
+//
+// A tile row holds D bf16 (D / 8 chunks); chunk c of row r is stored at chunk
+// position c ^ swz<D>(r) of that row.  gfx950's LDS has 64 four-byte banks,
+// so a 256-byte line spans them all.  Both MFMA operand reads of a tile are
+// then free of bank conflicts:
+//   row reads        16 lanes read one chunk of 16 consecutive rows
+//                    (r0 a multiple of 16): swz is a bijection on those rows
+//                    within each bank line;
+//   transposing      a half-wave reads the same four chunks 4g .. 4g + 3 of
+//   reads            rows 4h .. 4h + 3 of an 8-row group: swz sends them to
+//                    four different chunk groups (or bank-line halves).
+// D = 64 (two rows per line): swz = 4 * bit1(r) + bits 2..3 of r.
+// D = 128 (one row per line): swz = 4 * (r & 3) + bits 2..3 of r.
+// Both depend on bits 0..3 of r only, so row offsets that are multiples of
+// 16 keep a lane's swizzle.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  return D == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+}
+
+// Element offset of chunk c of row r in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  return r * D + 8 * (c ^ swz<D>(r));
+}
+
+// Element offset for the transposing read (see tr_lane_offset) of rows
+// 8 * half + 4 hl .. of a 16-row group, columns 32 db .. 32 db + 31, in a
+// swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz_tr_off(int lane, int half, int db) {
+  const int i16 = lane & 15, hl = lane >> 5, b4 = (lane >> 4) & 1;
+  const int r = 8 * half + 4 * hl + (i16 >> 2);
+  const int c = 4 * db + 2 * b4 + ((i16 & 3) >> 1);
+  return swz_off<D>(r, c) + 4 * (i16 & 1);
+}
+
+// The 8-row operand for one MFMA k-step of a swizzled tile: two transposing
+// reads at the lane's offsets for the two halves of the 16-row group.
+__device__ __forceinline__ bf16x8 lds_read_tr8_at(const uint16_t *base, int off0, int off1) {
+  const s16x4 lo = lds_read_tr(base + off0);
+  const s16x4 hi = lds_read_tr(base + off1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Global -> LDS copies.  `desc` is a raw buffer descriptor (dma_desc) over
+// the source; lane l writes the bytes at byte offset `off` of the source to
+// lds + 16 l (dma16) or lds + 4 l (dma4); `lds` must be the same for the
+// whole wave; offsets past the descriptor's range write zeros.
+//
+// The copies are issued as inline assembly: the compiler's wait insertion
+// cannot tell a copy's LDS destination from the tile being read and would
+// wait for every copy in flight before each LDS read, which would serialise
+// the prefetch.  The caller waits for its own copies (wait_vmem_loads)
+// before the barrier that hands the tile to the other waves.  Copies the
+// compiler does not count can only make its own count-based waits for
+// other loads stricter, since loads complete in issue order.
+__device__ __forceinline__ i32x4 dma_desc(const void *p, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *lds) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)lds;
+}
+__device__ __forceinline__ void dma16(i32x4 desc, uint32_t off, void *lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(desc), "{m0}"(lds_addr(lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(i32x4 desc, uint32_t off, void *lds) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(desc), "{m0}"(lds_addr(lds))
+               : "memory");
+}
+
+// Fill the R rows of a swizzled tile from rows row0 .. row0 + R - 1 of a
+// row-major bf16 matrix with row stride `stride` elements.  The tile is cut
+// into 1 KB pieces (64 chunk positions); wave w of NW copies pieces w,
+// w + NW, ...; lane l of a piece fetches the chunk that belongs at position l.
+// Rows outside the buffer's range arrive as zeros.
+template <int D, int R, int NW>
+__device__ __forceinline__ void dma_tile(i32x4 src, int stride, int row0, uint16_t *tile,
+                                         int wave, int lane) {
+  constexpr int NPIECE = R * D * 2 / 1024;
+  static_assert(NPIECE % NW == 0, "tile pieces per wave");
+#pragma unroll
+  for (int i = 0; i < NPIECE / NW; ++i) {
+    const int piece = wave + NW * i;
+    const int pos = piece * 64 + lane;
+    const int r = pos / (D / 8), pc = pos % (D / 8);
+    const int c = pc ^ swz<D>(r);
+    dma16(src, ((uint32_t)(row0 + r) * (uint32_t)stride + 8 * c) * 2u, tile + piece * 512);
+  }
+}
+
 // Bijective key reordering inside each group of 16 keys used for the
 // transposed V tile: swaps bits 2 and 3 of the key offset, so that the eight
 // keys one MFMA B-operand lane supplies (see the forward kernel) are
