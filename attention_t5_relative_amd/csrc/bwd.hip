@@ -100,14 +100,10 @@ __device__ __forceinline__ bf16x8 frag(const uint32_t (&w)[4]) {
 // ---------------------------------------------------------------------------
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE>
 __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdArgs a) {
-  constexpr int NCH = D / 8;
-  constexpr int LOADS = BC * NCH / NT;
-  // K is read both row-wise (S^T = K Q^T) and transposed (dQ^T = K^T dS^T):
-  // its pitch suits the transposing read; V is only read row-wise.
-  constexpr int KP = D + 16;
-  constexpr int VP = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BC * VP];
+  // K and V tiles, swizzled (see swz): K is read both row-wise
+  // (S^T = K Q^T) and transposed (dQ^T = K^T dS^T), V row-wise
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BC * D];
   __shared__ float lut[BIAS == kBiasT5 ? 2 * kMaxDistance + 1 : 1];
 
   const int tid = threadIdx.x;
@@ -156,25 +152,22 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
 
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
   const int nkt = (kend + BC - 1) / BC;
-  i32x4 sreg[LOADS];
-  auto gload = [&](rsrc_t r, int j0) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      sreg[u] = buf_load16(r, ((uint32_t)(j0 + row) * (uint32_t)HD + col * 8) * 2u);
-    }
+  // one key tile to LDS by buffer-to-LDS copies split over the four waves
+  const i32x4 dk_src = dma_desc(a.k + base, nrec), dv_src = dma_desc(a.v + base, nrec);
+  auto fill = [&](int j0, int buf) {
+    dma_tile<D, BC, 4>(dk_src, HD, j0, ks[buf], wave, lane);
+    dma_tile<D, BC, 4>(dv_src, HD, j0, vs[buf], wave, lane);
   };
-  auto lstore = [&](uint16_t *dst, int pitch) {
+  // row-wise operands: row il, chunk 2s + hl; transposed K operand: the two
+  // halves of each 16-row group, per 32-column block
+  int kof[D / 16], tro[D / 32][2];
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      *reinterpret_cast<i32x4 *>(&dst[row * pitch + col * 8]) = sreg[u];
-    }
-  };
-
-  const int koff = il * KP + 8 * hl;
-  const int voff = il * VP + 8 * hl;
-  const int ktro = tr_lane_offset(lane, KP);
+  for (int s = 0; s < D / 16; ++s) kof[s] = swz_off<D>(il, 2 * s + hl);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    tro[db][0] = swz_tr_off<D>(lane, 0, db);
+    tro[db][1] = swz_tr_off<D>(lane, 1, db);
+  }
   const float c = a.scale_log2;
   const float dscale = a.scale;
 
@@ -211,18 +204,13 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   }
   dc = half_sum(dc);
   if ((__builtin_bit_cast(uint32_t, dc) & 0x7f800000u) == 0x7f800000u) dc = 0.f;
-  if (nkt > 0) {
-    gload(rk, 0);
-    lstore(ks[0], KP);
-    gload(rv, 0);
-    lstore(vs[0], VP);
-  }
+  if (nkt > 0) fill(0, 0);
+  wait_vmem_loads();
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int j0 = kt * BC;
     const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) gload(rk, j0 + BC);
+    if (kt + 1 < nkt) fill(j0 + BC, buf ^ 1);
     const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + 31));
     f32x16 sacc[2], pacc[2];
     if (active) {
@@ -232,18 +220,12 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
         pacc[kb] = f32x16{};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8 *>(&ks[buf][koff + 32 * kb * KP + 16 * s]);
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8 *>(&vs[buf][voff + 32 * kb * VP + 16 * s]);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&ks[buf][kof[s] + 32 * kb * D]);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&vs[buf][kof[s] + 32 * kb * D]);
           sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
           pacc[kb] = mfma32(vf, df[s], pacc[kb]);
         }
       }
-    }
-    if (more) {
-      lstore(ks[buf ^ 1], KP);
-      gload(rv, j0 + BC);
     }
     if (active) {
       float bconst;
@@ -273,14 +255,15 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             const bf16x8 kt8 =
-                lds_read_tr8(&ks[buf][ktro + (32 * kb + 16 * u) * KP + 32 * db], KP);
+                lds_read_tr8_at(&ks[buf][(32 * kb + 16 * u) * D], tro[db][0], tro[db][1]);
             aacc[db] = mfma32(kt8, xhb, aacc[db]);
             aacc[db] = mfma32(kt8, xlb, aacc[db]);
             bacc[db] = mfma32(kt8, phb, bacc[db]);
           }
         }
     }
-    if (more) lstore(vs[buf ^ 1], VP);
+    // the next tile's copies have landed (each wave waits for its own)
+    wait_vmem_loads();
     __syncthreads();
   }
   const float dd = half_sum(dsum);   // D_i - Dc_i

@@ -50,6 +50,13 @@ __device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
 // tell across iterations that they have arrived, waits for all outstanding
 // loads - including prefetches issued in the loop - at their first use.
 __device__ __forceinline__ void wait_vmem_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Wait until at most N of this wave's vector-memory loads are in flight (they
+// complete in issue order, so every older one has landed).
+template <int N>
+__device__ __forceinline__ void wait_vmem_loads_but() {
+  static_assert(N >= 0 && N <= 15, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
 
 // D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.  Lane l holds
 // row (l % 32) of A and column (l % 32) of B, each with 8 consecutive k values

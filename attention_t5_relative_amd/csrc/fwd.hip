@@ -12,14 +12,17 @@
 //   O^T (dims x queries) = V^T P^T reuses P straight from the score
 //   accumulators as the MFMA B operand; its A operand (each lane: one dim,
 //   the 8 keys matching its P values) comes from the row-major V tile through
-//   the transposing LDS read, so K and V are staged the same way.
+//   the transposing LDS read, so K and V are staged the same way: unpadded,
+//   swizzled tiles (no bank conflicts on either read) copied from global
+//   memory straight into LDS.
 //
 // Latency.  With operands read from LDS right before each MFMA, every MFMA
 // waits out an LDS round trip; measured per 64-key tile that cost more than
 // the softmax itself.  So the K operands of a tile are read in one batch
 // before its QK^T products, and the V operands are read before the softmax,
-// whose VALU work covers their latency.  K and V tiles are fetched from
-// global memory one full iteration before they are written to LDS.
+// whose VALU work covers their latency.  K and V tiles are requested from
+// global memory two iterations ahead (one at head_dim 128) into a ring of
+// LDS buffers.
 #include "fa_device.h"
 
 namespace fa {
@@ -47,8 +50,6 @@ struct FwdArgs {
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
-  constexpr int NCH = D / 8;                  // 16-byte chunks per row
-  constexpr int LOADS = BC * NCH / NT;        // K (and V) chunks per thread per tile
   constexpr int NVF = D / 8;                  // V operand fragments per tile
   // Register budget: at head_dim 64 the K operands of both 32-key blocks are
   // read in one batch and every V operand before the softmax; at 128 the K
@@ -56,16 +57,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   constexpr int KBATCH = D == 64 ? 2 : 1;     // key blocks per K read batch
   constexpr int NKF = KBATCH * (D / 16);      // K fragments per batch
   constexpr int VPRE = D == 64 ? NVF : NVF / 4;
-  // Row pitches (elements).  K rows are read 16 B per lane by 8 consecutive
-  // rows at once: a pitch of an odd number of 16-byte slots keeps those reads
-  // on distinct banks.  V is read with the transposing read, 4 rows x 32 B per
-  // 16 lanes: a pitch of 2 (mod 8) slots keeps those on distinct banks.
-  constexpr int KP = D + 8;
-  constexpr int VP = D + 16;
-  static_assert(LOADS * NT == BC * NCH, "tile split");
-
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BC * VP];
+  // K and V tiles, swizzled (see swz; K read row-wise, V transposed), in a
+  // ring of NBUF buffers filled NBUF - 1 tiles ahead by buffer-to-LDS copies
+  // (head_dim 128 keeps two, so that two workgroups still fit on a CU).
+  constexpr int NBUF = D == 64 ? 3 : 2;
+  constexpr int PER_FILL = 2 * BC * D * 2 / 1024 / (NT / 64);   // copies per wave per tile
+  __shared__ __attribute__((aligned(16))) uint16_t ks[NBUF][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[NBUF][BC * D];
   __shared__ float lut[BIAS == kBiasT5 ? 2 * kMaxDistance + 1 : 1];
 
   const int tid = threadIdx.x;
@@ -95,8 +93,6 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   const size_t base = ((size_t)tok0 * a.heads + h) * D;
   const uint32_t nrec = ((uint32_t)(L - 1) * (uint32_t)HD + D) * 2u;
   const rsrc_t rq = make_rsrc(a.q + base, nrec);
-  const rsrc_t rk = make_rsrc(a.k + base, nrec);
-  const rsrc_t rv = make_rsrc(a.v + base, nrec);
   const rsrc_t ro = make_rsrc(a.o + base, nrec);
 
   const int q0 = qt * BR;
@@ -124,26 +120,23 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
   const int nkt = (kend + BC - 1) / BC;
 
-  // staging: chunk c = tid + NT*u is row c / NCH, 16-byte column c % NCH
-  i32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](i32x4 (&r)[LOADS], rsrc_t src, int j0) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      r[u] = buf_load16(src, ((uint32_t)(j0 + row) * (uint32_t)HD + col * 8) * 2u);
-    }
-  };
-  auto lstore = [&](const i32x4 (&r)[LOADS], uint16_t *dst, int pitch) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + NT * u, row = c / NCH, col = c % NCH;
-      *reinterpret_cast<i32x4 *>(&dst[row * pitch + col * 8]) = r[u];
-    }
+  const i32x4 dk_src = dma_desc(a.k + base, nrec), dv_src = dma_desc(a.v + base, nrec);
+  auto fill = [&](int j0, int buf) {
+    dma_tile<D, BC, NT / 64>(dk_src, HD, j0, ks[buf], wave, lane);
+    dma_tile<D, BC, NT / 64>(dv_src, HD, j0, vs[buf], wave, lane);
   };
 
-  // per-lane LDS offsets (elements); the rest of each address is a constant
-  const int koff = il * KP + 8 * hl;                       // + 32kb*KP + 16s
-  const int voff = tr_lane_offset(lane, VP);               // + (32kb + 16u) * VP + 32db
+  // per-lane LDS offsets (elements); the rest of each address is a constant:
+  // K row il, chunk 2s + hl (+ 32kb rows); V transposed, the two halves of
+  // each 16-row group per 32-column block (+ 32kb + 16u rows)
+  int kof[D / 16], tro[D / 32][2];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) kof[s] = swz_off<D>(il, 2 * s + hl);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    tro[db][0] = swz_tr_off<D>(lane, 0, db);
+    tro[db][1] = swz_tr_off<D>(lane, 1, db);
+  }
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -152,48 +145,41 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};
   const float c = a.scale_log2;
 
-  // Tile 0 goes to LDS now; tile 1 waits in registers.  From then on,
-  // iteration kt writes tile kt + 1 to the other buffer (last read in
-  // iteration kt - 1, before the barrier that ended it) and fetches tile
-  // kt + 2, so each global load has a whole iteration to arrive.
-  if (nkt > 0) {
-    gload(kreg, rk, 0);
-    gload(vreg, rv, 0);
-    lstore(kreg, ks[0], KP);
-    lstore(vreg, vs[0], VP);
-  }
+  // Tiles 0 .. NBUF - 2 are requested now.  Iteration kt requests tile
+  // kt + NBUF - 1 into the buffer read in iteration kt - 1 (free since the
+  // barrier that ended it) and ends once tile kt + 1 has landed: its own
+  // request may stay in flight for NBUF - 2 more iterations.
+  // Q (and the bias table) first: the compiler counts only its own loads,
+  // so they must be retired before the copies it cannot see are in flight
   wait_vmem_loads();
-  if (nkt > 1) {
-    gload(kreg, rk, BC);
-    gload(vreg, rv, BC);
-  }
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t)
+    if (t < nkt) fill(t * BC, t);
+  if (NBUF == 3 && nkt > 1)
+    wait_vmem_loads_but<(NBUF - 2) * PER_FILL>();
+  else
+    wait_vmem_loads();
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int j0 = kt * BC;
-    const int buf = kt & 1;
+    const int buf = kt % NBUF;
+    const bool ahead = kt + NBUF - 1 < nkt;
+    if (ahead) fill(j0 + (NBUF - 1) * BC, (kt + NBUF - 1) % NBUF);
     // a causal wave starts work once the tile reaches its last row
     const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + 31));
 
     // K operands in batches of KBATCH key blocks
-    const uint16_t *kb_s = ks[buf] + koff;
+    const uint16_t *kb_s = ks[buf];
     auto kread = [&](bf16x8 (&kf)[NKF], int kb0) {
 #pragma unroll
       for (int i = 0; i < NKF; ++i) {
         const int kb = kb0 + i / (D / 16), s = i % (D / 16);
-        kf[i] = *reinterpret_cast<const bf16x8 *>(kb_s + 32 * kb * KP + 16 * s);
+        kf[i] = *reinterpret_cast<const bf16x8 *>(kb_s + kof[s] + 32 * kb * D);
       }
     };
     bf16x8 kf[NKF];
     if (active) kread(kf, 0);
-    if (kt + 1 < nkt) {
-      lstore(kreg, ks[buf ^ 1], KP);
-      lstore(vreg, vs[buf ^ 1], VP);
-    }
-    if (kt + 2 < nkt) {
-      gload(kreg, rk, j0 + 2 * BC);
-      gload(vreg, rv, j0 + 2 * BC);
-    }
 
     if (active) {
       f32x16 sacc[2];
@@ -208,10 +194,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
 
       // V operands (fragment i: dims 32db, keys 32kb + 16u), read now so the
       // softmax below covers their latency
-      const uint16_t *vt_s = vs[buf] + voff;
+      const uint16_t *vt_s = vs[buf];
       auto vread = [&](int i) {
         const int db = i >> 2, kb = (i >> 1) & 1, u = i & 1;
-        return lds_read_tr8(vt_s + (32 * kb + 16 * u) * VP + 32 * db, VP);
+        return lds_read_tr8_at(vt_s + (32 * kb + 16 * u) * D, tro[db][0], tro[db][1]);
       };
       bf16x8 vf[NVF];
 #pragma unroll
@@ -273,6 +259,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
         oacc[db] = mfma32(vf[i], pb[kb][u], oacc[db]);
       }
     }
+    // tile kt + 1 has landed (each wave waits for its own copies)
+    if (NBUF == 3 && ahead)
+      wait_vmem_loads_but<(NBUF - 2) * PER_FILL>();
+    else
+      wait_vmem_loads();
     __syncthreads();
   }
 
