@@ -21,8 +21,7 @@
 // the softmax itself.  So the K operands of a tile are read in one batch
 // before its QK^T products, and the V operands are read before the softmax,
 // whose VALU work covers their latency.  K and V tiles are requested from
-// global memory two iterations ahead (one at head_dim 128) into a ring of
-// LDS buffers.
+// global memory one iteration ahead into double-buffered LDS.
 #include "fa_device.h"
 
 namespace fa {
@@ -49,7 +48,7 @@ struct FwdArgs {
 };
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(NT, D == 64 ? 3 : 2) void fwd_kernel(const FwdArgs a) {
   constexpr int NVF = D / 8;                  // V operand fragments per tile
   // Register budget: at head_dim 64 the K operands of both 32-key blocks are
   // read in one batch and every V operand before the softmax; at 128 the K
@@ -58,9 +57,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(const FwdArgs a) {
   constexpr int NKF = KBATCH * (D / 16);      // K fragments per batch
   constexpr int VPRE = D == 64 ? NVF : NVF / 4;
   // K and V tiles, swizzled (see swz; K read row-wise, V transposed), in a
-  // ring of NBUF buffers filled NBUF - 1 tiles ahead by buffer-to-LDS copies
-  // (head_dim 128 keeps two, so that two workgroups still fit on a CU).
-  constexpr int NBUF = D == 64 ? 3 : 2;
+  // ring of NBUF buffers filled NBUF - 1 tiles ahead by buffer-to-LDS copies.
+  // Two buffers: at head_dim 64 that leaves LDS (and registers) for three
+  // workgroups per CU, which measured faster than a deeper ring with two.
+  constexpr int NBUF = 2;
   constexpr int PER_FILL = 2 * BC * D * 2 / 1024 / (NT / 64);   // copies per wave per tile
   __shared__ __attribute__((aligned(16))) uint16_t ks[NBUF][BC * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs[NBUF][BC * D];
