@@ -484,162 +484,114 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   for (int qb = qb_first; qb < nqb; ++qb) {
     const int q0 = qb * QB;
     const int buf = (qb - qb_first) & 1;
-    const bool more = qb + 1 < nqb;
-    if (more) fill(q0 + QB, buf ^ 1);
+    if (qb + 1 < nqb) fill(q0 + QB, buf ^ 1);
 
-    // Whole query block unmasked with one bias value: straight-line code
-    // over its row blocks, so that one block's softmax can issue while the
-    // other's products run.
-    // (head_dim 128 has one row block per query block: no gain there)
-    bool qfast = QB / 32 >= 2 && wave_live && q0 + QB <= L && kw0 + 32 <= L &&
-                 (!CAUSAL || kw0 + 31 <= q0);
-    float qconst = 0.f;
-    int qlo = 0;
-    if constexpr (BIAS == kBiasT5) {
-      qlo = min(max(kw0 - (q0 + QB - 1), -sat), sat);
-      const int qhi = min(max(kw0 + 31 - q0, -sat), sat);
-      qfast = qfast && qlo == qhi;
-      qconst = lut[qlo + sat];
-    } else if constexpr (BIAS == kBiasAlibi) {
-      qfast = false;
-    }
-    if (qfast) {
-      // order: S/dP(0), softmax(0), S/dP(1), dV/dK(0), softmax(1), dV/dK(1)
-      float tsum = 0.f;
-      float p[QB / 32][16], ds[QB / 32][16];
-      auto soft = [&](int rb, const f32x16 &sacc, const f32x16 &pacc) {
-        block_p_fast(buf, rb, sacc, qconst, p[rb]);
+    // Every row block takes the same path (products, P, dS, products); only
+    // the computation of P branches, so the dK / dV accumulators stay in
+    // place.  A block with no visible pair runs fully masked (P = 0).
+    f32x16 sacc[QB / 32], pacc[QB / 32];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds[rb][r] = p[rb][r] * pacc[r];
-        if constexpr (DBIAS) {
+    for (int rb = 0; rb < QB / 32; ++rb) block_sdp(buf, rb, sacc[rb], pacc[rb]);
+#pragma unroll
+    for (int rb = 0; rb < QB / 32; ++rb) {
+      const int irow0 = q0 + 32 * rb;
+      const int rmin = kw0 - (irow0 + 31), rmax = kw0 + 31 - irow0;
+      const bool none = !wave_live || irow0 >= L || (CAUSAL && rmin > 0);
+      const bool mask_c = CAUSAL && rmax > 0;
+      const bool mask_r = irow0 + 32 > L;
+      const bool mask_k = kw0 + 32 > L;
+      bool uniform = (BIAS == kBiasNone);
+      float bconst = 0.f;
+      int ulo = 0;
+      if constexpr (BIAS == kBiasT5) {
+        ulo = min(max(rmin, -sat), sat);
+        const int uhi = min(max(rmax, -sat), sat);
+        uniform = (ulo == uhi);
+        bconst = lut[ulo + sat];
+      }
+      const bool fast = uniform && !none && !mask_c && !mask_r && !mask_k;
+      // The fast/slow choice is made once per block, outside the element
+      // loops.
+      float p[16], ds[16];
+      if (fast) {
+        block_p_fast(buf, rb, sacc[rb], bconst, p);
+      } else {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const f32x4 l4 =
+              *reinterpret_cast<const f32x4 *>(&lses[buf][32 * rb + 8 * qq + 4 * hl]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * qq + e;
+            const int roff = 8 * qq + e;
+            const int rr = myk - (irow0 + 4 * hl + roff);
+            float t = sacc[rb][r] * c;
+            if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
+            if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+            // non-short-circuit operators keep this straight-line code
+            const bool dead = none | (mask_c & (rr > 0)) | (mask_r & (irow0 + 4 * hl + roff >= L)) |
+                              (mask_k & (myk >= L));
+            // the mask as an additive -inf (exp2(-inf) = 0): a select
+            // between the whole argument and -inf would be turned into a
+            // branch around the table read
+            p[r] = __builtin_amdgcn_exp2f(fmaf(-l4[e], kLog2e, t) + (dead ? -INFINITY : 0.f));
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = p[r] * pacc[rb][r];
+      if constexpr (DBIAS) {
+        if (fast) {
           float t4[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            t4[k] = (ds[rb][k] + ds[rb][k + 4]) + (ds[rb][k + 8] + ds[rb][k + 12]);
-          tsum += (t4[0] + t4[1]) + (t4[2] + t4[3]);
-        }
-      };
-      {
-        f32x16 sacc, pacc;
-        block_sdp(buf, 0, sacc, pacc);
-        soft(0, sacc, pacc);
-      }
-#pragma unroll
-      for (int rb = 1; rb < QB / 32; ++rb) {
-        f32x16 sacc, pacc;
-        block_sdp(buf, rb, sacc, pacc);
-        block_dvdk(buf, rb - 1, p[rb - 1], ds[rb - 1]);
-        soft(rb, sacc, pacc);
-      }
-      block_dvdk(buf, QB / 32 - 1, p[QB / 32 - 1], ds[QB / 32 - 1]);
-      if constexpr (DBIAS) {
-        if (qlo <= 0) ub0 += tsum; else ub1 += tsum;
-      }
-    } else {
-#pragma unroll
-      for (int rb = 0; rb < QB / 32; ++rb) {
-        const int irow0 = q0 + 32 * rb;
-        const bool active = wave_live && irow0 < L && (!CAUSAL || kw0 <= irow0 + 31);
-        if (!active) continue;
-        f32x16 sacc, pacc;
-        block_sdp(buf, rb, sacc, pacc);
-        const int rmin = kw0 - (irow0 + 31), rmax = kw0 + 31 - irow0;
-        const bool mask_c = CAUSAL && rmax > 0;
-        const bool mask_r = irow0 + 32 > L;
-        const bool mask_k = kw0 + 32 > L;
-        bool uniform = (BIAS == kBiasNone);
-        float bconst = 0.f;
-        int ulo = 0;
-        if constexpr (BIAS == kBiasT5) {
-          ulo = min(max(rmin, -sat), sat);
-          const int uhi = min(max(rmax, -sat), sat);
-          uniform = (ulo == uhi);
-          bconst = lut[ulo + sat];
-        }
-        const bool fast = uniform && !mask_c && !mask_r && !mask_k;
-        // The fast/slow choice is made once per block, outside the element
-        // loops.
-        float p[16], ds[16];
-        if (fast) {
-          block_p_fast(buf, rb, sacc, bconst, p);
+          for (int k = 0; k < 4; ++k) t4[k] = (ds[k] + ds[k + 4]) + (ds[k + 8] + ds[k + 12]);
+          const float t = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+          if (ulo <= 0) ub0 += t; else ub1 += t;
         } else {
+          // Near the diagonal the bucket varies within the block, but it is
+          // constant along each diagonal (fixed key - query).  The block's
+          // dS goes to this wave's scratch tile, row = query, column = key;
+          // after the block's products, lane (hl, c) sums diagonal c
+          // (hl = 0: entries (row, row + c)) or c - 32 (hl = 1: entries
+          // (row, row + c - 32)), reading with pitch kTilePitch + 1 - 64
+          // distinct distances, so each lane owns one bin and no LDS atomics
+          // are needed.  Masked pairs carry dS = 0.  LDS operations of one
+          // wave complete in order, so no barrier separates the writes from
+          // the reads.
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const f32x4 l4 =
-                *reinterpret_cast<const f32x4 *>(&lses[buf][32 * rb + 8 * qq + 4 * hl]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * qq + e;
-              const int roff = 8 * qq + e;
-              const int rr = myk - (irow0 + 4 * hl + roff);
-              float t = sacc[r] * c;
-              if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
-              if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
-              // non-short-circuit operators keep this straight-line code
-              const bool dead = (mask_c & (rr > 0)) | (mask_r & (irow0 + 4 * hl + roff >= L)) |
-                                (mask_k & (myk >= L));
-              // the mask as an additive -inf (exp2(-inf) = 0): a select
-              // between the whole argument and -inf would be turned into a
-              // branch around the table read
-              p[r] = __builtin_amdgcn_exp2f(fmaf(-l4[e], kLog2e, t) + (dead ? -INFINITY : 0.f));
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
+            mytile[row * kTilePitch + il] = ds[r];
           }
         }
+      }
+      block_dvdk(buf, rb, p, ds);
+      if constexpr (DBIAS) {
+        if (!fast) {
+          // diagonal il (hl = 0) covers rows below 32 - il, diagonal il - 32
+          // (hl = 1) the others; a lane reads all 32 rows of its line (the
+          // entries of the other rows lie outside the tile's row or in the
+          // guard and are discarded), all reads before the masked tree sum
+          float col[32];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = p[r] * pacc[r];
-        if constexpr (DBIAS) {
-          if (fast) {
-            float t4[4];
+          for (int row = 0; row < 32; ++row)
+            col[row] = mytile[row * (kTilePitch + 1) + il - 32 * hl];
+          // (opaque to the compiler: 32 masks hoisted out of the loop would
+          // hold 64 scalar registers for the whole kernel)
+          int lim = 32 - il;
+          asm volatile("" : "+v"(lim));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) t4[k] = (ds[k] + ds[k + 4]) + (ds[k + 8] + ds[k + 12]);
-            const float t = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-            if (ulo <= 0) ub0 += t; else ub1 += t;
-          } else {
-            // Near the diagonal the bucket varies within the block, but it
-            // is constant along each diagonal (fixed key - query).  The
-            // block's dS goes to this wave's scratch tile, row = query,
-            // column = key; after the block's products, lane (hl, c) sums
-            // diagonal c (hl = 0: entries (row, row + c)) or c - 32 (hl = 1:
-            // entries (row, row + c - 32)), reading with pitch kTilePitch + 1
-            // - 64 distinct distances, so each lane owns one bin and no LDS
-            // atomics are needed.  Masked pairs carry dS = 0.  LDS
-            // operations of one wave complete in order, so no barrier
-            // separates the writes from the reads.
+          for (int row = 0; row < 32; ++row)
+            col[row] = ((row < lim) == (hl == 0)) ? col[row] : 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = 8 * (r >> 2) + 4 * hl + (r & 3);
-              mytile[row * kTilePitch + il] = ds[r];
-            }
-          }
-        }
-        block_dvdk(buf, rb, p, ds);
-        if constexpr (DBIAS) {
-          if (!fast) {
-            // diagonal il (hl = 0) covers rows below 32 - il, diagonal il - 32
-            // (hl = 1) the others; a lane reads all 32 rows of its line (the
-            // entries of the other rows lie outside the tile's row or in the
-            // guard and are discarded), all reads before the masked tree sum
-            float col[32];
+          for (int w = 16; w >= 1; w >>= 1)
 #pragma unroll
-            for (int row = 0; row < 32; ++row)
-              col[row] = mytile[row * (kTilePitch + 1) + il - 32 * hl];
-            // (opaque to the compiler: 32 masks hoisted out of the loop
-            // would hold 64 scalar registers for the whole kernel)
-            int lim = 32 - il;
-            asm volatile("" : "+v"(lim));
-#pragma unroll
-            for (int row = 0; row < 32; ++row)
-              col[row] = ((row < lim) == (hl == 0)) ? col[row] : 0.f;
-#pragma unroll
-            for (int w = 16; w >= 1; w >>= 1)
-#pragma unroll
-              for (int k = 0; k < w; ++k) col[k] += col[k + w];
-            const float gsum = col[0];
-            const int dd = kw0 - irow0 + (hl ? il - 32 : il);   // key - query
-            if (dd <= -sat) ub0 += gsum;
-            else if (dd >= sat) ub1 += gsum;
-            else mybins[dd + sat] += gsum;
-          }
+            for (int k = 0; k < w; ++k) col[k] += col[k + w];
+          const float gsum = col[0];
+          const int dd = kw0 - irow0 + (hl ? il - 32 : il);   // key - query
+          if (dd <= -sat) ub0 += gsum;
+          else if (dd >= sat) ub1 += gsum;
+          else mybins[dd + sat] += gsum;
         }
       }
     }
