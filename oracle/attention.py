@@ -11,6 +11,9 @@ Definitions followed (FAT5 report, section "Noyau CUDA", kernel v2 forward):
 
     S  = scale * Q K^T                    (scores)
     S' = S + bias                         (bias from the per-head table T, or ALiBi)
+
+and the report's first kernel, handed the bias matrix B itself (same
+section, kernel v1): S' = S + B.
     P  = softmax(S') over keys            (row-wise)
     O  = P V
 
@@ -34,6 +37,10 @@ Readings taken where the pages are silent:
   exact rotation is rounded once to bf16 (nearest, ties to even) before the
   scores.  Gradients flow through the rotation as if the rounding were the
   identity.
+* Dense bias (kernel v1): the pages say only that the kernel loads B and
+  adds it to S.  Read here as one [S, S] matrix per (batch, head), given as
+  [Bb, H, S, S] with Bb = 1 (shared by the whole batch) or Bb = B; its
+  gradient is dS, summed over the batch when Bb = 1.
 * Causal: key j is visible to query i iff j <= i.
 * Packed batches: a query attends only keys of its own sequence; positions are
   local to the sequence.
@@ -136,11 +143,14 @@ def rope_unrotate(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarr
 
 def bias_matrix(seqlen: int, head: int, *, bias: str, table=None, num_buckets: int = 32,
                 max_distance: int = 128, bidirectional: bool = True,
-                slopes=None) -> Optional[np.ndarray]:
+                slopes=None, dense=None) -> Optional[np.ndarray]:
     """Additive bias [S, S] (rows = query i, columns = key j) for one head, or
-    None when there is no bias."""
+    None when there is no bias.  ``dense`` is the head's own [S, S] matrix
+    (bias "dense")."""
     if bias == "none":
         return None
+    if bias == "dense":
+        return np.asarray(dense, dtype=np.float64)
     i = np.arange(seqlen)[:, None]
     j = np.arange(seqlen)[None, :]
     if bias == "t5":
@@ -152,7 +162,7 @@ def bias_matrix(seqlen: int, head: int, *, bias: str, table=None, num_buckets: i
 
 
 def _scores(qh, kh, head, *, scale, causal, bias, table, num_buckets, max_distance,
-            bidirectional, slopes, rope_base, rope_round=True):
+            bidirectional, slopes, rope_base, rope_round=True, dense=None):
     S = qh.shape[0]
     pos = np.arange(S)
     if rope_base is not None:
@@ -162,7 +172,8 @@ def _scores(qh, kh, head, *, scale, causal, bias, table, num_buckets, max_distan
             qh, kh = bf16_round_exact(qh), bf16_round_exact(kh)
     s = scale * (qh @ kh.T)
     bm = bias_matrix(S, head, bias=bias, table=table, num_buckets=num_buckets,
-                     max_distance=max_distance, bidirectional=bidirectional, slopes=slopes)
+                     max_distance=max_distance, bidirectional=bidirectional, slopes=slopes,
+                     dense=dense)
     if bm is not None:
         s = s + bm
     if causal:
@@ -184,7 +195,7 @@ def _softmax_rows(s):
 
 def head_fwd(qh, kh, vh, head, *, scale=1.0, causal=False, bias="none", table=None,
              num_buckets=32, max_distance=128, bidirectional=True, slopes=None,
-             rope_base=None, rope_round=True):
+             rope_base=None, rope_round=True, dense=None):
     """Forward for one head: qh, kh, vh float64 [S, D] -> (O [S, D], LSE [S]).
 
     ``rope_round=False`` skips the bf16 rounding of the rotated q, k (only the
@@ -192,20 +203,22 @@ def head_fwd(qh, kh, vh, head, *, scale=1.0, causal=False, bias="none", table=No
     s, _, _ = _scores(qh, kh, head, scale=scale, causal=causal, bias=bias, table=table,
                       num_buckets=num_buckets, max_distance=max_distance,
                       bidirectional=bidirectional, slopes=slopes, rope_base=rope_base,
-                      rope_round=rope_round)
+                      rope_round=rope_round, dense=dense)
     P, lse = _softmax_rows(s)
     return P @ vh, lse
 
 
 def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", table=None,
              num_buckets=32, max_distance=128, bidirectional=True, slopes=None,
-             rope_base=None, rope_round=True):
-    """Backward for one head -> (dq, dk, dv [S, D], dtable_h [num_buckets] or None)."""
+             rope_base=None, rope_round=True, dense=None):
+    """Backward for one head -> (dq, dk, dv [S, D], bias gradient): the bias
+    gradient is dtable_h [num_buckets] for T5, dS [S, S] for a dense bias,
+    None otherwise."""
     S = qh.shape[0]
     s, qr, kr = _scores(qh, kh, head, scale=scale, causal=causal, bias=bias, table=table,
                         num_buckets=num_buckets, max_distance=max_distance,
                         bidirectional=bidirectional, slopes=slopes, rope_base=rope_base,
-                        rope_round=rope_round)
+                        rope_round=rope_round, dense=dense)
     P, _ = _softmax_rows(s)
     dP = doh @ vh.T
     Drow = (P * dP).sum(axis=1)
@@ -223,6 +236,8 @@ def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", tab
         j = np.arange(S)[None, :]
         b = t5_bucket(j - i, num_buckets, max_distance, bidirectional)
         dtab = np.bincount(b.ravel(), weights=dS.ravel(), minlength=num_buckets)
+    if bias == "dense":
+        dtab = dS
     return dq, dk, dv, dtab
 
 
@@ -237,6 +252,16 @@ def _kw(kw):
     return {k: kw[k] for k in keys if k in kw}
 
 
+def _head_kw(kw, b, h):
+    """Per-head keyword arguments: a dense bias [Bb, H, S, S] is sliced to
+    the head's own matrix (batch index 0 when Bb == 1)."""
+    hk = _kw(kw)
+    if kw.get("bias") == "dense":
+        dense = kw["dense"]
+        hk["dense"] = dense[b if dense.shape[0] > 1 else 0, h]
+    return hk
+
+
 def attention_fwd(q, k, v, pairs=None, **kw):
     """Dense forward.  q, k, v float64 [B, S, H, D].
 
@@ -248,28 +273,37 @@ def attention_fwd(q, k, v, pairs=None, **kw):
     LSE = np.full((B, H, S), np.nan)
     todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in todo:
-        o, lse = head_fwd(q[b, :, h], k[b, :, h], v[b, :, h], h, **_kw(kw))
+        o, lse = head_fwd(q[b, :, h], k[b, :, h], v[b, :, h], h, **_head_kw(kw, b, h))
         O[b, :, h] = o
         LSE[b, h] = lse
     return O, LSE
 
 
 def attention_bwd(q, k, v, do, pairs=None, **kw):
-    """Dense backward.  Returns dq, dk, dv [B, S, H, D] and dtable [nb, H]
-    (None without T5 bias).  With ``pairs``, only those heads are computed
-    (others NaN) and dtable sums over the computed heads only."""
+    """Dense backward.  Returns dq, dk, dv [B, S, H, D] and the bias
+    gradient: dtable [nb, H] for T5, dbias [Bb, H, S, S] for a dense bias
+    (summed over the batch when Bb == 1), None otherwise.  With ``pairs``,
+    only those heads are computed (others NaN) and the bias gradient sums over
+    the computed heads only."""
     B, S, H, D = q.shape
     dq = np.full(q.shape, np.nan)
     dk = np.full(q.shape, np.nan)
     dv = np.full(q.shape, np.nan)
     nb = kw.get("num_buckets", 32)
-    dtable = np.zeros((nb, H)) if kw.get("bias") == "t5" else None
+    dtable = None
+    if kw.get("bias") == "t5":
+        dtable = np.zeros((nb, H))
+    elif kw.get("bias") == "dense":
+        dtable = np.zeros(kw["dense"].shape)
     todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in todo:
-        a, bb, c, dt = head_bwd(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], h, **_kw(kw))
+        a, bb, c, dt = head_bwd(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], h,
+                                **_head_kw(kw, b, h))
         dq[b, :, h], dk[b, :, h], dv[b, :, h] = a, bb, c
-        if dtable is not None:
+        if kw.get("bias") == "t5":
             dtable[:, h] += dt
+        elif kw.get("bias") == "dense":
+            dtable[b if dtable.shape[0] > 1 else 0, h] += dt
     return dq, dk, dv, dtable
 
 

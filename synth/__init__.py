@@ -12,6 +12,7 @@ from .gen import (  # noqa: F401
     DenseInputs,
     VarlenInputs,
     draw_dense,
+    draw_dense_bias,
     draw_varlen,
     alibi_slope_values,
 )

@@ -121,6 +121,13 @@ def draw_dense(seed: int, B: int, S: int, H: int, D: int, *, num_buckets: int = 
     return DenseInputs(q, k, v, do, table)
 
 
+def draw_dense_bias(seed: int, Bb: int, H: int, S: int, sigma: float = 1.0) -> np.ndarray:
+    """A dense additive bias matrix [Bb, H, S, S] as bf16 bits: N(0, sigma)
+    values rounded once to bfloat16 (row = query, column = key)."""
+    rng = np.random.default_rng(seed)
+    return bf16_round((sigma * rng.standard_normal(size=(Bb, H, S, S))).astype(np.float32))
+
+
 def draw_varlen(seed: int, total: int, H: int, D: int, *, num_buckets: int = 32,
                 lengths: Optional[np.ndarray] = None, with_dout: bool = True,
                 with_table: bool = True, mu: float = 6.0, sigma: float = 1.0,

@@ -289,6 +289,61 @@ def test_against_torch_sdpa_and_autograd(causal, bidirectional):
     np.testing.assert_allclose(torch.logsumexp(s, -1).numpy(), LSE, atol=1e-12)
 
 
+@pytest.mark.parametrize("Bb,causal", [(1, False), (2, True), (1, True)])
+def test_dense_bias_against_torch_sdpa_and_autograd(Bb, causal):
+    """Dense bias (kernel v1): O, LSE, dq, dk, dv and dBias against PyTorch's
+    attention with the bias as attn_mask and its autograd gradient (summed
+    over the batch by broadcasting when Bb == 1)."""
+    rng = np.random.default_rng(13)
+    B, S, H, D = 2, 23, 3, 8
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    dense = rng.standard_normal((Bb, H, S, S))
+    kw = dict(scale=0.6, causal=causal, bias="dense", dense=dense)
+    O, LSE = oracle.attention_fwd(q, k, v, **kw)
+    dq, dk, dv, dbias = oracle.attention_bwd(q, k, v, do, **kw)
+    assert dbias.shape == dense.shape
+
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3), requires_grad=True) for x in (q, k, v))
+    tb = torch.tensor(dense, requires_grad=True)
+    mask = tb
+    if causal:
+        mask = tb.masked_fill(torch.triu(torch.ones(S, S, dtype=torch.bool), 1), float("-inf"))
+    tO = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.6)
+    np.testing.assert_allclose(tO.detach().numpy().transpose(0, 2, 1, 3), O, atol=1e-12)
+    tO.backward(torch.tensor(do.transpose(0, 2, 1, 3)))
+    np.testing.assert_allclose(tq.grad.numpy().transpose(0, 2, 1, 3), dq, atol=1e-11)
+    np.testing.assert_allclose(tk.grad.numpy().transpose(0, 2, 1, 3), dk, atol=1e-11)
+    np.testing.assert_allclose(tv.grad.numpy().transpose(0, 2, 1, 3), dv, atol=1e-11)
+    np.testing.assert_allclose(tb.grad.numpy(), dbias, atol=1e-11)
+    s = torch.einsum("bhid,bhjd->bhij", tq.detach(), tk.detach()) * 0.6 + mask.detach()
+    np.testing.assert_allclose(torch.logsumexp(s, -1).numpy(), LSE, atol=1e-12)
+
+
+def test_dense_bias_reproduces_t5_mode():
+    """The T5 bias materialised as a dense matrix gives the T5 results, and
+    the dense gradient summed over each bucket's pairs is the table gradient."""
+    rng = np.random.default_rng(17)
+    B, S, H, D, nb, md = 2, 40, 2, 8, 16, 24
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    table = rng.normal(0, 0.5, (nb, H))
+    for causal, bidir in ((False, True), (True, False)):
+        t5 = dict(scale=1.0, causal=causal, bias="t5", table=table, num_buckets=nb,
+                  max_distance=md, bidirectional=bidir)
+        buckets = np.array([[bucket_exact(j - i, nb, md, bidir) for j in range(S)]
+                            for i in range(S)])
+        dense = table[buckets].transpose(2, 0, 1)[None]          # [1, H, S, S]
+        dn = dict(scale=1.0, causal=causal, bias="dense", dense=dense)
+        for a, b in zip(oracle.attention_fwd(q, k, v, **t5), oracle.attention_fwd(q, k, v, **dn)):
+            np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+        g5 = oracle.attention_bwd(q, k, v, do, **t5)
+        gd = oracle.attention_bwd(q, k, v, do, **dn)
+        for a, b in zip(g5[:3], gd[:3]):
+            np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+        per_bucket = np.stack([np.bincount(buckets.ravel(), weights=gd[3][0, h].ravel(),
+                                           minlength=nb) for h in range(H)], axis=1)
+        np.testing.assert_allclose(per_bucket, g5[3], rtol=0, atol=1e-11)
+
+
 # ---------------------------------------------------------------------------
 # Backward against central finite differences of the oracle forward
 # ---------------------------------------------------------------------------
