@@ -1,12 +1,13 @@
 """libfat5attn for MI355X: exact attention with T5 relative-position bias,
-ALiBi and RoPE, dense or packed, forward and backward, in hand-written HIP
-kernels for gfx950 behind a C ABI (include/fat5attn.h).
+ALiBi, RoPE or a dense bias matrix, dense or packed, forward and backward,
+in hand-written HIP kernels for gfx950 behind a C ABI (include/fat5attn.h).
 
 Importing this package does not load the library; the first call does, and it
 raises if ``libfat5attn.so`` has not been built (there is no fallback path).
 """
 from .api import (  # noqa: F401
     ALiBi,
+    DenseBias,
     T5Bias,
     alibi_slopes,
     attention,

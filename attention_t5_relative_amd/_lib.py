@@ -24,6 +24,7 @@ FA_KERNEL_BWD_DKV = 2
 FA_BIAS_NONE = 0
 FA_BIAS_T5 = 1
 FA_BIAS_ALIBI = 2
+FA_BIAS_DENSE = 3
 
 c_i32 = ctypes.c_int32
 c_f32 = ctypes.c_float
@@ -32,7 +33,8 @@ c_ptr = ctypes.c_void_p
 
 class FaBias(ctypes.Structure):
     _fields_ = [("mode", c_i32), ("num_buckets", c_i32), ("max_distance", c_i32),
-                ("bidirectional", c_i32), ("table", c_ptr), ("slopes", c_ptr)]
+                ("bidirectional", c_i32), ("table", c_ptr), ("slopes", c_ptr),
+                ("dense", c_ptr), ("dense_batch", c_i32), ("reserved2", c_i32)]
 
 
 class FaFwdParams(ctypes.Structure):

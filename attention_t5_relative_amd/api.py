@@ -34,7 +34,15 @@ class ALiBi:
     slopes: torch.Tensor
 
 
-BiasSpec = Optional[Union[T5Bias, ALiBi]]
+@dataclass
+class DenseBias:
+    """A dense additive bias matrix (the report's first kernel): bf16
+    [Bb, H, S, S] with Bb = 1 (shared by the batch) or B; row = query,
+    column = key."""
+    matrix: torch.Tensor
+
+
+BiasSpec = Optional[Union[T5Bias, ALiBi, DenseBias]]
 
 
 def alibi_slopes(heads: int, device=None) -> torch.Tensor:
@@ -66,7 +74,8 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
         raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
-def _bias_struct(bias: BiasSpec, heads: int, device) -> FaBias:
+def _bias_struct(bias: BiasSpec, heads: int, device, batch: Optional[int] = None,
+                 seqlen: Optional[int] = None) -> FaBias:
     b = FaBias()
     if bias is None:
         b.mode = _lib.FA_BIAS_NONE
@@ -81,9 +90,28 @@ def _bias_struct(bias: BiasSpec, heads: int, device) -> FaBias:
         _need(bias.slopes, "bias.slopes", torch.float32, (heads,), device)
         b.mode = _lib.FA_BIAS_ALIBI
         b.slopes = bias.slopes.data_ptr()
+    elif isinstance(bias, DenseBias):
+        if seqlen is None:
+            raise ValueError("a dense bias matrix is for the dense entry points only")
+        m = bias.matrix
+        if m.dim() != 4 or m.shape[0] not in (1, batch):
+            raise ValueError(f"bias.matrix must be [1 or {batch}, H, S, S]")
+        _need(m, "bias.matrix", torch.bfloat16, (m.shape[0], heads, seqlen, seqlen), device)
+        b.mode = _lib.FA_BIAS_DENSE
+        b.dense = m.data_ptr()
+        b.dense_batch = m.shape[0]
     else:
-        raise TypeError("bias must be None, T5Bias or ALiBi")
+        raise TypeError("bias must be None, T5Bias, ALiBi or DenseBias")
     return b
+
+
+def _dbias_shape(bias: BiasSpec, heads: int):
+    """Shape of the bias gradient fa_bwd writes (None when the mode has none)."""
+    if isinstance(bias, T5Bias):
+        return (bias.num_buckets, heads)
+    if isinstance(bias, DenseBias):
+        return tuple(bias.matrix.shape)
+    return None
 
 
 def _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base) -> FaFwdParams:
@@ -100,7 +128,7 @@ def _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base) -> FaFwdParams:
     p.scale = float(scale)
     p.rope_base = float(rope_base or 0.0)
     p.q, p.k, p.v, p.o, p.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr()
-    p.bias = _bias_struct(bias, H, dev)
+    p.bias = _bias_struct(bias, H, dev, B, S)
     return p
 
 
@@ -164,14 +192,15 @@ def fa_varlen_fwd(q, k, v, o, lse, cu_seqlens, max_seqlen, *, scale=1.0, causal=
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, scale=1.0, causal=False,
            bias: BiasSpec = None, rope_base=0.0, workspace=None, stream=None) -> None:
-    """Dense backward into dq, dk, dv [B,S,H,D] bf16 and dtable [nb,H] fp32."""
+    """Dense backward into dq, dk, dv [B,S,H,D] bf16 and the bias gradient
+    ``dtable``: fp32 [nb,H] for T5Bias, fp32 [Bb,H,S,S] for DenseBias."""
     lib = _lib.load()
     p = FaBwdParams()
     p.f = _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base)
     for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _need(t, name, torch.bfloat16, q.shape, q.device)
     if dtable is not None:
-        _need(dtable, "dtable", torch.float32, (p.f.bias.num_buckets, q.shape[2]), q.device)
+        _need(dtable, "dtable", torch.float32, _dbias_shape(bias, q.shape[2]), q.device)
     p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
     p.dtable = _ptr(dtable)
     ws, wsb = _workspace(lib.fa_bwd_workspace_size(ctypes.byref(p)), q.device, workspace)
@@ -238,15 +267,22 @@ class _Attention(torch.autograd.Function):
         dtable = None
         if isinstance(ctx.bias, T5Bias) and ctx.bias.table.requires_grad:
             dtable = torch.empty_like(ctx.bias.table)
+        if isinstance(ctx.bias, DenseBias) and ctx.bias.matrix.requires_grad:
+            dtable = torch.empty(ctx.bias.matrix.shape, dtype=torch.float32, device=q.device)
         fa_bwd(q, k, v, o, lse, do.contiguous(), dq, dk, dv, dtable, scale=ctx.scale,
                causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
+        if isinstance(ctx.bias, DenseBias) and dtable is not None:
+            dtable = dtable.to(ctx.bias.matrix.dtype)   # a leaf's gradient keeps its dtype
         return dq, dk, dv, dtable, None, None, None, None, None
 
 
 def attention(q, k, v, *, bias: BiasSpec = None, causal=False, scale=1.0, rope_base=0.0,
               return_lse=False):
-    """Exact attention with optional T5/ALiBi bias and RoPE; q, k, v [B,S,H,D] bf16."""
+    """Exact attention with optional T5 / ALiBi / dense bias and RoPE; q, k, v
+    [B,S,H,D] bf16."""
     table = bias.table if isinstance(bias, T5Bias) else None
+    if isinstance(bias, DenseBias):
+        table = bias.matrix
     slopes = bias.slopes if isinstance(bias, ALiBi) else None
     o, lse = _Attention.apply(q, k, v, table, slopes, bias, scale, causal, rope_base)
     return (o, lse) if return_lse else o

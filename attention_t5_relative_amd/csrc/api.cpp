@@ -171,8 +171,15 @@ fa_status check_common(int heads, int head_dim, int causal, float scale, float r
     case FA_BIAS_ALIBI:
       if (!bias.slopes) return fail(FA_ERR_INVALID, "bias.slopes is NULL");
       break;
+    case FA_BIAS_DENSE:
+      if (!bias.dense) return fail(FA_ERR_INVALID, "bias.dense is NULL");
+      if (maxlen > fa::kMaxDenseSeqlen)
+        return fail(FA_ERR_UNSUPPORTED, "a dense bias needs seqlen <= %d (got %lld)",
+                    fa::kMaxDenseSeqlen, maxlen);
+      break;
     default: return fail(FA_ERR_INVALID, "bias.mode=%d is not a fa_bias_mode", bias.mode);
   }
+  if (bias.reserved2 != 0) return fail(FA_ERR_INVALID, "bias.reserved2 must be 0");
   return FA_OK;
 }
 
@@ -185,6 +192,11 @@ fa_status check_fwd_impl(const fa_fwd_params *p) {
     return fail(FA_ERR_UNSUPPORTED, "batch * seqlen * heads must stay below 2^31");
   if (!empty && (!p->q || !p->k || !p->v || !p->o || !p->lse))
     return fail(FA_ERR_INVALID, "q, k, v, o and lse must be non-NULL");
+  if (p->bias.mode == FA_BIAS_DENSE && p->bias.dense_batch != 1 &&
+      p->bias.dense_batch != p->batch)
+    return fail(FA_ERR_INVALID, "bias.dense_batch=%d must be 1 or batch=%d", p->bias.dense_batch,
+                p->batch);
+  if (empty && p->bias.mode == FA_BIAS_DENSE) return FA_OK;
   return check_common(p->heads, p->head_dim, p->causal, p->scale, p->rope_base, p->bias,
                       p->seqlen);
 }
@@ -198,6 +210,8 @@ fa_status check_varlen_fwd_impl(const fa_varlen_fwd_params *p) {
     return fail(FA_ERR_INVALID, "q, k, v, o and lse must be non-NULL");
   if ((long long)p->total * p->heads >= (1LL << 31))
     return fail(FA_ERR_UNSUPPORTED, "total * heads must stay below 2^31");
+  if (p->bias.mode == FA_BIAS_DENSE)
+    return fail(FA_ERR_UNSUPPORTED, "a dense bias matrix is for the dense entry points only");
   return check_common(p->heads, p->head_dim, p->causal, p->scale, p->rope_base, p->bias,
                       p->max_seqlen);
 }
@@ -224,6 +238,10 @@ fa::Problem make_problem(const fa_fwd_params &f) {
   p.cu_seqlens = nullptr;
   p.table = f.bias.table;
   p.slopes = f.bias.slopes;
+  if (p.bias == FA_BIAS_DENSE) {
+    p.dense = static_cast<const uint16_t *>(f.bias.dense);
+    p.dense_batch = f.bias.dense_batch;
+  }
   if (p.bias == FA_BIAS_T5)
     p.t5 = geometry(f.bias.num_buckets, f.bias.max_distance, f.bias.bidirectional);
   return p;
@@ -288,9 +306,10 @@ FwdLayout fwd_layout(const fa::Problem &p) {
 
 struct BwdLayout {
   size_t qrot = 0, krot = 0, dq_f32 = 0, dk_f32 = 0, delta = 0, part = 0, prefix = 0, sched = 0,
-         total = 0;
+         dense_ws = 0, total = 0;
   int nsched = 0;
   bool has_part = false;
+  bool has_dense_ws = false;   // per-batch dense bias gradients, summed afterwards
 };
 
 BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
@@ -316,6 +335,9 @@ BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
     const int nb = p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp;
     L.part = c.take((size_t)fa::bwd_num_parts(p, L.nsched) * nb * 4);
   }
+  L.has_dense_ws = want_dtable && p.bias == FA_BIAS_DENSE && p.dense_batch == 1 && p.nbatch > 1;
+  if (L.has_dense_ws)
+    L.dense_ws = c.take((size_t)p.nbatch * p.heads * p.seqlen * p.seqlen * 4);
   L.total = c.off;
   return L;
 }
@@ -361,10 +383,16 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
                 ws == nullptr ? (size_t)0 : ws_bytes);
   hipError_t e;
   const bool t5grad = dtable != nullptr && p.bias == FA_BIAS_T5;
+  const bool densegrad = dtable != nullptr && p.bias == FA_BIAS_DENSE;
   const int nb = p.bias == FA_BIAS_T5 ? (p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp) : 0;
   if (p.total == 0 || (!p.varlen && (p.nbatch == 0 || p.seqlen == 0))) {
     if (t5grad) {
       e = fa::launch_fill_f32(dtable, (size_t)nb * p.heads, 0.f, s);
+      if (e != hipSuccess) return hip_fail(e, "fill");
+    }
+    if (densegrad) {   // an empty batch contributes nothing to a shared matrix
+      e = fa::launch_fill_f32(dtable, (size_t)p.dense_batch * p.heads * p.seqlen * p.seqlen, 0.f,
+                              s);
       if (e != hipSuccess) return hip_fail(e, "fill");
     }
     return FA_OK;
@@ -382,6 +410,13 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   b.delta = at<float>(ws, L.delta);
   b.part = L.has_part ? at<float>(ws, L.part) : nullptr;
   b.dtable = t5grad ? dtable : nullptr;
+  b.dbias = densegrad ? dtable : nullptr;
+  b.dbias_batch = L.has_dense_ws ? at<float>(ws, L.dense_ws) : nullptr;
+  if (densegrad && p.causal && !L.has_dense_ws) {
+    // pairs with key > query: the key-parallel kernel skips most of them
+    e = fa::launch_zero_upper(dtable, p.dense_batch * p.heads, p.seqlen, s);
+    if (e != hipSuccess) return hip_fail(e, "dense bias gradient fill");
+  }
   const bool rope = p.rope_base > 0.f;
   if (rope) {
     e = fa::launch_rope_pair(p, q, k, at<void>(ws, L.qrot), at<void>(ws, L.krot), s);
@@ -406,6 +441,11 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   if (e != hipSuccess) return hip_fail(e, "backward dkv kernel");
   e = fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdReduce, s);
   if (e != hipSuccess) return hip_fail(e, "table-gradient reduction");
+  if (L.has_dense_ws) {
+    e = fa::launch_batch_sum(b.dbias_batch, dtable, p.nbatch, p.heads, p.seqlen, p.causal != 0,
+                             s);
+    if (e != hipSuccess) return hip_fail(e, "dense bias gradient batch sum");
+  }
   if (rope) {
     e = fa::launch_rope_grad(p, b.dq_f32, dq, s);
     if (e == hipSuccess) e = fa::launch_rope_grad(p, b.dk_f32, dk, s);

@@ -46,6 +46,9 @@ struct BwdArgs {
   float *part;             // [nb, nwg] table-gradient partials
   const int4 *sched;       // packed batches: {token0, length, head, tile}
   const float *table, *slopes;
+  const uint16_t *dense;   // dense bias bf16 [dense_batch, H, S, S]
+  float *dbias;            // dense bias gradient fp32, one [S, S] per (batch, head)
+  int32_t dense_batch;
   int32_t nbatch, seqlen, heads, total;
   int32_t ntile;           // dense: tiles of 128 per sequence
   int32_t nwg;
@@ -55,7 +58,7 @@ struct BwdArgs {
 };
 
 struct Work {
-  int h, tile, tok0, L;
+  int b, h, tile, tok0, L;   // b: batch index (dense only)
   int part;                // table-gradient partial slot (reduction order)
   size_t lse_base;         // index of row 0 in lse / delta
 };
@@ -67,6 +70,7 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int g, Work &w) {
   if constexpr (VARLEN) {
     const int4 e = a.sched[g];
     if (e.y <= 0) return false;
+    w.b = 0;
     w.tok0 = e.x;
     w.L = e.y;
     w.h = e.z;
@@ -78,6 +82,7 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int g, Work &w) {
     tile_order(g, a.nbatch * a.heads, a.ntile, pair, w.tile);
     w.part = pair * a.ntile + w.tile;
     const int b = pair / a.heads;
+    w.b = b;
     w.h = pair - b * a.heads;
     w.tok0 = b * a.seqlen;
     w.L = a.seqlen;
@@ -149,6 +154,11 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   }
   float slope_l2 = 0.f;
   if constexpr (BIAS == kBiasAlibi) slope_l2 = -a.slopes[h] * kLog2e;
+  rsrc_t rbias = make_rsrc(nullptr, 0u);
+  if constexpr (BIAS == kBiasDense) {
+    const size_t mat = (size_t)(a.dense_batch == 1 ? 0 : w.b) * a.heads + h;
+    rbias = make_rsrc(a.dense + mat * L * L, (uint32_t)L * (uint32_t)L * 2u);
+  }
 
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
   const int nkt = (kend + BC - 1) / BC;
@@ -212,6 +222,9 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
     const int buf = kt & 1;
     if (kt + 1 < nkt) fill(j0 + BC, buf ^ 1);
     const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + 31));
+    uint16_t bv[2][16];
+    if constexpr (BIAS == kBiasDense)
+      if (active) dense_row_load(rbias, myrow, L, j0, hl, bv);
     f32x16 sacc[2], pacc[2];
     if (active) {
 #pragma unroll
@@ -230,7 +243,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
     if (active) {
       float bconst;
       const bool fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut,
-                                                  slope_l2, bconst);
+                                                  slope_l2, bconst, bv);
       const float cc = fast ? c : 1.f;
       const float sub = bconst - lse2;
       // per 16-key group: P o (dP - Dc) as hi + lo fragments and P as bf16,
@@ -385,6 +398,16 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   }
   float slope_l2 = 0.f;
   if constexpr (BIAS == kBiasAlibi) slope_l2 = -a.slopes[h] * kLog2e;
+  // dense bias: this (batch, head)'s [S, S] matrix; its gradient goes to the
+  // (batch, head) matrix of a.dbias
+  rsrc_t rbias = make_rsrc(nullptr, 0u), rdbias = make_rsrc(nullptr, 0u);
+  if constexpr (BIAS == kBiasDense) {
+    const size_t mat = (size_t)(a.dense_batch == 1 ? 0 : w.b) * a.heads + h;
+    rbias = make_rsrc(a.dense + mat * L * L, (uint32_t)L * (uint32_t)L * 2u);
+    if constexpr (DBIAS)
+      rdbias = make_rsrc(a.dbias + ((size_t)w.b * a.heads + h) * L * L,
+                         (uint32_t)L * (uint32_t)L * 4u);
+  }
   float *const mybins = bins + wave * nbin;
   float *const mytile = tiles + wave * (32 * kTilePitch);
 
@@ -510,6 +533,19 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
         bconst = lut[ulo + sat];
       }
       const bool fast = uniform && !none && !mask_c && !mask_r && !mask_k;
+      // dense bias and its gradient: element r is row irow0 + 4hl + roff(r),
+      // key myk; the lane's own part of the address is voff, the row offset
+      // roff(r) * S (the same for the whole wave) goes in the scalar offset
+      // (rows past the matrix fall outside the buffer: loads read 0, stores
+      // are dropped; a key past S reads the next row and is masked)
+      const uint32_t dvoff = (uint32_t)(irow0 + 4 * hl) * (uint32_t)L + (uint32_t)myk;
+      uint16_t bkv[16];
+      if constexpr (BIAS == kBiasDense) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          bkv[r] = buf_load_u16(rbias, dvoff * 2u,
+                                (uint32_t)(8 * (r >> 2) + (r & 3)) * (uint32_t)L * 2u);
+      }
       // The fast/slow choice is made once per block, outside the element
       // loops.
       float p[16], ds[16];
@@ -528,6 +564,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
             float t = sacc[rb][r] * c;
             if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
             if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+            if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bkv[r]), kLog2e, t);
             // non-short-circuit operators keep this straight-line code
             const bool dead = none | (mask_c & (rr > 0)) | (mask_r & (irow0 + 4 * hl + roff >= L)) |
                               (mask_k & (myk >= L));
@@ -540,7 +577,16 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) ds[r] = p[r] * pacc[rb][r];
-      if constexpr (DBIAS) {
+      if constexpr (DBIAS && BIAS == kBiasDense) {
+        // dL/dB = dS for every pair of the block (0 where masked)
+        if (myk < L) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            buf_store_f32(rdbias, dvoff * 4u, (uint32_t)(8 * (r >> 2) + (r & 3)) * (uint32_t)L * 4u,
+                          ds[r]);
+        }
+      }
+      if constexpr (DBIAS && BIAS == kBiasT5) {
         if (fast) {
           float t4[4];
 #pragma unroll
@@ -566,7 +612,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
         }
       }
       block_dvdk(buf, rb, p, ds);
-      if constexpr (DBIAS) {
+      if constexpr (DBIAS && BIAS == kBiasT5) {
         if (!fast) {
           // diagonal il (hl = 0) covers rows below 32 - il, diagonal il - 32
           // (hl = 1) the others; a lane reads all 32 rows of its line (the
@@ -628,7 +674,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       }
     }
 
-  if constexpr (DBIAS) {
+  if constexpr (DBIAS && BIAS == kBiasT5) {
     // saturated-block sums: reduce over the wave, then fold into the end bins
     float s0 = ub0, s1 = ub1;
 #pragma unroll
@@ -748,7 +794,7 @@ hipError_t launch_dkv_t(const BwdArgs &a, hipStream_t s) {
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 hipError_t launch_pair(const BwdArgs &a, int phase, bool rope, bool dbias, hipStream_t s) {
   if (phase == kBwdPre) return launch_dq_t<D, BIAS, CAUSAL, VARLEN>(a, rope, s);
-  if constexpr (BIAS == kBiasT5) {
+  if constexpr (BIAS == kBiasT5 || BIAS == kBiasDense) {
     if (dbias)
       return rope ? launch_dkv_t<D, BIAS, CAUSAL, VARLEN, true, true>(a, s)
                   : launch_dkv_t<D, BIAS, CAUSAL, VARLEN, false, true>(a, s);
@@ -760,11 +806,16 @@ hipError_t launch_pair(const BwdArgs &a, int phase, bool rope, bool dbias, hipSt
 template <int D, int BIAS>
 hipError_t launch_b(const BwdArgs &a, int phase, bool causal, bool varlen, bool rope, bool dbias,
                     hipStream_t s) {
-  if (causal)
-    return varlen ? launch_pair<D, BIAS, true, true>(a, phase, rope, dbias, s)
-                  : launch_pair<D, BIAS, true, false>(a, phase, rope, dbias, s);
-  return varlen ? launch_pair<D, BIAS, false, true>(a, phase, rope, dbias, s)
-                : launch_pair<D, BIAS, false, false>(a, phase, rope, dbias, s);
+  if constexpr (BIAS == kBiasDense) {   // dense entry points only
+    return causal ? launch_pair<D, BIAS, true, false>(a, phase, rope, dbias, s)
+                  : launch_pair<D, BIAS, false, false>(a, phase, rope, dbias, s);
+  } else {
+    if (causal)
+      return varlen ? launch_pair<D, BIAS, true, true>(a, phase, rope, dbias, s)
+                    : launch_pair<D, BIAS, true, false>(a, phase, rope, dbias, s);
+    return varlen ? launch_pair<D, BIAS, false, true>(a, phase, rope, dbias, s)
+                  : launch_pair<D, BIAS, false, false>(a, phase, rope, dbias, s);
+  }
 }
 
 template <int D>
@@ -773,6 +824,7 @@ hipError_t launch_d(const BwdArgs &a, int phase, int bias, bool causal, bool var
   switch (bias) {
     case kBiasT5: return launch_b<D, kBiasT5>(a, phase, causal, varlen, rope, dbias, s);
     case kBiasAlibi: return launch_b<D, kBiasAlibi>(a, phase, causal, varlen, rope, dbias, s);
+    case kBiasDense: return launch_b<D, kBiasDense>(a, phase, causal, varlen, rope, dbias, s);
     default: return launch_b<D, kBiasNone>(a, phase, causal, varlen, rope, dbias, s);
   }
 }
@@ -806,6 +858,9 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.sched = sched;
   a.table = p.table;
   a.slopes = p.slopes;
+  a.dense = p.dense;
+  a.dense_batch = p.dense_batch;
+  a.dbias = b.dbias_batch ? b.dbias_batch : b.dbias;
   a.nbatch = p.nbatch;
   a.seqlen = p.seqlen;
   a.heads = p.heads;
@@ -824,9 +879,9 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   }
   if (a.nwg <= 0) return hipSuccess;
   const bool rope = p.rope_base > 0.f;
-  const bool dbias = b.part != nullptr;
+  const bool dbias = b.part != nullptr || a.dbias != nullptr;
   if (phase == kBwdReduce) {
-    if (!dbias) return hipSuccess;
+    if (b.part == nullptr) return hipSuccess;
     hipLaunchKernelGGL(dbias_reduce_kernel, dim3(a.nb * p.heads), dim3(256), 0, s, a.part,
                        sched, a.nwg, p.nbatch, p.heads, a.ntile, b.dtable);
     return hipGetLastError();

@@ -34,6 +34,17 @@ __device__ __forceinline__ i32x4 buf_load16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
+// One bf16 (as its 16 bits) at byte offset `off`.
+__device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+// The same at byte offset voff (per lane) + soff (the same for the wave).
+__device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)voff, (int)soff, 0);
+}
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, i32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
@@ -73,6 +84,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+__device__ __forceinline__ float bf16_bits(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
@@ -171,10 +185,13 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
 // Otherwise the scores are finished in place in log2 units (scaled, biased,
 // masked to -inf) and bconst is 0, so fma(s, 1, 0) gives them.
 // The causal mask hides keys after the query; keys at or past L are masked.
+// A dense bias arrives as the lane's own values bv (bf16 bits, same order
+// as sacc; see dense_row_load).
 template <int BIAS, bool CAUSAL>
 __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0, int il, int hl,
                                              int L, float c, int sat, const float *lut,
-                                             float slope_l2, float &bconst) {
+                                             float slope_l2, float &bconst,
+                                             const uint16_t (&bv)[2][16]) {
   const int rmin = j0 - (row0 + 31), rmax = j0 + 63 - row0;
   const bool mask_c = CAUSAL && rmax > 0;
   const bool mask_l = j0 + 64 > L;
@@ -198,6 +215,7 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
       float t = sacc[kb][r] * c;
       if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
       if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+      if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bv[kb][r]), kLog2e, t);
       if (mask_c && rr > 0) t = -INFINITY;
       if (mask_l && jb + off >= L) t = -INFINITY;
       sacc[kb][r] = t;
@@ -205,6 +223,21 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
       if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
   return false;
+}
+
+// The dense bias values one lane needs for a 64-key tile of the query-
+// parallel kernels: row `row` (the lane's query), keys j0 + 32kb + 8(r/4) +
+// 4hl + r%4, from a buffer over one [S, S] bf16 matrix (row stride S).
+// Rows past the matrix read as 0; keys past S read the next row, which the
+// key mask then hides.
+__device__ __forceinline__ void dense_row_load(rsrc_t rb, int row, int S, int j0, int hl,
+                                               uint16_t (&bv)[2][16]) {
+  const uint32_t base = (uint32_t)row * (uint32_t)S + (uint32_t)(j0 + 4 * hl);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      bv[kb][r] = buf_load_u16(rb, (base + 32 * kb + 8 * (r >> 2) + (r & 3)) * 2u);
 }
 
 // Per-lane LDS element offset for the transposing read that assembles an

@@ -12,6 +12,7 @@ namespace fa {
 constexpr int kMaxThresholds = 128;   // (buckets per side) - (exact buckets) - 1 <= 127
 constexpr int kMaxDistance = 1024;    // bounds the per-distance bias table in LDS
 constexpr int kMaxSeqlen = 65536;
+constexpr int kMaxDenseSeqlen = 16384; // a dense bias matrix (and its fp32 gradient) < 2^32 bytes
 
 // T5 bucket boundaries for one (num_buckets, max_distance, bidirectional).
 // For n >= me, bucket(n) = me + #{k : thr[k] <= n}; `sat` is the first n of
@@ -25,7 +26,7 @@ struct T5Geometry {
   int32_t thr[kMaxThresholds];
 };
 
-enum BiasKind : int32_t { kBiasNone = 0, kBiasT5 = 1, kBiasAlibi = 2 };
+enum BiasKind : int32_t { kBiasNone = 0, kBiasT5 = 1, kBiasAlibi = 2, kBiasDense = 3 };
 
 // One attention problem, dense or packed, as the kernels see it.
 struct Problem {
@@ -42,6 +43,8 @@ struct Problem {
   const int32_t *cu_seqlens;
   const float *table;
   const float *slopes;
+  const uint16_t *dense;  // bf16 [dense_batch, H, S, S] (kBiasDense)
+  int32_t dense_batch;    // 1 (shared by the batch) or nbatch
   T5Geometry t5;
 };
 
@@ -61,6 +64,8 @@ struct BwdBuffers {
   float *delta;            // fp32, lse layout
   float *part;             // fp32 [num_buckets, parts] (T5 table gradient) or nullptr
   float *dtable;           // [num_buckets, H] or nullptr
+  float *dbias;            // dense bias gradient fp32 [dense_batch, H, S, S] or nullptr
+  float *dbias_batch;      // per-batch gradients [B, H, S, S] summed into dbias, or nullptr
 };
 
 // Launchers (return the first HIP error, hipSuccess otherwise).
@@ -82,6 +87,13 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
 hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
                              hipStream_t s);
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
+// Dense bias gradient helpers: zero the pairs with key > query of `count`
+// [S, S] matrices (causal: the backward never visits most of them), and sum
+// `nbatch` [H, S, S] slabs into one (pairs with key > query set to 0 when
+// causal, without reading them).
+hipError_t launch_zero_upper(float *m, int count, int S, hipStream_t s);
+hipError_t launch_batch_sum(const float *src, float *dst, int nbatch, int heads, int S,
+                            bool causal, hipStream_t s);
 
 
 }  // namespace fa

@@ -41,6 +41,8 @@ struct FwdArgs {
   float *lse;
   const int4 *sched;     // packed batches: {token0, length, head, q-tile}
   const float *table, *slopes;
+  const uint16_t *dense;  // dense bias bf16 [dense_batch, H, S, S]
+  int32_t dense_batch;
   int32_t nbatch, seqlen, heads, total;
   int32_t nq, nwg;
   float scale_log2;      // scale * log2(e)
@@ -48,7 +50,8 @@ struct FwdArgs {
 };
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NT, D == 64 ? 3 : 2) void fwd_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd_kernel(
+    const FwdArgs a) {
   constexpr int NVF = D / 8;                  // V operand fragments per tile
   // Register budget: at head_dim 64 the K operands of both 32-key blocks are
   // read in one batch and every V operand before the softmax; at 128 the K
@@ -116,6 +119,12 @@ __global__ __launch_bounds__(NT, D == 64 ? 3 : 2) void fwd_kernel(const FwdArgs 
   }
   float slope_l2 = 0.f;
   if constexpr (BIAS == kBiasAlibi) slope_l2 = -a.slopes[h] * kLog2e;
+  // dense bias: this (batch, head)'s [S, S] matrix
+  rsrc_t rbias = make_rsrc(nullptr, 0u);
+  if constexpr (BIAS == kBiasDense) {
+    const size_t mat = (size_t)(a.dense_batch == 1 ? 0 : bidx) * a.heads + h;
+    rbias = make_rsrc(a.dense + mat * L * L, (uint32_t)L * (uint32_t)L * 2u);
+  }
 
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
   const int nkt = (kend + BC - 1) / BC;
@@ -180,6 +189,9 @@ __global__ __launch_bounds__(NT, D == 64 ? 3 : 2) void fwd_kernel(const FwdArgs 
     };
     bf16x8 kf[NKF];
     if (active) kread(kf, 0);
+    uint16_t bv[2][16];
+    if constexpr (BIAS == kBiasDense)
+      if (active) dense_row_load(rbias, wrow0 + il, L, j0, hl, bv);
 
     if (active) {
       f32x16 sacc[2];
@@ -206,7 +218,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 3 : 2) void fwd_kernel(const FwdArgs 
       // Element (kb, r): key j0 + 32kb + 8(r/4) + 4hl + r%4, query wrow0 + il.
       float bconst;
       const bool fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut,
-                                                  slope_l2, bconst);
+                                                  slope_l2, bconst, bv);
       float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
@@ -297,11 +309,16 @@ hipError_t launch_t(const FwdArgs &a, int grid, hipStream_t s) {
 
 template <int D, int BIAS>
 hipError_t launch_b(const FwdArgs &a, int grid, bool causal, bool varlen, hipStream_t s) {
-  if (causal)
-    return varlen ? launch_t<D, BIAS, true, true>(a, grid, s)
-                  : launch_t<D, BIAS, true, false>(a, grid, s);
-  return varlen ? launch_t<D, BIAS, false, true>(a, grid, s)
-                : launch_t<D, BIAS, false, false>(a, grid, s);
+  if constexpr (BIAS == kBiasDense) {   // dense entry points only
+    return causal ? launch_t<D, BIAS, true, false>(a, grid, s)
+                  : launch_t<D, BIAS, false, false>(a, grid, s);
+  } else {
+    if (causal)
+      return varlen ? launch_t<D, BIAS, true, true>(a, grid, s)
+                    : launch_t<D, BIAS, true, false>(a, grid, s);
+    return varlen ? launch_t<D, BIAS, false, true>(a, grid, s)
+                  : launch_t<D, BIAS, false, false>(a, grid, s);
+  }
 }
 
 template <int D>
@@ -310,6 +327,7 @@ hipError_t launch_d(const FwdArgs &a, int grid, int bias, bool causal, bool varl
   switch (bias) {
     case kBiasT5: return launch_b<D, kBiasT5>(a, grid, causal, varlen, s);
     case kBiasAlibi: return launch_b<D, kBiasAlibi>(a, grid, causal, varlen, s);
+    case kBiasDense: return launch_b<D, kBiasDense>(a, grid, causal, varlen, s);
     default: return launch_b<D, kBiasNone>(a, grid, causal, varlen, s);
   }
 }
@@ -329,6 +347,8 @@ hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sc
   a.sched = sched;
   a.table = p.table;
   a.slopes = p.slopes;
+  a.dense = p.dense;
+  a.dense_batch = p.dense_batch;
   a.nbatch = p.nbatch;
   a.seqlen = p.seqlen;
   a.heads = p.heads;

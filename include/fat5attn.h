@@ -76,10 +76,17 @@ typedef enum {
   FA_ERR_HIP = -4          /* a HIP launch failed                            */
 } fa_status;
 
-typedef enum { FA_BIAS_NONE = 0, FA_BIAS_T5 = 1, FA_BIAS_ALIBI = 2 } fa_bias_mode;
+typedef enum {
+  FA_BIAS_NONE = 0,
+  FA_BIAS_T5 = 1,
+  FA_BIAS_ALIBI = 2,
+  FA_BIAS_DENSE = 3
+} fa_bias_mode;
 
 /* Additive score bias.  FAT5 report, "Noyau CUDA": the second kernel is
- * handed the compact bucket tensor T instead of a dense bias matrix. */
+ * handed the compact bucket tensor T instead of a dense bias matrix; the
+ * first kernel was handed the bias matrix B itself (FA_BIAS_DENSE: memory
+ * quadratic in the sequence length, dense entry points only). */
 typedef struct {
   int32_t mode;            /* fa_bias_mode                                     */
   int32_t num_buckets;     /* T5 only                                          */
@@ -87,6 +94,11 @@ typedef struct {
   int32_t bidirectional;   /* T5 only: 1 encoder style, 0 decoder style        */
   const float *table;      /* T5: device fp32 [num_buckets, H]                 */
   const float *slopes;     /* ALiBi: device fp32 [H]                           */
+  const void *dense;       /* DENSE: device bf16 [dense_batch, H, S, S], row =
+                              query, column = key, added to scale * Q K^T     */
+  int32_t dense_batch;     /* DENSE: 1 (one matrix per head, shared by the
+                              batch) or B; S <= 16384                         */
+  int32_t reserved2;       /* must be 0                                        */
 } fa_bias;
 
 /* Dense forward: q, k, v [B, S, H, D] bf16 in; o [B, S, H, D] bf16 and
@@ -113,9 +125,12 @@ typedef struct {
  * recomputed from fp32 P; dO_i . O_i only centres that sum, so an O other than
  * the forward's costs accuracy, not correctness (a non-finite centre is
  * dropped).  dout [B, S, H, D] bf16 in; dq, dk,
- * dv [B, S, H, D] bf16 out; dtable fp32 [num_buckets, H] out (T5 only, may be
- * NULL to skip the bias gradient): the sum over the batch and over every
- * visible (query, key) pair in bucket b of dL/dS'. */
+ * dv [B, S, H, D] bf16 out.  dtable is the bias gradient (may be NULL to skip
+ * it): T5, fp32 [num_buckets, H], the sum over the batch and over every
+ * visible (query, key) pair in bucket b of dL/dS'; DENSE, fp32
+ * [dense_batch, H, S, S], dL/dS' itself (0 for masked pairs), summed over
+ * the batch when dense_batch is 1 (that case needs B*H*S*S*4 bytes of
+ * workspace when B > 1); other modes ignore it. */
 typedef struct {
   fa_fwd_params f;
   const void *dout;

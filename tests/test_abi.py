@@ -53,7 +53,7 @@ def test_status_strings_and_version(lib):
 
 STRUCTS = {
     "fa_bias": (_lib.FaBias, ["mode", "num_buckets", "max_distance", "bidirectional", "table",
-                              "slopes"]),
+                              "slopes", "dense", "dense_batch", "reserved2"]),
     "fa_fwd_params": (_lib.FaFwdParams, ["batch", "seqlen", "heads", "head_dim", "causal",
                                          "scale", "rope_base", "reserved", "q", "k", "v", "o",
                                          "lse", "bias"]),
@@ -128,6 +128,16 @@ def _dense(**kw):
     ({"bias_mode": _lib.FA_BIAS_ALIBI, "bias_slopes": 0x3000}, _lib.FA_OK),
     ({"bias_mode": _lib.FA_BIAS_NONE, "bias_table": None}, _lib.FA_OK),
     ({"bias_bidirectional": 0, "bias_num_buckets": 31}, _lib.FA_OK),
+    ({"bias_reserved2": 1}, _lib.FA_ERR_INVALID),
+    ({"bias_mode": _lib.FA_BIAS_DENSE}, _lib.FA_ERR_INVALID),   # dense NULL
+    ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense": 0x6000, "bias_dense_batch": 1}, _lib.FA_OK),
+    ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense": 0x6000, "bias_dense_batch": 2}, _lib.FA_OK),
+    ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense": 0x6000, "bias_dense_batch": 3},
+     _lib.FA_ERR_INVALID),
+    ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense": 0x6000, "bias_dense_batch": 0},
+     _lib.FA_ERR_INVALID),
+    ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense": 0x6000, "bias_dense_batch": 1,
+      "seqlen": 20000}, _lib.FA_ERR_UNSUPPORTED),
 ])
 def test_dense_checks(lib, change, status):
     p = _dense(**change)
@@ -170,6 +180,9 @@ def test_varlen_checks(lib):
     b.f = p
     b.dout = b.dq = b.dk = b.dv = 0x4000
     assert lib.fa_check_varlen_bwd(ctypes.byref(b)) == _lib.FA_OK
+    # a dense bias matrix belongs to the dense entry points
+    p.bias.mode, p.bias.dense, p.bias.dense_batch = _lib.FA_BIAS_DENSE, 0x6000, 1
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == _lib.FA_ERR_UNSUPPORTED
 
 
 def test_workspace_sizes(lib):
@@ -181,6 +194,23 @@ def test_workspace_sizes(lib):
     assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == 2 * ((one + 255) // 256 * 256)
     # a call that needs a workspace refuses without one
     assert lib.fa_fwd(ctypes.byref(p), None, 0, None) == _lib.FA_ERR_WORKSPACE
+
+
+def test_dense_bias_gradient_workspace(lib):
+    """A shared (dense_batch 1) dense bias over B > 1 sums per-batch
+    gradients from the workspace; one matrix per batch needs none."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    b = _lib.FaBwdParams()
+    b.f = _dense(bias_mode=_lib.FA_BIAS_DENSE, bias_dense=0x6000, bias_dense_batch=1)
+    b.dout = b.dq = b.dk = b.dv = 0x4000
+    B, S, H = b.f.batch, b.f.seqlen, b.f.heads
+    delta = a256(B * S * H * 4)
+    assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == delta           # no gradient asked
+    b.dtable = 0x7000
+    assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == delta + a256(B * H * S * S * 4)
+    b.f.bias.dense_batch = B
+    assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == delta
 
 
 def test_t5_buckets_checks(lib):
