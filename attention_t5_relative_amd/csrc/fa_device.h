@@ -230,14 +230,31 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
 // 4hl + r%4, from a buffer over one [S, S] bf16 matrix (row stride S).
 // Rows past the matrix read as 0; keys past S read the next row, which the
 // key mask then hides.
+// When S is a multiple of 4, each group of 4 keys starts 8-byte aligned and
+// is fetched with one 8-byte load.
 __device__ __forceinline__ void dense_row_load(rsrc_t rb, int row, int S, int j0, int hl,
                                                uint16_t (&bv)[2][16]) {
   const uint32_t base = (uint32_t)row * (uint32_t)S + (uint32_t)(j0 + 4 * hl);
+  if ((S & 3) == 0) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      bv[kb][r] = buf_load_u16(rb, (base + 32 * kb + 8 * (r >> 2) + (r & 3)) * 2u);
+      for (int g = 0; g < 4; ++g) {
+        const uint2 w = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, (int)((base + 32 * kb + 8 * g) * 2u),
+                                                        0, 0));
+        bv[kb][4 * g] = (uint16_t)w.x;
+        bv[kb][4 * g + 1] = (uint16_t)(w.x >> 16);
+        bv[kb][4 * g + 2] = (uint16_t)w.y;
+        bv[kb][4 * g + 3] = (uint16_t)(w.y >> 16);
+      }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        bv[kb][r] = buf_load_u16(rb, (base + 32 * kb + 8 * (r >> 2) + (r & 3)) * 2u);
+  }
 }
 
 // Per-lane LDS element offset for the transposing read that assembles an

@@ -14,7 +14,14 @@ HIP events through the library's fa_set_kernel_timer hook, on the stream it
 runs on) against the 2.5 PFLOP/s dense bf16 MFMA peak.  "cpu_baseline" times
 the fp64 NumPy oracle on a bounded sample of the same workload on the host.
 
+``--bias dense`` runs the same step with the report's first-kernel semantics
+instead: a dense bf16 bias matrix [1, H, S, S] shared by the batch, and its
+fp32 gradient.  Its line is bound by HBM traffic (the matrix is read by all
+three kernels and its gradient written per batch, then summed), so
+"roofline" there counts algorithmic bytes.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+                    [--bias t5|dense]
 """
 from __future__ import annotations
 
@@ -30,7 +37,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd+bwd TFLOP/s (fraction of bf16 MFMA peak), T5-bias, seq 4096 d64"
+METRIC_DENSE = ("attention fwd+bwd TFLOP/s, dense bias matrix (first-kernel semantics), "
+                "seq 4096 d64")
 PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_GBS = 8000.0           # MI355X HBM3E
 B, S, H, D = 8, 4096, 12, 64
 NB, MD = 32, 128
 SEED = 3
@@ -83,8 +93,9 @@ def _traffic(kernel: str):
         return None
 
 
-def cpu_baseline(inp, pairs):
-    """The fp64 oracle, as it stands, on `pairs` (batch, head) of the workload."""
+def cpu_baseline(inp, pairs, dense=None):
+    """The fp64 oracle, as it stands, on `pairs` (batch, head) of the workload
+    (with `dense`, the dense bias matrix [1, H, S, S] as float64)."""
     import numpy as np
     import oracle
     try:
@@ -96,6 +107,8 @@ def cpu_baseline(inp, pairs):
     q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
     kw = dict(scale=1.0, causal=True, bias="t5", table=inp.table, num_buckets=NB,
               max_distance=MD, bidirectional=False)
+    if dense is not None:
+        kw = dict(scale=1.0, causal=True, bias="dense", dense=dense)
     t0 = time.perf_counter()
     oracle.attention_fwd(q, k, v, pairs=pairs, **kw)
     oracle.attention_bwd(q, k, v, do, pairs=pairs, **kw)
@@ -115,6 +128,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=12)
+    ap.add_argument("--bias", choices=("t5", "dense"), default="t5")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB before the "
                          "timed steps (a known-size kernel to calibrate HBM byte counters)")
@@ -140,12 +154,18 @@ def main(argv=None):
             torch.bfloat16).to(dev)
 
     q, k, v, do = (up(getattr(inp, n)) for n in ("q", "k", "v", "do"))
-    table = torch.from_numpy(inp.table).to(dev)
-    bias = fa.T5Bias(table, NB, MD, bidirectional=False)
+    dense_bits = None
+    if a.bias == "dense":
+        dense_bits = synth.draw_dense_bias(SEED + 100, 1, H, S)
+        bias = fa.DenseBias(up(dense_bits))
+        dtable = torch.empty((1, H, S, S), dtype=torch.float32, device=dev)
+    else:
+        table = torch.from_numpy(inp.table).to(dev)
+        bias = fa.T5Bias(table, NB, MD, bidirectional=False)
+        dtable = torch.empty_like(table)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    dtable = torch.empty_like(table)
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
 
     def step():
@@ -203,9 +223,31 @@ def main(argv=None):
     dom = max(kernel_ms, key=kernel_ms.get)
     achieved = algo[dom] / (kernel_ms[dom] * 1e-3) / 1e12
     value = step_flops / (ms_step * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                "traffic": _traffic(dom)}
+    if a.bias == "dense":
+        # algorithmic bytes per launch: the bf16 tensors each kernel must read
+        # and write once, plus one bias element per visible pair (bf16) and,
+        # for dkv, one fp32 gradient element per visible pair and batch
+        t_bytes = B * S * H * D * 2
+        rows = B * H * S * 4
+        pairs = B * H * S * (S + 1) / 2
+        abytes = {"fwd": 4 * t_bytes + rows + pairs * 2,
+                  "bwd_dq": 6 * t_bytes + 2 * rows + pairs * 2,
+                  "bwd_dkv": 6 * t_bytes + 2 * rows + pairs * (2 + 4)}
+        gbs = abytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1), "peak": PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None}
 
+    workload = ("causal decoder self-attention fwd+bwd with unidirectional T5 bias "
+                "(32 buckets, max distance 128), B8 H12 S4096 D64, scale 1")
+    if a.bias == "dense":
+        workload = ("causal decoder self-attention fwd+bwd with a dense bf16 bias matrix "
+                    "[1, H, S, S] shared by the batch and its fp32 gradient, B8 H12 S4096 D64, "
+                    "scale 1")
     line = {
-        "metric": METRIC,
+        "metric": METRIC if a.bias == "t5" else METRIC_DENSE,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -218,8 +260,7 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "causal decoder self-attention fwd+bwd with unidirectional T5 bias "
-                        "(32 buckets, max distance 128), B8 H12 S4096 D64, scale 1",
+            "workload": workload,
             "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
             "parallelism": "none (one GPU)",
             "frac_of_peak": round(value / PEAK_TFLOPS, 4),
@@ -227,20 +268,15 @@ def main(argv=None):
             "fwd_tflops": round(fwd_flops / (kernel_ms["fwd"] * 1e-3) / 1e12, 2),
             "host_wall_ms_per_step": round(wall / a.steps * 1e3, 4),
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": dom,
-            "achieved": round(achieved, 2),
-            "peak": PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_TFLOPS, 4),
-            "traffic": _traffic(dom),
-        },
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:
         pairs = [(i % B, (5 * i + 1) % H) for i in range(min(a.cpu_pairs, B * H))]
-        line["cpu_baseline"] = cpu_baseline(inp, pairs)
+        dense = None
+        if dense_bits is not None:
+            dense = synth.bf16_bits_to_f32(dense_bits).astype(np.float64)
+        line["cpu_baseline"] = cpu_baseline(inp, pairs, dense)
     print(json.dumps(line), flush=True)
     return 0
 
