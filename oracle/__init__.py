@@ -19,6 +19,8 @@ Sources (the pages this method is described on):
   kernels also serve ALiBi and RoPE.
 * Blog on DataCollatorWithFlattening and flash_attn_varlen_func: packed
   batches attend only within each example.
+* FAT5 report, Triton-kernel section and "Torch vs Triton": the fused
+  RMSNorm layer and cross-entropy loss with z-loss (``oracle.norm_loss``).
 
 The pages print no formula for the T5 buckets, ALiBi or RoPE, no backward
 equations and no worked numbers; the readings taken here are listed in the
@@ -38,4 +40,10 @@ from .attention import (  # noqa: F401
     varlen_attention_fwd,
     varlen_attention_bwd,
     segment_ids,
+)
+from .norm_loss import (  # noqa: F401
+    cross_entropy_bwd,
+    cross_entropy_fwd,
+    rmsnorm_bwd,
+    rmsnorm_fwd,
 )
