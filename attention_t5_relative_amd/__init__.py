@@ -11,12 +11,18 @@ from .api import (  # noqa: F401
     T5Bias,
     alibi_slopes,
     attention,
+    cross_entropy,
     fa_bwd,
+    fa_ce_bwd,
+    fa_ce_fwd,
     fa_fwd,
     fa_fwd_workspace_size,
+    fa_rmsnorm_bwd,
+    fa_rmsnorm_fwd,
     fa_t5_buckets,
     fa_varlen_bwd,
     fa_varlen_fwd,
+    rms_norm,
     varlen_attention,
 )
 from ._lib import LIB_PATH, FaError, load  # noqa: F401

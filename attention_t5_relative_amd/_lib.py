@@ -20,6 +20,10 @@ FA_ERR_HIP = -4
 FA_KERNEL_FWD = 0
 FA_KERNEL_BWD_DQ = 1
 FA_KERNEL_BWD_DKV = 2
+FA_KERNEL_RMSNORM_FWD = 3
+FA_KERNEL_RMSNORM_BWD = 4
+FA_KERNEL_CE_FWD = 5
+FA_KERNEL_CE_BWD = 6
 
 FA_BIAS_NONE = 0
 FA_BIAS_T5 = 1
@@ -61,6 +65,24 @@ class FaVarlenBwdParams(ctypes.Structure):
                 ("dv", c_ptr), ("dtable", c_ptr)]
 
 
+class FaRmsnormFwdParams(ctypes.Structure):
+    _fields_ = [("rows", c_i32), ("dim", c_i32), ("eps", c_f32), ("reserved", c_i32),
+                ("x", c_ptr), ("w", c_ptr), ("y", c_ptr), ("rstd", c_ptr)]
+
+
+class FaRmsnormBwdParams(ctypes.Structure):
+    _fields_ = [("f", FaRmsnormFwdParams), ("dy", c_ptr), ("dx", c_ptr), ("dw", c_ptr)]
+
+
+class FaCeFwdParams(ctypes.Structure):
+    _fields_ = [("rows", c_i32), ("vocab", c_i32), ("z_loss", c_f32), ("ignore_index", c_i32),
+                ("logits", c_ptr), ("labels", c_ptr), ("loss", c_ptr), ("lse", c_ptr)]
+
+
+class FaCeBwdParams(ctypes.Structure):
+    _fields_ = [("f", FaCeFwdParams), ("dloss", c_ptr), ("dlogits", c_ptr)]
+
+
 # Every symbol the header declares, with its ctypes signature.
 SIGNATURES = {
     "fa_check_fwd": (c_i32, [ctypes.POINTER(FaFwdParams)]),
@@ -76,6 +98,12 @@ SIGNATURES = {
     "fa_varlen_fwd": (c_i32, [ctypes.POINTER(FaVarlenFwdParams), c_ptr, ctypes.c_size_t, c_ptr]),
     "fa_varlen_bwd": (c_i32, [ctypes.POINTER(FaVarlenBwdParams), c_ptr, ctypes.c_size_t, c_ptr]),
     "fa_t5_buckets": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr, c_ptr]),
+    "fa_rmsnorm_fwd": (c_i32, [ctypes.POINTER(FaRmsnormFwdParams), c_ptr]),
+    "fa_rmsnorm_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(FaRmsnormBwdParams)]),
+    "fa_rmsnorm_bwd": (c_i32, [ctypes.POINTER(FaRmsnormBwdParams), c_ptr, ctypes.c_size_t,
+                               c_ptr]),
+    "fa_ce_fwd": (c_i32, [ctypes.POINTER(FaCeFwdParams), c_ptr]),
+    "fa_ce_bwd": (c_i32, [ctypes.POINTER(FaCeBwdParams), c_ptr]),
     "fa_set_kernel_timer": (c_i32, [c_i32, c_ptr, c_ptr]),
     "fa_status_str": (ctypes.c_char_p, [c_i32]),
     "fa_last_error": (ctypes.c_char_p, []),

@@ -320,3 +320,138 @@ def varlen_attention(q, k, v, cu_seqlens, max_seqlen, *, bias: BiasSpec = None, 
     o, lse = _VarlenAttention.apply(q, k, v, table, cu_seqlens, max_seqlen, bias, scale, causal,
                                     rope_base)
     return (o, lse) if return_lse else o
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm and cross-entropy with z-loss (the report's two other fused kernels)
+# ---------------------------------------------------------------------------
+
+
+def _rms_params(x, w, y, rstd, eps) -> _lib.FaRmsnormFwdParams:
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, dim]")
+    rows, dim = x.shape
+    _need(x, "x", torch.bfloat16, (rows, dim))
+    _need(w, "w", torch.bfloat16, (dim,), x.device)
+    _need(y, "y", torch.bfloat16, (rows, dim), x.device)
+    _need(rstd, "rstd", torch.float32, (rows,), x.device)
+    p = _lib.FaRmsnormFwdParams()
+    p.rows, p.dim, p.eps = rows, dim, float(eps)
+    p.x, p.w, p.y, p.rstd = x.data_ptr(), w.data_ptr(), y.data_ptr(), rstd.data_ptr()
+    return p
+
+
+def fa_rmsnorm_fwd(x, w, y, rstd, *, eps=1e-6, stream=None) -> None:
+    """y = x / sqrt(mean x^2 + eps) * w into y [rows, dim] bf16, rstd [rows] fp32."""
+    lib = _lib.load()
+    p = _rms_params(x, w, y, rstd, eps)
+    check(lib.fa_rmsnorm_fwd(ctypes.byref(p), _stream(x.device, stream)), "fa_rmsnorm_fwd")
+
+
+def fa_rmsnorm_bwd(x, w, rstd, dy, dx, dw=None, *, eps=1e-6, workspace=None,
+                   stream=None) -> None:
+    """dx [rows, dim] bf16 and dw [dim] fp32 (optional) of RMSNorm."""
+    lib = _lib.load()
+    p = _lib.FaRmsnormBwdParams()
+    p.f = _rms_params(x, w, x, rstd, eps)   # y is not read by the backward
+    _need(dy, "dy", torch.bfloat16, x.shape, x.device)
+    _need(dx, "dx", torch.bfloat16, x.shape, x.device)
+    if dw is not None:
+        _need(dw, "dw", torch.float32, (x.shape[1],), x.device)
+    p.dy, p.dx, p.dw = dy.data_ptr(), dx.data_ptr(), _ptr(dw)
+    ws, wsb = _workspace(lib.fa_rmsnorm_bwd_workspace_size(ctypes.byref(p)), x.device, workspace)
+    check(lib.fa_rmsnorm_bwd(ctypes.byref(p), _ptr(ws), wsb, _stream(x.device, stream)),
+          "fa_rmsnorm_bwd")
+
+
+def _ce_params(logits, labels, loss, lse, z_loss, ignore_index) -> _lib.FaCeFwdParams:
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, vocab]")
+    rows, vocab = logits.shape
+    _need(logits, "logits", torch.bfloat16, (rows, vocab))
+    _need(labels, "labels", torch.int32, (rows,), logits.device)
+    _need(loss, "loss", torch.float32, (rows,), logits.device)
+    _need(lse, "lse", torch.float32, (rows,), logits.device)
+    p = _lib.FaCeFwdParams()
+    p.rows, p.vocab, p.z_loss, p.ignore_index = rows, vocab, float(z_loss), int(ignore_index)
+    p.logits, p.labels = logits.data_ptr(), labels.data_ptr()
+    p.loss, p.lse = loss.data_ptr(), lse.data_ptr()
+    return p
+
+
+def fa_ce_fwd(logits, labels, loss, lse, *, z_loss=0.0, ignore_index=-100, stream=None) -> None:
+    """Per-row loss lse - z_y + z_loss lse^2 into loss [rows] and lse [rows] (fp32)."""
+    lib = _lib.load()
+    p = _ce_params(logits, labels, loss, lse, z_loss, ignore_index)
+    check(lib.fa_ce_fwd(ctypes.byref(p), _stream(logits.device, stream)), "fa_ce_fwd")
+
+
+def fa_ce_bwd(logits, labels, lse, dloss, dlogits, *, z_loss=0.0, ignore_index=-100,
+              stream=None) -> None:
+    """dlogits [rows, vocab] bf16 for dL/dloss = dloss [rows] (may be logits itself)."""
+    lib = _lib.load()
+    p = _lib.FaCeBwdParams()
+    p.f = _ce_params(logits, labels, lse, lse, z_loss, ignore_index)   # loss is not read
+    _need(dloss, "dloss", torch.float32, (logits.shape[0],), logits.device)
+    _need(dlogits, "dlogits", torch.bfloat16, logits.shape, logits.device)
+    p.dloss, p.dlogits = dloss.data_ptr(), dlogits.data_ptr()
+    check(lib.fa_ce_bwd(ctypes.byref(p), _stream(logits.device, stream)), "fa_ce_bwd")
+
+
+class _RMSNorm(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, w, eps):
+        y = torch.empty_like(x)
+        rstd = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+        fa_rmsnorm_fwd(x, w, y, rstd, eps=eps)
+        ctx.save_for_backward(x, w, rstd)
+        ctx.eps = eps
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w, rstd = ctx.saved_tensors
+        dx = torch.empty_like(x)
+        dw = torch.empty(w.shape, dtype=torch.float32, device=w.device) if w.requires_grad else None
+        fa_rmsnorm_bwd(x, w, rstd, dy.contiguous(), dx, dw, eps=ctx.eps)
+        return dx, (None if dw is None else dw.to(w.dtype)), None
+
+
+def rms_norm(x, w, eps=1e-6):
+    """RMSNorm over the last dimension of bf16 x (any leading shape), weight w [dim]."""
+    shape = x.shape
+    return _RMSNorm.apply(x.reshape(-1, shape[-1]).contiguous(), w, eps).reshape(shape)
+
+
+class _CrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, labels, z_loss, ignore_index):
+        rows = logits.shape[0]
+        loss = torch.empty(rows, dtype=torch.float32, device=logits.device)
+        lse = torch.empty_like(loss)
+        fa_ce_fwd(logits, labels, loss, lse, z_loss=z_loss, ignore_index=ignore_index)
+        ctx.save_for_backward(logits, labels, lse)
+        ctx.z_loss, ctx.ignore_index = z_loss, ignore_index
+        return loss
+
+    @staticmethod
+    def backward(ctx, dloss):
+        logits, labels, lse = ctx.saved_tensors
+        dlogits = torch.empty_like(logits)
+        fa_ce_bwd(logits, labels, lse, dloss.contiguous().float(), dlogits, z_loss=ctx.z_loss,
+                  ignore_index=ctx.ignore_index)
+        return dlogits, None, None, None
+
+
+def cross_entropy(logits, labels, *, z_loss=0.0, ignore_index=-100, reduction="mean"):
+    """Cross-entropy with z-loss over bf16 logits [rows, vocab] and int labels [rows];
+    reduction 'none' returns the per-row loss, 'mean' averages over the rows whose
+    label is not ignored, 'sum' adds them."""
+    loss = _CrossEntropy.apply(logits.contiguous(), labels.to(torch.int32).contiguous(),
+                               float(z_loss), int(ignore_index))
+    if reduction == "none":
+        return loss
+    if reduction == "sum":
+        return loss.sum()
+    valid = ((labels != ignore_index) & (labels >= 0) & (labels < logits.shape[1])).sum()
+    return loss.sum() / valid.clamp(min=1)

@@ -557,6 +557,113 @@ fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes
                  p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm and cross-entropy
+// ---------------------------------------------------------------------------
+static fa_status check_rms_fwd(const fa_rmsnorm_fwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID, "params is NULL");
+  if (p->rows < 0) return fail(FA_ERR_INVALID, "rows=%d is negative", p->rows);
+  if (p->dim <= 0) return fail(FA_ERR_INVALID, "dim=%d must be > 0", p->dim);
+  if (p->dim % 8 != 0 || p->dim > fa::kRmsMaxDim)
+    return fail(FA_ERR_UNSUPPORTED, "dim=%d must be a multiple of 8 and at most %d", p->dim,
+                fa::kRmsMaxDim);
+  if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(FA_ERR_INVALID, "eps must be >= 0");
+  if (p->reserved != 0) return fail(FA_ERR_INVALID, "reserved must be 0");
+  if (p->rows > 0 && (!p->x || !p->w || !p->y || !p->rstd))
+    return fail(FA_ERR_INVALID, "x, w, y and rstd must be non-NULL");
+  return FA_OK;
+}
+
+static fa_status check_rms_bwd(const fa_rmsnorm_bwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID, "params is NULL");
+  const fa_status st = check_rms_fwd(&p->f);
+  if (st != FA_OK) return st;
+  if (p->f.rows > 0 && (!p->dy || !p->dx)) return fail(FA_ERR_INVALID, "dy, dx must be non-NULL");
+  return FA_OK;
+}
+
+static fa_status check_ce_fwd(const fa_ce_fwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID, "params is NULL");
+  if (p->rows < 0) return fail(FA_ERR_INVALID, "rows=%d is negative", p->rows);
+  if (p->vocab <= 0) return fail(FA_ERR_INVALID, "vocab=%d must be > 0", p->vocab);
+  if (p->vocab % 8 != 0) return fail(FA_ERR_UNSUPPORTED, "vocab=%d must be a multiple of 8",
+                                     p->vocab);
+  if (!std::isfinite(p->z_loss) || p->z_loss < 0.f)
+    return fail(FA_ERR_INVALID, "z_loss must be finite and >= 0");
+  if (p->rows > 0 && (!p->logits || !p->labels || !p->loss || !p->lse))
+    return fail(FA_ERR_INVALID, "logits, labels, loss and lse must be non-NULL");
+  return FA_OK;
+}
+
+fa_status fa_rmsnorm_fwd(const fa_rmsnorm_fwd_params *p, hipStream_t stream) {
+  g_last_error.clear();
+  const fa_status st = check_rms_fwd(p);
+  if (st != FA_OK) return st;
+  if (p->rows == 0) return FA_OK;
+  const hipError_t e = timed(FA_KERNEL_RMSNORM_FWD, stream, [&] {
+    return fa::launch_rmsnorm_fwd(p->x, p->w, p->y, p->rstd, p->rows, p->dim, p->eps, stream);
+  });
+  return e == hipSuccess ? FA_OK : hip_fail(e, "rmsnorm forward");
+}
+
+size_t fa_rmsnorm_bwd_workspace_size(const fa_rmsnorm_bwd_params *p) {
+  g_last_error.clear();
+  if (check_rms_bwd(p) != FA_OK) return (size_t)-1;
+  if (p->f.rows == 0 || p->dw == nullptr) return 0;
+  return (size_t)fa::rmsnorm_bwd_grid(p->f.rows) * p->f.dim * 4;
+}
+
+fa_status fa_rmsnorm_bwd(const fa_rmsnorm_bwd_params *p, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  g_last_error.clear();
+  const fa_status st = check_rms_bwd(p);
+  if (st != FA_OK) return st;
+  hipError_t e;
+  if (p->f.rows == 0) {
+    if (p->dw == nullptr) return FA_OK;
+    e = fa::launch_fill_f32(p->dw, (size_t)p->f.dim, 0.f, stream);   // empty sum
+    return e == hipSuccess ? FA_OK : hip_fail(e, "fill");
+  }
+  const size_t need = fa_rmsnorm_bwd_workspace_size(p);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  float *part = need > 0 ? static_cast<float *>(ws) : nullptr;
+  e = timed(FA_KERNEL_RMSNORM_BWD, stream, [&] {
+    return fa::launch_rmsnorm_bwd(p->f.x, p->f.w, p->f.rstd, p->dy, p->dx, nullptr, part,
+                                  p->f.rows, p->f.dim, stream);
+  });
+  if (e == hipSuccess && p->dw != nullptr)
+    e = fa::launch_rmsnorm_dw(part, p->dw, p->f.rows, p->f.dim, stream);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "rmsnorm backward");
+}
+
+fa_status fa_ce_fwd(const fa_ce_fwd_params *p, hipStream_t stream) {
+  g_last_error.clear();
+  const fa_status st = check_ce_fwd(p);
+  if (st != FA_OK) return st;
+  if (p->rows == 0) return FA_OK;
+  const hipError_t e = timed(FA_KERNEL_CE_FWD, stream, [&] {
+    return fa::launch_ce_fwd(p->logits, p->labels, p->loss, p->lse, p->rows, p->vocab, p->z_loss,
+                             p->ignore_index, stream);
+  });
+  return e == hipSuccess ? FA_OK : hip_fail(e, "cross-entropy forward");
+}
+
+fa_status fa_ce_bwd(const fa_ce_bwd_params *p, hipStream_t stream) {
+  g_last_error.clear();
+  if (!p) return fail(FA_ERR_INVALID, "params is NULL");
+  const fa_status st = check_ce_fwd(&p->f);
+  if (st != FA_OK) return st;
+  if (p->f.rows == 0) return FA_OK;
+  if (!p->dloss || !p->dlogits) return fail(FA_ERR_INVALID, "dloss, dlogits must be non-NULL");
+  const hipError_t e = timed(FA_KERNEL_CE_BWD, stream, [&] {
+    return fa::launch_ce_bwd(p->f.logits, p->f.labels, p->f.lse, p->dloss, p->dlogits, p->f.rows,
+                             p->f.vocab, p->f.z_loss, p->f.ignore_index, stream);
+  });
+  return e == hipSuccess ? FA_OK : hip_fail(e, "cross-entropy backward");
+}
+
 fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t max_distance,
                         int32_t bidirectional, int32_t *out, hipStream_t stream) {
   g_last_error.clear();

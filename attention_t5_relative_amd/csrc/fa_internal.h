@@ -92,6 +92,24 @@ hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
 // `nbatch` [H, S, S] slabs into one (pairs with key > query set to 0 when
 // causal, without reading them).
 hipError_t launch_zero_upper(float *m, int count, int S, hipStream_t s);
+
+// RMSNorm and cross-entropy (norm_loss.hip).  rmsnorm_bwd's dw partials are
+// one fp32 row per workgroup: rmsnorm_bwd_grid(rows) * dim floats.
+constexpr int kRmsMaxDim = 8192;
+constexpr int kRmsBwdMaxGrid = 1024;
+int rmsnorm_chunks_per_lane(int dim);
+int rmsnorm_bwd_grid(int rows);
+hipError_t launch_rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int rows,
+                              int dim, float eps, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const void *x, const void *w, const float *rstd, const void *dy,
+                              void *dx, float *dw, float *part, int rows, int dim,
+                              hipStream_t s);
+hipError_t launch_rmsnorm_dw(const float *part, float *dw, int rows, int dim, hipStream_t s);
+hipError_t launch_ce_fwd(const void *z, const int32_t *labels, float *loss, float *lse, int rows,
+                         int vocab, float z_loss, int ignore, hipStream_t s);
+hipError_t launch_ce_bwd(const void *z, const int32_t *labels, const float *lse,
+                         const float *dloss, void *dz, int rows, int vocab, float z_loss,
+                         int ignore, hipStream_t s);
 hipError_t launch_batch_sum(const float *src, float *dst, int nbatch, int heads, int S,
                             bool causal, hipStream_t s);
 

@@ -20,8 +20,13 @@ fp32 gradient.  Its line is bound by HBM traffic (the matrix is read by all
 three kernels and its gradient written per batch, then summed), so
 "roofline" there counts algorithmic bytes.
 
+``--workload rmsnorm`` and ``--workload ce`` time the report's two other fused
+kernels (RMSNorm, cross-entropy with z-loss) forward + backward on the same
+32768 tokens (width 768; T5 vocabulary 32128); both are bound by HBM, so their
+value is algorithmic GB/s (each tensor read or written once per pass).
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-                    [--bias t5|dense]
+                    [--bias t5|dense] [--workload attention|rmsnorm|ce]
 """
 from __future__ import annotations
 
@@ -121,6 +126,149 @@ def cpu_baseline(inp, pairs, dense=None):
                       f"flop count per pair as the GPU value"}
 
 
+NL_ROWS, RMS_DIM, CE_VOCAB, Z_LOSS = 32768, 768, 32128, 1e-4
+
+
+def bench_norm_loss(a):
+    """RMSNorm or cross-entropy (+ z-loss) forward + backward, GB/s."""
+    import numpy as np
+    import torch
+
+    import attention_t5_relative_amd as fa
+    import synth
+    from attention_t5_relative_amd import _lib
+
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    N = NL_ROWS
+    if a.workload == "rmsnorm":
+        d = RMS_DIM
+        xb, wb, dyb = synth.draw_rmsnorm(SEED, N, d)
+        x, w, dy = up(xb), up(wb), up(dyb)
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        rstd = torch.empty(N, dtype=torch.float32, device=dev)
+        dw = torch.empty(d, dtype=torch.float32, device=dev)
+        lib = _lib.load()
+        p = _lib.FaRmsnormBwdParams()
+        p.f = fa.api._rms_params(x, w, y, rstd, 1e-6)
+        p.dy, p.dx, p.dw = dy.data_ptr(), dx.data_ptr(), dw.data_ptr()
+        ws = torch.empty(max(1, lib.fa_rmsnorm_bwd_workspace_size(ctypes.byref(p))),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.fa_rmsnorm_fwd(x, w, y, rstd, eps=1e-6)
+            fa.fa_rmsnorm_bwd(x, w, rstd, dy, dx, dw, eps=1e-6, workspace=ws)
+
+        kernels = {"rmsnorm_fwd": _lib.FA_KERNEL_RMSNORM_FWD,
+                   "rmsnorm_bwd": _lib.FA_KERNEL_RMSNORM_BWD}
+        t = N * d * 2
+        abytes = {"rmsnorm_fwd": 2 * t + 2 * d + 4 * N,          # x in, y out, w, rstd
+                  "rmsnorm_bwd": 3 * t + 2 * d + 4 * N}          # x, dy in, dx out (dw partials extra)
+        step_bytes = abytes["rmsnorm_fwd"] + abytes["rmsnorm_bwd"] + 4 * d
+        metric = "rmsnorm fwd+bwd GB/s (algorithmic bytes), 32768 x 768 bf16"
+        workload = ("RMSNorm (no mean, no bias, eps 1e-6) forward + backward (dx, dw) over "
+                    "32768 rows x 768 bf16, weight bf16, dw fp32")
+        cfg = {"rows": N, "dim": d}
+    else:
+        V = CE_VOCAB
+        zb, yb, gb = synth.draw_cross_entropy(SEED, N, V)
+        z = up(zb)
+        lab = torch.from_numpy(yb).to(dev)
+        g = torch.from_numpy(gb).to(dev)
+        loss = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = torch.empty_like(loss)
+        dz = torch.empty_like(z)
+        del zb
+
+        def step():
+            fa.fa_ce_fwd(z, lab, loss, lse, z_loss=Z_LOSS)
+            fa.fa_ce_bwd(z, lab, lse, g, dz, z_loss=Z_LOSS)
+
+        kernels = {"ce_fwd": _lib.FA_KERNEL_CE_FWD, "ce_bwd": _lib.FA_KERNEL_CE_BWD}
+        t = N * V * 2
+        abytes = {"ce_fwd": t + 4 * N + 8 * N,            # logits, labels in; loss, lse out
+                  "ce_bwd": 2 * t + 12 * N}                # logits in, dlogits out; labels, lse, dloss
+        step_bytes = abytes["ce_fwd"] + abytes["ce_bwd"]
+        metric = "cross-entropy + z-loss fwd+bwd GB/s (algorithmic bytes), 32768 x 32128 bf16"
+        workload = ("per-row cross-entropy with z-loss 1e-4 forward + backward over 32768 rows "
+                    "x 32128 bf16 logits (T5 vocabulary), 10% ignored labels")
+        cfg = {"rows": N, "vocab": V, "z_loss": Z_LOSS}
+
+    lib = _lib.load()
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    hip = _hip()
+    evs = {n: [(_event(hip), _event(hip)) for _ in range(a.steps)] for n in kernels}
+    t_start, t_stop = _event(hip), _event(hip)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.hipEventRecord(t_start, ctypes.c_void_p(stream))
+    for i in range(a.steps):
+        for n, kid in kernels.items():
+            lib.fa_set_kernel_timer(kid, evs[n][i][0], evs[n][i][1])
+        step()
+    hip.hipEventRecord(t_stop, ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    for kid in kernels.values():
+        lib.fa_set_kernel_timer(kid, None, None)
+    ms_step = _elapsed(hip, t_start, t_stop) / a.steps
+    kernel_ms = {n: sum(_elapsed(hip, s0, s1) for s0, s1 in evs[n]) / a.steps for n in kernels}
+    dom = max(kernel_ms, key=kernel_ms.get)
+    gbs = abytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": metric, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict({"workload": workload, "parallelism": "none (one GPU)",
+                        "kernel_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
+                        "frac_of_hbm_peak": round(value / PEAK_GBS, 4)}, **cfg),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = norm_loss_cpu_baseline(a.workload)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def norm_loss_cpu_baseline(workload):
+    """The fp64 oracle on a bounded sample of the rows, scaled to GB/s of the
+    same algorithmic bytes per row."""
+    import numpy as np
+    import oracle
+    import synth
+    rows = NL_ROWS if workload == "rmsnorm" else 2048
+    t0 = time.perf_counter()
+    if workload == "rmsnorm":
+        xb, wb, dyb = synth.draw_rmsnorm(SEED, rows, RMS_DIM)
+        x, w, dy = (synth.bf16_bits_to_f32(b).astype(np.float64) for b in (xb, wb, dyb))
+        t0 = time.perf_counter()
+        oracle.rmsnorm_fwd(x, w, 1e-6)
+        oracle.rmsnorm_bwd(x, w, dy, 1e-6)
+        per_row = 10 * RMS_DIM + 8
+    else:
+        zb, yb, gb = synth.draw_cross_entropy(SEED, rows, CE_VOCAB)
+        z = synth.bf16_bits_to_f32(zb).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.cross_entropy_fwd(z, yb, Z_LOSS)
+        oracle.cross_entropy_bwd(z, yb, gb.astype(np.float64), Z_LOSS)
+        per_row = 6 * CE_VOCAB + 24
+    dt = time.perf_counter() - t0
+    return {"value": round(rows * per_row / dt / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",   # element-wise NumPy: one thread
+            "sample": f"{rows} of {NL_ROWS} rows of the same workload, fp64 NumPy on the host "
+                      f"({dt:.2f} s); same algorithmic bytes per row as the GPU value"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +277,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=12)
     ap.add_argument("--bias", choices=("t5", "dense"), default="t5")
+    ap.add_argument("--workload", choices=("attention", "rmsnorm", "ce"), default="attention")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB before the "
                          "timed steps (a known-size kernel to calibrate HBM byte counters)")
@@ -145,6 +294,9 @@ def main(argv=None):
     import attention_t5_relative_amd as fa
     import synth
     from attention_t5_relative_amd import _lib
+
+    if a.workload != "attention":
+        return bench_norm_loss(a)
 
     dev = torch.device("cuda:0")
     inp = synth.draw_dense(SEED, B, S, H, D)

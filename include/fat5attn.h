@@ -194,6 +194,76 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *ws, size_t ws_bytes
 fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * The report's two other fused kernels (FAT5 report, section on the Triton
+ * kernels; benchmarks under "Torch vs Triton").  Both entry points take a
+ * stream, allocate nothing and follow the conventions above.
+ * ------------------------------------------------------------------------- */
+
+/* RMSNorm (the layer of Zhang & Sennrich the report cites, as T5 uses it: no
+ * mean subtraction, no bias): y = x / sqrt(mean_j x_j^2 + eps) * w per row.
+ * x, y bf16 [rows, dim]; w bf16 [dim]; rstd fp32 [rows] out, the reciprocal
+ * root mean square the backward reads.  dim a multiple of 8, at most 8192;
+ * eps finite and >= 0. */
+typedef struct {
+  int32_t rows;
+  int32_t dim;
+  float eps;
+  int32_t reserved;        /* must be 0                                        */
+  const void *x;
+  const void *w;
+  void *y;
+  float *rstd;
+} fa_rmsnorm_fwd_params;
+
+/* RMSNorm backward: dy bf16 [rows, dim] in; dx bf16 [rows, dim] out and dw
+ * fp32 [dim] out (the sum over rows; may be NULL).  f.rstd is READ (the
+ * forward's output for the same x); f.y is not used.  With dw, the call
+ * needs fa_rmsnorm_bwd_workspace_size bytes of workspace (one fp32 row of
+ * partial sums per workgroup, added in a fixed order). */
+typedef struct {
+  fa_rmsnorm_fwd_params f;
+  const void *dy;
+  void *dx;
+  float *dw;
+} fa_rmsnorm_bwd_params;
+
+fa_status fa_rmsnorm_fwd(const fa_rmsnorm_fwd_params *p, hipStream_t stream);
+size_t fa_rmsnorm_bwd_workspace_size(const fa_rmsnorm_bwd_params *p);
+fa_status fa_rmsnorm_bwd(const fa_rmsnorm_bwd_params *p, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Cross-entropy with z-loss (the z-loss of de Brebisson & Vincent the report
+ * cites), per row of bf16 logits z [rows, vocab] with int32 label y:
+ * lse = log sum_v exp z_v, loss = lse - z_y + z_loss * lse^2.  Rows whose
+ * label equals ignore_index or lies outside [0, vocab) get loss 0 and no
+ * gradient (their lse is still written).  loss, lse fp32 [rows] out; the
+ * mean over rows is the caller's.  vocab a multiple of 8; logits finite;
+ * z_loss finite and >= 0. */
+typedef struct {
+  int32_t rows;
+  int32_t vocab;
+  float z_loss;
+  int32_t ignore_index;
+  const void *logits;
+  const int32_t *labels;
+  float *loss;
+  float *lse;
+} fa_ce_fwd_params;
+
+/* Backward: dloss fp32 [rows] in (dL/dloss per row, e.g. 1/count for a
+ * mean); dlogits bf16 [rows, vocab] out = dloss * (softmax(z) * (1 + 2 z_loss
+ * lse) - onehot(y)), 0 for ignored rows.  f.lse is READ (the forward's);
+ * f.loss is not used.  dlogits may be f.logits itself (in place). */
+typedef struct {
+  fa_ce_fwd_params f;
+  const float *dloss;
+  void *dlogits;
+} fa_ce_bwd_params;
+
+fa_status fa_ce_fwd(const fa_ce_fwd_params *p, hipStream_t stream);
+fa_status fa_ce_bwd(const fa_ce_bwd_params *p, hipStream_t stream);
+
 /* Test hook: out[i * klen + j] = T5 bucket of (query i, key j), computed on
  * the device by the same threshold code the attention kernels use.  out is a
  * device int32 [qlen, klen]. */
@@ -205,7 +275,11 @@ typedef enum {
   FA_KERNEL_FWD = 0,       /* the attention forward kernel                       */
   FA_KERNEL_BWD_DQ = 1,    /* backward, query-parallel: D_i and dQ               */
   FA_KERNEL_BWD_DKV = 2,   /* backward, key-parallel: dK, dV and table gradient  */
-  FA_KERNEL_COUNT = 3
+  FA_KERNEL_RMSNORM_FWD = 3,
+  FA_KERNEL_RMSNORM_BWD = 4, /* dx and the dw partials (not their final sum)     */
+  FA_KERNEL_CE_FWD = 5,
+  FA_KERNEL_CE_BWD = 6,
+  FA_KERNEL_COUNT = 7
 } fa_kernel;
 
 /* Benchmark hook.  While set, every launch of `kernel` is bracketed by

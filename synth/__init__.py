@@ -13,6 +13,8 @@ from .gen import (  # noqa: F401
     VarlenInputs,
     draw_dense,
     draw_dense_bias,
+    draw_rmsnorm,
+    draw_cross_entropy,
     draw_varlen,
     alibi_slope_values,
 )

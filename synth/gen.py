@@ -26,10 +26,11 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     normal draws, so no NaN handling is needed; infinities pass through.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> np.uint64(16)) & np.uint64(1)
-    rounded = (bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return rounded.astype(np.uint16)
+    bits = x.view(np.uint32)
+    # bits + 0x7FFF + lsb stays below 2^32 for every non-NaN pattern (the
+    # largest, -inf, is 0xFF800000)
+    rounded = bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -126,6 +127,31 @@ def draw_dense_bias(seed: int, Bb: int, H: int, S: int, sigma: float = 1.0) -> n
     values rounded once to bfloat16 (row = query, column = key)."""
     rng = np.random.default_rng(seed)
     return bf16_round((sigma * rng.standard_normal(size=(Bb, H, S, S))).astype(np.float32))
+
+
+def draw_rmsnorm(seed: int, rows: int, dim: int):
+    """RMSNorm inputs as bf16 bits: x, dy ~ N(0, 1) [rows, dim] and the weight
+    w ~ N(1, 0.25) [dim]."""
+    rng = np.random.default_rng(seed)
+    x = _normal_bf16(rng, (rows, dim))
+    dy = _normal_bf16(rng, (rows, dim))
+    w = bf16_round((1.0 + 0.25 * rng.standard_normal(dim)).astype(np.float32))
+    return x, w, dy
+
+
+def draw_cross_entropy(seed: int, rows: int, vocab: int, sigma: float = 3.0,
+                       ignore_frac: float = 0.1, ignore_index: int = -100):
+    """Cross-entropy inputs: logits ~ N(0, sigma) as bf16 bits [rows, vocab],
+    int32 labels uniform over the vocabulary with a fraction set to the
+    ignore index, and dL/dloss per row ~ U(0.5, 1.5) / rows (fp32)."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((rows, vocab), dtype=np.float32)
+    z *= np.float32(sigma)
+    z = bf16_round(z)
+    y = rng.integers(0, vocab, rows).astype(np.int32)
+    y[rng.random(rows) < ignore_frac] = ignore_index
+    g = (rng.uniform(0.5, 1.5, rows) / max(rows, 1)).astype(np.float32)
+    return z, y, g
 
 
 def draw_varlen(seed: int, total: int, H: int, D: int, *, num_buckets: int = 32,

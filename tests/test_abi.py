@@ -39,9 +39,9 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_kernel_timer_ids(lib):
-    assert lib.fa_set_kernel_timer(3, None, None) == _lib.FA_ERR_INVALID
+    assert lib.fa_set_kernel_timer(7, None, None) == _lib.FA_ERR_INVALID
     assert lib.fa_set_kernel_timer(-1, None, None) == _lib.FA_ERR_INVALID
-    for k in range(3):
+    for k in range(7):
         assert lib.fa_set_kernel_timer(k, None, None) == _lib.FA_OK
 
 
@@ -63,6 +63,12 @@ STRUCTS = {
                                                       "cu_seqlens", "q", "k", "v", "o", "lse",
                                                       "bias"]),
     "fa_varlen_bwd_params": (_lib.FaVarlenBwdParams, ["f", "dout", "dq", "dk", "dv", "dtable"]),
+    "fa_rmsnorm_fwd_params": (_lib.FaRmsnormFwdParams, ["rows", "dim", "eps", "reserved", "x",
+                                                        "w", "y", "rstd"]),
+    "fa_rmsnorm_bwd_params": (_lib.FaRmsnormBwdParams, ["f", "dy", "dx", "dw"]),
+    "fa_ce_fwd_params": (_lib.FaCeFwdParams, ["rows", "vocab", "z_loss", "ignore_index",
+                                              "logits", "labels", "loss", "lse"]),
+    "fa_ce_bwd_params": (_lib.FaCeBwdParams, ["f", "dloss", "dlogits"]),
 }
 
 
@@ -218,3 +224,50 @@ def test_t5_buckets_checks(lib):
     assert lib.fa_t5_buckets(-1, 4, 32, 128, 1, 0x1000, None) == _lib.FA_ERR_INVALID
     assert lib.fa_t5_buckets(4, 4, 32, 128, 1, None, None) == _lib.FA_ERR_INVALID
     assert lib.fa_t5_buckets(0, 0, 32, 128, 1, None, None) == _lib.FA_OK
+
+
+def test_rmsnorm_checks_and_workspace(lib):
+    p = _lib.FaRmsnormBwdParams()
+    p.f.rows, p.f.dim, p.f.eps = 100, 768, 1e-6
+    p.f.x = p.f.w = p.f.y = p.f.rstd = 0x1000
+    p.dy = p.dx = 0x2000
+    assert lib.fa_rmsnorm_bwd_workspace_size(ctypes.byref(p)) == 0        # no dw: none
+    p.dw = 0x3000
+    assert lib.fa_rmsnorm_bwd_workspace_size(ctypes.byref(p)) == 25 * 768 * 4   # one row per wg
+    for field, val, status in (("dim", 100, _lib.FA_ERR_UNSUPPORTED),
+                               ("dim", 16384, _lib.FA_ERR_UNSUPPORTED),
+                               ("dim", 0, _lib.FA_ERR_INVALID),
+                               ("rows", -1, _lib.FA_ERR_INVALID),
+                               ("eps", -1.0, _lib.FA_ERR_INVALID),
+                               ("eps", float("inf"), _lib.FA_ERR_INVALID),
+                               ("reserved", 1, _lib.FA_ERR_INVALID),
+                               ("x", None, _lib.FA_ERR_INVALID)):
+        q = _lib.FaRmsnormFwdParams.from_buffer_copy(p.f)
+        setattr(q, field, val)
+        assert lib.fa_rmsnorm_fwd(ctypes.byref(q), None) == status, (field, val)
+        assert lib.fa_last_error() != b""
+    p.dx = None
+    assert lib.fa_rmsnorm_bwd(ctypes.byref(p), None, 0, None) == _lib.FA_ERR_INVALID
+    p.dx = 0x2000
+    # dw asked: the call refuses without its workspace
+    assert lib.fa_rmsnorm_bwd(ctypes.byref(p), None, 0, None) == _lib.FA_ERR_WORKSPACE
+
+
+def test_cross_entropy_checks(lib):
+    p = _lib.FaCeBwdParams()
+    p.f.rows, p.f.vocab, p.f.z_loss, p.f.ignore_index = 10, 32128, 1e-4, -100
+    p.f.logits = p.f.labels = p.f.loss = p.f.lse = 0x1000
+    for field, val, status in (("vocab", 1001, _lib.FA_ERR_UNSUPPORTED),
+                               ("vocab", 0, _lib.FA_ERR_INVALID),
+                               ("rows", -3, _lib.FA_ERR_INVALID),
+                               ("z_loss", -1.0, _lib.FA_ERR_INVALID),
+                               ("z_loss", float("nan"), _lib.FA_ERR_INVALID),
+                               ("labels", None, _lib.FA_ERR_INVALID)):
+        q = _lib.FaCeFwdParams.from_buffer_copy(p.f)
+        setattr(q, field, val)
+        assert lib.fa_ce_fwd(ctypes.byref(q), None) == status, (field, val)
+    assert lib.fa_ce_bwd(ctypes.byref(p), None) == _lib.FA_ERR_INVALID   # dloss, dlogits NULL
+    q = _lib.FaCeFwdParams.from_buffer_copy(p.f)
+    q.rows = 0
+    q.logits = q.labels = q.loss = q.lse = None
+    assert lib.fa_ce_fwd(ctypes.byref(q), None) == _lib.FA_OK            # empty: nothing to do
