@@ -336,6 +336,13 @@ __device__ __forceinline__ bf16x8 lds_read_tr8_at(const uint16_t *base, int off0
 // before the barrier that hands the tile to the other waves.  Copies the
 // compiler does not count can only make its own count-based waits for
 // other loads stricter, since loads complete in issue order.
+//
+// The hazard checks of the compiler do not look inside inline assembly, so
+// each copy opens with the wait states the CDNA ISA requires before it:
+// one after a scalar write of M0 (the LDS address of an LDS-bound buffer
+// load) and five after a vector instruction that writes an SGPR the buffer
+// load reads (the descriptor may be restored from a spill with
+// v_readlane_b32 just before the copy).  `s_nop 4` gives five.
 __device__ __forceinline__ i32x4 dma_desc(const void *p, uint32_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(p);
   return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
@@ -344,13 +351,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void *lds) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)lds;
 }
 __device__ __forceinline__ void dma16(i32x4 desc, uint32_t off, void *lds) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(off), "s"(desc), "{m0}"(lds_addr(lds))
                : "memory");
 }
 __device__ __forceinline__ void dma4(i32x4 desc, uint32_t off, void *lds) {
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(off), "s"(desc), "{m0}"(lds_addr(lds))
                : "memory");

@@ -99,15 +99,33 @@ __global__ __launch_bounds__(kNT) void rmsnorm_bwd_kernel(const uint16_t *x, con
   const int waves = gridDim.x * (kNT / 64);
   const uint32_t bytes = (uint32_t)dim * 2u;
   const rsrc_t rw = make_rsrc(w, bytes);
-  float wf[K][8], acc[K][8];
+  // Up to 4096 columns the weights stay unpacked in registers; wider rows
+  // keep them as bf16 pairs (the float copy would not fit beside x, dy and
+  // the dw partial) and unpack them where they are used.
+  constexpr bool kPackW = K > 8;
+  float wf[kPackW ? 1 : K][8], acc[K][8];
+  i32x4 wp[kPackW ? K : 1];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    unpack8(buf_load16(rw, (uint32_t)(lane + 64 * k) * 16u), wf[k]);
+    const i32x4 v = buf_load16(rw, (uint32_t)(lane + 64 * k) * 16u);
+    if constexpr (kPackW) wp[k] = v;
+    else unpack8(v, wf[k]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
   }
+  const auto weights = [&](int k, float (&g)[8]) {
+    if constexpr (kPackW) unpack8(wp[k], g);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = wf[k][e];
+  };
   const float inv_dim = 1.f / (float)dim;
   for (int row = blockIdx.x * (kNT / 64) + wave; row < rows; row += waves) {
+    if constexpr (kPackW) {
+      // keeps the unpacking inside the loop instead of hoisted out of it
+#pragma unroll
+      for (int k = 0; k < K; ++k) asm volatile("" : "+v"(wp[k]));
+    }
     const rsrc_t rx = make_rsrc(x + (size_t)row * dim, bytes);
     const rsrc_t rdy = make_rsrc(dy + (size_t)row * dim, bytes);
     const rsrc_t rdx = make_rsrc(dx + (size_t)row * dim, bytes);
@@ -121,21 +139,26 @@ __global__ __launch_bounds__(kNT) void rmsnorm_bwd_kernel(const uint16_t *x, con
     float dot = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      float f[8], g[8];
+      float f[8], g[8], wk[8];
       unpack8(xv[k], f);
       unpack8(dv[k], g);
+      weights(k, wk);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot = fmaf(g[e] * wf[k][e], f[e], dot);
+      for (int e = 0; e < 8; ++e) dot = fmaf(g[e] * wk[e], f[e], dot);
     }
     const float cc = wave_sum(dot) * inv_dim * r * r;
+    // unpack x and dy again below rather than keep both float copies live
+#pragma unroll
+    for (int k = 0; k < K; ++k) asm volatile("" : "+v"(xv[k]), "+v"(dv[k]));
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      float f[8], g[8], o[8];
+      float f[8], g[8], o[8], wk[8];
       unpack8(xv[k], f);
       unpack8(dv[k], g);
+      weights(k, wk);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        o[e] = r * fmaf(-f[e], cc, g[e] * wf[k][e]);
+        o[e] = r * fmaf(-f[e], cc, g[e] * wk[e]);
         acc[k][e] = fmaf(g[e] * f[e], r, acc[k][e]);
       }
       buf_store16(rdx, (uint32_t)(lane + 64 * k) * 16u, pack8(o));
