@@ -323,7 +323,7 @@ BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
     L.dq_f32 = c.take(elems * 4);
     L.dk_f32 = c.take(elems * 4);
   }
-  L.delta = c.take(tokens * p.heads * 4);
+  L.delta = c.take(2 * tokens * p.heads * 4);   // -D, then -lse / scale (lse layout each)
   if (p.varlen) {
     const int bt = fa::bwd_tile();
     L.nsched = p.heads * ((p.total + bt - 1) / bt + p.nbatch);

@@ -43,6 +43,7 @@ struct BwdArgs {
   uint16_t *dq, *dk, *dv;  // bf16 outputs
   float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
   float *delta;            // -D_i, same layout as lse
+  float *nls;              // -lse_i / scale, same layout (seed of the dkv kernel's S)
   float *part;             // [nb, nwg] table-gradient partials
   const int4 *sched;       // packed batches: {token0, length, head, tile}
   const float *table, *slopes;
@@ -280,7 +281,10 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
     __syncthreads();
   }
   const float dd = half_sum(dsum);   // D_i - Dc_i
-  if (hl == 0 && myrow < L) a.delta[w.lse_base + myrow] = -(dc + dd);
+  if (hl == 0 && myrow < L) {
+    a.delta[w.lse_base + myrow] = -(dc + dd);
+    a.nls[w.lse_base + myrow] = -a.lse[w.lse_base + myrow] / a.scale;
+  }
   f32x16 qacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -337,11 +341,11 @@ __host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
 __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdArgs a) {
   constexpr int QB = DkvTile<D>::QB;
-  // Q and dO blocks as swizzled tiles (see swz), with the rows' LSE and -D
-  // (64 entries: the 4-byte copy fills one per lane)
+  // Q and dO blocks as swizzled tiles (see swz), with the rows' -lse/scale
+  // and -D (64 entries: the 4-byte copy fills one per lane)
   __shared__ __attribute__((aligned(16))) uint16_t qs[2][QB * D];
   __shared__ __attribute__((aligned(16))) uint16_t dos[2][QB * D];
-  __shared__ __attribute__((aligned(16))) float lses[2][64];
+  __shared__ __attribute__((aligned(16))) float nlss[2][64];
   __shared__ __attribute__((aligned(16))) float ndls[2][64];
   __shared__ float ubin[4][2];
   extern __shared__ __attribute__((aligned(16))) float dyn[];
@@ -427,12 +431,12 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   // one query block to LDS by buffer-to-LDS copies: Q and dO tiles split
   // over the four waves, LSE and -D one 4-byte copy each
   const i32x4 dq_src = dma_desc(a.q + base, nrec), ddo_src = dma_desc(a.dout + base, nrec);
-  const i32x4 dlse_src = dma_desc(a.lse + w.lse_base, (uint32_t)L * 4u);
+  const i32x4 dlse_src = dma_desc(a.nls + w.lse_base, (uint32_t)L * 4u);
   const i32x4 dnd_src = dma_desc(a.delta + w.lse_base, (uint32_t)L * 4u);
   auto fill = [&](int q0, int buf) {
     dma_tile<D, QB, 4>(dq_src, HD, q0, qs[buf], wave, lane);
     dma_tile<D, QB, 4>(ddo_src, HD, q0, dos[buf], wave, lane);
-    if (wave == 0) dma4(dlse_src, (uint32_t)(q0 + lane) * 4u, lses[buf]);
+    if (wave == 0) dma4(dlse_src, (uint32_t)(q0 + lane) * 4u, nlss[buf]);
     if (wave == 1) dma4(dnd_src, (uint32_t)(q0 + lane) * 4u, ndls[buf]);
   };
 
@@ -450,17 +454,22 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   if (qb_first < nqb) fill(qb_first * QB, 0);
   wait_vmem_loads();
   __syncthreads();
-  // S and dP - D of one 32-row block: each lane holds key myk and rows
-  // irow0 + 8(r/4) + 4hl + r%4.  The dP accumulator starts at -D_i, read
-  // from LDS straight into the MFMA's C operand.
+  // S - lse/scale and dP - D of one 32-row block: each lane holds key myk
+  // and rows irow0 + 8(r/4) + 4hl + r%4.  Both accumulators start at their
+  // row's offset (-lse_i / scale, -D_i), read from LDS straight into the
+  // MFMAs' C operands, so that P = exp2(scale log2(e) acc + bias) costs one
+  // VALU operation before the exponential.
   auto block_sdp = [&](int buf, int rb, f32x16 &sacc, f32x16 &pacc) {
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&ndls[buf][32 * rb + 8 * qq + 4 * hl]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&nlss[buf][32 * rb + 8 * qq + 4 * hl]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pacc[4 * qq + e] = d4[e];
+      for (int e = 0; e < 4; ++e) {
+        pacc[4 * qq + e] = d4[e];
+        sacc[4 * qq + e] = l4[e];
+      }
     }
-    sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       const int at = aof[s] + 32 * rb * D;
@@ -469,15 +478,9 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
     }
   };
   // P of a block whose bias is the constant bconst and that has no mask
-  auto block_p_fast = [&](int buf, int rb, const f32x16 &sacc, float bconst, float (&p)[16]) {
+  auto block_p_fast = [&](const f32x16 &sacc, float bconst, float (&p)[16]) {
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lses[buf][32 * rb + 8 * qq + 4 * hl]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p[4 * qq + e] =
-            __builtin_amdgcn_exp2f(fmaf(sacc[4 * qq + e], c, fmaf(-l4[e], kLog2e, bconst)));
-    }
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, bconst));
   };
   // dV^T += dO^T P and dK^T += Q^T dS (unscaled): P / dS from registers as
   // the B operand (k = the block's rows), dO^T / Q^T through transposing
@@ -550,12 +553,10 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       // loops.
       float p[16], ds[16];
       if (fast) {
-        block_p_fast(buf, rb, sacc[rb], bconst, p);
+        block_p_fast(sacc[rb], bconst, p);
       } else {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const f32x4 l4 =
-              *reinterpret_cast<const f32x4 *>(&lses[buf][32 * rb + 8 * qq + 4 * hl]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * qq + e;
@@ -571,7 +572,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
             // the mask as an additive -inf (exp2(-inf) = 0): a select
             // between the whole argument and -inf would be turned into a
             // branch around the table read
-            p[r] = __builtin_amdgcn_exp2f(fmaf(-l4[e], kLog2e, t) + (dead ? -INFINITY : 0.f));
+            p[r] = __builtin_amdgcn_exp2f(t + (dead ? -INFINITY : 0.f));
           }
         }
       }
@@ -854,6 +855,7 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.dq_f32 = b.dq_f32;
   a.dk_f32 = b.dk_f32;
   a.delta = b.delta;
+  a.nls = b.delta + (size_t)p.total * p.heads;
   a.part = b.part;
   a.sched = sched;
   a.table = p.table;

@@ -61,7 +61,7 @@ struct BwdBuffers {
   const float *lse;
   void *dq, *dk, *dv;      // bf16 outputs
   float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
-  float *delta;            // fp32, lse layout
+  float *delta;            // fp32, two lse-layout arrays: -D, then -lse / scale
   float *part;             // fp32 [num_buckets, parts] (T5 table gradient) or nullptr
   float *dtable;           // [num_buckets, H] or nullptr
   float *dbias;            // dense bias gradient fp32 [dense_batch, H, S, S] or nullptr

@@ -211,7 +211,7 @@ def test_dense_bias_gradient_workspace(lib):
     b.f = _dense(bias_mode=_lib.FA_BIAS_DENSE, bias_dense=0x6000, bias_dense_batch=1)
     b.dout = b.dq = b.dk = b.dv = 0x4000
     B, S, H = b.f.batch, b.f.seqlen, b.f.heads
-    delta = a256(B * S * H * 4)
+    delta = a256(2 * B * S * H * 4)   # -D and -lse/scale per row
     assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == delta           # no gradient asked
     b.dtable = 0x7000
     assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == delta + a256(B * H * S * S * 4)
