@@ -518,8 +518,49 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
     f32x16 sacc[QB / 32], pacc[QB / 32];
 #pragma unroll
     for (int rb = 0; rb < QB / 32; ++rb) block_sdp(buf, rb, sacc[rb], pacc[rb]);
+
+    // When every row block of the iteration is unmasked with a constant
+    // bias, all of them go through one straight-line path (no branch between
+    // the blocks, so the compiler can overlap one block's products with the
+    // next block's exponentials); otherwise each block branches on its own.
+    bool all_fast = BIAS == kBiasT5;
+    float bcv[QB / 32];
+    int ulov[QB / 32];
 #pragma unroll
     for (int rb = 0; rb < QB / 32; ++rb) {
+      const int irow0 = q0 + 32 * rb;
+      const int rmin = kw0 - (irow0 + 31), rmax = kw0 + 31 - irow0;
+      bool uni = true;
+      bcv[rb] = 0.f;
+      ulov[rb] = 0;
+      if constexpr (BIAS == kBiasT5) {
+        ulov[rb] = min(max(rmin, -sat), sat);
+        uni = ulov[rb] == min(max(rmax, -sat), sat);
+        bcv[rb] = lut[ulov[rb] + sat];
+      }
+      all_fast = all_fast && uni && wave_live && irow0 + 32 <= L && kw0 + 32 <= L &&
+                 !(CAUSAL && rmax > 0);
+    }
+    if (all_fast) {
+#pragma unroll
+      for (int rb = 0; rb < QB / 32; ++rb) {
+        float p[16], ds[16];
+        block_p_fast(sacc[rb], bcv[rb], p);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = p[r] * pacc[rb][r];
+        if constexpr (DBIAS && BIAS == kBiasT5) {
+          float t4[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) t4[k] = (ds[k] + ds[k + 4]) + (ds[k + 8] + ds[k + 12]);
+          const float t = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+          if (ulov[rb] <= 0) ub0 += t; else ub1 += t;
+        }
+        block_dvdk(buf, rb, p, ds);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < QB / 32; ++rb) {
+      if (all_fast) break;
       const int irow0 = q0 + 32 * rb;
       const int rmin = kw0 - (irow0 + 31), rmax = kw0 + 31 - irow0;
       const bool none = !wave_live || irow0 >= L || (CAUSAL && rmin > 0);
