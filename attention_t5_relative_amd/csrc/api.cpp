@@ -210,6 +210,9 @@ fa_status check_varlen_fwd_impl(const fa_varlen_fwd_params *p) {
     return fail(FA_ERR_INVALID, "q, k, v, o and lse must be non-NULL");
   if ((long long)p->total * p->heads >= (1LL << 31))
     return fail(FA_ERR_UNSUPPORTED, "total * heads must stay below 2^31");
+  // schedule entries (16 bytes each) for the smallest tile, 32 rows
+  if (8LL * ((p->heads + 7) / 8) * ((long long)p->total / 32 + p->nseq + 1) >= (1LL << 27))
+    return fail(FA_ERR_UNSUPPORTED, "too many sequences or tokens for the tile schedule");
   if (p->bias.mode == FA_BIAS_DENSE)
     return fail(FA_ERR_UNSUPPORTED, "a dense bias matrix is for the dense entry points only");
   return check_common(p->heads, p->head_dim, p->causal, p->scale, p->rope_base, p->bias,
@@ -296,8 +299,8 @@ FwdLayout fwd_layout(const fa::Problem &p) {
   }
   if (p.varlen) {
     const int br = fa::fwd_tile_rows(p.head_dim);
-    L.nsched = p.heads * ((p.total + br - 1) / br + p.nbatch);
-    L.prefix = c.take((size_t)(p.nbatch + 1) * 4);
+    L.nsched = fa::sched_entries(p.total, p.nbatch, p.heads, br);
+    L.prefix = c.take((size_t)fa::sched_prefix_ints(p.nbatch) * 4);
     L.sched = c.take((size_t)L.nsched * 16);
   }
   L.total = c.off;
@@ -326,8 +329,8 @@ BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
   L.delta = c.take(2 * tokens * p.heads * 4);   // -D, then -lse / scale (lse layout each)
   if (p.varlen) {
     const int bt = fa::bwd_tile();
-    L.nsched = p.heads * ((p.total + bt - 1) / bt + p.nbatch);
-    L.prefix = c.take((size_t)(p.nbatch + 1) * 4);
+    L.nsched = fa::sched_entries(p.total, p.nbatch, p.heads, bt);
+    L.prefix = c.take((size_t)fa::sched_prefix_ints(p.nbatch) * 4);
     L.sched = c.take((size_t)L.nsched * 16);
   }
   L.has_part = want_dtable && p.bias == FA_BIAS_T5;

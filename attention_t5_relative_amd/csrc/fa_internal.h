@@ -72,6 +72,10 @@ struct BwdBuffers {
 int fwd_tile_rows(int head_dim);
 hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sched, int nsched,
                            hipStream_t s);
+// Packed-batch schedule: entries for `total` tokens in `nseq` sequences
+// (a multiple of 8; see sched_kernel) and the int32 scratch it needs.
+int sched_entries(int total, int nseq, int heads, int tile);
+int sched_prefix_ints(int nseq);
 hipError_t launch_sched(const int32_t *cu, int nseq, int heads, int tile, int nentries,
                         int32_t *prefix, int4 *sched, hipStream_t s);
 // Rotates q and k (bf16 [tokens, H, D]) into qo and ko.

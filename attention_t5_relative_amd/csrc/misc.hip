@@ -8,54 +8,85 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Packed batches: map every workgroup id to {token0, length, head, tile} so
-// the attention kernels need a single load to find their work.  One
-// workgroup: an exclusive scan of (tiles per sequence * heads) into `prefix`,
-// then a binary search per entry.  Entries past the real work get length -1.
+// the attention kernels need a single load to find their work.
+//
+// Workgroup ids are dispatched to the 8 XCDs in turn, and the kernels give
+// XCD x the contiguous range of entries [x per, (x + 1) per), per = n / 8
+// (xcd_remap).  A sequence's work grows with its length squared, so handing
+// out whole sequences in order would load the XCDs very unevenly.  Instead
+// the (sequence, head) pairs go round-robin over the XCDs: pair s H + h to
+// XCD (s H + h) mod 8.  All tiles of a pair stay on one XCD, so its K and V
+// are reused from that XCD's L2.  Within an XCD the entries follow the
+// sequences in order, then the pair's heads, then its tiles, longest causal
+// rows first.
+//
+// One workgroup.  For each XCD x, an exclusive scan over the sequences of
+// (tiles of s) * (pairs of s on x) goes into prefix[x][s]; then every entry
+// finds its sequence by binary search.  Entries past an XCD's work get
+// length -1.  n must be a multiple of 8 and per at least every XCD's count
+// (sched_entries gives such an n).
 // ---------------------------------------------------------------------------
 constexpr int SCHED_NT = 256;
+
+// pairs of sequence s on XCD x: heads h = r, r + 8, ... below H with
+// r = (x - s H) mod 8
+__device__ __forceinline__ int xcd_first_head(int s, int heads, int x) {
+  return ((x - (int)(((long long)s * heads) & 7)) + 8) & 7;
+}
+__device__ __forceinline__ int xcd_pairs(int s, int heads, int x) {
+  const int r = xcd_first_head(s, heads, x);
+  return r < heads ? (heads - 1 - r) / 8 + 1 : 0;
+}
 
 __global__ __launch_bounds__(SCHED_NT) void sched_kernel(const int32_t *cu, int nseq, int heads,
                                                           int tile, int nentries, int32_t *prefix,
                                                           int4 *sched) {
   __shared__ int scan[SCHED_NT];
   const int tid = threadIdx.x;
-  int carry = 0;
-  for (int c0 = 0; c0 < nseq; c0 += SCHED_NT) {
-    const int s = c0 + tid;
-    int cnt = 0;
-    if (s < nseq) {
-      const int len = cu[s + 1] - cu[s];
-      cnt = ((len + tile - 1) / tile) * heads;
-    }
-    scan[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < SCHED_NT; off <<= 1) {
-      const int add = tid >= off ? scan[tid - off] : 0;
+  for (int x = 0; x < 8; ++x) {
+    int32_t *px = prefix + (size_t)x * (nseq + 1);
+    int carry = 0;
+    for (int c0 = 0; c0 < nseq; c0 += SCHED_NT) {
+      const int s = c0 + tid;
+      int cnt = 0;
+      if (s < nseq) {
+        const int len = cu[s + 1] - cu[s];
+        cnt = ((len + tile - 1) / tile) * xcd_pairs(s, heads, x);
+      }
+      scan[tid] = cnt;
       __syncthreads();
-      scan[tid] += add;
+      for (int off = 1; off < SCHED_NT; off <<= 1) {
+        const int add = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += add;
+        __syncthreads();
+      }
+      if (s < nseq) px[s] = carry + scan[tid] - cnt;
+      carry += scan[SCHED_NT - 1];
       __syncthreads();
     }
-    if (s < nseq) prefix[s] = carry + scan[tid] - cnt;
-    carry += scan[SCHED_NT - 1];
-    __syncthreads();
+    if (tid == 0) px[nseq] = carry;
   }
-  if (tid == 0) prefix[nseq] = carry;
   __syncthreads();
   __threadfence_block();
+  const int per = nentries >> 3;
   for (int gidx = tid; gidx < nentries; gidx += SCHED_NT) {
     int4 e = {0, -1, 0, 0};
-    if (gidx < carry) {
-      int lo = 0, hi = nseq - 1;   // last s with prefix[s] <= gidx
+    const int x = gidx / per, local = gidx - x * per;
+    const int32_t *px = prefix + (size_t)x * (nseq + 1);
+    if (x < 8 && local < px[nseq]) {
+      int lo = 0, hi = nseq - 1;   // last s with px[s] <= local
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (prefix[mid] <= gidx) lo = mid; else hi = mid - 1;
+        if (px[mid] <= local) lo = mid; else hi = mid - 1;
       }
       const int s = lo;
       const int t0 = cu[s], len = cu[s + 1] - t0;
       const int nt = (len + tile - 1) / tile;
-      const int rem = gidx - prefix[s];
-      const int hh = rem / nt;
-      const int t = nt - 1 - (rem - hh * nt);   // longest causal rows first
+      const int k = local - px[s];
+      const int j = k / nt;
+      const int hh = xcd_first_head(s, heads, x) + 8 * j;
+      const int t = nt - 1 - (k - j * nt);   // longest causal rows first
       e = int4{t0, len, hh, t};
     }
     sched[gidx] = e;
@@ -165,6 +196,15 @@ __global__ __launch_bounds__(256) void fill_kernel(float *p, size_t n, float v) 
 }
 
 }  // namespace
+
+int sched_entries(int total, int nseq, int heads, int tile) {
+  // every XCD holds at most ceil(H / 8) pairs of each sequence, and a
+  // sequence of length L has at most L / tile + 1 tiles
+  const long long per = (long long)((heads + 7) / 8) * ((total + tile - 1) / tile + nseq);
+  return (int)(8 * per);
+}
+
+int sched_prefix_ints(int nseq) { return 8 * (nseq + 1); }
 
 hipError_t launch_sched(const int32_t *cu, int nseq, int heads, int tile, int nentries,
                         int32_t *prefix, int4 *sched, hipStream_t s) {
