@@ -16,17 +16,22 @@ namespace {
 // out whole sequences in order would load the XCDs very unevenly.  Instead
 // the (sequence, head) pairs go round-robin over the XCDs: pair s H + h to
 // XCD (s H + h) mod 8.  All tiles of a pair stay on one XCD, so its K and V
-// are reused from that XCD's L2.  Within an XCD the entries follow the
-// sequences in order, then the pair's heads, then its tiles, longest causal
-// rows first.
+// are reused from that XCD's L2.  Sequences are taken longest first (by
+// tile count, ties in index order; up to kSortMax sequences, beyond that in
+// index order), so each XCD starts its heaviest pairs first and the short
+// ones fill the end.  Within an XCD the entries follow the sequences in that
+// order, then the pair's heads, then its tiles, longest causal rows first.
 //
-// One workgroup.  For each XCD x, an exclusive scan over the sequences of
-// (tiles of s) * (pairs of s on x) goes into prefix[x][s]; then every entry
-// finds its sequence by binary search.  Entries past an XCD's work get
-// length -1.  n must be a multiple of 8 and per at least every XCD's count
-// (sched_entries gives such an n).
+// One workgroup.  A bitonic sort in LDS ranks the sequences.  For each XCD
+// x, an exclusive scan over the ranks of (tiles) * (pairs on x) goes into
+// prefix[x][rank]; then every entry finds its rank by binary search.
+// Entries past an XCD's work get length -1.  n must be a multiple of 8 and
+// per at least every XCD's count (sched_entries gives such an n).  The
+// order decides only which workgroup computes what, never a result.
 // ---------------------------------------------------------------------------
 constexpr int SCHED_NT = 256;
+constexpr int kSortMax = 2048;     // sequences ranked by length
+constexpr int kSortIdxBits = 19;   // sort key: (4095 - tiles) << 19 | index
 
 // pairs of sequence s on XCD x: heads h = r, r + 8, ... below H with
 // r = (x - s H) mod 8
@@ -42,7 +47,38 @@ __global__ __launch_bounds__(SCHED_NT) void sched_kernel(const int32_t *cu, int 
                                                           int tile, int nentries, int32_t *prefix,
                                                           int4 *sched) {
   __shared__ int scan[SCHED_NT];
+  __shared__ int order[kSortMax];
   const int tid = threadIdx.x;
+  const bool ranked = nseq <= kSortMax;
+  if (ranked) {
+    int n2 = 1;
+    while (n2 < nseq) n2 <<= 1;
+    for (int i = tid; i < n2; i += SCHED_NT) {
+      int key = 0x7fffffff;
+      if (i < nseq) {
+        const int nt = (cu[i + 1] - cu[i] + tile - 1) / tile;
+        key = ((4095 - min(nt, 4095)) << kSortIdxBits) | i;
+      }
+      order[i] = key;
+    }
+    __syncthreads();
+    for (int k = 2; k <= n2; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += SCHED_NT) {
+          const int l = i ^ j;
+          if (l > i) {
+            const int a = order[i], b = order[l];
+            if (((i & k) == 0) == (a > b)) {
+              order[i] = b;
+              order[l] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+  }
+  // sequence of rank r
+  auto seq_of = [&](int r) { return ranked ? (order[r] & ((1 << kSortIdxBits) - 1)) : r; };
   for (int x = 0; x < 8; ++x) {
     int32_t *px = prefix + (size_t)x * (nseq + 1);
     int carry = 0;
@@ -50,7 +86,8 @@ __global__ __launch_bounds__(SCHED_NT) void sched_kernel(const int32_t *cu, int 
       const int s = c0 + tid;
       int cnt = 0;
       if (s < nseq) {
-        const int len = cu[s + 1] - cu[s];
+        const int q = seq_of(s);
+        const int len = cu[q + 1] - cu[q];
         cnt = ((len + tile - 1) / tile) * xcd_pairs(s, heads, x);
       }
       scan[tid] = cnt;
@@ -80,8 +117,8 @@ __global__ __launch_bounds__(SCHED_NT) void sched_kernel(const int32_t *cu, int 
         const int mid = (lo + hi + 1) >> 1;
         if (px[mid] <= local) lo = mid; else hi = mid - 1;
       }
-      const int s = lo;
-      const int t0 = cu[s], len = cu[s + 1] - t0;
+      const int s = lo, q = seq_of(s);
+      const int t0 = cu[q], len = cu[q + 1] - t0;
       const int nt = (len + tile - 1) / tile;
       const int k = local - px[s];
       const int j = k / nt;
