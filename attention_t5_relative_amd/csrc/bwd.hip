@@ -110,7 +110,8 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   // (S^T = K Q^T) and transposed (dQ^T = K^T dS^T), V row-wise
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][BC * D];
-  __shared__ float lut[BIAS == kBiasT5 ? 2 * kMaxDistance + 1 : 1];
+  __shared__ float lut_mem[BIAS == kBiasT5 ? 2 * (kMaxDistance + kLutPad) + 1 : 1];
+  const float *const lut = lut_mem + (BIAS == kBiasT5 ? a.t5.sat + kLutPad : 0);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,9 +150,13 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
 
   int sat = 0;
   if constexpr (BIAS == kBiasT5) {
+    // bias (log2 units) by relative position r = j - i (see kLutPad)
     sat = a.t5.sat;
-    for (int x = tid; x <= 2 * sat; x += NT)
-      lut[x] = a.table[t5_bucket_dev(x - sat, a.t5) * a.heads + h] * kLog2e;
+    for (int x = tid; x <= 2 * (sat + kLutPad); x += NT) {
+      const int r = x - sat - kLutPad;
+      lut_mem[x] = (CAUSAL && r > 0) ? -INFINITY
+                                     : a.table[t5_bucket_dev(r, a.t5) * a.heads + h] * kLog2e;
+    }
   }
   float slope_l2 = 0.f;
   if constexpr (BIAS == kBiasAlibi) slope_l2 = -a.slopes[h] * kLog2e;
@@ -324,8 +329,9 @@ struct DkvTile {
   static constexpr int QB = (D == 64) ? 64 : 32;   // query rows per block
 };
 
-// Dynamic LDS of the dkv kernel: the T5 bias table by distance, then
-// (with the table gradient) the bucket of each distance, one array of
+// Dynamic LDS of the dkv kernel: the T5 bias table by distance (2 (sat +
+// kLutPad) + 1 entries, see kLutPad), then (with the table gradient) the
+// bucket of each distance in [-sat, sat], one array of
 // 2 * sat + 1 distance bins per wave, and one 32 x 40 fp32 scratch tile per
 // wave for the diagonal sums, with kTileGuard floats on either side of the
 // tiles (the diagonal reads of masked-out rows reach up to 32 floats past a
@@ -335,7 +341,8 @@ constexpr int kTileGuard = 32;
 __host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
   if (!t5) return 0;
   const size_t n = (size_t)(2 * sat + 1);
-  return n * 4 + (dbias ? n * 4 + 4 * n * 4 + (4 * 32 * kTilePitch + 2 * kTileGuard) * 4 : 0);
+  const size_t nl = (size_t)(2 * (sat + kLutPad) + 1);
+  return nl * 4 + (dbias ? n * 4 + 4 * n * 4 + (4 * 32 * kTilePitch + 2 * kTileGuard) * 4 : 0);
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
@@ -383,18 +390,23 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   }
 
   int sat = 0;
-  float *lut = dyn;
-  int *bkt = reinterpret_cast<int *>(dyn + (2 * a.t5.sat + 1));
-  float *bins = dyn + 2 * (2 * a.t5.sat + 1);
+  const int nlut = 2 * (a.t5.sat + kLutPad) + 1;
+  float *const lut_mem = dyn;
+  const float *const lut = lut_mem + (a.t5.sat + kLutPad);   // distance 0
+  int *bkt = reinterpret_cast<int *>(dyn + nlut);
   const int nbin = 2 * a.t5.sat + 1;
+  float *bins = dyn + nlut + nbin;
   float *const tiles = bins + 4 * nbin + kTileGuard;
   if constexpr (BIAS == kBiasT5) {
     sat = a.t5.sat;
-    for (int x = tid; x < nbin; x += NT) {
-      const int b = t5_bucket_dev(x - sat, a.t5);
-      lut[x] = a.table[b * a.heads + h] * kLog2e;
-      if constexpr (DBIAS) {
-        bkt[x] = b;
+    for (int x = tid; x < nlut; x += NT) {
+      const int r = x - sat - kLutPad;
+      lut_mem[x] = (CAUSAL && r > 0) ? -INFINITY
+                                     : a.table[t5_bucket_dev(r, a.t5) * a.heads + h] * kLog2e;
+    }
+    if constexpr (DBIAS) {
+      for (int x = tid; x < nbin; x += NT) {
+        bkt[x] = t5_bucket_dev(x - sat, a.t5);
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) bins[w4 * nbin + x] = 0.f;
       }
@@ -536,7 +548,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       if constexpr (BIAS == kBiasT5) {
         ulov[rb] = min(max(rmin, -sat), sat);
         uni = ulov[rb] == min(max(rmax, -sat), sat);
-        bcv[rb] = lut[ulov[rb] + sat];
+        bcv[rb] = lut[ulov[rb]];
       }
       all_fast = all_fast && uni && wave_live && irow0 + 32 <= L && kw0 + 32 <= L &&
                  !(CAUSAL && rmax > 0);
@@ -574,7 +586,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
         ulo = min(max(rmin, -sat), sat);
         const int uhi = min(max(rmax, -sat), sat);
         uniform = (ulo == uhi);
-        bconst = lut[ulo + sat];
+        bconst = lut[ulo];
       }
       const bool fast = uniform && !none && !mask_c && !mask_r && !mask_k;
       // dense bias and its gradient: element r is row irow0 + 4hl + roff(r),
@@ -596,20 +608,25 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
       if (fast) {
         block_p_fast(sacc[rb], bconst, p);
       } else {
+        // T5: this lane's distances are rbase - roff, roff in [0, 27]; one
+        // clamped base for the block (see kLutPad), and the causal mask is
+        // in the table
+        const int rbase = myk - (irow0 + 4 * hl);
+        const float *const lb = lut + min(max(rbase - 27, -sat - kLutPad), sat + kLutPad - 27);
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * qq + e;
             const int roff = 8 * qq + e;
-            const int rr = myk - (irow0 + 4 * hl + roff);
+            const int rr = rbase - roff;
             float t = sacc[rb][r] * c;
-            if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
+            if constexpr (BIAS == kBiasT5) t = fmaf(sacc[rb][r], c, lb[27 - roff]);
             if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
             if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bkv[r]), kLog2e, t);
             // non-short-circuit operators keep this straight-line code
-            const bool dead = none | (mask_c & (rr > 0)) | (mask_r & (irow0 + 4 * hl + roff >= L)) |
-                              (mask_k & (myk >= L));
+            const bool dead = none | (BIAS != kBiasT5 && mask_c & (rr > 0)) |
+                              (mask_r & (irow0 + 4 * hl + roff >= L)) | (mask_k & (myk >= L));
             // the mask as an additive -inf (exp2(-inf) = 0): a select
             // between the whole argument and -inf would be turned into a
             // branch around the table read

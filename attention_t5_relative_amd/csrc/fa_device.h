@@ -154,12 +154,16 @@ __device__ __forceinline__ int t5_bucket_dev(int r, const T5Geometry &g) {
   return off + b;
 }
 
-// Row sum of a packed pair of bf16 values added to acc (v_dot2c_f32_bf16
-// with the pair (1, 1)).
-__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-}
+// The T5 bias by relative distance r (log2 units) lives in LDS for r in
+// [-sat - kLutPad, sat + kLutPad]; past +-sat every entry repeats the
+// saturated bucket, and under a causal mask the entries for r > 0 are -inf.
+// A lane's distances in a 64-key tile are rbase + off, off in [0, 59], so
+// each element reads its entry at a fixed offset from one per-lane base,
+// with no clamp per element and no causal test.  The base itself is clamped
+// to [-sat - kLutPad, sat + kLutPad - 59]: a clamp moves it only when all
+// the lane's distances are saturated on that side (kLutPad > 59), and the
+// entries it then reads hold the same saturated value.
+constexpr int kLutPad = 96;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -200,12 +204,24 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
   if constexpr (BIAS == kBiasT5) {
     const int lo = min(max(rmin, -sat), sat), hi = min(max(rmax, -sat), sat);
     uniform = (lo == hi);
-    bconst = lut[lo + sat];
+    bconst = lut[lo];
   }
   if (uniform && !mask_c && !mask_l) return true;
   bconst = 0.f;
   const int rbase = j0 - (row0 + il) + 4 * hl;
   const int jb = j0 + 4 * hl;
+  if constexpr (BIAS == kBiasT5) {
+    const float *lb = lut + min(max(rbase, -sat - kLutPad), sat + kLutPad - 59);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+        const float t = fmaf(sacc[kb][r], c, lb[off]);
+        sacc[kb][r] = (mask_l && jb + off >= L) ? -INFINITY : t;
+      }
+    return false;
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -213,7 +229,6 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
       const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
       const int rr = rbase + off;
       float t = sacc[kb][r] * c;
-      if constexpr (BIAS == kBiasT5) t += lut[min(max(rr, -sat), sat) + sat];
       if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
       if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bv[kb][r]), kLog2e, t);
       if (mask_c && rr > 0) t = -INFINITY;

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
   constexpr int PER_FILL = 2 * BC * D * 2 / 1024 / (NT / 64);   // copies per wave per tile
   __shared__ __attribute__((aligned(16))) uint16_t ks[NBUF][BC * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs[NBUF][BC * D];
-  __shared__ float lut[BIAS == kBiasT5 ? 2 * kMaxDistance + 1 : 1];
+  __shared__ float lut_mem[BIAS == kBiasT5 ? 2 * (kMaxDistance + kLutPad) + 1 : 1];
+  const float *const lut = lut_mem + (BIAS == kBiasT5 ? a.t5.sat + kLutPad : 0);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,10 +113,13 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
 
   int sat = 0;
   if constexpr (BIAS == kBiasT5) {
-    // bias (log2 units) by relative position r = j - i, clamped to [-sat, sat]
+    // bias (log2 units) by relative position r = j - i (see kLutPad)
     sat = a.t5.sat;
-    for (int x = tid; x <= 2 * sat; x += NT)
-      lut[x] = a.table[t5_bucket_dev(x - sat, a.t5) * a.heads + h] * kLog2e;
+    for (int x = tid; x <= 2 * (sat + kLutPad); x += NT) {
+      const int r = x - sat - kLutPad;
+      lut_mem[x] = (CAUSAL && r > 0) ? -INFINITY
+                                     : a.table[t5_bucket_dev(r, a.t5) * a.heads + h] * kLog2e;
+    }
   }
   float slope_l2 = 0.f;
   if constexpr (BIAS == kBiasAlibi) slope_l2 = -a.slopes[h] * kLog2e;
