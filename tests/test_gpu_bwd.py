@@ -86,6 +86,34 @@ def test_backward_small(case):
         assert np.abs(out["dtable"].sum(axis=0)).max() <= 1e-3 * np.abs(dtab).max() + 1e-4
 
 
+GEOMS = [
+    # B, S, H, D, causal, bidirectional, num_buckets, max_distance
+    (1, 300, 2, 64, False, True, 8, 16),
+    (1, 300, 2, 64, True, False, 8, 16),
+    (1, 260, 1, 128, True, True, 6, 10),
+    (1, 1100, 1, 64, False, True, 32, 1024),
+    (1, 1100, 1, 64, True, False, 32, 1024),
+    (1, 400, 2, 128, False, False, 17, 300),
+]
+
+
+@pytest.mark.parametrize("case", GEOMS, ids=lambda c: "s{}d{}-c{}-bi{}-nb{}-md{}".format(
+    c[1], c[3], int(c[4]), int(c[5]), c[6], c[7]))
+def test_backward_t5_geometries(case):
+    """Short and long saturation distances and odd bucket counts (the bias
+    table's clamped per-lane base and the table-gradient bins)."""
+    B, S, H, D, causal, bidi, nb, md = case
+    inp = synth.draw_dense(11 * S + nb, B, S, H, D, num_buckets=nb)
+    out, kw = run_dense_bwd(inp, causal=causal, kind="t5", scale=1.0, bidirectional=bidi,
+                            nb=nb, md=md)
+    dq, dk, dv, dtab = oracle.attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                            inp.f64("do"), **kw)
+    assert_grad(out["dq"], dq, "dQ")
+    assert_grad(out["dk"], dk, "dK")
+    assert_grad(out["dv"], dv, "dV")
+    assert_dtable(out["dtable"], dtab)
+
+
 def test_backward_o_only_centres():
     """The backward reads O only as the centre dO.O of its D accumulation.
     With another O, dK, dV and the table gradient still meet the gate (D

@@ -70,6 +70,32 @@ def test_forward_small(case):
     assert_lse(lse, LSE)
 
 
+# Other T5 geometries: a short saturation distance (most tiles saturated,
+# the per-lane table base clamped on both sides), the largest one the
+# kernels take, and an odd bucket count; causal and not, both head sizes.
+GEOMS = [
+    # B, S, H, D, causal, bidirectional, num_buckets, max_distance
+    (1, 300, 2, 64, False, True, 8, 16),
+    (1, 300, 2, 64, True, False, 8, 16),
+    (1, 260, 1, 128, True, True, 6, 10),
+    (1, 1100, 1, 64, False, True, 32, 1024),
+    (1, 1100, 1, 64, True, False, 32, 1024),
+    (1, 400, 2, 128, False, False, 17, 300),
+]
+
+
+@pytest.mark.parametrize("case", GEOMS, ids=lambda c: "s{}d{}-c{}-bi{}-nb{}-md{}".format(
+    c[1], c[3], int(c[4]), int(c[5]), c[6], c[7]))
+def test_forward_t5_geometries(case):
+    B, S, H, D, causal, bidi, nb, md = case
+    inp = synth.draw_dense(7 * S + nb, B, S, H, D, num_buckets=nb, with_dout=False)
+    o, lse, kw = run_dense(inp, causal=causal, kind="t5", scale=1.0, bidirectional=bidi,
+                           nb=nb, md=md)
+    O, LSE = oracle.attention_fwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), **kw)
+    assert_o(o, O)
+    assert_lse(lse, LSE)
+
+
 def test_forward_c1_full():
     """B1 H2 S128 D64, bidirectional T5 (32 buckets, distance 128), scale 1."""
     c = synth.config_by_name("c1")
