@@ -345,9 +345,21 @@ __host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
   return nl * 4 + (dbias ? n * 4 + 4 * n * 4 + (4 * 32 * kTilePitch + 2 * kTileGuard) * 4 : 0);
 }
 
+// Workgroups per CU.  At head_dim 128 with ALiBi the keys' V rows (the B
+// operand of dP) stay in LDS and are read per block, which leaves room for
+// two workgroups per CU without spilling; the other head_dim 128 variants
+// (T5 with its table gradient, RoPE, the dense bias) need the registers and
+// run one.
+template <int D, int BIAS>
+constexpr int dkv_wgs() {
+  return D == 64 || BIAS == kBiasAlibi ? 2 : 1;
+}
+
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
-__global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const BwdArgs a) {
   constexpr int QB = DkvTile<D>::QB;
+  constexpr bool kVInLds = D == 128 && BIAS == kBiasAlibi;
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[kVInLds ? BKV * D : 8];
   // Q and dO blocks as swizzled tiles (see swz), with the rows' -lse/scale
   // and -D (64 entries: the 4-byte copy fills one per lane)
   __shared__ __attribute__((aligned(16))) uint16_t qs[2][QB * D];
@@ -381,13 +393,15 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
   const rsrc_t rdo = make_rsrc(a.dout + base, nrec);
 
   // this wave's 32 keys as the B operand of S = Q K^T and dP = dO V^T
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16], vf[kVInLds ? 1 : D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const uint32_t off = ((uint32_t)myk * (uint32_t)HD + 16 * s + 8 * hl) * 2u;
     kf[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-    vf[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+    if constexpr (!kVInLds) vf[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
   }
+  if constexpr (kVInLds)
+    dma_tile<D, BKV, 4>(dma_desc(a.v + base, nrec), HD, kt0, vtile, wave, lane);
 
   int sat = 0;
   const int nlut = 2 * (a.t5.sat + kLutPad) + 1;
@@ -486,7 +500,12 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dkv_kernel(const BwdA
     for (int s = 0; s < D / 16; ++s) {
       const int at = aof[s] + 32 * rb * D;
       sacc = mfma32(*reinterpret_cast<const bf16x8 *>(&qs[buf][at]), kf[s], sacc);
-      pacc = mfma32(*reinterpret_cast<const bf16x8 *>(&dos[buf][at]), vf[s], pacc);
+      bf16x8 vs;
+      if constexpr (kVInLds)
+        vs = *reinterpret_cast<const bf16x8 *>(&vtile[swz_off<D>(32 * wave + il, 2 * s + hl)]);
+      else
+        vs = vf[s];
+      pacc = mfma32(*reinterpret_cast<const bf16x8 *>(&dos[buf][at]), vs, pacc);
     }
   };
   // P of a block whose bias is the constant bconst and that has no mask
