@@ -209,6 +209,24 @@ def test_varlen_backward_small(causal, kind, rope):
         assert_dtable(out["dtable"], dtab)
 
 
+@pytest.mark.parametrize("nseq", [2048, 2100])
+def test_varlen_many_sequences(nseq):
+    """Thousands of short sequences and a few long ones, three heads: the
+    schedule ranks sequences by length up to 2048 of them and keeps index
+    order beyond; both must cover every (sequence, head, tile) once."""
+    rng = np.random.default_rng(nseq)
+    lengths = rng.integers(1, 25, size=nseq)
+    lengths[[5, nseq // 2, nseq - 1]] = [300, 129, 200]
+    inp = synth.draw_varlen(nseq, int(lengths.sum()), 3, 64, lengths=lengths)
+    out, kw = run_varlen_bwd(inp, 3, causal=True, scale=1.0, kind="t5", bidirectional=False)
+    dq, dk, dv, dtab = oracle.varlen_attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                                   inp.f64("do"), inp.cu_seqlens, **kw)
+    assert_grad(out["dq"], dq, "dQ")
+    assert_grad(out["dk"], dk, "dK")
+    assert_grad(out["dv"], dv, "dV")
+    assert_dtable(out["dtable"], dtab)
+
+
 def test_varlen_c4_full_size_two_heads():
     c = synth.config_by_name("c4")
     inp = synth.draw_varlen(c.seed, c.varlen_total, c.heads, c.head_dim)
