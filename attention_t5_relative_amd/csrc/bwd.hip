@@ -34,7 +34,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int BR = 128;    // dq: query rows per workgroup
-constexpr int BC = 64;     // dq: keys per tile
+constexpr int BC = 64;     // dq: keys per tile at head_dim 64 (32 at 128)
 constexpr int BKV = 128;   // dkv: keys per workgroup
 
 struct BwdArgs {
@@ -104,12 +104,26 @@ __device__ __forceinline__ bf16x8 frag(const uint32_t (&w)[4]) {
 // ---------------------------------------------------------------------------
 // dq kernel
 // ---------------------------------------------------------------------------
+// Workgroups per CU of the dq kernel (the dense bias's per-tile values
+// need more registers than two workgroups leave at head_dim 128).
+template <int D, int BIAS>
+constexpr int dq_wgs() {
+  return D == 64 || BIAS != kBiasDense ? 2 : 1;
+}
+
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE>
-__global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const BwdArgs a) {
   // K and V tiles, swizzled (see swz): K is read both row-wise
-  // (S^T = K Q^T) and transposed (dQ^T = K^T dS^T), V row-wise
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BC * D];
+  // (S^T = K Q^T) and transposed (dQ^T = K^T dS^T), V row-wise.  At
+  // head_dim 128 the tiles hold 32 keys and the workgroup's dO rows (the B
+  // operand of dP^T) sit in LDS rather than in 32 VGPRs, which fits two
+  // workgroups per CU.
+  constexpr int KT = D == 64 ? BC : 32;   // keys per tile
+  constexpr int NKB = KT / 32;
+  constexpr bool kDoInLds = D == 128;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dost[kDoInLds ? BR * D : 8];
   __shared__ float lut_mem[BIAS == kBiasT5 ? 2 * (kMaxDistance + kLutPad) + 1 : 1];
   const float *const lut = lut_mem + (BIAS == kBiasT5 ? a.t5.sat + kLutPad : 0);
 
@@ -146,6 +160,8 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
     df[s] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
     of[s] = buf_load16(ro, off);
   }
+  if constexpr (kDoInLds)
+    dma_tile<D, BR, 4>(dma_desc(a.dout + base, nrec), HD, q0, dost, wave, lane);
   const float lse2 = myrow < L ? a.lse[w.lse_base + myrow] * kLog2e : 0.f;
 
   int sat = 0;
@@ -167,12 +183,12 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   }
 
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
-  const int nkt = (kend + BC - 1) / BC;
+  const int nkt = (kend + KT - 1) / KT;
   // one key tile to LDS by buffer-to-LDS copies split over the four waves
   const i32x4 dk_src = dma_desc(a.k + base, nrec), dv_src = dma_desc(a.v + base, nrec);
   auto fill = [&](int j0, int buf) {
-    dma_tile<D, BC, 4>(dk_src, HD, j0, ks[buf], wave, lane);
-    dma_tile<D, BC, 4>(dv_src, HD, j0, vs[buf], wave, lane);
+    dma_tile<D, KT, 4>(dk_src, HD, j0, ks[buf], wave, lane);
+    dma_tile<D, KT, 4>(dv_src, HD, j0, vs[buf], wave, lane);
   };
   // row-wise operands: row il, chunk 2s + hl; transposed K operand: the two
   // halves of each 16-row group, per 32-column block
@@ -224,39 +240,49 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dq_kernel(const BwdAr
   wait_vmem_loads();
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    const int j0 = kt * BC;
+    const int j0 = kt * KT;
     const int buf = kt & 1;
-    if (kt + 1 < nkt) fill(j0 + BC, buf ^ 1);
+    if (kt + 1 < nkt) fill(j0 + KT, buf ^ 1);
     const bool active = wave_live && (!CAUSAL || (j0 <= wrow0 + 31));
     uint16_t bv[2][16];
     if constexpr (BIAS == kBiasDense)
       if (active) dense_row_load(rbias, myrow, L, j0, hl, bv);
-    f32x16 sacc[2], pacc[2];
+    f32x16 sacc[NKB], pacc[NKB];
     if (active) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         sacc[kb] = f32x16{};
         pacc[kb] = f32x16{};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&ks[buf][kof[s] + 32 * kb * D]);
           const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&vs[buf][kof[s] + 32 * kb * D]);
+          bf16x8 dfs;
+          if constexpr (kDoInLds)
+            dfs = *reinterpret_cast<const bf16x8 *>(&dost[kof[s] + 32 * wave * D]);
+          else
+            dfs = df[s];
           sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
-          pacc[kb] = mfma32(vf, df[s], pacc[kb]);
+          pacc[kb] = mfma32(vf, dfs, pacc[kb]);
         }
       }
     }
     if (active) {
       float bconst;
-      const bool fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut,
-                                                  slope_l2, bconst, bv);
+      bool fast;
+      if constexpr (NKB == 2)
+        fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut, slope_l2,
+                                          bconst, bv);
+      else
+        fast = score_block_T<BIAS, CAUSAL>(sacc[0], j0, wrow0, il, hl, L, c, sat, lut,
+                                           slope_l2, bconst, bv[0]);
       const float cc = fast ? c : 1.f;
       const float sub = bconst - lse2;
       // per 16-key group: P o (dP - Dc) as hi + lo fragments and P as bf16,
       // consumed at once by A^T += K^T (P o (dP - Dc))^T and B^T += K^T P^T,
       // K's operand by transposing reads
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           uint32_t xh[4], xl[4], ph[4];

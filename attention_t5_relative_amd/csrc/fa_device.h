@@ -240,6 +240,52 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
   return false;
 }
 
+// The same for one 32-key block (keys jb0 .. jb0 + 31; bv its dense bias
+// values), for the query-parallel kernel's 32-key tiles.
+template <int BIAS, bool CAUSAL>
+__device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, int il, int hl,
+                                              int L, float c, int sat, const float *lut,
+                                              float slope_l2, float &bconst,
+                                              const uint16_t (&bv)[16]) {
+  const int rmin = jb0 - (row0 + 31), rmax = jb0 + 31 - row0;
+  const bool mask_c = CAUSAL && rmax > 0;
+  const bool mask_l = jb0 + 32 > L;
+  bool uniform = (BIAS == kBiasNone);
+  bconst = 0.f;
+  if constexpr (BIAS == kBiasT5) {
+    const int lo = min(max(rmin, -sat), sat), hi = min(max(rmax, -sat), sat);
+    uniform = (lo == hi);
+    bconst = lut[lo];
+  }
+  if (uniform && !mask_c && !mask_l) return true;
+  bconst = 0.f;
+  const int rbase = jb0 - (row0 + il) + 4 * hl;
+  const int jb = jb0 + 4 * hl;
+  if constexpr (BIAS == kBiasT5) {
+    // offsets 0 .. 27 from one clamped base (see kLutPad)
+    const float *lb = lut + min(max(rbase, -sat - kLutPad), sat + kLutPad - 27);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = 8 * (r >> 2) + (r & 3);
+      const float t = fmaf(sacc[r], c, lb[off]);
+      sacc[r] = (mask_l && jb + off >= L) ? -INFINITY : t;
+    }
+    return false;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int off = 8 * (r >> 2) + (r & 3);
+    const int rr = rbase + off;
+    float t = sacc[r] * c;
+    if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
+    if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bv[r]), kLog2e, t);
+    if (mask_c && rr > 0) t = -INFINITY;
+    if (mask_l && jb + off >= L) t = -INFINITY;
+    sacc[r] = t;
+  }
+  return false;
+}
+
 // The dense bias values one lane needs for a 64-key tile of the query-
 // parallel kernels: row `row` (the lane's query), keys j0 + 32kb + 8(r/4) +
 // 4hl + r%4, from a buffer over one [S, S] bf16 matrix (row stride S).
