@@ -371,20 +371,20 @@ __host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
   return nl * 4 + (dbias ? n * 4 + 4 * n * 4 + (4 * 32 * kTilePitch + 2 * kTileGuard) * 4 : 0);
 }
 
-// Workgroups per CU.  At head_dim 128 with ALiBi the keys' V rows (the B
-// operand of dP) stay in LDS and are read per block, which leaves room for
-// two workgroups per CU without spilling; the other head_dim 128 variants
-// (T5 with its table gradient, RoPE, the dense bias) need the registers and
-// run one.
+// Workgroups per CU.  At head_dim 128 with ALiBi or no bias the keys' V
+// rows (the B operand of dP) stay in LDS and are read per block, and the
+// row offsets of the Q/dO operands are computed where they are used, which
+// leaves room for two workgroups per CU without spilling; the T5 (with its
+// table gradient) and dense-bias variants need the registers and run one.
 template <int D, int BIAS>
 constexpr int dkv_wgs() {
-  return D == 64 || BIAS == kBiasAlibi ? 2 : 1;
+  return D == 64 || BIAS == kBiasAlibi || BIAS == kBiasNone ? 2 : 1;
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
 __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const BwdArgs a) {
   constexpr int QB = DkvTile<D>::QB;
-  constexpr bool kVInLds = D == 128 && BIAS == kBiasAlibi;
+  constexpr bool kVInLds = D == 128 && (BIAS == kBiasAlibi || BIAS == kBiasNone);
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kVInLds ? BKV * D : 8];
   // Q and dO blocks as swizzled tiles (see swz), with the rows' -lse/scale
   // and -D (64 entries: the 4-byte copy fills one per lane)
@@ -494,9 +494,15 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
 
   // row-wise A operand: row il, chunk 2s + hl; transposed A operand: the
   // two halves of each 16-row group, per 32-column block
-  int aof[D / 16], tro[D / 32][2];
+  int aof[kVInLds ? 1 : D / 16], tro[D / 32][2];
+  if constexpr (!kVInLds) {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) aof[s] = swz_off<D>(il, 2 * s + hl);
+    for (int s = 0; s < D / 16; ++s) aof[s] = swz_off<D>(il, 2 * s + hl);
+  }
+  // swz_off(il, 2s + hl) = il D + 8 (hl ^ (w & 1)) + 16 (s ^ (w >> 1)), w = swz(il)
+  const int aw = swz<D>(il);
+  const int abase = il * D + 8 * (hl ^ (aw & 1));
+  auto aoff = [&](int s) { return kVInLds ? abase + 16 * (s ^ (aw >> 1)) : aof[s]; };
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     tro[db][0] = swz_tr_off<D>(lane, 0, db);
@@ -524,7 +530,7 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
     }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const int at = aof[s] + 32 * rb * D;
+      const int at = aoff(s) + 32 * rb * D;
       sacc = mfma32(*reinterpret_cast<const bf16x8 *>(&qs[buf][at]), kf[s], sacc);
       bf16x8 vs;
       if constexpr (kVInLds)
@@ -624,7 +630,9 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
       const bool mask_c = CAUSAL && rmax > 0;
       const bool mask_r = irow0 + 32 > L;
       const bool mask_k = kw0 + 32 > L;
-      bool uniform = (BIAS == kBiasNone);
+      // (with V in LDS, blocks without a bias take the masked path too: one
+      // path for P keeps the register count down)
+      bool uniform = (BIAS == kBiasNone) && !kVInLds;
       float bconst = 0.f;
       int ulo = 0;
       if constexpr (BIAS == kBiasT5) {
