@@ -191,7 +191,7 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
 // The causal mask hides keys after the query; keys at or past L are masked.
 // A dense bias arrives as the lane's own values bv (bf16 bits, same order
 // as sacc; see dense_row_load).
-template <int BIAS, bool CAUSAL>
+template <int BIAS, bool CAUSAL, bool ALIBI_LINEAR = true>
 __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0, int il, int hl,
                                              int L, float c, int sat, const float *lut,
                                              float slope_l2, float &bconst,
@@ -221,6 +221,24 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
         sacc[kb][r] = (mask_l && jb + off >= L) ? -INFINITY : t;
       }
     return false;
+  }
+  if constexpr (BIAS == kBiasAlibi && ALIBI_LINEAR) {
+    // all distances of the tile on one side of 0 and no mask: the bias is
+    // linear in the key offset, -slope |r| = sl (rbase + off)
+    if (!mask_c && !mask_l && (rmax <= 0 || rmin >= 0)) {
+      const float sl = rmax <= 0 ? -slope_l2 : slope_l2;
+      const float b0 = sl * (float)rbase;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float bq = fmaf((float)(32 * kb + 8 * q), sl, b0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[kb][4 * q + e] = fmaf(sacc[kb][4 * q + e], c, fmaf((float)e, sl, bq));
+        }
+      return false;
+    }
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -271,6 +289,21 @@ __device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, i
       sacc[r] = (mask_l && jb + off >= L) ? -INFINITY : t;
     }
     return false;
+  }
+  if constexpr (BIAS == kBiasAlibi) {
+    // one-sided and unmasked: the bias is linear in the key offset
+    if (!mask_c && !mask_l && (rmax <= 0 || rmin >= 0)) {
+      const float sl = rmax <= 0 ? -slope_l2 : slope_l2;
+      const float b0 = sl * (float)rbase;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float bq = fmaf((float)(8 * q), sl, b0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sacc[4 * q + e] = fmaf(sacc[4 * q + e], c, fmaf((float)e, sl, bq));
+      }
+      return false;
+    }
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {

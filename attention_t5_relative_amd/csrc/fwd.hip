@@ -221,8 +221,10 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
 
       // Element (kb, r): key j0 + 32kb + 8(r/4) + 4hl + r%4, query wrow0 + il.
       float bconst;
-      const bool fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut,
-                                                  slope_l2, bconst, bv);
+      // (the linear ALiBi path would not fit the 168 VGPRs of three
+      // workgroups per CU at head_dim 64)
+      const bool fast = score_tile_T<BIAS, CAUSAL, D == 128>(sacc, j0, wrow0, il, hl, L, c, sat,
+                                                            lut, slope_l2, bconst, bv);
       float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
