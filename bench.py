@@ -25,8 +25,16 @@ kernels (RMSNorm, cross-entropy with z-loss) forward + backward on the same
 32768 tokens (width 768; T5 vocabulary 32128); both are bound by HBM, so their
 value is algorithmic GB/s (each tensor read or written once per pass).
 
+``--workload encoder|varlen|alibi|rope`` time the other attention workloads
+the same way (forward + backward, kernel times by HIP events): the
+bidirectional T5 encoder B16 H12 S1024 D64; 32768 packed tokens with
+lognormal lengths (12 heads, D64, bidirectional T5); and the long-context
+causal B2 H16 S16384 D128 run with ALiBi or with RoPE.  Their lines carry
+no cpu_baseline.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-                    [--bias t5|dense] [--workload attention|rmsnorm|ce]
+                    [--bias t5|dense]
+                    [--workload attention|rmsnorm|ce|encoder|varlen|alibi|rope]
 """
 from __future__ import annotations
 
@@ -269,6 +277,137 @@ def norm_loss_cpu_baseline(workload):
                       f"({dt:.2f} s); same algorithmic bytes per row as the GPU value"}
 
 
+OTHER_ATTENTION = ("encoder", "varlen", "alibi", "rope")
+
+
+def bench_other_attention(a):
+    """Forward + backward of one of the other attention workloads; one JSON
+    line with the FlashAttention-convention TFLOP/s of the step."""
+    import numpy as np
+    import torch
+
+    import attention_t5_relative_amd as fa
+    import synth
+    from attention_t5_relative_amd import _lib
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(SEED)
+
+    def rnd(shape):
+        return torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+
+    lib = _lib.load()
+    name = a.workload
+    if name == "varlen":
+        H, Dh = 12, 64
+        lens = synth.draw_varlen_lengths(np.random.default_rng(SEED), 32768)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        T = int(lens.sum())
+        q, k, v, do = (rnd((T, H, Dh)) for _ in range(4))
+        table = torch.randn((NB, H), generator=gen, device=dev) * 0.5
+        bias = fa.T5Bias(table, NB, MD, True)
+        dtable = torch.empty_like(table)
+        o = torch.empty_like(q)
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+        mx = int(lens.max())
+        fwd_flops = 4.0 * H * Dh * float((lens.astype(np.float64) ** 2).sum())
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        p = _lib.FaVarlenBwdParams()
+        p.f = fa.api._varlen_params(q, k, v, o, lse, cu, mx, 1.0, False, bias, 0.0)
+        p.dout, p.dq, p.dk, p.dv, p.dtable = (do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                              dv.data_ptr(), dtable.data_ptr())
+        wsb = torch.empty(lib.fa_varlen_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8,
+                          device=dev)
+
+        def step():
+            fa.fa_varlen_fwd(q, k, v, o, lse, cu, mx, scale=1.0, causal=False, bias=bias)
+            fa.fa_varlen_bwd(q, k, v, o, lse, do, dq, dk, dv, cu, mx, dtable, scale=1.0,
+                             causal=False, bias=bias, workspace=wsb)
+        workload = ("packed encoder self-attention fwd+bwd, 32768 tokens in "
+                    f"{len(lens)} sequences (lognormal lengths, 16..4096), H12 D64, "
+                    "bidirectional T5 bias, scale 1")
+        shape = {"tokens": T, "sequences": int(len(lens)), "heads": H, "head_dim": Dh,
+                 "causal": False}
+    else:
+        if name == "encoder":
+            Bq, Sq, H, Dh, causal, scale, rope = 16, 1024, 12, 64, False, 1.0, 0.0
+            table = torch.randn((NB, H), generator=gen, device=dev) * 0.5
+            bias, dtable = fa.T5Bias(table, NB, MD, True), torch.empty_like(table)
+            workload = ("encoder self-attention fwd+bwd, B16 H12 S1024 D64, bidirectional T5 "
+                        "bias (32 buckets, max distance 128), scale 1")
+        else:
+            Bq, Sq, H, Dh, causal, scale = 2, 16384, 16, 128, True, 128 ** -0.5
+            dtable = None
+            if name == "alibi":
+                bias, rope = fa.ALiBi(fa.alibi_slopes(H, dev)), 0.0
+                workload = ("long-context causal attention fwd+bwd, B2 H16 S16384 D128, ALiBi "
+                            "slopes 2^(-8h/16), scale 1/sqrt(128)")
+            else:
+                bias, rope = None, 10000.0
+                workload = ("long-context causal attention fwd+bwd, B2 H16 S16384 D128, RoPE "
+                            "base 10000 in the kernels, scale 1/sqrt(128)")
+        q, k, v, do = (rnd((Bq, Sq, H, Dh)) for _ in range(4))
+        o = torch.empty_like(q)
+        lse = torch.empty((Bq, H, Sq), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        fwd_flops = 4.0 * Bq * H * Sq * Sq * Dh / (2.0 if causal else 1.0)
+        p = _lib.FaBwdParams()
+        p.f = fa.api._fwd_params(q, k, v, o, lse, scale, causal, bias, rope)
+        p.dout, p.dq, p.dk, p.dv = do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+        p.dtable = None if dtable is None else dtable.data_ptr()
+        wsb = torch.empty(max(1, lib.fa_bwd_workspace_size(ctypes.byref(p))), dtype=torch.uint8,
+                          device=dev)
+
+        def step():
+            fa.fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, bias=bias, rope_base=rope)
+            fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, scale=scale, causal=causal,
+                      bias=bias, rope_base=rope, workspace=wsb)
+        shape = {"batch": Bq, "heads": H, "seq_len": Sq, "head_dim": Dh, "causal": causal}
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    hip = _hip()
+    kernels = {"fwd": _lib.FA_KERNEL_FWD, "bwd_dq": _lib.FA_KERNEL_BWD_DQ,
+               "bwd_dkv": _lib.FA_KERNEL_BWD_DKV}
+    evs = {n: [(_event(hip), _event(hip)) for _ in range(a.steps)] for n in kernels}
+    t_start, t_stop = _event(hip), _event(hip)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.hipEventRecord(t_start, ctypes.c_void_p(stream))
+    for i in range(a.steps):
+        for n, kid in kernels.items():
+            lib.fa_set_kernel_timer(kid, evs[n][i][0], evs[n][i][1])
+        step()
+    hip.hipEventRecord(t_stop, ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    for kid in kernels.values():
+        lib.fa_set_kernel_timer(kid, None, None)
+    ms_step = _elapsed(hip, t_start, t_stop) / a.steps
+    kernel_ms = {n: sum(_elapsed(hip, s0, s1) for s0, s1 in evs[n]) / a.steps for n in kernels}
+    algo = {"fwd": fwd_flops, "bwd_dq": 1.5 * fwd_flops, "bwd_dkv": 2.0 * fwd_flops}
+    dom = max(kernel_ms, key=kernel_ms.get)
+    achieved = algo[dom] / (kernel_ms[dom] * 1e-3) / 1e12
+    value = 3.5 * fwd_flops / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": f"attention fwd+bwd TFLOP/s, {name} workload",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": dict({"workload": workload, "parallelism": "none (one GPU)",
+                        "frac_of_peak": round(value / PEAK_TFLOPS, 4),
+                        "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()}}, **shape),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,7 +416,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=12)
     ap.add_argument("--bias", choices=("t5", "dense"), default="t5")
-    ap.add_argument("--workload", choices=("attention", "rmsnorm", "ce"), default="attention")
+    ap.add_argument("--workload", choices=("attention", "rmsnorm", "ce") + OTHER_ATTENTION,
+                    default="attention")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB before the "
                          "timed steps (a known-size kernel to calibrate HBM byte counters)")
@@ -295,6 +435,8 @@ def main(argv=None):
     import synth
     from attention_t5_relative_amd import _lib
 
+    if a.workload in OTHER_ATTENTION:
+        return bench_other_attention(a)
     if a.workload != "attention":
         return bench_norm_loss(a)
 
