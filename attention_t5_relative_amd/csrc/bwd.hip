@@ -80,7 +80,7 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int g, Work &w) {
     w.lse_base = (size_t)w.h * a.total + w.tok0;
   } else {
     int pair;
-    tile_order(g, a.nbatch * a.heads, a.ntile, pair, w.tile);
+    tile_order<4>(g, a.nbatch * a.heads, a.ntile, pair, w.tile);   // 2 workgroups per CU
     w.part = pair * a.ntile + w.tile;
     const int b = pair / a.heads;
     w.b = b;

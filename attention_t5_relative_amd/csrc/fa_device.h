@@ -118,21 +118,26 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 // Dense grids: logical id g -> (pair, rank), pair = (batch, head) and rank 0
 // the heaviest tile of a pair (most key or query tiles to visit).  When the
 // pairs split evenly over the 8 XCDs, the ids an XCD receives (a contiguous
-// range, see xcd_remap) cover its own pairs in groups of kPairGroup, each
-// group rank-major: heavy tiles start early (longest-processing-time order;
-// with plain pair-major order the heaviest tiles of the last pairs start last
-// and run nearly alone at the end), while the tiles running at any time
-// belong to few pairs, whose K and V stay in the XCD's L2.  Otherwise the
-// order is pair-major.
-constexpr int kPairGroup = 4;
+// range, see xcd_remap) cover its own pairs in groups of G, each group
+// rank-major: heavy tiles start early (longest-processing-time order; with
+// plain pair-major order the heaviest tiles of the last pairs start last and
+// run nearly alone at the end), while the tiles running at any time belong
+// to few pairs, whose K and V stay in the XCD's L2.  Otherwise the order is
+// pair-major.  The best G depends on the workgroups an XCD runs at once:
+// with G pairs of 32 causal tiles per group, a group's light tiles must
+// overlap the next group's heavy ones without leaving slots idle at the end
+// (a list-scheduling simulation of 12 pairs per XCD: G = 4 is ideal for 64
+// concurrent workgroups, G = 3 or 6 for 96; G = 6 measured best for the
+// forward's 96).
+template <int G>
 __device__ __forceinline__ void tile_order(int g, int npairs, int ntile, int &pair, int &rank) {
   const int pp = npairs >> 3;
-  if ((npairs & 7) == 0 && pp % kPairGroup == 0) {
-    const int per = pp * ntile, gsz = kPairGroup * ntile;
+  if ((npairs & 7) == 0 && pp % G == 0) {
+    const int per = pp * ntile, gsz = G * ntile;
     const int x = g / per, r = g - x * per;
     const int gi = r / gsz, rg = r - gi * gsz;
-    rank = rg / kPairGroup;
-    pair = x * pp + gi * kPairGroup + (rg - rank * kPairGroup);
+    rank = rg / G;
+    pair = x * pp + gi * G + (rg - rank * G);
   } else {
     pair = g / ntile;
     rank = g - pair * ntile;

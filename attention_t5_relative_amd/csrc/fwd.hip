@@ -85,7 +85,7 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
     if (L <= 0) return;
   } else {
     int pair, rank;
-    tile_order(g, a.nbatch * a.heads, a.nq, pair, rank);
+    tile_order<6>(g, a.nbatch * a.heads, a.nq, pair, rank);   // 3 workgroups per CU
     qt = a.nq - 1 - rank;                     // longest causal rows first
     bidx = pair / a.heads;
     h = pair - bidx * a.heads;
