@@ -129,10 +129,13 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 // (a list-scheduling simulation of 12 pairs per XCD: G = 4 is ideal for 64
 // concurrent workgroups, G = 3 or 6 for 96; G = 6 measured best for the
 // forward's 96).
-template <int G>
+// G is the largest divisor of the XCD's pair count up to GMAX.
+template <int GMAX>
 __device__ __forceinline__ void tile_order(int g, int npairs, int ntile, int &pair, int &rank) {
   const int pp = npairs >> 3;
-  if ((npairs & 7) == 0 && pp % G == 0) {
+  int G = GMAX;
+  while (G > 1 && pp % G != 0) --G;
+  if ((npairs & 7) == 0 && pp > 0) {
     const int per = pp * ntile, gsz = G * ntile;
     const int x = g / per, r = g - x * per;
     const int gi = r / gsz, rg = r - gi * gsz;
