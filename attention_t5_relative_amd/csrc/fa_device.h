@@ -31,9 +31,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 __device__ __forceinline__ i32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
-__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
-}
 // One bf16 (as its 16 bits) at byte offset `off`.
 __device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
@@ -88,8 +85,6 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
 __device__ __forceinline__ float bf16_bits(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
-
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 // Max / sum of a value over the two half-waves (lanes l and l ^ 32), with
 // v_permlane32_swap (a VALU lane exchange, no LDS round trip).  Both lanes of
@@ -359,24 +354,6 @@ __device__ __forceinline__ void dense_row_load(rsrc_t rb, int row, int S, int j0
   }
 }
 
-// Per-lane LDS element offset for the transposing read that assembles an
-// MFMA operand of 8 rows x 1 column from a row-major tile with row pitch
-// `pitch`: the lane's own column is (lane % 32) and the 8 rows are, for
-// k-slot v of half-wave hl, 4hl + v (v < 4) and 8 + 4hl + (v - 4), relative
-// to a 16-row group.  Add (16-row group start) * pitch + 32 * column block
-// for the first four rows, and 8 * pitch more for the last four.
-__device__ __forceinline__ int tr_lane_offset(int lane, int pitch) {
-  const int i16 = lane & 15, hl = lane >> 5;
-  return (4 * hl + (i16 >> 2)) * pitch + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-}
-
-// The 8-row operand for one MFMA k-step, read as two transposing reads.
-__device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t *p, int pitch) {
-  const s16x4 lo = lds_read_tr(p);
-  const s16x4 hi = lds_read_tr(p + 8 * pitch);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 // ---------------------------------------------------------------------------
 // Unpadded bf16 tiles in LDS, swizzled by 16-byte chunk, filled straight from
 // global memory by buffer-to-LDS copies.
@@ -483,14 +460,6 @@ __device__ __forceinline__ void dma_tile(i32x4 src, int stride, int row0, uint16
     const int c = pc ^ swz<D>(r);
     dma16(src, ((uint32_t)(row0 + r) * (uint32_t)stride + 8 * c) * 2u, tile + piece * 512);
   }
-}
-
-// Bijective key reordering inside each group of 16 keys used for the
-// transposed V tile: swaps bits 2 and 3 of the key offset, so that the eight
-// keys one MFMA B-operand lane supplies (see the forward kernel) are
-// contiguous.
-__device__ __forceinline__ int key_perm16(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
 }  // namespace fa
