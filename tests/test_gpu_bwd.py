@@ -209,6 +209,24 @@ def test_varlen_backward_small(causal, kind, rope):
         assert_dtable(out["dtable"], dtab)
 
 
+@pytest.mark.parametrize("causal,kind,rope", [(True, "alibi", None), (False, "none", 10000.0),
+                                              (True, "t5", None)])
+def test_varlen_backward_head_dim_128(causal, kind, rope):
+    """Packed sequences at head_dim 128 (32-key dq tiles, V rows in LDS for
+    the dkv kernel without a T5 bias)."""
+    lengths = np.array([1, 130, 300, 64, 257, 33])
+    inp = synth.draw_varlen(41, int(lengths.sum()), 2, 128, lengths=lengths)
+    out, kw = run_varlen_bwd(inp, 2, causal=causal, scale=128 ** -0.5, kind=kind,
+                             bidirectional=not causal, rope_base=rope)
+    dq, dk, dv, dtab = oracle.varlen_attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                                   inp.f64("do"), inp.cu_seqlens, **kw)
+    assert_grad(out["dq"], dq, "dQ")
+    assert_grad(out["dk"], dk, "dK")
+    assert_grad(out["dv"], dv, "dV")
+    if dtab is not None:
+        assert_dtable(out["dtable"], dtab)
+
+
 @pytest.mark.parametrize("nseq", [2048, 2100])
 def test_varlen_many_sequences(nseq):
     """Thousands of short sequences and a few long ones, three heads: the
