@@ -384,9 +384,11 @@ __device__ __forceinline__ int swz_off(int r, int c) {
   return r * D + 8 * (c ^ swz<D>(r));
 }
 
-// Element offset for the transposing read (see tr_lane_offset) of rows
-// 8 * half + 4 hl .. of a 16-row group, columns 32 db .. 32 db + 31, in a
-// swizzled tile.
+// Element offset for the transposing read that assembles an MFMA operand of
+// 8 rows x 1 column: the lane's own column is 32 db + (lane % 32) and its 8
+// rows are, for k-slot v of half-wave hl, 4 hl + v (v < 4) and
+// 8 + 4 hl + (v - 4) relative to a 16-row group.  half = 0 gives the offset
+// for the first four rows, half = 1 for the last four, in a swizzled tile.
 template <int D>
 __device__ __forceinline__ int swz_tr_off(int lane, int half, int db) {
   const int i16 = lane & 15, hl = lane >> 5, b4 = (lane >> 4) & 1;
