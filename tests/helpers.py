@@ -8,7 +8,7 @@ import torch
 import oracle
 import synth
 
-# Gates:
+# Parity gates (elementwise against the fp64 oracle):
 #   O:           max |gpu - ref| <= 2e-2 and mean |gpu - ref| <= 2e-3
 #   dQ, dK, dV:  e = |gpu - ref| / max(1, |ref|): max e <= 2e-2, mean e <= 2e-3
 #   dtable:      ||gpu - ref||_F / ||ref||_F <= 1e-2
