@@ -74,6 +74,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16) += A(16x32) * B(32x16), bf16 in, fp32 accumulate.  Lane l holds
+// row (l % 16) of A and column (l % 16) of B, each with the 8 consecutive k
+// values 8 (l / 16) .. 8 (l / 16) + 7; the accumulator holds, in register r,
+// the element (row 4 (l / 16) + r, column l % 16).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(uint32_t, v);

@@ -16,6 +16,15 @@
 //   swizzled tiles (no bank conflicts on either read) copied from global
 //   memory straight into LDS.
 //
+// Normalisation.  O is divided by the sum of the bf16 weights that actually
+// multiply V (P rounded to bf16 for the PV product), not by the fp32 sum of
+// P: the rounding error of a row's dominant weight, up to 2^-9 of it, then
+// cancels between numerator and denominator instead of reaching O.  (The
+// lazy rescale below leaves the dominant weight at exp2 of a non-integer,
+// so that error is not otherwise zero.)  The bf16 sum costs no VALU work: a
+// 16x16x32 MFMA per 16-key fragment of P adds its keys against a constant
+// 0/1 operand.  The LSE keeps the fp32 sum, exact to fp32.
+//
 // Latency.  With operands read from LDS right before each MFMA, every MFMA
 // waits out an LDS round trip; measured per 64-key tile that cost more than
 // the softmax itself.  So the K operands of a tile are read in one batch
@@ -156,6 +165,22 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+  // Sum of the bf16 weights per query: P's fragment (lane (hl, il): query
+  // il, 8 keys of half-wave hl), read as a 16x16x32 B operand, holds query
+  // 16 ((l / 16) & 1) + (l % 16) in k-group l / 16.  With A[i][k] = 1 when
+  // k-group and row agree on that query half ((k / 8) & 1 == (i / 4) & 1),
+  // output row i sums the 16 keys of query 16 ((i / 4) & 1) + column, and
+  // lane l's rows 4 (l / 16) .. + 3 are its own query il.
+  // (At head_dim 128 the operand is rebuilt from one register in each
+  // iteration: four registers held across the loop would spill the dense-
+  // bias variant.)
+  f32x4 wsum = f32x4{};
+  const int selw = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? 0x3f803f80 : 0;
+  auto sel_operand = [&]() {
+    int w = selw;
+    if constexpr (D == 128) asm volatile("" : "+v"(w));
+    return __builtin_bit_cast(bf16x8, i32x4{w, w, w, w});
+  };
   const float c = a.scale_log2;
 
   // Tiles 0 .. NBUF - 2 are requested now.  Iteration kt requests tile
@@ -240,7 +265,10 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
         const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.f;
         if (need) m_run = tmax;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lsum[e] *= alpha;
+        for (int e = 0; e < 4; ++e) {
+          lsum[e] *= alpha;
+          wsum[e] *= alpha;
+        }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -270,11 +298,12 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
 
 #pragma unroll
       for (int i = VPRE; i < NVF; ++i) vf[i] = vread(i);
-      // O^T += V^T P^T
+      // O^T += V^T P^T, and the bf16 weight sums
 #pragma unroll
       for (int i = 0; i < NVF; ++i) {
         const int db = i >> 2, kb = (i >> 1) & 1, u = i & 1;
         oacc[db] = mfma32(vf[i], pb[kb][u], oacc[db]);
+        if (db == 0) wsum = mfma16(sel_operand(), pb[kb][u], wsum);
       }
     }
     // tile kt + 1 has landed (each wave waits for its own copies)
@@ -287,7 +316,7 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
 
   const int myrow = wrow0 + il;
   const float l_tot = half_sum((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = wsum[0] > 0.f ? 1.f / wsum[0] : 0.f;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll

@@ -198,8 +198,9 @@ def head_fwd(qh, kh, vh, head, *, scale=1.0, causal=False, bias="none", table=No
              rope_base=None, rope_round=True, dense=None):
     """Forward for one head: qh, kh, vh float64 [S, D] -> (O [S, D], LSE [S]).
 
-    ``rope_round=False`` skips the bf16 rounding of the rotated q, k (only the
-    finite-difference pin uses it: a rounding step has no derivative)."""
+    ``rope_round=False`` skips the bf16 rounding of the rotated q, k: the
+    exact rotation (the finite-difference pin needs it, since a rounding step
+    has no derivative; the GPU tests also measure the kernels against it)."""
     s, _, _ = _scores(qh, kh, head, scale=scale, causal=causal, bias=bias, table=table,
                       num_buckets=num_buckets, max_distance=max_distance,
                       bidirectional=bidirectional, slopes=slopes, rope_base=rope_base,
@@ -248,7 +249,7 @@ def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", tab
 
 def _kw(kw):
     keys = ("scale", "causal", "bias", "table", "num_buckets", "max_distance",
-            "bidirectional", "slopes", "rope_base")
+            "bidirectional", "slopes", "rope_base", "rope_round")
     return {k: kw[k] for k in keys if k in kw}
 
 

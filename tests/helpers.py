@@ -70,7 +70,56 @@ def assert_dtable(got, ref, what="dtable"):
 
 
 def oracle_kwargs(bias, causal, scale, table=None, slopes=None, nb=32, md=128,
-                  bidirectional=True, rope_base=None):
+                  bidirectional=True, rope_base=None, rope_round=True):
     return dict(scale=scale, causal=causal, bias=bias, table=table, num_buckets=nb,
                 max_distance=md, bidirectional=bidirectional, slopes=slopes,
-                rope_base=rope_base)
+                rope_base=rope_base, rope_round=rope_round)
+
+
+def nan_like(t: torch.Tensor) -> torch.Tensor:
+    """An output buffer pre-filled with NaN: any element a kernel fails to
+    write stays NaN and fails the finiteness checks."""
+    return torch.full_like(t, float("nan"))
+
+
+def pmap(fn, items, workers=8):
+    """fn over items on a thread pool (NumPy releases the GIL in its array
+    work, so independent oracle heads run side by side); results in order."""
+    from concurrent.futures import ThreadPoolExecutor
+    items = list(items)
+    if len(items) <= 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(max_workers=min(workers, len(items))) as ex:
+        return list(ex.map(fn, items))
+
+
+def log_margin(what: str, **errs):
+    """Append one line of measured errors to $FA_PARITY_LOG (if set)."""
+    import json
+    import os
+    path = os.environ.get("FA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(case=what, **{k: float(v) for k, v in errs.items()})) + "\n")
+
+
+def check_exact_rotation(got, reading, exact, what, scale, head_dim, gate):
+    """RoPE against the exact rotation (no bf16 rounding of the rotated q, k).
+
+    `reading` is the oracle's result under the RoPE reading (rotated q, k
+    rounded once to bf16), `exact` the oracle's result without the rounding,
+    `gate` the assert_* function of the output.  At the usual softmax scale
+    (at most 1/sqrt(D), as the long-context workload uses) the kernel must
+    meet the output's own gate against the exact rotation.  At larger scales
+    the rounding of the rotated operands is itself beyond the gate (scores
+    of std 8 at scale 1, D 64), so the kernel must then stay within 1.25x
+    the reading's own distance from the exact rotation (plus 1e-3).
+    Returns (kernel max error, reading max error) against the exact result."""
+    e_k = norm_err(got, exact)[0]
+    e_r = norm_err(reading, exact)[0]
+    if scale * np.sqrt(head_dim) <= 1.0 + 1e-6:
+        gate(got, exact, f"{what} (exact rotation)")
+    else:
+        assert e_k <= 1.25 * e_r + 1e-3, (
+            f"{what}: {e_k:.3e} from the exact rotation, the reading's own rounding {e_r:.3e}")
+    return e_k, e_r
