@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     attention,
     cross_entropy,
     fa_bwd,
+    fa_bwd_noalloc,
     fa_ce_bwd,
     fa_ce_fwd,
     fa_fwd,

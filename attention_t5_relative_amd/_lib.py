@@ -25,6 +25,8 @@ FA_KERNEL_RMSNORM_BWD = 4
 FA_KERNEL_CE_FWD = 5
 FA_KERNEL_CE_BWD = 6
 
+FA_BWD_NOALLOC_MAX_BYTES = 16 << 20
+
 FA_BIAS_NONE = 0
 FA_BIAS_T5 = 1
 FA_BIAS_ALIBI = 2
@@ -95,6 +97,7 @@ SIGNATURES = {
     "fa_varlen_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(FaVarlenBwdParams)]),
     "fa_fwd": (c_i32, [ctypes.POINTER(FaFwdParams), c_ptr, ctypes.c_size_t, c_ptr]),
     "fa_bwd": (c_i32, [ctypes.POINTER(FaBwdParams), c_ptr, ctypes.c_size_t, c_ptr]),
+    "fa_bwd_noalloc": (c_i32, [ctypes.POINTER(FaBwdParams), c_ptr]),
     "fa_varlen_fwd": (c_i32, [ctypes.POINTER(FaVarlenFwdParams), c_ptr, ctypes.c_size_t, c_ptr]),
     "fa_varlen_bwd": (c_i32, [ctypes.POINTER(FaVarlenBwdParams), c_ptr, ctypes.c_size_t, c_ptr]),
     "fa_t5_buckets": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr, c_ptr]),

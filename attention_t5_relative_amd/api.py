@@ -207,6 +207,22 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, scale=1.0, causal=
     check(lib.fa_bwd(ctypes.byref(p), _ptr(ws), wsb, _stream(q.device, stream)), "fa_bwd")
 
 
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, scale=1.0, causal=False,
+                   bias: BiasSpec = None, rope_base=0.0, stream=None) -> None:
+    """fa_bwd with the library's static scratch instead of a workspace: the
+    call allocates nothing (torch included)."""
+    lib = _lib.load()
+    p = FaBwdParams()
+    p.f = _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base)
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, torch.bfloat16, q.shape, q.device)
+    if dtable is not None:
+        _need(dtable, "dtable", torch.float32, _dbias_shape(bias, q.shape[2]), q.device)
+    p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    p.dtable = _ptr(dtable)
+    check(lib.fa_bwd_noalloc(ctypes.byref(p), _stream(q.device, stream)), "fa_bwd_noalloc")
+
+
 def fa_varlen_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, max_seqlen, dtable=None, *,
                   scale=1.0, causal=False, bias: BiasSpec = None, rope_base=0.0, workspace=None,
                   stream=None) -> None:

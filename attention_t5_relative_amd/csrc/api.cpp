@@ -457,6 +457,36 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   return FA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch for fa_bwd_noalloc.  Each GPU holds its own copy of this
+// array from the library's first use on it until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory, so the
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = FA_BWD_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;   // device ordinal -> address of its scratch
+
+fa_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -550,6 +580,25 @@ fa_status fa_bwd(const fa_bwd_params *p, void *ws, size_t ws_bytes, hipStream_t 
   if (st != FA_OK) return st;
   return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dout, p->dq,
                  p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
+}
+
+fa_status fa_bwd_noalloc(const fa_bwd_params *p, hipStream_t stream) {
+  const fa_status st = fa_check_bwd(p);
+  if (st != FA_OK) return st;
+  const fa::Problem pr = make_problem(p->f);
+  const size_t need = bwd_layout(pr, p->dtable != nullptr).total;
+  if (need > kScratchBytes)
+    return fail(FA_ERR_UNSUPPORTED,
+                "fa_bwd_noalloc: this problem needs %zu bytes of scratch; the static scratch "
+                "holds %zu (use fa_bwd with a workspace)",
+                need, kScratchBytes);
+  void *ws = nullptr;
+  if (need > 0) {
+    const fa_status s2 = scratch_of_current_device(&ws);
+    if (s2 != FA_OK) return s2;
+  }
+  return run_bwd(pr, p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dout, p->dq, p->dk, p->dv,
+                 p->dtable, ws, need, stream);
 }
 
 fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes,

@@ -188,6 +188,22 @@ fa_status fa_fwd(const fa_fwd_params *p, void *ws, size_t ws_bytes, hipStream_t 
 /* Backward: dQ, dK, dV and the table gradient (the report trains T, so its
  * gradient is implied; it prints no backward). */
 fa_status fa_bwd(const fa_bwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream);
+/* Backward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same contract and results as fa_bwd, bit for bit,
+ * except that its scratch space (the same layout fa_bwd_workspace_size
+ * sizes) lives in a static device array of FA_BWD_NOALLOC_MAX_BYTES inside
+ * the library: each GPU the library runs on holds one until the process
+ * ends.  Problems needing more scratch return FA_ERR_UNSUPPORTED before
+ * anything is enqueued (RoPE, and a dense bias matrix shared by a batch of
+ * more than one, need workspaces of their own size: use fa_bwd).  Every call
+ * on one GPU uses that GPU's array, so calls that overlap in time on one GPU
+ * (two streams, two threads) race and must be serialised by the caller.
+ * The call itself allocates nothing; its first call on a device looks up
+ * the array's device address once. */
+#define FA_BWD_NOALLOC_MAX_BYTES (16u << 20)
+fa_status fa_bwd_noalloc(const fa_bwd_params *p, hipStream_t stream);
+
 /* Packed variants (packing blog: flash_attn_varlen_func semantics). */
 fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *ws, size_t ws_bytes,
                         hipStream_t stream);

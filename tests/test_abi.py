@@ -271,3 +271,18 @@ def test_cross_entropy_checks(lib):
     q.rows = 0
     q.logits = q.labels = q.loss = q.lse = None
     assert lib.fa_ce_fwd(ctypes.byref(q), None) == _lib.FA_OK            # empty: nothing to do
+
+
+def test_noalloc_backward_rejects_problems_beyond_its_scratch(lib):
+    """The size check runs on the host before any HIP call: a RoPE backward
+    (rotated q, k copies) needs far more than the static scratch."""
+    p = _lib.FaBwdParams()
+    f = p.f
+    f.batch, f.seqlen, f.heads, f.head_dim, f.causal = 2, 16384, 16, 128, 1
+    f.scale, f.rope_base = 0.088, 10000.0
+    fake = 0x1000   # never dereferenced: the call returns before any launch
+    f.q = f.k = f.v = f.o = f.lse = fake
+    p.dout = p.dq = p.dk = p.dv = fake
+    assert lib.fa_bwd_noalloc(ctypes.byref(p), None) == _lib.FA_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.fa_last_error()
+    assert lib.fa_bwd_workspace_size(ctypes.byref(p)) > _lib.FA_BWD_NOALLOC_MAX_BYTES

@@ -85,11 +85,15 @@ def test_every_lds_copy_follows_five_wait_states(code_objects):
 
 def test_no_kernel_uses_scratch(code_objects):
     readelf = _tool("llvm-readelf")
+    kernels = 0
     for obj in code_objects:
         notes = subprocess.run([readelf, "--notes", str(obj)], capture_output=True, text=True,
                                check=True).stdout
         spills = re.findall(r"\.(?:s|v)gpr_spill_count:\s+(\d+)", notes)
-        assert spills, "no kernel metadata found"
+        kernels += len(spills)
+        if not spills:   # a code object holding device data only (the static scratch)
+            continue
         assert all(int(n) == 0 for n in spills), f"{obj.name}: spill counts {set(spills)}"
         priv = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", notes)
         assert all(int(n) == 0 for n in priv), f"{obj.name}: private segment {set(priv)}"
+    assert kernels > 0, "no kernel metadata found"
