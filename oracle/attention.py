@@ -211,10 +211,14 @@ def head_fwd(qh, kh, vh, head, *, scale=1.0, causal=False, bias="none", table=No
 
 def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", table=None,
              num_buckets=32, max_distance=128, bidirectional=True, slopes=None,
-             rope_base=None, rope_round=True, dense=None):
+             rope_base=None, rope_round=True, dense=None, dlse=None):
     """Backward for one head -> (dq, dk, dv [S, D], bias gradient): the bias
     gradient is dtable_h [num_buckets] for T5, dS [S, S] for a dense bias,
-    None otherwise."""
+    None otherwise.
+
+    ``dlse`` [S] (optional) is the loss gradient with respect to the returned
+    LSE.  LSE_i is the log-sum-exp of row i of S', whose derivative with
+    respect to S'_ij is P_ij, so it adds dlse_i * P_ij to dS_ij."""
     S = qh.shape[0]
     s, qr, kr = _scores(qh, kh, head, scale=scale, causal=causal, bias=bias, table=table,
                         num_buckets=num_buckets, max_distance=max_distance,
@@ -224,6 +228,8 @@ def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", tab
     dP = doh @ vh.T
     Drow = (P * dP).sum(axis=1)
     dS = P * (dP - Drow[:, None])
+    if dlse is not None:
+        dS = dS + P * np.asarray(dlse, dtype=np.float64)[:, None]
     dv = P.T @ doh
     dq = scale * (dS @ kr)
     dk = scale * (dS.T @ qr)
@@ -280,12 +286,13 @@ def attention_fwd(q, k, v, pairs=None, **kw):
     return O, LSE
 
 
-def attention_bwd(q, k, v, do, pairs=None, **kw):
+def attention_bwd(q, k, v, do, pairs=None, dlse=None, **kw):
     """Dense backward.  Returns dq, dk, dv [B, S, H, D] and the bias
     gradient: dtable [nb, H] for T5, dbias [Bb, H, S, S] for a dense bias
     (summed over the batch when Bb == 1), None otherwise.  With ``pairs``,
     only those heads are computed (others NaN) and the bias gradient sums over
-    the computed heads only."""
+    the computed heads only.  ``dlse`` [B, H, S] (optional): the gradient with
+    respect to the returned LSE."""
     B, S, H, D = q.shape
     dq = np.full(q.shape, np.nan)
     dk = np.full(q.shape, np.nan)
@@ -299,6 +306,7 @@ def attention_bwd(q, k, v, do, pairs=None, **kw):
     todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in todo:
         a, bb, c, dt = head_bwd(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], h,
+                                dlse=None if dlse is None else dlse[b, h],
                                 **_head_kw(kw, b, h))
         dq[b, :, h], dk[b, :, h], dv[b, :, h] = a, bb, c
         if kw.get("bias") == "t5":
@@ -340,7 +348,8 @@ def varlen_attention_fwd(q, k, v, cu_seqlens, seqs=None, heads=None, **kw):
     return O, LSE
 
 
-def varlen_attention_bwd(q, k, v, do, cu_seqlens, seqs=None, heads=None, **kw):
+def varlen_attention_bwd(q, k, v, do, cu_seqlens, seqs=None, heads=None, dlse=None, **kw):
+    """Packed backward; ``dlse`` [H, T] (optional) as in attention_bwd."""
     T, H, D = q.shape
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     dq = np.full(q.shape, np.nan)
@@ -355,7 +364,8 @@ def varlen_attention_bwd(q, k, v, do, cu_seqlens, seqs=None, heads=None, **kw):
         if e == a:
             continue
         for h in heads:
-            r = head_bwd(q[a:e, h], k[a:e, h], v[a:e, h], do[a:e, h], h, **_kw(kw))
+            r = head_bwd(q[a:e, h], k[a:e, h], v[a:e, h], do[a:e, h], h,
+                         dlse=None if dlse is None else dlse[h, a:e], **_kw(kw))
             dq[a:e, h], dk[a:e, h], dv[a:e, h] = r[0], r[1], r[2]
             if dtable is not None:
                 dtable[:, h] += r[3]

@@ -289,6 +289,39 @@ def test_against_torch_sdpa_and_autograd(causal, bidirectional):
     np.testing.assert_allclose(torch.logsumexp(s, -1).numpy(), LSE, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_gradient_against_torch_autograd(causal):
+    """A loss that uses both O and LSE: the oracle's dq, dk, dv and table
+    gradient with dlse against torch's autograd of a plain fp64 statement
+    (scores, logsumexp, softmax, P V) written here without SDPA."""
+    rng = np.random.default_rng(19)
+    B, S, H, D, nb, md = 2, 29, 2, 8, 16, 40
+    q, k, v, do = (rng.standard_normal((B, S, H, D)) for _ in range(4))
+    dlse = rng.standard_normal((B, H, S))
+    table = rng.normal(0, 0.5, (nb, H))
+    kw = dict(scale=0.8, causal=causal, bias="t5", table=table, num_buckets=nb, max_distance=md,
+              bidirectional=not causal)
+    dq, dk, dv, dtab = oracle.attention_bwd(q, k, v, do, dlse=dlse, **kw)
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3), requires_grad=True) for x in (q, k, v))
+    buckets = torch.tensor(np.stack([[bucket_exact(int(jj - ii), nb, md, not causal)
+                                      for jj in range(S)] for ii in range(S)]))
+    ttab = torch.tensor(table, requires_grad=True)
+    s = tq @ tk.transpose(-1, -2) * 0.8 + ttab[buckets].permute(2, 0, 1)[None]
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(S, S, dtype=torch.bool), 1), float("-inf"))
+    lse = torch.logsumexp(s, -1)
+    o = torch.softmax(s, -1) @ tv
+    loss = (o * torch.tensor(do.transpose(0, 2, 1, 3))).sum() + (lse * torch.tensor(dlse)).sum()
+    loss.backward()
+    np.testing.assert_allclose(tq.grad.numpy().transpose(0, 2, 1, 3), dq, atol=1e-11)
+    np.testing.assert_allclose(tk.grad.numpy().transpose(0, 2, 1, 3), dk, atol=1e-11)
+    np.testing.assert_allclose(tv.grad.numpy().transpose(0, 2, 1, 3), dv, atol=1e-11)
+    np.testing.assert_allclose(ttab.grad.numpy(), dtab, atol=1e-11)
+    # with dlse the table gradient no longer sums to zero over buckets: it sums
+    # to the total of dlse over the head's rows (each row of P sums to one)
+    np.testing.assert_allclose(dtab.sum(axis=0), dlse.sum(axis=(0, 2)), atol=1e-11)
+
+
 @pytest.mark.parametrize("Bb,causal", [(1, False), (2, True), (1, True)])
 def test_dense_bias_against_torch_sdpa_and_autograd(Bb, causal):
     """Dense bias (kernel v1): O, LSE, dq, dk, dv and dBias against PyTorch's
@@ -361,12 +394,13 @@ def test_backward_matches_finite_differences(case):
     kw = dict(scale=case["scale"], causal=case["causal"], bias=case["bias"], table=table,
               num_buckets=nb, max_distance=md, bidirectional=case["bidirectional"],
               slopes=slopes, rope_base=case["rope_base"], rope_round=False)
-    dq, dk, dv, dtab = head_bwd(q, k, v, do, head, **kw)
+    dlse = rng.standard_normal(S)
+    dq, dk, dv, dtab = head_bwd(q, k, v, do, head, dlse=dlse, **kw)
 
     def loss(q_, k_, v_, table_):
         kw2 = dict(kw, table=table_)
-        O, _ = head_fwd(q_, k_, v_, head, **kw2)
-        return float((O * do).sum())
+        O, lse = head_fwd(q_, k_, v_, head, **kw2)
+        return float((O * do).sum() + (lse * dlse).sum())
 
     h = 1e-6
     for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
