@@ -52,7 +52,7 @@ class FaFwdParams(ctypes.Structure):
 
 class FaBwdParams(ctypes.Structure):
     _fields_ = [("f", FaFwdParams), ("dout", c_ptr), ("dq", c_ptr), ("dk", c_ptr),
-                ("dv", c_ptr), ("dtable", c_ptr)]
+                ("dv", c_ptr), ("dtable", c_ptr), ("dlse", c_ptr)]
 
 
 class FaVarlenFwdParams(ctypes.Structure):
@@ -64,7 +64,7 @@ class FaVarlenFwdParams(ctypes.Structure):
 
 class FaVarlenBwdParams(ctypes.Structure):
     _fields_ = [("f", FaVarlenFwdParams), ("dout", c_ptr), ("dq", c_ptr), ("dk", c_ptr),
-                ("dv", c_ptr), ("dtable", c_ptr)]
+                ("dv", c_ptr), ("dtable", c_ptr), ("dlse", c_ptr)]
 
 
 class FaRmsnormFwdParams(ctypes.Structure):

@@ -190,43 +190,50 @@ def fa_varlen_fwd(q, k, v, o, lse, cu_seqlens, max_seqlen, *, scale=1.0, causal=
           "fa_varlen_fwd")
 
 
-def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, scale=1.0, causal=False,
-           bias: BiasSpec = None, rope_base=0.0, workspace=None, stream=None) -> None:
-    """Dense backward into dq, dk, dv [B,S,H,D] bf16 and the bias gradient
-    ``dtable``: fp32 [nb,H] for T5Bias, fp32 [Bb,H,S,S] for DenseBias."""
-    lib = _lib.load()
+def _bwd_params(q, k, v, o, lse, dout, dq, dk, dv, dtable, dlse, scale, causal, bias,
+                rope_base) -> FaBwdParams:
     p = FaBwdParams()
     p.f = _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base)
     for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _need(t, name, torch.bfloat16, q.shape, q.device)
     if dtable is not None:
         _need(dtable, "dtable", torch.float32, _dbias_shape(bias, q.shape[2]), q.device)
+    if dlse is not None:
+        _need(dlse, "dlse", torch.float32, lse.shape, q.device)
     p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
     p.dtable = _ptr(dtable)
+    p.dlse = _ptr(dlse)
+    return p
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, dlse=None, scale=1.0,
+           causal=False, bias: BiasSpec = None, rope_base=0.0, workspace=None,
+           stream=None) -> None:
+    """Dense backward into dq, dk, dv [B,S,H,D] bf16 and the bias gradient
+    ``dtable``: fp32 [nb,H] for T5Bias, fp32 [Bb,H,S,S] for DenseBias.
+    ``dlse`` (optional, fp32 [B,H,S]) is the gradient with respect to lse."""
+    lib = _lib.load()
+    p = _bwd_params(q, k, v, o, lse, dout, dq, dk, dv, dtable, dlse, scale, causal, bias,
+                    rope_base)
     ws, wsb = _workspace(lib.fa_bwd_workspace_size(ctypes.byref(p)), q.device, workspace)
     check(lib.fa_bwd(ctypes.byref(p), _ptr(ws), wsb, _stream(q.device, stream)), "fa_bwd")
 
 
-def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, scale=1.0, causal=False,
-                   bias: BiasSpec = None, rope_base=0.0, stream=None) -> None:
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, dlse=None, scale=1.0,
+                   causal=False, bias: BiasSpec = None, rope_base=0.0, stream=None) -> None:
     """fa_bwd with the library's static scratch instead of a workspace: the
     call allocates nothing (torch included)."""
     lib = _lib.load()
-    p = FaBwdParams()
-    p.f = _fwd_params(q, k, v, o, lse, scale, causal, bias, rope_base)
-    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
-        _need(t, name, torch.bfloat16, q.shape, q.device)
-    if dtable is not None:
-        _need(dtable, "dtable", torch.float32, _dbias_shape(bias, q.shape[2]), q.device)
-    p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
-    p.dtable = _ptr(dtable)
+    p = _bwd_params(q, k, v, o, lse, dout, dq, dk, dv, dtable, dlse, scale, causal, bias,
+                    rope_base)
     check(lib.fa_bwd_noalloc(ctypes.byref(p), _stream(q.device, stream)), "fa_bwd_noalloc")
 
 
 def fa_varlen_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, max_seqlen, dtable=None, *,
-                  scale=1.0, causal=False, bias: BiasSpec = None, rope_base=0.0, workspace=None,
-                  stream=None) -> None:
-    """Packed backward into dq, dk, dv [T,H,D] bf16 and dtable [nb,H] fp32."""
+                  dlse=None, scale=1.0, causal=False, bias: BiasSpec = None, rope_base=0.0,
+                  workspace=None, stream=None) -> None:
+    """Packed backward into dq, dk, dv [T,H,D] bf16 and dtable [nb,H] fp32;
+    ``dlse`` (optional, fp32 [H,T]) is the gradient with respect to lse."""
     lib = _lib.load()
     p = FaVarlenBwdParams()
     p.f = _varlen_params(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, bias, rope_base)
@@ -234,8 +241,11 @@ def fa_varlen_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, max_seqlen, dta
         _need(t, name, torch.bfloat16, q.shape, q.device)
     if dtable is not None:
         _need(dtable, "dtable", torch.float32, (p.f.bias.num_buckets, q.shape[1]), q.device)
+    if dlse is not None:
+        _need(dlse, "dlse", torch.float32, lse.shape, q.device)
     p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
     p.dtable = _ptr(dtable)
+    p.dlse = _ptr(dlse)
     ws, wsb = _workspace(lib.fa_varlen_bwd_workspace_size(ctypes.byref(p)), q.device, workspace)
     check(lib.fa_varlen_bwd(ctypes.byref(p), _ptr(ws), wsb, _stream(q.device, stream)),
           "fa_varlen_bwd")
@@ -265,6 +275,16 @@ def fa_fwd_workspace_size(q, *, causal=False, scale=1.0, bias: BiasSpec = None,
 # ---------------------------------------------------------------------------
 
 
+def _output_grads(do, dlse, o):
+    """The gradients autograd hands back for (O, LSE), either of which may be
+    None when the loss does not use that output: a missing dO is zero, a
+    missing dLSE is left out of the call."""
+    do = torch.zeros_like(o) if do is None else do.to(o.dtype).contiguous()
+    if dlse is not None:
+        dlse = dlse.to(torch.float32).contiguous()
+    return do, dlse
+
+
 class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, table, slopes, bias, scale, causal, rope_base):
@@ -274,18 +294,20 @@ class _Attention(torch.autograd.Function):
         fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, bias=bias, rope_base=rope_base)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.bias, ctx.scale, ctx.causal, ctx.rope_base = bias, scale, causal, rope_base
+        ctx.set_materialize_grads(False)
         return o, lse
 
     @staticmethod
     def backward(ctx, do, dlse):
         q, k, v, o, lse = ctx.saved_tensors
+        do, dlse = _output_grads(do, dlse, o)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dtable = None
         if isinstance(ctx.bias, T5Bias) and ctx.bias.table.requires_grad:
             dtable = torch.empty_like(ctx.bias.table)
         if isinstance(ctx.bias, DenseBias) and ctx.bias.matrix.requires_grad:
             dtable = torch.empty(ctx.bias.matrix.shape, dtype=torch.float32, device=q.device)
-        fa_bwd(q, k, v, o, lse, do.contiguous(), dq, dk, dv, dtable, scale=ctx.scale,
+        fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, dlse=dlse, scale=ctx.scale,
                causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
         if isinstance(ctx.bias, DenseBias) and dtable is not None:
             dtable = dtable.to(ctx.bias.matrix.dtype)   # a leaf's gradient keeps its dtype
@@ -315,16 +337,18 @@ class _VarlenAttention(torch.autograd.Function):
         ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
         ctx.max_seqlen, ctx.bias, ctx.scale = max_seqlen, bias, scale
         ctx.causal, ctx.rope_base = causal, rope_base
+        ctx.set_materialize_grads(False)
         return o, lse
 
     @staticmethod
     def backward(ctx, do, dlse):
         q, k, v, o, lse, cu = ctx.saved_tensors
+        do, dlse = _output_grads(do, dlse, o)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dtable = None
         if isinstance(ctx.bias, T5Bias) and ctx.bias.table.requires_grad:
             dtable = torch.empty_like(ctx.bias.table)
-        fa_varlen_bwd(q, k, v, o, lse, do.contiguous(), dq, dk, dv, cu, ctx.max_seqlen, dtable,
+        fa_varlen_bwd(q, k, v, o, lse, do, dq, dk, dv, cu, ctx.max_seqlen, dtable, dlse=dlse,
                       scale=ctx.scale, causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
         return dq, dk, dv, dtable, None, None, None, None, None, None
 
@@ -459,15 +483,10 @@ class _CrossEntropy(torch.autograd.Function):
         return dlogits, None, None, None
 
 
-def cross_entropy(logits, labels, *, z_loss=0.0, ignore_index=-100, reduction="mean"):
-    """Cross-entropy with z-loss over bf16 logits [rows, vocab] and int labels [rows];
-    reduction 'none' returns the per-row loss, 'mean' averages over the rows whose
-    label is not ignored, 'sum' adds them."""
-    loss = _CrossEntropy.apply(logits.contiguous(), labels.to(torch.int32).contiguous(),
+def cross_entropy(logits, labels, *, z_loss=0.0, ignore_index=-100):
+    """Per-row cross-entropy with z-loss over bf16 logits [rows, vocab] and int
+    labels [rows]: fp32 [rows], 0 for ignored rows.  Any reduction over the
+    rows (a mean over the non-ignored ones, a sum) is the caller's, as in the
+    C ABI: the kernels compute per-row losses and their gradients."""
+    return _CrossEntropy.apply(logits.contiguous(), labels.to(torch.int32).contiguous(),
                                float(z_loss), int(ignore_index))
-    if reduction == "none":
-        return loss
-    if reduction == "sum":
-        return loss.sum()
-    valid = ((labels != ignore_index) & (labels >= 0) & (labels < logits.shape[1])).sum()
-    return loss.sum() / valid.clamp(min=1)

@@ -196,7 +196,16 @@ fa_status check_fwd_impl(const fa_fwd_params *p) {
       p->bias.dense_batch != p->batch)
     return fail(FA_ERR_INVALID, "bias.dense_batch=%d must be 1 or batch=%d", p->bias.dense_batch,
                 p->batch);
-  if (empty && p->bias.mode == FA_BIAS_DENSE) return FA_OK;
+  if (empty && p->bias.mode == FA_BIAS_DENSE) {
+    // nothing to compute, but the backward still clears a gradient of
+    // dense_batch * heads * seqlen^2 floats: its size must be valid
+    if (p->heads < 1) return fail(FA_ERR_INVALID, "heads=%d must be >= 1", p->heads);
+    if (p->seqlen > fa::kMaxDenseSeqlen)
+      return fail(FA_ERR_UNSUPPORTED, "a dense bias needs seqlen <= %d (got %d)",
+                  fa::kMaxDenseSeqlen, p->seqlen);
+    if (p->bias.reserved2 != 0) return fail(FA_ERR_INVALID, "bias.reserved2 must be 0");
+    return FA_OK;
+  }
   return check_common(p->heads, p->head_dim, p->causal, p->scale, p->rope_base, p->bias,
                       p->seqlen);
 }
@@ -378,8 +387,8 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
 }
 
 fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void *v,
-                  const void *o, const float *lse, const void *dout, void *dq, void *dk, void *dv,
-                  float *dtable, void *ws, size_t ws_bytes, hipStream_t s) {
+                  const void *o, const float *lse, const float *dlse, const void *dout, void *dq,
+                  void *dk, void *dv, float *dtable, void *ws, size_t ws_bytes, hipStream_t s) {
   const BwdLayout L = bwd_layout(p, dtable != nullptr);
   if (L.total > 0 && (ws == nullptr || ws_bytes < L.total))
     return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
@@ -407,6 +416,7 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   b.o = o;
   b.dout = dout;
   b.lse = lse;
+  b.dlse = dlse;
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;
@@ -578,7 +588,7 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *ws, size_t ws_bytes
 fa_status fa_bwd(const fa_bwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
   const fa_status st = fa_check_bwd(p);
   if (st != FA_OK) return st;
-  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dout, p->dq,
+  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse, p->dout, p->dq,
                  p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
 }
 
@@ -597,7 +607,7 @@ fa_status fa_bwd_noalloc(const fa_bwd_params *p, hipStream_t stream) {
     const fa_status s2 = scratch_of_current_device(&ws);
     if (s2 != FA_OK) return s2;
   }
-  return run_bwd(pr, p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dout, p->dq, p->dk, p->dv,
+  return run_bwd(pr, p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse, p->dout, p->dq, p->dk, p->dv,
                  p->dtable, ws, need, stream);
 }
 
@@ -605,7 +615,7 @@ fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes
                         hipStream_t stream) {
   const fa_status st = fa_check_varlen_bwd(p);
   if (st != FA_OK) return st;
-  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dout, p->dq,
+  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse, p->dout, p->dq,
                  p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
 }
 

@@ -42,6 +42,7 @@ constexpr int BKV = 128;   // dkv: keys per workgroup
 struct BwdArgs {
   const uint16_t *q, *k, *v, *o, *dout;
   const float *lse;
+  const float *dlse;       // gradient with respect to lse (lse layout) or nullptr
   uint16_t *dq, *dk, *dv;  // bf16 outputs
   float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
   float *delta;            // -D_i, same layout as lse
@@ -165,6 +166,10 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
   if constexpr (kDoInLds)
     dma_tile<D, BR, 4>(dma_desc(a.dout + base, nrec), HD, q0, dost, wave, lane);
   const float lse2 = myrow < L ? a.lse[w.lse_base + myrow] * kLog2e : 0.f;
+  // A gradient dlse_i with respect to the returned LSE adds dlse_i P_ij to
+  // dS_ij: the same as replacing D_i by D_i - dlse_i everywhere below
+  // (here and, through -D, in the dkv kernel).
+  const float dl = (a.dlse != nullptr && myrow < L) ? a.dlse[w.lse_base + myrow] : 0.f;
 
   int sat = 0;
   if constexpr (BIAS == kBiasT5) {
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
     wait_vmem_loads();
     __syncthreads();
   }
-  const float dd = half_sum(dsum);   // D_i - Dc_i
+  const float dd = half_sum(dsum) - dl;   // D_i - dlse_i - Dc_i
   if (hl == 0 && myrow < L) {
     a.delta[w.lse_base + myrow] = -(dc + dd);
     a.nls[w.lse_base + myrow] = -a.lse[w.lse_base + myrow] / a.scale;
@@ -963,6 +968,7 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.o = static_cast<const uint16_t *>(b.o);
   a.dout = static_cast<const uint16_t *>(b.dout);
   a.lse = b.lse;
+  a.dlse = b.dlse;
   a.dq = static_cast<uint16_t *>(b.dq);
   a.dk = static_cast<uint16_t *>(b.dk);
   a.dv = static_cast<uint16_t *>(b.dv);

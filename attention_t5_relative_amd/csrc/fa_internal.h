@@ -59,6 +59,7 @@ struct BwdBuffers {
   const void *o;           // bf16 forward output (centres the dq accumulation)
   const void *dout;
   const float *lse;
+  const float *dlse;       // gradient with respect to lse (same layout) or nullptr
   void *dq, *dk, *dv;      // bf16 outputs
   float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
   float *delta;            // fp32, two lse-layout arrays: -D, then -lse / scale

@@ -138,6 +138,10 @@ typedef struct {
   void *dk;
   void *dv;
   float *dtable;
+  const float *dlse;       /* may be NULL: gradient of the loss with respect to
+                              f.lse, fp32 [B, H, S]; LSE_i's derivative with
+                              respect to S'_ij is P_ij, so it adds dlse_i P_ij
+                              to dS_ij                                        */
 } fa_bwd_params;
 
 /* Packed forward: q, k, v, o [total, H, D] bf16; lse [H, total] fp32;
@@ -168,6 +172,7 @@ typedef struct {
   void *dk;
   void *dv;
   float *dtable;
+  const float *dlse;       /* may be NULL: fp32 [H, total], as in fa_bwd_params */
 } fa_varlen_bwd_params;
 
 /* Host-only argument checks (no HIP call, nothing enqueued). */

@@ -57,12 +57,13 @@ STRUCTS = {
     "fa_fwd_params": (_lib.FaFwdParams, ["batch", "seqlen", "heads", "head_dim", "causal",
                                          "scale", "rope_base", "reserved", "q", "k", "v", "o",
                                          "lse", "bias"]),
-    "fa_bwd_params": (_lib.FaBwdParams, ["f", "dout", "dq", "dk", "dv", "dtable"]),
+    "fa_bwd_params": (_lib.FaBwdParams, ["f", "dout", "dq", "dk", "dv", "dtable", "dlse"]),
     "fa_varlen_fwd_params": (_lib.FaVarlenFwdParams, ["nseq", "total", "max_seqlen", "heads",
                                                       "head_dim", "causal", "scale", "rope_base",
                                                       "cu_seqlens", "q", "k", "v", "o", "lse",
                                                       "bias"]),
-    "fa_varlen_bwd_params": (_lib.FaVarlenBwdParams, ["f", "dout", "dq", "dk", "dv", "dtable"]),
+    "fa_varlen_bwd_params": (_lib.FaVarlenBwdParams, ["f", "dout", "dq", "dk", "dv", "dtable",
+                                                      "dlse"]),
     "fa_rmsnorm_fwd_params": (_lib.FaRmsnormFwdParams, ["rows", "dim", "eps", "reserved", "x",
                                                         "w", "y", "rstd"]),
     "fa_rmsnorm_bwd_params": (_lib.FaRmsnormBwdParams, ["f", "dy", "dx", "dw"]),
@@ -144,6 +145,15 @@ def _dense(**kw):
      _lib.FA_ERR_INVALID),
     ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense": 0x6000, "bias_dense_batch": 1,
       "seqlen": 20000}, _lib.FA_ERR_UNSUPPORTED),
+    # an empty batch with a dense bias: nothing is computed, but the backward
+    # clears dense_batch * heads * seqlen^2 gradient floats, so those sizes are
+    # still checked (pointers may be NULL)
+    ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense_batch": 1, "batch": 0, "q": None},
+     _lib.FA_OK),
+    ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense_batch": 1, "batch": 0, "heads": -1},
+     _lib.FA_ERR_INVALID),
+    ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense_batch": 1, "batch": 0, "seqlen": 20000},
+     _lib.FA_ERR_UNSUPPORTED),
 ])
 def test_dense_checks(lib, change, status):
     p = _dense(**change)

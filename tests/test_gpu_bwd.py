@@ -270,3 +270,67 @@ def test_autograd_wrapper_matches_oracle():
     assert_grad(to_f64(k.grad), dk, "dK")
     assert_grad(to_f64(v.grad), dv, "dV")
     assert_dtable(table.grad.cpu().numpy().astype(np.float64), dtab)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_lse_gradient(causal):
+    """A loss that uses the returned LSE: dlse adds dlse_i P_ij to dS_ij, in
+    dQ, dK and the table gradient (dV does not depend on it)."""
+    inp = synth.draw_dense(81, 2, 300, 3, 64)
+    q, k, v, do = (bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    B, S, H, D = q.shape
+    bias = fa.T5Bias(torch.from_numpy(inp.table).cuda(), 32, 128, not causal)
+    o, lse = nan_like(q), torch.full((B, H, S), float("nan"), device="cuda")
+    fa.fa_fwd(q, k, v, o, lse, causal=causal, bias=bias)
+    dlse = torch.from_numpy(np.random.default_rng(5).standard_normal((B, H, S)).astype(
+        np.float32)).cuda()
+    dq, dk, dv = nan_like(q), nan_like(q), nan_like(q)
+    dtable = torch.full((32, H), float("nan"), device="cuda")
+    fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, dlse=dlse, causal=causal, bias=bias)
+    torch.cuda.synchronize()
+    kw = oracle_kwargs("t5", causal, 1.0, inp.table, None, 32, 128, not causal, None)
+    g = oracle.attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do"),
+                             dlse=dlse.cpu().numpy().astype(np.float64), **kw)
+    for name, got, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), g[:3]):
+        assert_grad(to_f64(got), ref, name)
+    assert_dtable(dtable.cpu().numpy().astype(np.float64), g[3])
+
+
+def test_lse_gradient_packed_and_autograd():
+    """The packed backward with dlse, and the autograd wrapper with a loss
+    that uses both outputs."""
+    lengths = np.array([1, 130, 17, 256, 64])
+    inp = synth.draw_varlen(83, int(lengths.sum()), 2, 64, lengths=lengths)
+    q, k, v, do = (bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    T, H = q.shape[:2]
+    cu = torch.from_numpy(inp.cu_seqlens).cuda()
+    table = torch.from_numpy(inp.table).cuda()
+    rng = np.random.default_rng(6)
+    dlse = torch.from_numpy(rng.standard_normal((H, T)).astype(np.float32)).cuda()
+    for t in (q, k, v):
+        t.requires_grad_(True)
+    table.requires_grad_(True)
+    o, lse = fa.varlen_attention(q, k, v, cu, int(lengths.max()),
+                                 bias=fa.T5Bias(table, 32, 128, True), return_lse=True)
+    ((o.float() * do.float()).sum() + (lse * dlse).sum()).backward()
+    torch.cuda.synchronize()
+    kw = oracle_kwargs("t5", False, 1.0, inp.table, None, 32, 128, True, None)
+    g = oracle.varlen_attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do"),
+                                    inp.cu_seqlens, dlse=dlse.cpu().numpy().astype(np.float64),
+                                    **kw)
+    for name, got, ref in zip(("dQ", "dK", "dV"), (q.grad, k.grad, v.grad), g[:3]):
+        assert_grad(to_f64(got), ref, name)
+    assert_dtable(table.grad.cpu().numpy().astype(np.float64), g[3])
+    # a loss of the LSE alone: dO is zero
+    for t in (q, k, v, table):
+        t.grad = None
+    o, lse = fa.varlen_attention(q, k, v, cu, int(lengths.max()),
+                                 bias=fa.T5Bias(table, 32, 128, True), return_lse=True)
+    (lse * dlse).sum().backward()
+    torch.cuda.synchronize()
+    g = oracle.varlen_attention_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"),
+                                    np.zeros_like(inp.f64("do")), inp.cu_seqlens,
+                                    dlse=dlse.cpu().numpy().astype(np.float64), **kw)
+    for name, got, ref in zip(("dQ", "dK"), (q.grad, k.grad), g[:2]):
+        assert_grad(to_f64(got), ref, name + " (LSE loss only)")
+    assert float(v.grad.abs().max()) == 0.0

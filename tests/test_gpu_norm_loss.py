@@ -129,8 +129,8 @@ def test_cross_entropy_backward_in_place():
 
 
 def test_autograd_wrappers():
-    """rms_norm and cross_entropy as torch autograd functions (mean reduction
-    over the non-ignored rows)."""
+    """rms_norm and cross_entropy as torch autograd functions; the caller
+    takes the mean of the per-row losses over the non-ignored rows."""
     xb, wb, _ = synth.draw_rmsnorm(21, 16, 256)
     x = bf16_tensor(xb).requires_grad_(True)
     w = bf16_tensor(wb).requires_grad_(True)
@@ -138,7 +138,9 @@ def test_autograd_wrappers():
     assert y.shape == (4, 4, 256)
     zb, lab, _ = synth.draw_cross_entropy(22, 16, 256)
     logits = y.view(16, 256)
-    loss = fa.cross_entropy(logits, torch.from_numpy(lab).cuda(), z_loss=1e-4)
+    rows = fa.cross_entropy(logits, torch.from_numpy(lab).cuda(), z_loss=1e-4)
+    assert rows.shape == (16,) and rows.dtype == torch.float32
+    loss = rows.sum() / int(((lab >= 0) & (lab < 256)).sum())
     loss.backward()
     # the same chain in fp64 autograd
     tx = torch.tensor(f64(xb), requires_grad=True)
