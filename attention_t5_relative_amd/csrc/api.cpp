@@ -293,18 +293,25 @@ struct Carve {
   }
 };
 
+// RoPE (cos, sin) table: one fp64 pair per (position, dim pair).
+size_t rope_table_bytes(const fa::Problem &p) {
+  return (size_t)p.seqlen * (p.head_dim / 2) * 16;
+}
+
 struct FwdLayout {
-  size_t qrot = 0, krot = 0, prefix = 0, sched = 0, total = 0;
+  size_t krot = 0, rope_cs = 0, prefix = 0, sched = 0, total = 0;
   int nsched = 0;
 };
 
+// The forward rotates Q rows in registers from the (cos, sin) table; K,
+// which every query tile streams through LDS, is rotated once into a copy.
 FwdLayout fwd_layout(const fa::Problem &p) {
   FwdLayout L;
   Carve c;
   const size_t tokens = (size_t)p.total;
   if (p.rope_base > 0.f) {
-    L.qrot = c.take(tokens * p.heads * p.head_dim * 2);
     L.krot = c.take(tokens * p.heads * p.head_dim * 2);
+    L.rope_cs = c.take(rope_table_bytes(p));
   }
   if (p.varlen) {
     const int br = fa::fwd_tile_rows(p.head_dim);
@@ -317,7 +324,7 @@ FwdLayout fwd_layout(const fa::Problem &p) {
 }
 
 struct BwdLayout {
-  size_t qrot = 0, krot = 0, dq_f32 = 0, dk_f32 = 0, delta = 0, part = 0, prefix = 0, sched = 0,
+  size_t qrot = 0, krot = 0, rope_cs = 0, delta = 0, part = 0, prefix = 0, sched = 0,
          dense_ws = 0, total = 0;
   int nsched = 0;
   bool has_part = false;
@@ -329,11 +336,12 @@ BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
   Carve c;
   const size_t tokens = (size_t)p.total;
   const size_t elems = tokens * p.heads * p.head_dim;
+  // Both backward kernels stream one of Q, K through LDS: each is rotated
+  // once into a copy; dQ and dK are turned back in the kernels' epilogues.
   if (p.rope_base > 0.f) {
     L.qrot = c.take(elems * 2);
     L.krot = c.take(elems * 2);
-    L.dq_f32 = c.take(elems * 4);
-    L.dk_f32 = c.take(elems * 4);
+    L.rope_cs = c.take(rope_table_bytes(p));
   }
   L.delta = c.take(2 * tokens * p.heads * 4);   // -D, then -lse / scale (lse layout each)
   if (p.varlen) {
@@ -366,13 +374,14 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
     return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 ws == nullptr ? (size_t)0 : ws_bytes);
   if (p.total == 0 || (!p.varlen && (p.nbatch == 0 || p.seqlen == 0))) return FA_OK;
-  fa::FwdBuffers b{q, k, v, o, lse};
+  fa::FwdBuffers b{q, k, v, o, lse, nullptr};
   hipError_t e;
   if (p.rope_base > 0.f) {
-    e = fa::launch_rope_pair(p, q, k, at<void>(ws, L.qrot), at<void>(ws, L.krot), s);
+    e = fa::launch_rope_table(p, at<double2>(ws, L.rope_cs), s);
+    if (e == hipSuccess) e = fa::launch_rope_rotate(p, k, at<void>(ws, L.krot), nullptr, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "rope");
-    b.q = at<void>(ws, L.qrot);
     b.k = at<void>(ws, L.krot);
+    b.rope_cs = at<double2>(ws, L.rope_cs);
   }
   const int4 *sched = nullptr;
   if (p.varlen) {
@@ -430,14 +439,14 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
     e = fa::launch_zero_upper(dtable, p.dense_batch * p.heads, p.seqlen, s);
     if (e != hipSuccess) return hip_fail(e, "dense bias gradient fill");
   }
-  const bool rope = p.rope_base > 0.f;
-  if (rope) {
-    e = fa::launch_rope_pair(p, q, k, at<void>(ws, L.qrot), at<void>(ws, L.krot), s);
+  if (p.rope_base > 0.f) {
+    e = fa::launch_rope_table(p, at<double2>(ws, L.rope_cs), s);
+    if (e == hipSuccess)
+      e = fa::launch_rope_rotate(p, q, at<void>(ws, L.qrot), k, at<void>(ws, L.krot), s);
     if (e != hipSuccess) return hip_fail(e, "rope");
     b.q = at<void>(ws, L.qrot);
     b.k = at<void>(ws, L.krot);
-    b.dq_f32 = at<float>(ws, L.dq_f32);
-    b.dk_f32 = at<float>(ws, L.dk_f32);
+    b.rope_cs = at<double2>(ws, L.rope_cs);
   }
   const int4 *sched = nullptr;
   if (p.varlen) {
@@ -458,11 +467,6 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
     e = fa::launch_batch_sum(b.dbias_batch, dtable, p.nbatch, p.heads, p.seqlen, p.causal != 0,
                              s);
     if (e != hipSuccess) return hip_fail(e, "dense bias gradient batch sum");
-  }
-  if (rope) {
-    e = fa::launch_rope_grad(p, b.dq_f32, dq, s);
-    if (e == hipSuccess) e = fa::launch_rope_grad(p, b.dk_f32, dk, s);
-    if (e != hipSuccess) return hip_fail(e, "rope gradient");
   }
   return FA_OK;
 }

@@ -44,7 +44,7 @@ struct BwdArgs {
   const float *lse;
   const float *dlse;       // gradient with respect to lse (lse layout) or nullptr
   uint16_t *dq, *dk, *dv;  // bf16 outputs
-  float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
+  const double2 *rope_cs;   // RoPE: (cos, sin) [seqlen, D/2], or nullptr
   float *delta;            // -D_i, same layout as lse
   float *nls;              // -lse_i / scale, same layout (seed of the dkv kernel's S)
   float *part;             // [nb, nwg] table-gradient partials
@@ -104,6 +104,31 @@ __device__ __forceinline__ bf16x8 frag(const uint32_t (&w)[4]) {
   return __builtin_bit_cast(bf16x8, i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
 }
 
+// RoPE: turn back the pairs of a row's gradient held in MFMA accumulators
+// (lane: dims 32db + 8(r/4) + 4hl + r%4 of row t, i.e. pairs 16db + 4(r/4) +
+// 2hl + {0, 1}) with the fp64 (cos, sin) table cs [npos, D/2]: a gradient
+// with respect to the rotated row becomes one with respect to the row before
+// the rotation.  Rows past the table read (cos, sin) = 0; they are past the
+// sequence and never stored.
+template <int D>
+__device__ __forceinline__ void rope_unrotate_acc(f32x16 (&acc)[D / 32], const double2 *cs,
+                                                  int npos, int t, int hl) {
+  const rsrc_t rcs = make_rsrc(cs, (uint32_t)npos * (uint32_t)(D / 2) * 16u);
+  const uint32_t t0 = ((uint32_t)t * (uint32_t)(D / 2) + 2 * hl) * 16u;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const RopeCs2 c = rope_cs2(rcs, t0 + (16 * db + 4 * rq) * 16u);
+      const double a0 = acc[db][4 * rq], a1 = acc[db][4 * rq + 1], a2 = acc[db][4 * rq + 2],
+                   a3 = acc[db][4 * rq + 3];
+      acc[db][4 * rq] = (float)fma(a0, c.c0, a1 * c.s0);
+      acc[db][4 * rq + 1] = (float)fma(a1, c.c0, -a0 * c.s0);
+      acc[db][4 * rq + 2] = (float)fma(a2, c.c1, a3 * c.s1);
+      acc[db][4 * rq + 3] = (float)fma(a3, c.c1, -a2 * c.s1);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dq kernel
 // ---------------------------------------------------------------------------
@@ -114,7 +139,7 @@ constexpr int dq_wgs() {
   return D == 64 || BIAS != kBiasDense ? 2 : 1;
 }
 
-template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE>
+template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const BwdArgs a) {
   // K and V tiles, swizzled (see swz): K is read both row-wise
   // (S^T = K Q^T) and transposed (dQ^T = K^T dS^T), V row-wise.  At
@@ -329,29 +354,20 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
 #pragma unroll
     for (int r = 0; r < 16; ++r) qacc[db][r] = dscale * fmaf(-dd, bacc[db][r], aacc[db][r]);
 
-  // dQ row myrow: lane holds dims 32db + 8(r/4) + 4hl + r%4
-  if constexpr (ROPE) {
-    const rsrc_t rdq = make_rsrc(a.dq_f32 + base, nrec * 2u);
+  // dQ row myrow: lane holds dims 32db + 8(r/4) + 4hl + r%4.  With RoPE the
+  // gradient is with respect to the rotated row: turn each pair back
+  // (pairs 16db + 4(r/4) + 2hl + {0, 1}) before rounding to bf16.
+  if (a.rope_cs != nullptr)
+    rope_unrotate_acc<D>(qacc, a.rope_cs, a.seqlen, myrow, hl);
+  const rsrc_t rdq = make_rsrc(a.dq + base, nrec);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const f32x4 v4 = {qacc[db][4 * rq], qacc[db][4 * rq + 1], qacc[db][4 * rq + 2],
-                          qacc[db][4 * rq + 3]};
-        buf_store16(rdq, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 4u,
-                    __builtin_bit_cast(i32x4, v4));
-      }
-  } else {
-    const rsrc_t rdq = make_rsrc(a.dq + base, nrec);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        i32x2 w2 = {(int)pack_bf16x2(qacc[db][4 * rq], qacc[db][4 * rq + 1]),
-                    (int)pack_bf16x2(qacc[db][4 * rq + 2], qacc[db][4 * rq + 3])};
-        buf_store8(rdq, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 2u, w2);
-      }
-  }
+    for (int rq = 0; rq < 4; ++rq) {
+      i32x2 w2 = {(int)pack_bf16x2(qacc[db][4 * rq], qacc[db][4 * rq + 1]),
+                  (int)pack_bf16x2(qacc[db][4 * rq + 2], qacc[db][4 * rq + 3])};
+      buf_store8(rdq, ((uint32_t)myrow * (uint32_t)HD + 32 * db + 8 * rq + 4 * hl) * 2u, w2);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -388,7 +404,7 @@ constexpr int dkv_wgs() {
   return D == 64 || BIAS == kBiasAlibi || BIAS == kBiasNone ? 2 : 1;
 }
 
-template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
+template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool DBIAS>
 __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const BwdArgs a) {
   constexpr int QB = DkvTile<D>::QB;
   constexpr bool kVInLds = D == 128 && (BIAS == kBiasAlibi || BIAS == kBiasNone);
@@ -771,8 +787,12 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dkacc[db][r] *= dscale;
+  // with RoPE, dK with respect to the unrotated key row
+  if (a.rope_cs != nullptr)
+    rope_unrotate_acc<D>(dkacc, a.rope_cs, a.seqlen, myk, hl);
   // dK, dV of key myk: lane holds dims 32db + 8(r/4) + 4hl + r%4
   const rsrc_t rdv = make_rsrc(a.dv + base, nrec);
+  const rsrc_t rdk = make_rsrc(a.dk + base, nrec);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -781,17 +801,9 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
       i32x2 v2 = {(int)pack_bf16x2(dvacc[db][4 * rq], dvacc[db][4 * rq + 1]),
                   (int)pack_bf16x2(dvacc[db][4 * rq + 2], dvacc[db][4 * rq + 3])};
       buf_store8(rdv, el * 2u, v2);
-      if constexpr (ROPE) {
-        const rsrc_t rdk = make_rsrc(a.dk_f32 + base, nrec * 2u);
-        const f32x4 k4 = {dkacc[db][4 * rq], dkacc[db][4 * rq + 1], dkacc[db][4 * rq + 2],
-                          dkacc[db][4 * rq + 3]};
-        buf_store16(rdk, el * 4u, __builtin_bit_cast(i32x4, k4));
-      } else {
-        const rsrc_t rdk = make_rsrc(a.dk + base, nrec);
-        i32x2 k2 = {(int)pack_bf16x2(dkacc[db][4 * rq], dkacc[db][4 * rq + 1]),
-                    (int)pack_bf16x2(dkacc[db][4 * rq + 2], dkacc[db][4 * rq + 3])};
-        buf_store8(rdk, el * 2u, k2);
-      }
+      i32x2 k2 = {(int)pack_bf16x2(dkacc[db][4 * rq], dkacc[db][4 * rq + 1]),
+                  (int)pack_bf16x2(dkacc[db][4 * rq + 2], dkacc[db][4 * rq + 3])};
+      buf_store8(rdk, el * 2u, k2);
     }
 
   if constexpr (DBIAS && BIAS == kBiasT5) {
@@ -887,20 +899,15 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *part, co
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
-hipError_t launch_dq_t(const BwdArgs &a, bool rope, hipStream_t s) {
-  if (rope)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BIAS, CAUSAL, VARLEN, true>), dim3(a.nwg), dim3(NT), 0,
-                       s, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BIAS, CAUSAL, VARLEN, false>), dim3(a.nwg), dim3(NT), 0,
-                       s, a);
+hipError_t launch_dq_t(const BwdArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BIAS, CAUSAL, VARLEN>), dim3(a.nwg), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool ROPE, bool DBIAS>
+template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool DBIAS>
 hipError_t launch_dkv_t(const BwdArgs &a, hipStream_t s) {
   const size_t dyn = dkv_dyn_bytes(a.t5.sat, BIAS == kBiasT5, DBIAS);
-  auto kern = bwd_dkv_kernel<D, BIAS, CAUSAL, VARLEN, ROPE, DBIAS>;
+  auto kern = bwd_dkv_kernel<D, BIAS, CAUSAL, VARLEN, DBIAS>;
   if (dyn > 16384) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -912,40 +919,37 @@ hipError_t launch_dkv_t(const BwdArgs &a, hipStream_t s) {
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
-hipError_t launch_pair(const BwdArgs &a, int phase, bool rope, bool dbias, hipStream_t s) {
-  if (phase == kBwdPre) return launch_dq_t<D, BIAS, CAUSAL, VARLEN>(a, rope, s);
+hipError_t launch_pair(const BwdArgs &a, int phase, bool dbias, hipStream_t s) {
+  if (phase == kBwdPre) return launch_dq_t<D, BIAS, CAUSAL, VARLEN>(a, s);
   if constexpr (BIAS == kBiasT5 || BIAS == kBiasDense) {
-    if (dbias)
-      return rope ? launch_dkv_t<D, BIAS, CAUSAL, VARLEN, true, true>(a, s)
-                  : launch_dkv_t<D, BIAS, CAUSAL, VARLEN, false, true>(a, s);
+    if (dbias) return launch_dkv_t<D, BIAS, CAUSAL, VARLEN, true>(a, s);
   }
-  return rope ? launch_dkv_t<D, BIAS, CAUSAL, VARLEN, true, false>(a, s)
-              : launch_dkv_t<D, BIAS, CAUSAL, VARLEN, false, false>(a, s);
+  return launch_dkv_t<D, BIAS, CAUSAL, VARLEN, false>(a, s);
 }
 
 template <int D, int BIAS>
-hipError_t launch_b(const BwdArgs &a, int phase, bool causal, bool varlen, bool rope, bool dbias,
+hipError_t launch_b(const BwdArgs &a, int phase, bool causal, bool varlen, bool dbias,
                     hipStream_t s) {
   if constexpr (BIAS == kBiasDense) {   // dense entry points only
-    return causal ? launch_pair<D, BIAS, true, false>(a, phase, rope, dbias, s)
-                  : launch_pair<D, BIAS, false, false>(a, phase, rope, dbias, s);
+    return causal ? launch_pair<D, BIAS, true, false>(a, phase, dbias, s)
+                  : launch_pair<D, BIAS, false, false>(a, phase, dbias, s);
   } else {
     if (causal)
-      return varlen ? launch_pair<D, BIAS, true, true>(a, phase, rope, dbias, s)
-                    : launch_pair<D, BIAS, true, false>(a, phase, rope, dbias, s);
-    return varlen ? launch_pair<D, BIAS, false, true>(a, phase, rope, dbias, s)
-                  : launch_pair<D, BIAS, false, false>(a, phase, rope, dbias, s);
+      return varlen ? launch_pair<D, BIAS, true, true>(a, phase, dbias, s)
+                    : launch_pair<D, BIAS, true, false>(a, phase, dbias, s);
+    return varlen ? launch_pair<D, BIAS, false, true>(a, phase, dbias, s)
+                  : launch_pair<D, BIAS, false, false>(a, phase, dbias, s);
   }
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs &a, int phase, int bias, bool causal, bool varlen, bool rope,
-                    bool dbias, hipStream_t s) {
+hipError_t launch_d(const BwdArgs &a, int phase, int bias, bool causal, bool varlen, bool dbias,
+                    hipStream_t s) {
   switch (bias) {
-    case kBiasT5: return launch_b<D, kBiasT5>(a, phase, causal, varlen, rope, dbias, s);
-    case kBiasAlibi: return launch_b<D, kBiasAlibi>(a, phase, causal, varlen, rope, dbias, s);
-    case kBiasDense: return launch_b<D, kBiasDense>(a, phase, causal, varlen, rope, dbias, s);
-    default: return launch_b<D, kBiasNone>(a, phase, causal, varlen, rope, dbias, s);
+    case kBiasT5: return launch_b<D, kBiasT5>(a, phase, causal, varlen, dbias, s);
+    case kBiasAlibi: return launch_b<D, kBiasAlibi>(a, phase, causal, varlen, dbias, s);
+    case kBiasDense: return launch_b<D, kBiasDense>(a, phase, causal, varlen, dbias, s);
+    default: return launch_b<D, kBiasNone>(a, phase, causal, varlen, dbias, s);
   }
 }
 
@@ -972,8 +976,7 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.dq = static_cast<uint16_t *>(b.dq);
   a.dk = static_cast<uint16_t *>(b.dk);
   a.dv = static_cast<uint16_t *>(b.dv);
-  a.dq_f32 = b.dq_f32;
-  a.dk_f32 = b.dk_f32;
+  a.rope_cs = b.rope_cs;
   a.delta = b.delta;
   a.nls = b.delta + (size_t)p.total * p.heads;
   a.part = b.part;
@@ -1000,7 +1003,6 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
     a.nwg = p.nbatch * p.heads * a.ntile;
   }
   if (a.nwg <= 0) return hipSuccess;
-  const bool rope = p.rope_base > 0.f;
   const bool dbias = b.part != nullptr || a.dbias != nullptr;
   if (phase == kBwdReduce) {
     if (b.part == nullptr) return hipSuccess;
@@ -1008,8 +1010,8 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
                        sched, a.nwg, p.nbatch, p.heads, a.ntile, b.dtable);
     return hipGetLastError();
   }
-  return p.head_dim == 64 ? launch_d<64>(a, phase, p.bias, p.causal, p.varlen, rope, dbias, s)
-                          : launch_d<128>(a, phase, p.bias, p.causal, p.varlen, rope, dbias, s);
+  return p.head_dim == 64 ? launch_d<64>(a, phase, p.bias, p.causal, p.varlen, dbias, s)
+                          : launch_d<128>(a, phase, p.bias, p.causal, p.varlen, dbias, s);
 }
 
 }  // namespace fa

@@ -94,6 +94,43 @@ __device__ __forceinline__ float bf16_bits(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// fp64 -> bf16 bits with one rounding to nearest, ties to even: round to
+// fp32 with round-to-odd (truncate, then set the last bit if anything was
+// dropped), which keeps enough information for the final fp32 -> bf16
+// rounding to be the correctly rounded result.
+__device__ __forceinline__ uint32_t bf16_bits_rne(double x) {
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != x) {
+    if (fabs(back) > fabs(x)) u -= 1;   // step back toward zero
+    u |= 1u;
+  }
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// (cos, sin) of the RoPE angles of two consecutive pairs, fp64, from one
+// 32-byte entry pair of the table.
+struct RopeCs2 {
+  double c0, s0, c1, s1;
+};
+__device__ __forceinline__ RopeCs2 rope_cs2(rsrc_t r, uint32_t off) {
+  const i32x4 a = buf_load16(r, off), b = buf_load16(r, off + 16u);
+  const auto da = __builtin_bit_cast(__attribute__((ext_vector_type(2))) double, a);
+  const auto dbv = __builtin_bit_cast(__attribute__((ext_vector_type(2))) double, b);
+  return RopeCs2{da[0], da[1], dbv[0], dbv[1]};
+}
+
+// RoPE on registers: the pair (x0, x1) held as one bf16x2 word, turned by the
+// angle with (cos, sin) = (c, s): exact in fp64 (a product of bf16 and fp64
+// values, summed with one fma), then rounded once to bf16, which is what a
+// rotation computed exactly and stored in bf16 gives.
+__device__ __forceinline__ uint32_t rope_rotate_pair(uint32_t w, double c, double s) {
+  const double x0 = (double)bf16_lo(w), x1 = (double)bf16_hi(w);
+  return bf16_bits_rne(fma(x0, c, -x1 * s)) | (bf16_bits_rne(fma(x0, s, x1 * c)) << 16);
+}
+
 // Max / sum of a value over the two half-waves (lanes l and l ^ 32), with
 // v_permlane32_swap (a VALU lane exchange, no LDS round trip).  Both lanes of
 // a pair get the same result, bit for bit.

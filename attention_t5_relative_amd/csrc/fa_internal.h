@@ -49,19 +49,20 @@ struct Problem {
 };
 
 struct FwdBuffers {
-  const void *q, *k, *v;   // bf16 (already rotated when RoPE is on)
+  const void *q, *k, *v;   // bf16; k already rotated when RoPE is on
   void *o;
   float *lse;
+  const double2 *rope_cs;   // RoPE fp64 (cos, sin) table [seqlen, D/2] or nullptr
 };
 
 struct BwdBuffers {
-  const void *q, *k, *v;   // bf16 (rotated when RoPE is on)
+  const void *q, *k, *v;   // bf16 (q, k rotated when RoPE is on)
   const void *o;           // bf16 forward output (centres the dq accumulation)
   const void *dout;
   const float *lse;
   const float *dlse;       // gradient with respect to lse (same layout) or nullptr
   void *dq, *dk, *dv;      // bf16 outputs
-  float *dq_f32, *dk_f32;  // fp32 dQ, dK in the rotated space (RoPE only)
+  const double2 *rope_cs;   // RoPE fp64 (cos, sin) table [seqlen, D/2] or nullptr
   float *delta;            // fp32, two lse-layout arrays: -D, then -lse / scale
   float *part;             // fp32 [num_buckets, parts] (T5 table gradient) or nullptr
   float *dtable;           // [num_buckets, H] or nullptr
@@ -79,11 +80,12 @@ int sched_entries(int total, int nseq, int heads, int tile);
 int sched_prefix_ints(int nseq);
 hipError_t launch_sched(const int32_t *cu, int nseq, int heads, int tile, int nentries,
                         int32_t *prefix, int4 *sched, hipStream_t s);
-// Rotates q and k (bf16 [tokens, H, D]) into qo and ko.
-hipError_t launch_rope_pair(const Problem &p, const void *q, const void *k, void *qo, void *ko,
-                            hipStream_t s);
-// Un-rotates an fp32 gradient [tokens, H, D] into bf16 g_out.
-hipError_t launch_rope_grad(const Problem &p, const float *g_rot, void *g_out, hipStream_t s);
+// RoPE: cs[t][p] = (cos, sin) of t * base^(-2p/D) for t < p.seqlen (dense S,
+// packed max_seqlen), fp64 [seqlen, D/2] pairs; and rotation of one or two
+// bf16 [tokens, H, D] tensors (x1 / y1 may be nullptr).
+hipError_t launch_rope_table(const Problem &p, double2 *cs, hipStream_t s);
+hipError_t launch_rope_rotate(const Problem &p, const void *x0, void *y0, const void *x1,
+                              void *y1, hipStream_t s);
 int bwd_tile();
 int64_t bwd_num_parts(const Problem &p, int nsched);
 enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2 };   // dq, dkv, table reduce

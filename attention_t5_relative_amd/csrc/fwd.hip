@@ -51,6 +51,7 @@ struct FwdArgs {
   const int4 *sched;     // packed batches: {token0, length, head, q-tile}
   const float *table, *slopes;
   const uint16_t *dense;  // dense bias bf16 [dense_batch, H, S, S]
+  const double2 *rope_cs;  // RoPE: (cos, sin) [seqlen, D/2], or nullptr
   int32_t dense_batch;
   int32_t nbatch, seqlen, heads, total;
   int32_t nq, nwg;
@@ -119,6 +120,24 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
   for (int s = 0; s < D / 16; ++s)
     qf[s] = __builtin_bit_cast(
         bf16x8, buf_load16(rq, ((uint32_t)(wrow0 + il) * (uint32_t)HD + 16 * s + 8 * hl) * 2u));
+  if (a.rope_cs != nullptr) {
+    // RoPE: the row's position is its index in the sequence; fragment s holds
+    // pairs 8s + 4hl .. + 3 as its four 32-bit words.  Rows past the table
+    // read (cos, sin) = 0 (they are past the sequence and never stored).
+    const rsrc_t rcs = make_rsrc(a.rope_cs, (uint32_t)a.seqlen * (uint32_t)(D / 2) * 16u);
+    const uint32_t t0 = ((uint32_t)(wrow0 + il) * (uint32_t)(D / 2) + 4 * hl) * 16u;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      i32x4 w = __builtin_bit_cast(i32x4, qf[s]);
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const RopeCs2 c = rope_cs2(rcs, t0 + (8u * s + e) * 16u);
+        w[e] = (int)rope_rotate_pair((uint32_t)w[e], c.c0, c.s0);
+        w[e + 1] = (int)rope_rotate_pair((uint32_t)w[e + 1], c.c1, c.s1);
+      }
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
 
   int sat = 0;
   if constexpr (BIAS == kBiasT5) {
@@ -383,6 +402,7 @@ hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sc
   a.table = p.table;
   a.slopes = p.slopes;
   a.dense = p.dense;
+  a.rope_cs = b.rope_cs;
   a.dense_batch = p.dense_batch;
   a.nbatch = p.nbatch;
   a.seqlen = p.seqlen;

@@ -1,6 +1,6 @@
 // Small kernels around the attention kernels: the packed-batch tile schedule,
-// RoPE rotation of q/k and un-rotation of their gradients, the T5 bucket test
-// hook and a fill kernel.
+// the RoPE angle table and rotation of whole q / k tensors, the T5 bucket
+// test hook and a fill kernel.
 #include "fa_device.h"
 
 namespace fa {
@@ -131,11 +131,19 @@ __global__ __launch_bounds__(SCHED_NT) void sched_kernel(const int32_t *cu, int 
 }
 
 // ---------------------------------------------------------------------------
-// RoPE.  Thread (token, pair p) computes the angle pos * base^(-2p/D) and its
-// cosine and sine in fp64 (positions reach 65535, where an fp32 angle would
-// already be off by ~4e-3 rad), rotates that pair of every head in fp64 and
-// rounds the result once to bf16.  The attention kernels then run on these
-// bf16 rotated q and k, as a full-bf16 pipeline feeds them.
+// RoPE.  The pair (2p, 2p + 1) at position t turns by t * base^(-2p/D).
+//
+// rope_table_kernel writes cs[t][p] = (cos, sin) of that angle for every
+// position t < npos, in fp64 (positions reach 65535, where an fp32 angle
+// would already be off by ~4e-3 rad; and an fp32 cos / sin would move about
+// one rotated value in 10^4 to the neighbouring bf16).  The attention kernels
+// read it to rotate Q rows in registers and to rotate dQ and dK back in
+// their epilogues.
+//
+// rope_rotate_kernel rotates whole tensors that the kernels stream through
+// LDS (K in the forward, Q and K in the backward): thread (token, pair p)
+// rotates that pair of every head in fp64 and rounds the result once to
+// bf16, as a full-bf16 pipeline hands rotated operands to the kernels.
 // ---------------------------------------------------------------------------
 constexpr int ROPE_NT = 256;
 
@@ -149,68 +157,38 @@ __device__ __forceinline__ int token_position(int token, int seqlen, const int32
   return token - cu[lo];
 }
 
-__device__ __forceinline__ void rope_cs(int pos, int p, int D, double log2base, double &c,
-                                        double &s) {
+__device__ __forceinline__ void rope_angle_cs(int pos, int p, int D, double log2base, double &c,
+                                              double &s) {
   const double theta = exp2(-(2.0 * p / D) * log2base);
   sincos((double)pos * theta, &s, &c);
 }
 
-// fp64 -> bf16 with one rounding to nearest, ties to even: round to fp32 with
-// round-to-odd (truncate, then set the last bit if anything was dropped),
-// which keeps enough information for the final fp32 -> bf16 rounding to be
-// the correctly rounded result.
-__device__ __forceinline__ uint32_t bf16_bits_rne(double x) {
-  const float f = (float)x;
-  uint32_t u = __float_as_uint(f);
-  const double back = (double)f;
-  if (back != x) {
-    if (fabs(back) > fabs(x)) u -= 1;   // step back toward zero
-    u |= 1u;
-  }
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+__global__ __launch_bounds__(ROPE_NT) void rope_table_kernel(double2 *cs, int npos, int D,
+                                                              double log2base) {
+  const int half = D / 2;
+  const long long idx = (long long)blockIdx.x * ROPE_NT + threadIdx.x;
+  if (idx >= (long long)npos * half) return;
+  const int t = (int)(idx / half), p = (int)(idx - (long long)t * half);
+  double c, s;
+  rope_angle_cs(t, p, D, log2base, c, s);
+  cs[idx] = double2{c, s};
 }
 
-__device__ __forceinline__ uint32_t rot_pack(uint32_t w, double c, double s) {
-  const double x0 = (double)bf16_lo(w), x1 = (double)bf16_hi(w);
-  return bf16_bits_rne(fma(x0, c, -x1 * s)) | (bf16_bits_rne(fma(x0, s, x1 * c)) << 16);
-}
-
-__global__ __launch_bounds__(ROPE_NT) void rope_fwd_kernel(const uint32_t *q, const uint32_t *k,
-                                                            uint32_t *qo, uint32_t *ko,
-                                                            int tokens, int heads, int D,
-                                                            int seqlen, const int32_t *cu,
-                                                            int nseq, double log2base) {
+__global__ __launch_bounds__(ROPE_NT) void rope_rotate_kernel(const uint32_t *x0, uint32_t *y0,
+                                                               const uint32_t *x1, uint32_t *y1,
+                                                               int tokens, int heads, int D,
+                                                               int seqlen, const int32_t *cu,
+                                                               int nseq, double log2base) {
   const int half = D / 2;
   const long long idx = (long long)blockIdx.x * ROPE_NT + threadIdx.x;
   if (idx >= (long long)tokens * half) return;
   const int token = (int)(idx / half), p = (int)(idx - (long long)token * half);
   double c, s;
-  rope_cs(token_position(token, seqlen, cu, nseq), p, D, log2base, c, s);
+  rope_angle_cs(token_position(token, seqlen, cu, nseq), p, D, log2base, c, s);
   for (int hh = 0; hh < heads; ++hh) {
     const size_t w = ((size_t)token * heads + hh) * half + p;
-    qo[w] = rot_pack(q[w], c, s);
-    ko[w] = rot_pack(k[w], c, s);
-  }
-}
-
-// Gradients come back w.r.t. the rotated rows (fp32); rotating by the
-// opposite angle maps them to the unrotated q / k, rounded once to bf16.
-__global__ __launch_bounds__(ROPE_NT) void rope_grad_kernel(const float2 *g, uint32_t *out,
-                                                             int tokens, int heads, int D,
-                                                             int seqlen, const int32_t *cu,
-                                                             int nseq, double log2base) {
-  const int half = D / 2;
-  const long long idx = (long long)blockIdx.x * ROPE_NT + threadIdx.x;
-  if (idx >= (long long)tokens * half) return;
-  const int token = (int)(idx / half), p = (int)(idx - (long long)token * half);
-  double cd, sd;
-  rope_cs(token_position(token, seqlen, cu, nseq), p, D, log2base, cd, sd);
-  const float c = (float)cd, s = (float)sd;
-  for (int hh = 0; hh < heads; ++hh) {
-    const size_t w = ((size_t)token * heads + hh) * half + p;
-    const float2 x = g[w];
-    out[w] = pack_bf16x2(fmaf(x.x, c, x.y * s), fmaf(-x.x, s, x.y * c));
+    y0[w] = rope_rotate_pair(x0[w], c, s);
+    if (x1 != nullptr) y1[w] = rope_rotate_pair(x1[w], c, s);
   }
 }
 
@@ -250,29 +228,27 @@ hipError_t launch_sched(const int32_t *cu, int nseq, int heads, int tile, int ne
   return hipGetLastError();
 }
 
-hipError_t launch_rope_pair(const Problem &p, const void *q, const void *k, void *qo, void *ko,
-                            hipStream_t s) {
-  const int tokens = p.varlen ? p.total : p.nbatch * p.seqlen;
-  const long long n = (long long)tokens * (p.head_dim / 2);
+hipError_t launch_rope_table(const Problem &p, double2 *cs, hipStream_t s) {
+  const int npos = p.seqlen;
+  const long long n = (long long)npos * (p.head_dim / 2);
   if (n == 0) return hipSuccess;
   const int grid = (int)((n + ROPE_NT - 1) / ROPE_NT);
-  hipLaunchKernelGGL(rope_fwd_kernel, dim3(grid), dim3(ROPE_NT), 0, s,
-                     static_cast<const uint32_t *>(q), static_cast<const uint32_t *>(k),
-                     static_cast<uint32_t *>(qo), static_cast<uint32_t *>(ko), tokens, p.heads,
-                     p.head_dim, p.seqlen, p.varlen ? p.cu_seqlens : nullptr, p.nbatch,
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(ROPE_NT), 0, s, cs, npos, p.head_dim,
                      log2((double)p.rope_base));
   return hipGetLastError();
 }
 
-hipError_t launch_rope_grad(const Problem &p, const float *g_rot, void *g_out, hipStream_t s) {
+hipError_t launch_rope_rotate(const Problem &p, const void *x0, void *y0, const void *x1,
+                              void *y1, hipStream_t s) {
   const int tokens = p.varlen ? p.total : p.nbatch * p.seqlen;
   const long long n = (long long)tokens * (p.head_dim / 2);
   if (n == 0) return hipSuccess;
   const int grid = (int)((n + ROPE_NT - 1) / ROPE_NT);
-  hipLaunchKernelGGL(rope_grad_kernel, dim3(grid), dim3(ROPE_NT), 0, s,
-                     reinterpret_cast<const float2 *>(g_rot), static_cast<uint32_t *>(g_out),
-                     tokens, p.heads, p.head_dim, p.seqlen, p.varlen ? p.cu_seqlens : nullptr,
-                     p.nbatch, log2((double)p.rope_base));
+  hipLaunchKernelGGL(rope_rotate_kernel, dim3(grid), dim3(ROPE_NT), 0, s,
+                     static_cast<const uint32_t *>(x0), static_cast<uint32_t *>(y0),
+                     static_cast<const uint32_t *>(x1), static_cast<uint32_t *>(y1), tokens,
+                     p.heads, p.head_dim, p.seqlen, p.varlen ? p.cu_seqlens : nullptr, p.nbatch,
+                     log2((double)p.rope_base));
   return hipGetLastError();
 }
 

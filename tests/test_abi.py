@@ -205,11 +205,23 @@ def test_workspace_sizes(lib):
     p = _dense()
     assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == 0
     p.rope_base = 10000.0
-    # rotated copies of q and k, each 256-byte aligned
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+    # the forward: a rotated copy of k and the fp64 (cos, sin) table [S, D/2] (q is
+    # rotated in registers); each region 256-byte aligned
     one = 2 * 100 * 3 * 64 * 2
-    assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == 2 * ((one + 255) // 256 * 256)
+    table = 100 * 32 * 16
+    assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == a256(one) + a256(table)
     # a call that needs a workspace refuses without one
     assert lib.fa_fwd(ctypes.byref(p), None, 0, None) == _lib.FA_ERR_WORKSPACE
+    # the backward: rotated copies of q and k, the table, -D and -lse/scale
+    # (dQ and dK are turned back inside the kernels: no fp32 copies)
+    b = _lib.FaBwdParams()
+    b.f = p
+    b.dout = b.dq = b.dk = b.dv = 0x4000
+    delta = a256(2 * 2 * 100 * 3 * 4)
+    assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == 2 * a256(one) + a256(table) + delta
 
 
 def test_dense_bias_gradient_workspace(lib):
