@@ -378,7 +378,9 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
   hipError_t e;
   if (p.rope_base > 0.f) {
     e = fa::launch_rope_table(p, at<double2>(ws, L.rope_cs), s);
-    if (e == hipSuccess) e = fa::launch_rope_rotate(p, k, at<void>(ws, L.krot), nullptr, nullptr, s);
+    if (e == hipSuccess)
+      e = fa::launch_rope_rotate(p, at<double2>(ws, L.rope_cs), k, at<void>(ws, L.krot), nullptr,
+                                 nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "rope");
     b.k = at<void>(ws, L.krot);
     b.rope_cs = at<double2>(ws, L.rope_cs);
@@ -442,7 +444,8 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   if (p.rope_base > 0.f) {
     e = fa::launch_rope_table(p, at<double2>(ws, L.rope_cs), s);
     if (e == hipSuccess)
-      e = fa::launch_rope_rotate(p, q, at<void>(ws, L.qrot), k, at<void>(ws, L.krot), s);
+      e = fa::launch_rope_rotate(p, at<double2>(ws, L.rope_cs), q, at<void>(ws, L.qrot), k,
+                                 at<void>(ws, L.krot), s);
     if (e != hipSuccess) return hip_fail(e, "rope");
     b.q = at<void>(ws, L.qrot);
     b.k = at<void>(ws, L.krot);

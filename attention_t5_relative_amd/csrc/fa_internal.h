@@ -84,8 +84,8 @@ hipError_t launch_sched(const int32_t *cu, int nseq, int heads, int tile, int ne
 // packed max_seqlen), fp64 [seqlen, D/2] pairs; and rotation of one or two
 // bf16 [tokens, H, D] tensors (x1 / y1 may be nullptr).
 hipError_t launch_rope_table(const Problem &p, double2 *cs, hipStream_t s);
-hipError_t launch_rope_rotate(const Problem &p, const void *x0, void *y0, const void *x1,
-                              void *y1, hipStream_t s);
+hipError_t launch_rope_rotate(const Problem &p, const double2 *cs, const void *x0, void *y0,
+                              const void *x1, void *y1, hipStream_t s);
 int bwd_tile();
 int64_t bwd_num_parts(const Problem &p, int nsched);
 enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2 };   // dq, dkv, table reduce

@@ -141,9 +141,10 @@ __global__ __launch_bounds__(SCHED_NT) void sched_kernel(const int32_t *cu, int 
 // their epilogues.
 //
 // rope_rotate_kernel rotates whole tensors that the kernels stream through
-// LDS (K in the forward, Q and K in the backward): thread (token, pair p)
-// rotates that pair of every head in fp64 and rounds the result once to
-// bf16, as a full-bf16 pipeline hands rotated operands to the kernels.
+// LDS (K in the forward, Q and K in the backward), one 16-byte chunk (four
+// pairs) of one row per thread with the table's angles: exact in fp64 and
+// rounded once to bf16, as a full-bf16 pipeline hands rotated operands to
+// the kernels.
 // ---------------------------------------------------------------------------
 constexpr int ROPE_NT = 256;
 
@@ -174,22 +175,29 @@ __global__ __launch_bounds__(ROPE_NT) void rope_table_kernel(double2 *cs, int np
   cs[idx] = double2{c, s};
 }
 
-__global__ __launch_bounds__(ROPE_NT) void rope_rotate_kernel(const uint32_t *x0, uint32_t *y0,
-                                                               const uint32_t *x1, uint32_t *y1,
-                                                               int tokens, int heads, int D,
-                                                               int seqlen, const int32_t *cu,
-                                                               int nseq, double log2base) {
-  const int half = D / 2;
+__global__ __launch_bounds__(ROPE_NT) void rope_rotate_kernel(const i32x4 *x0, i32x4 *y0,
+                                                               const i32x4 *x1, i32x4 *y1,
+                                                               const double2 *cs, int tokens,
+                                                               int heads, int D, int seqlen,
+                                                               const int32_t *cu, int nseq) {
+  // one thread per 16-byte chunk (4 pairs) of one (token, head) row
+  const int chunks = D / 8;
   const long long idx = (long long)blockIdx.x * ROPE_NT + threadIdx.x;
-  if (idx >= (long long)tokens * half) return;
-  const int token = (int)(idx / half), p = (int)(idx - (long long)token * half);
-  double c, s;
-  rope_angle_cs(token_position(token, seqlen, cu, nseq), p, D, log2base, c, s);
-  for (int hh = 0; hh < heads; ++hh) {
-    const size_t w = ((size_t)token * heads + hh) * half + p;
-    y0[w] = rope_rotate_pair(x0[w], c, s);
-    if (x1 != nullptr) y1[w] = rope_rotate_pair(x1[w], c, s);
-  }
+  if (idx >= (long long)tokens * heads * chunks) return;
+  const long long row = idx / chunks;
+  const int c = (int)(idx - row * chunks);
+  const int token = (int)(row / heads);
+  const double2 *e = cs + (size_t)token_position(token, seqlen, cu, nseq) * (D / 2) + 4 * c;
+  const double2 a0 = e[0], a1 = e[1], a2 = e[2], a3 = e[3];
+  auto turn = [&](i32x4 w) {
+    w[0] = (int)rope_rotate_pair((uint32_t)w[0], a0.x, a0.y);
+    w[1] = (int)rope_rotate_pair((uint32_t)w[1], a1.x, a1.y);
+    w[2] = (int)rope_rotate_pair((uint32_t)w[2], a2.x, a2.y);
+    w[3] = (int)rope_rotate_pair((uint32_t)w[3], a3.x, a3.y);
+    return w;
+  };
+  y0[idx] = turn(x0[idx]);
+  if (x1 != nullptr) y1[idx] = turn(x1[idx]);
 }
 
 // ---------------------------------------------------------------------------
@@ -238,17 +246,16 @@ hipError_t launch_rope_table(const Problem &p, double2 *cs, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rope_rotate(const Problem &p, const void *x0, void *y0, const void *x1,
-                              void *y1, hipStream_t s) {
+hipError_t launch_rope_rotate(const Problem &p, const double2 *cs, const void *x0, void *y0,
+                              const void *x1, void *y1, hipStream_t s) {
   const int tokens = p.varlen ? p.total : p.nbatch * p.seqlen;
-  const long long n = (long long)tokens * (p.head_dim / 2);
+  const long long n = (long long)tokens * p.heads * (p.head_dim / 8);
   if (n == 0) return hipSuccess;
   const int grid = (int)((n + ROPE_NT - 1) / ROPE_NT);
   hipLaunchKernelGGL(rope_rotate_kernel, dim3(grid), dim3(ROPE_NT), 0, s,
-                     static_cast<const uint32_t *>(x0), static_cast<uint32_t *>(y0),
-                     static_cast<const uint32_t *>(x1), static_cast<uint32_t *>(y1), tokens,
-                     p.heads, p.head_dim, p.seqlen, p.varlen ? p.cu_seqlens : nullptr, p.nbatch,
-                     log2((double)p.rope_base));
+                     static_cast<const i32x4 *>(x0), static_cast<i32x4 *>(y0),
+                     static_cast<const i32x4 *>(x1), static_cast<i32x4 *>(y1), cs, tokens,
+                     p.heads, p.head_dim, p.seqlen, p.varlen ? p.cu_seqlens : nullptr, p.nbatch);
   return hipGetLastError();
 }
 
