@@ -259,14 +259,18 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
   const int rbase = j0 - (row0 + il) + 4 * hl;
   const int jb = j0 + 4 * hl;
   if constexpr (BIAS == kBiasT5) {
+    // the causal mask is in the table; the length mask is one compare per
+    // element against a per-lane limit (past every offset when the tile
+    // needs none)
     const float *lb = lut + min(max(rbase, -sat - kLutPad), sat + kLutPad - 59);
+    const int lim = mask_l ? L - jb : 64;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
         const float t = fmaf(sacc[kb][r], c, lb[off]);
-        sacc[kb][r] = (mask_l && jb + off >= L) ? -INFINITY : t;
+        sacc[kb][r] = off >= lim ? -INFINITY : t;
       }
     return false;
   }
@@ -328,13 +332,15 @@ __device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, i
   const int rbase = jb0 - (row0 + il) + 4 * hl;
   const int jb = jb0 + 4 * hl;
   if constexpr (BIAS == kBiasT5) {
-    // offsets 0 .. 27 from one clamped base (see kLutPad)
+    // offsets 0 .. 27 from one clamped base (see kLutPad); the length mask
+    // against a per-lane limit, as in score_tile_T
     const float *lb = lut + min(max(rbase, -sat - kLutPad), sat + kLutPad - 27);
+    const int lim = mask_l ? L - jb : 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int off = 8 * (r >> 2) + (r & 3);
       const float t = fmaf(sacc[r], c, lb[off]);
-      sacc[r] = (mask_l && jb + off >= L) ? -INFINITY : t;
+      sacc[r] = off >= lim ? -INFINITY : t;
     }
     return false;
   }

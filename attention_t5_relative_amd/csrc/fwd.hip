@@ -192,7 +192,8 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
   // lane l's rows 4 (l / 16) .. + 3 are its own query il.
   // (At head_dim 128 the operand is rebuilt from one register in each
   // iteration: four registers held across the loop would spill the dense-
-  // bias variant.)
+  // bias variant.  At 64 they fit, and rebuilding would cost four moves per
+  // product.)
   f32x4 wsum = f32x4{};
   const int selw = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? 0x3f803f80 : 0;
   auto sel_operand = [&]() {
@@ -269,9 +270,13 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
       // workgroups per CU at head_dim 64)
       const bool fast = score_tile_T<BIAS, CAUSAL, D == 128>(sacc, j0, wrow0, il, hl, L, c, sat,
                                                             lut, slope_l2, bconst, bv);
-      float m0 = -INFINITY, m1 = -INFINITY;
+      // row max: two chains of v_max3 (one instruction per two elements; the
+      // empty asm keeps the compiler from rebalancing them into a tree of
+      // two-input maxes, which takes half as many instructions again)
+      float m0 = fmaxf(sacc[0][0], sacc[0][1]), m1 = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
+      for (int r = 2; r < 16; r += 2) {
+        asm volatile("" : "+v"(m0), "+v"(m1));
         m0 = fmaxf(m0, fmaxf(sacc[0][r], sacc[0][r + 1]));
         m1 = fmaxf(m1, fmaxf(sacc[1][r], sacc[1][r + 1]));
       }
