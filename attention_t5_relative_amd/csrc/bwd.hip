@@ -95,9 +95,28 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int g, Work &w) {
   return true;
 }
 
-__device__ __forceinline__ void split_hi_lo(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+// A pair (x0, x1) as bf16 hi + lo pairs: hi = the nearest bf16 values, lo =
+// the rounded remainders (16 significant bits together).  The remainders
+// x - bf16(x), exact in fp32, come from one bf16 dot product each against
+// (-1, 0) and (0, -1): hi.lo * -1 + hi.hi * 0 + x0, instead of unpacking a
+// half and subtracting it.  The two constant pairs must reach the dot
+// product from registers (see NegPairs).
+struct NegPairs {
+  bf16x2 m10, m01;   // (-1, 0) and (0, -1)
+};
+__device__ __forceinline__ NegPairs neg_pairs() {
+  // kept opaque: as an inline constant the hardware would read the packed
+  // bf16 operand -1.0 differently
+  int a = 0x0000bf80, b = (int)0xbf800000u;
+  asm volatile("" : "+s"(a), "+s"(b));
+  return NegPairs{__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b)};
+}
+__device__ __forceinline__ void split_hi_lo(float x0, float x1, uint32_t &hi, uint32_t &lo,
+                                            const NegPairs &n) {
   hi = pack_bf16x2(x0, x1);
-  lo = pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
+  const bf16x2 h = __builtin_bit_cast(bf16x2, hi);
+  lo = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(h, n.m10, x0, false),
+                   __builtin_amdgcn_fdot2_f32_bf16(h, n.m01, x1, false));
 }
 
 __device__ __forceinline__ bf16x8 frag(const uint32_t (&w)[4]) {
@@ -234,6 +253,7 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
   }
   const float c = a.scale_log2;
   const float dscale = a.scale;
+  const NegPairs negp = neg_pairs();
 
   // One sweep over the keys.  dQ_i = scale * sum_j P_ij (dP_ij - D_i) k_j
   // needs D_i = sum_j P_ij dP_ij, known only after the last key, so it is
@@ -325,7 +345,7 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], cc, sub));
             const float x0 = p0 * (pacc[kb][r] - dc), x1 = p1 * (pacc[kb][r + 1] - dc);
             dsum += x0 + x1;
-            split_hi_lo(x0, x1, xh[e], xl[e]);
+            split_hi_lo(x0, x1, xh[e], xl[e], negp);
             ph[e] = pack_bf16x2(p0, p1);
           }
           const bf16x8 xhb = frag(xh), xlb = frag(xl), phb = frag(ph);
@@ -500,6 +520,7 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
 
   const float c = a.scale_log2;
   const float dscale = a.scale;
+  const NegPairs negp = neg_pairs();
   const int nqb = (L + QB - 1) / QB;
   const int qb_first = CAUSAL ? (kt0 / QB) : 0;
 
@@ -577,8 +598,8 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
       uint32_t pw[4], plw[4], hw[4], lw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        split_hi_lo(p[8 * u + 2 * e], p[8 * u + 2 * e + 1], pw[e], plw[e]);
-        split_hi_lo(ds[8 * u + 2 * e], ds[8 * u + 2 * e + 1], hw[e], lw[e]);
+        split_hi_lo(p[8 * u + 2 * e], p[8 * u + 2 * e + 1], pw[e], plw[e], negp);
+        split_hi_lo(ds[8 * u + 2 * e], ds[8 * u + 2 * e + 1], hw[e], lw[e], negp);
       }
       const bf16x8 pb = frag(pw), plb = frag(plw), hb = frag(hw), lb = frag(lw);
 #pragma unroll
