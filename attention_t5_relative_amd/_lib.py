@@ -26,6 +26,7 @@ FA_KERNEL_CE_FWD = 5
 FA_KERNEL_CE_BWD = 6
 
 FA_BWD_NOALLOC_MAX_BYTES = 16 << 20
+FA_MFMA_PROBE_LANES = 2048 * 256
 
 FA_BIAS_NONE = 0
 FA_BIAS_T5 = 1
@@ -108,6 +109,7 @@ SIGNATURES = {
     "fa_ce_fwd": (c_i32, [ctypes.POINTER(FaCeFwdParams), c_ptr]),
     "fa_ce_bwd": (c_i32, [ctypes.POINTER(FaCeBwdParams), c_ptr]),
     "fa_set_kernel_timer": (c_i32, [c_i32, c_ptr, c_ptr]),
+    "fa_mfma_probe": (c_i32, [c_i32, c_ptr, ctypes.POINTER(ctypes.c_double), c_ptr]),
     "fa_status_str": (ctypes.c_char_p, [c_i32]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_version": (ctypes.c_char_p, []),

@@ -595,8 +595,8 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *ws, size_t ws_bytes
 fa_status fa_bwd(const fa_bwd_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
   const fa_status st = fa_check_bwd(p);
   if (st != FA_OK) return st;
-  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse, p->dout, p->dq,
-                 p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
+  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse,
+                 p->dout, p->dq, p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
 }
 
 fa_status fa_bwd_noalloc(const fa_bwd_params *p, hipStream_t stream) {
@@ -614,16 +614,16 @@ fa_status fa_bwd_noalloc(const fa_bwd_params *p, hipStream_t stream) {
     const fa_status s2 = scratch_of_current_device(&ws);
     if (s2 != FA_OK) return s2;
   }
-  return run_bwd(pr, p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse, p->dout, p->dq, p->dk, p->dv,
-                 p->dtable, ws, need, stream);
+  return run_bwd(pr, p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse, p->dout, p->dq, p->dk,
+                 p->dv, p->dtable, ws, need, stream);
 }
 
 fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *ws, size_t ws_bytes,
                         hipStream_t stream) {
   const fa_status st = fa_check_varlen_bwd(p);
   if (st != FA_OK) return st;
-  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse, p->dout, p->dq,
-                 p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
+  return run_bwd(make_problem(p->f), p->f.q, p->f.k, p->f.v, p->f.o, p->f.lse, p->dlse,
+                 p->dout, p->dq, p->dk, p->dv, p->dtable, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -731,6 +731,19 @@ fa_status fa_ce_bwd(const fa_ce_bwd_params *p, hipStream_t stream) {
                              p->f.vocab, p->f.z_loss, p->f.ignore_index, stream);
   });
   return e == hipSuccess ? FA_OK : hip_fail(e, "cross-entropy backward");
+}
+
+fa_status fa_mfma_probe(int32_t iters, float *sink, double *flops, hipStream_t stream) {
+  g_last_error.clear();
+  static_assert(FA_MFMA_PROBE_LANES == fa::kMfmaProbeBlocks * fa::kMfmaProbeThreads,
+                "probe size");
+  if (iters < 1 || iters > (1 << 20))
+    return fail(FA_ERR_INVALID, "iters %d outside [1, 2^20]", iters);
+  if (!sink || !flops) return fail(FA_ERR_INVALID, "sink or flops is NULL");
+  const hipError_t e = fa::launch_mfma_probe(sink, iters, stream);
+  if (e != hipSuccess) return hip_fail(e, "mfma_probe");
+  *flops = (double)(FA_MFMA_PROBE_LANES / 64) * 4.0 * iters * (2.0 * 32 * 32 * 16);
+  return FA_OK;
 }
 
 fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t max_distance,

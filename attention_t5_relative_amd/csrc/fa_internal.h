@@ -94,6 +94,11 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
 hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
                              hipStream_t s);
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
+// MFMA throughput probe: kMfmaProbeBlocks x kMfmaProbeThreads lanes, each
+// wave 4 chains x iters v_mfma_f32_32x32x16_bf16; sink holds one float per lane.
+constexpr int kMfmaProbeBlocks = 2048;
+constexpr int kMfmaProbeThreads = 256;
+hipError_t launch_mfma_probe(float *sink, int iters, hipStream_t s);
 // Dense bias gradient helpers: zero the pairs with key > query of `count`
 // [S, S] matrices (causal: the backward never visits most of them), and sum
 // `nbatch` [H, S, S] slabs into one (pairs with key > query set to 0 when

@@ -1,6 +1,6 @@
 // Small kernels around the attention kernels: the packed-batch tile schedule,
 // the RoPE angle table and rotation of whole q / k tensors, the T5 bucket
-// test hook and a fill kernel.
+// test hook, a fill kernel and an MFMA throughput probe.
 #include "fa_device.h"
 
 namespace fa {
@@ -218,7 +218,39 @@ __global__ __launch_bounds__(256) void fill_kernel(float *p, size_t n, float v) 
   if (idx < n) p[idx] = v;
 }
 
+// ---------------------------------------------------------------------------
+// MFMA throughput probe: every wave issues only v_mfma_f32_32x32x16_bf16 in
+// four independent accumulator chains (no loads in the loop), so the chip's
+// sustained bf16 matrix rate can be measured under the same clock and power
+// limits as the attention kernels.  Operands are distinct non-trivial bf16
+// values per lane; each lane stores one sum so the work cannot be dropped.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kMfmaProbeThreads) void mfma_probe_kernel(float *sink, int iters) {
+  const int t = (int)(blockIdx.x * kMfmaProbeThreads + threadIdx.x);
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(1.0f + (float)((t * 7 + i) & 15) * 0.0625f);
+    b[i] = (__bf16)(0.5f - (float)((t * 5 + 3 * i) & 15) * 0.03125f);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = mfma32(a, b, c0);
+    c1 = mfma32(b, a, c1);
+    c2 = mfma32(a, a, c2);
+    c3 = mfma32(b, b, c3);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  sink[t] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(float *sink, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(kMfmaProbeBlocks), dim3(kMfmaProbeThreads), 0, s,
+                     sink, iters);
+  return hipGetLastError();
+}
 
 int sched_entries(int total, int nseq, int heads, int tile) {
   // every XCD holds at most ceil(H / 8) pairs of each sequence, and a

@@ -11,7 +11,9 @@ FlashAttention convention: forward 4*B*H*S^2*D/2 (causal), backward 2.5x the
 forward (5 GEMMs); the backward's D sweep and the hi/lo splits are extra work
 that is not counted.  "roofline" reports the dominant kernel (timed alone with
 HIP events through the library's fa_set_kernel_timer hook, on the stream it
-runs on) against the 2.5 PFLOP/s dense bf16 MFMA peak.  "cpu_baseline" times
+runs on) against the 2.5 PFLOP/s dense bf16 MFMA peak, credited with its share
+of the step's count: forward 1.0x (S, PV), dK/dV kernel 2.0x (S, dP, dV, dK),
+dQ kernel 0.5x (dQ), so the three shares sum to the step's 3.5x.  "cpu_baseline" times
 the fp64 NumPy oracle on a bounded sample of the same workload on the host.
 
 ``--bias dense`` runs the same step with the report's first-kernel semantics
@@ -26,11 +28,17 @@ kernels (RMSNorm, cross-entropy with z-loss) forward + backward on the same
 value is algorithmic GB/s (each tensor read or written once per pass).
 
 ``--workload encoder|varlen|alibi|rope`` time the other attention workloads
-the same way (forward + backward, kernel times by HIP events): the
-bidirectional T5 encoder B16 H12 S1024 D64; 32768 packed tokens with
-lognormal lengths (12 heads, D64, bidirectional T5); and the long-context
-causal B2 H16 S16384 D128 run with ALiBi or with RoPE.  Their lines carry
-no cpu_baseline.
+the same way (forward + backward, kernel times by HIP events), each on the
+seeded draw its parity test uses: the bidirectional T5 encoder B16 H12 S1024
+D64 (seed 2); 32768 packed tokens in 55 sequences of lognormal lengths (seed
+4; 12 heads, D64, bidirectional T5); and the long-context causal B2 H16
+S16384 D128 (seed 5) run with ALiBi or with RoPE.  Their cpu_baseline times
+the oracle on a few heads (one head at S16384).
+
+Every line reports the mean step over the K timed steps (ms_per_step, from
+which value follows), the median, p10 and p90 of the single steps, and one
+cold step run after 1 GiB has been written to evict the inputs from the
+caches.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                     [--bias t5|dense]
@@ -67,6 +75,7 @@ def _hip():
     lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                         ctypes.c_void_p]
     lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -80,6 +89,84 @@ def _elapsed(hip, a, b) -> float:
     ms = ctypes.c_float()
     assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
     return ms.value
+
+
+def run_timed(a, step, kernels, dev):
+    """W untimed warm-up steps, then K steps timed with HIP events on the
+    launch stream: the whole bracket (ms_per_step), each step on its own
+    (median, p10, p90) and each kernel of `kernels` through the library's
+    fa_set_kernel_timer hook.  Then one cold step: 1 GiB written first evicts
+    the inputs from the 256 MB Infinity Cache and the L2s."""
+    import numpy as np
+    import torch
+
+    from attention_t5_relative_amd import _lib
+    lib = _lib.load()
+    hip = _hip()
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = {n: [(_event(hip), _event(hip)) for _ in range(a.steps)] for n in kernels}
+    marks = [_event(hip) for _ in range(a.steps + 1)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    hip.hipEventRecord(marks[0], stream)
+    wall0 = time.perf_counter()
+    for i in range(a.steps):
+        for n, kid in kernels.items():
+            lib.fa_set_kernel_timer(kid, evs[n][i][0], evs[n][i][1])
+        step()
+        hip.hipEventRecord(marks[i + 1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for kid in kernels.values():
+        lib.fa_set_kernel_timer(kid, None, None)
+    steps_ms = np.array([_elapsed(hip, marks[i], marks[i + 1]) for i in range(a.steps)])
+    res = {
+        "ms_step": _elapsed(hip, marks[0], marks[-1]) / a.steps,
+        "kernel_ms": {n: sum(_elapsed(hip, s0, s1) for s0, s1 in evs[n]) / a.steps
+                      for n in kernels},
+        "host_wall_ms": wall / a.steps * 1e3,
+        "step_ms": {"median": round(float(np.median(steps_ms)), 4),
+                    "p10": round(float(np.percentile(steps_ms, 10)), 4),
+                    "p90": round(float(np.percentile(steps_ms, 90)), 4)},
+    }
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    c0, c1 = _event(hip), _event(hip)
+    scrub.fill_(1.0)
+    hip.hipEventRecord(c0, stream)
+    step()
+    hip.hipEventRecord(c1, stream)
+    torch.cuda.synchronize()
+    res["step_ms"]["cold_after_1GiB_scrub"] = round(_elapsed(hip, c0, c1), 4)
+    del scrub
+    return res
+
+
+def mfma_probe(dev, iters=20000, reps=3):
+    """The chip's sustained dense bf16 MFMA rate (TFLOP/s), measured by the
+    library's probe kernel: best of `reps` timed calls after one warm-up."""
+    import torch
+
+    from attention_t5_relative_amd import _lib
+    lib = _lib.load()
+    hip = _hip()
+    sink = torch.empty(_lib.FA_MFMA_PROBE_LANES, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    flops = ctypes.c_double()
+    best = 0.0
+    for r in range(reps + 1):
+        e0, e1 = _event(hip), _event(hip)
+        hip.hipEventRecord(e0, stream)
+        st = lib.fa_mfma_probe(iters, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops),
+                               stream)
+        if st != _lib.FA_OK:
+            raise RuntimeError(f"fa_mfma_probe: {lib.fa_last_error().decode()}")
+        hip.hipEventRecord(e1, stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            best = max(best, flops.value / (_elapsed(hip, e0, e1) * 1e-3) / 1e12)
+    return best
 
 
 def _traffic(kernel: str):
@@ -109,29 +196,17 @@ def _traffic(kernel: str):
 def cpu_baseline(inp, pairs, dense=None):
     """The fp64 oracle, as it stands, on `pairs` (batch, head) of the workload
     (with `dense`, the dense bias matrix [1, H, S, S] as float64)."""
-    import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0])
-    except Exception:  # noqa: BLE001
-        threads = 0
-    threads = threads or (os.cpu_count() or 1)
     q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
     kw = dict(scale=1.0, causal=True, bias="t5", table=inp.table, num_buckets=NB,
               max_distance=MD, bidirectional=False)
     if dense is not None:
         kw = dict(scale=1.0, causal=True, bias="dense", dense=dense)
-    t0 = time.perf_counter()
-    oracle.attention_fwd(q, k, v, pairs=pairs, **kw)
-    oracle.attention_bwd(q, k, v, do, pairs=pairs, **kw)
-    dt = time.perf_counter() - t0
+    work = [lambda: oracle.attention_fwd(q, k, v, pairs=pairs, **kw),
+            lambda: oracle.attention_bwd(q, k, v, do, pairs=pairs, **kw)]
     flops = 3.5 * 4.0 * S * S * D / 2.0 * len(pairs)
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{len(pairs)} of {B * H} (batch, head) pairs of the same workload, "
-                      f"fwd+bwd in fp64 NumPy on the host ({dt:.1f} s); same algorithmic "
-                      f"flop count per pair as the GPU value"}
+    return _time_oracle(work, flops, f"{len(pairs)} of {B * H} (batch, head) pairs of the "
+                                     "same workload")
 
 
 NL_ROWS, RMS_DIM, CE_VOCAB, Z_LOSS = 32768, 768, 32128, 1e-4
@@ -206,27 +281,8 @@ def bench_norm_loss(a):
                     "x 32128 bf16 logits (T5 vocabulary), 10% ignored labels")
         cfg = {"rows": N, "vocab": V, "z_loss": Z_LOSS}
 
-    lib = _lib.load()
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    hip = _hip()
-    evs = {n: [(_event(hip), _event(hip)) for _ in range(a.steps)] for n in kernels}
-    t_start, t_stop = _event(hip), _event(hip)
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    torch.cuda.synchronize()
-    hip.hipEventRecord(t_start, ctypes.c_void_p(stream))
-    for i in range(a.steps):
-        for n, kid in kernels.items():
-            lib.fa_set_kernel_timer(kid, evs[n][i][0], evs[n][i][1])
-        step()
-    hip.hipEventRecord(t_stop, ctypes.c_void_p(stream))
-    torch.cuda.synchronize()
-    for kid in kernels.values():
-        lib.fa_set_kernel_timer(kid, None, None)
-    ms_step = _elapsed(hip, t_start, t_stop) / a.steps
-    kernel_ms = {n: sum(_elapsed(hip, s0, s1) for s0, s1 in evs[n]) / a.steps for n in kernels}
+    t = run_timed(a, step, kernels, dev)
+    ms_step, kernel_ms = t["ms_step"], t["kernel_ms"]
     dom = max(kernel_ms, key=kernel_ms.get)
     gbs = abytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -237,6 +293,7 @@ def bench_norm_loss(a):
         "data": "synthetic",
         "config": dict({"workload": workload, "parallelism": "none (one GPU)",
                         "kernel_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
+                        "step_ms": t["step_ms"],
                         "frac_of_hbm_peak": round(value / PEAK_GBS, 4)}, **cfg),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None},
@@ -277,12 +334,99 @@ def norm_loss_cpu_baseline(workload):
                       f"({dt:.2f} s); same algorithmic bytes per row as the GPU value"}
 
 
-OTHER_ATTENTION = ("encoder", "varlen", "alibi", "rope")
+OTHER_ATTENTION = {"encoder": "c2", "varlen": "c4", "alibi": "c5a", "rope": "c5b"}
+
+# FlashAttention convention for a fwd+bwd step: the forward's two products
+# count 1.0x, the backward's five 2.5x.  Per kernel the step's 3.5x is split
+# so each product counts once: fwd S, PV = 1.0; dkv S, dP, dV, dK = 2.0; dq
+# dQ = 0.5.  OWN_PRODUCTS credits each kernel with every product its outputs
+# need (the dq kernel recomputes S and dP too): shown beside, never in value.
+CONVENTION = {"fwd": 1.0, "bwd_dq": 0.5, "bwd_dkv": 2.0}
+OWN_PRODUCTS = {"fwd": 1.0, "bwd_dq": 1.5, "bwd_dkv": 2.0}
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0])
+    except Exception:  # noqa: BLE001
+        threads = 0
+    return threads or (os.cpu_count() or 1)
+
+
+def _time_oracle(work, flops, sample):
+    """Run the oracle calls in `work` once on the host; TFLOP/s of the same
+    algorithmic count as the GPU value."""
+    threads = _oracle_threads()
+    t0 = time.perf_counter()
+    for fn in work:
+        fn()
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{sample}, fwd+bwd in fp64 NumPy on the host ({dt:.1f} s); same "
+                      f"algorithmic flop count per unit as the GPU value",
+            "host": _host_info(threads)}
+
+
+def _host_info(threads):
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "sched_affinity": len(os.sched_getaffinity(0)), "blas_threads": threads}
+
+
+def _attention_line(a, metric, workload, shape, t, fwd_flops, traffic=None):
+    """The JSON line of an attention fwd+bwd step from run_timed's result."""
+    ms_step, kernel_ms = t["ms_step"], t["kernel_ms"]
+    dom = max(kernel_ms, key=kernel_ms.get)
+
+    def tf(share, n):
+        return round(share * fwd_flops / (kernel_ms[n] * 1e-3) / 1e12, 2)
+
+    achieved = tf(CONVENTION[dom], dom)
+    value = 3.5 * fwd_flops / (ms_step * 1e-3) / 1e12
+    probe = t.get("mfma_probe_tflops")
+    extra = {}
+    if probe:
+        extra["mfma_probe"] = {"tflops": round(probe, 1),
+                               "step_frac_of_probe": round(value / probe, 4),
+                               "dominant_frac_of_probe": round(achieved / probe, 4)}
+    return {
+        "metric": metric, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict({"workload": workload, "parallelism": "none (one GPU)",
+                        "frac_of_peak": round(value / PEAK_TFLOPS, 4),
+                        "kernel_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
+                        "kernel_tflops_convention": {n: tf(CONVENTION[n], n) for n in kernel_ms},
+                        "kernel_tflops_own_products": {n: tf(OWN_PRODUCTS[n], n)
+                                                       for n in kernel_ms},
+                        "step_ms": t["step_ms"],
+                        "host_wall_ms_per_step": round(t["host_wall_ms"], 4)}, **extra, **shape),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+    }
+
+
+def _attn_kernels():
+    from attention_t5_relative_amd import _lib
+    return {"fwd": _lib.FA_KERNEL_FWD, "bwd_dq": _lib.FA_KERNEL_BWD_DQ,
+            "bwd_dkv": _lib.FA_KERNEL_BWD_DKV}
 
 
 def bench_other_attention(a):
-    """Forward + backward of one of the other attention workloads; one JSON
-    line with the FlashAttention-convention TFLOP/s of the step."""
+    """Forward + backward of one of the other attention workloads, on the
+    same seeded draw its parity test uses; one JSON line."""
     import numpy as np
     import torch
 
@@ -291,22 +435,23 @@ def bench_other_attention(a):
     from attention_t5_relative_amd import _lib
 
     dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(SEED)
-
-    def rnd(shape):
-        return torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
-
     lib = _lib.load()
-    name = a.workload
-    if name == "varlen":
-        H, Dh = 12, 64
-        lens = synth.draw_varlen_lengths(np.random.default_rng(SEED), 32768)
-        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    c = synth.config_by_name(OTHER_ATTENTION[a.workload])
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    H, Dh = c.heads, c.head_dim
+    table = slopes = None
+    if c.varlen_total:
+        inp = synth.draw_varlen(c.seed, c.varlen_total, H, Dh, num_buckets=c.num_buckets)
+        lens = inp.lengths
+        cu = torch.from_numpy(inp.cu_seqlens).to(dev)
         T = int(lens.sum())
-        q, k, v, do = (rnd((T, H, Dh)) for _ in range(4))
-        table = torch.randn((NB, H), generator=gen, device=dev) * 0.5
-        bias = fa.T5Bias(table, NB, MD, True)
+        q, k, v, do = (up(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+        table = torch.from_numpy(inp.table).to(dev)
+        bias = fa.T5Bias(table, c.num_buckets, c.max_distance, c.bidirectional)
         dtable = torch.empty_like(table)
         o = torch.empty_like(q)
         lse = torch.empty((H, T), dtype=torch.float32, device=dev)
@@ -314,98 +459,104 @@ def bench_other_attention(a):
         fwd_flops = 4.0 * H * Dh * float((lens.astype(np.float64) ** 2).sum())
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         p = _lib.FaVarlenBwdParams()
-        p.f = fa.api._varlen_params(q, k, v, o, lse, cu, mx, 1.0, False, bias, 0.0)
+        p.f = fa.api._varlen_params(q, k, v, o, lse, cu, mx, c.scale, c.causal, bias, 0.0)
         p.dout, p.dq, p.dk, p.dv, p.dtable = (do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                               dv.data_ptr(), dtable.data_ptr())
-        wsb = torch.empty(lib.fa_varlen_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8,
-                          device=dev)
+        wsb = torch.empty(max(1, lib.fa_varlen_bwd_workspace_size(ctypes.byref(p))),
+                          dtype=torch.uint8, device=dev)
 
         def step():
-            fa.fa_varlen_fwd(q, k, v, o, lse, cu, mx, scale=1.0, causal=False, bias=bias)
-            fa.fa_varlen_bwd(q, k, v, o, lse, do, dq, dk, dv, cu, mx, dtable, scale=1.0,
-                             causal=False, bias=bias, workspace=wsb)
-        workload = ("packed encoder self-attention fwd+bwd, 32768 tokens in "
-                    f"{len(lens)} sequences (lognormal lengths, 16..4096), H12 D64, "
-                    "bidirectional T5 bias, scale 1")
+            fa.fa_varlen_fwd(q, k, v, o, lse, cu, mx, scale=c.scale, causal=c.causal, bias=bias)
+            fa.fa_varlen_bwd(q, k, v, o, lse, do, dq, dk, dv, cu, mx, dtable, scale=c.scale,
+                             causal=c.causal, bias=bias, workspace=wsb)
+        workload = (f"packed encoder self-attention fwd+bwd, {T} tokens in {len(lens)} "
+                    "sequences (lognormal(6,1) lengths clipped to 16..4096, seed "
+                    f"{c.seed}), H{H} D{Dh}, bidirectional T5 bias (32 buckets, max distance "
+                    "128), scale 1")
         shape = {"tokens": T, "sequences": int(len(lens)), "heads": H, "head_dim": Dh,
-                 "causal": False}
+                 "causal": c.causal}
     else:
-        if name == "encoder":
-            Bq, Sq, H, Dh, causal, scale, rope = 16, 1024, 12, 64, False, 1.0, 0.0
-            table = torch.randn((NB, H), generator=gen, device=dev) * 0.5
-            bias, dtable = fa.T5Bias(table, NB, MD, True), torch.empty_like(table)
-            workload = ("encoder self-attention fwd+bwd, B16 H12 S1024 D64, bidirectional T5 "
-                        "bias (32 buckets, max distance 128), scale 1")
+        inp = synth.draw_dense(c.seed, c.batch, c.seqlen, H, Dh, num_buckets=c.num_buckets,
+                               with_table=c.bias == "t5")
+        q, k, v, do = (up(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+        Bq, Sq = c.batch, c.seqlen
+        rope = c.rope_base or 0.0
+        dtable = None
+        if c.bias == "t5":
+            table = torch.from_numpy(inp.table).to(dev)
+            bias = fa.T5Bias(table, c.num_buckets, c.max_distance, c.bidirectional)
+            dtable = torch.empty_like(table)
+            workload = (f"encoder self-attention fwd+bwd, B{Bq} H{H} S{Sq} D{Dh}, "
+                        "bidirectional T5 bias (32 buckets, max distance 128), scale 1")
+        elif c.bias == "alibi":
+            slopes = synth.alibi_slope_values(H)
+            bias = fa.ALiBi(torch.from_numpy(slopes).to(dev))
+            workload = (f"long-context causal attention fwd+bwd, B{Bq} H{H} S{Sq} D{Dh}, "
+                        "ALiBi slopes 2^(-8h/16), scale 1/sqrt(128)")
         else:
-            Bq, Sq, H, Dh, causal, scale = 2, 16384, 16, 128, True, 128 ** -0.5
-            dtable = None
-            if name == "alibi":
-                bias, rope = fa.ALiBi(fa.alibi_slopes(H, dev)), 0.0
-                workload = ("long-context causal attention fwd+bwd, B2 H16 S16384 D128, ALiBi "
-                            "slopes 2^(-8h/16), scale 1/sqrt(128)")
-            else:
-                bias, rope = None, 10000.0
-                workload = ("long-context causal attention fwd+bwd, B2 H16 S16384 D128, RoPE "
-                            "base 10000 in the kernels, scale 1/sqrt(128)")
-        q, k, v, do = (rnd((Bq, Sq, H, Dh)) for _ in range(4))
+            bias = None
+            workload = (f"long-context causal attention fwd+bwd, B{Bq} H{H} S{Sq} D{Dh}, RoPE "
+                        "base 10000 in the kernels, scale 1/sqrt(128)")
         o = torch.empty_like(q)
         lse = torch.empty((Bq, H, Sq), dtype=torch.float32, device=dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-        fwd_flops = 4.0 * Bq * H * Sq * Sq * Dh / (2.0 if causal else 1.0)
+        fwd_flops = 4.0 * Bq * H * Sq * Sq * Dh / (2.0 if c.causal else 1.0)
         p = _lib.FaBwdParams()
-        p.f = fa.api._fwd_params(q, k, v, o, lse, scale, causal, bias, rope)
+        p.f = fa.api._fwd_params(q, k, v, o, lse, c.scale, c.causal, bias, rope)
         p.dout, p.dq, p.dk, p.dv = do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
         p.dtable = None if dtable is None else dtable.data_ptr()
         wsb = torch.empty(max(1, lib.fa_bwd_workspace_size(ctypes.byref(p))), dtype=torch.uint8,
                           device=dev)
 
         def step():
-            fa.fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, bias=bias, rope_base=rope)
-            fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, scale=scale, causal=causal,
+            fa.fa_fwd(q, k, v, o, lse, scale=c.scale, causal=c.causal, bias=bias,
+                      rope_base=rope)
+            fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, scale=c.scale, causal=c.causal,
                       bias=bias, rope_base=rope, workspace=wsb)
-        shape = {"batch": Bq, "heads": H, "seq_len": Sq, "head_dim": Dh, "causal": causal}
+        shape = {"batch": Bq, "heads": H, "seq_len": Sq, "head_dim": Dh, "causal": c.causal}
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    hip = _hip()
-    kernels = {"fwd": _lib.FA_KERNEL_FWD, "bwd_dq": _lib.FA_KERNEL_BWD_DQ,
-               "bwd_dkv": _lib.FA_KERNEL_BWD_DKV}
-    evs = {n: [(_event(hip), _event(hip)) for _ in range(a.steps)] for n in kernels}
-    t_start, t_stop = _event(hip), _event(hip)
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    torch.cuda.synchronize()
-    hip.hipEventRecord(t_start, ctypes.c_void_p(stream))
-    for i in range(a.steps):
-        for n, kid in kernels.items():
-            lib.fa_set_kernel_timer(kid, evs[n][i][0], evs[n][i][1])
-        step()
-    hip.hipEventRecord(t_stop, ctypes.c_void_p(stream))
-    torch.cuda.synchronize()
-    for kid in kernels.values():
-        lib.fa_set_kernel_timer(kid, None, None)
-    ms_step = _elapsed(hip, t_start, t_stop) / a.steps
-    kernel_ms = {n: sum(_elapsed(hip, s0, s1) for s0, s1 in evs[n]) / a.steps for n in kernels}
-    algo = {"fwd": fwd_flops, "bwd_dq": 1.5 * fwd_flops, "bwd_dkv": 2.0 * fwd_flops}
-    dom = max(kernel_ms, key=kernel_ms.get)
-    achieved = algo[dom] / (kernel_ms[dom] * 1e-3) / 1e12
-    value = 3.5 * fwd_flops / (ms_step * 1e-3) / 1e12
-    line = {
-        "metric": f"attention fwd+bwd TFLOP/s, {name} workload",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": dict({"workload": workload, "parallelism": "none (one GPU)",
-                        "frac_of_peak": round(value / PEAK_TFLOPS, 4),
-                        "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()}}, **shape),
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
-        "cpu_baseline": None,
-    }
+    t = run_timed(a, step, _attn_kernels(), dev)
+    t["mfma_probe_tflops"] = mfma_probe(dev)
+    line = _attention_line(a, f"attention fwd+bwd TFLOP/s, {a.workload} workload ({c.name})",
+                           workload, shape, t, fwd_flops)
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = other_cpu_baseline(c, inp, slopes)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def other_cpu_baseline(c, inp, slopes):
+    """The oracle on a bounded sample of one side workload: whole heads
+    (dense) or whole sequences of a few heads (packed)."""
+    import numpy as np
+    import oracle
+    kw = dict(scale=c.scale, causal=c.causal, bias=c.bias, num_buckets=c.num_buckets,
+              max_distance=c.max_distance, bidirectional=c.bidirectional)
+    if c.bias == "t5":
+        kw["table"] = inp.table.astype(np.float64)
+    if c.bias == "alibi":
+        kw["slopes"] = slopes.astype(np.float64)
+    if c.rope_base:
+        kw["rope_base"] = c.rope_base
+    f = {n: inp.f64(n) for n in ("q", "k", "v", "do")}
+    if c.varlen_total:
+        heads = [0, 5, 11]
+        cu = inp.cu_seqlens
+        work = [lambda: oracle.varlen_attention_fwd(f["q"], f["k"], f["v"], cu, heads=heads,
+                                                    **kw),
+                lambda: oracle.varlen_attention_bwd(f["q"], f["k"], f["v"], f["do"], cu,
+                                                    heads=heads, **kw)]
+        flops = 3.5 * 4.0 * c.head_dim * float((inp.lengths.astype(np.float64) ** 2).sum())
+        return _time_oracle(work, flops * len(heads),
+                            f"all {len(inp.lengths)} sequences of heads {heads} of {c.heads}")
+    npairs = 1 if c.seqlen >= 16384 else 48
+    pairs = [(i % c.batch, (5 * i + 1) % c.heads) for i in range(npairs)]
+    work = [lambda: oracle.attention_fwd(f["q"], f["k"], f["v"], pairs=pairs, **kw),
+            lambda: oracle.attention_bwd(f["q"], f["k"], f["v"], f["do"], pairs=pairs, **kw)]
+    flops = 3.5 * 4.0 * c.seqlen * c.seqlen * c.head_dim / (2.0 if c.causal else 1.0)
+    return _time_oracle(work, flops * npairs,
+                        f"{npairs} of {c.batch * c.heads} (batch, head) pairs {pairs[:4]}"
+                        f"{'...' if npairs > 4 else ''} of the same workload")
 
 
 def main(argv=None):
@@ -416,7 +567,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=12)
     ap.add_argument("--bias", choices=("t5", "dense"), default="t5")
-    ap.add_argument("--workload", choices=("attention", "rmsnorm", "ce") + OTHER_ATTENTION,
+    ap.add_argument("--workload", choices=("attention", "rmsnorm", "ce") + tuple(OTHER_ATTENTION),
                     default="attention")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB before the "
@@ -460,7 +611,6 @@ def main(argv=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
 
     def step():
         fa.fa_fwd(q, k, v, o, lse, scale=1.0, causal=True, bias=bias)
@@ -474,56 +624,30 @@ def main(argv=None):
     p.dout, p.dq, p.dk, p.dv, p.dtable = (do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                           dv.data_ptr(), dtable.data_ptr())
     wsb = torch.empty(lib.fa_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=dev)
-    del ws
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
     if a.copy_mib > 0:
+        # one device-to-device copy of known size before the timed steps: the
+        # byte counters of this kernel calibrate FETCH_SIZE / WRITE_SIZE
         src = torch.ones(a.copy_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
-    hip = _hip()
-    kernels = {"fwd": _lib.FA_KERNEL_FWD, "bwd_dq": _lib.FA_KERNEL_BWD_DQ,
-               "bwd_dkv": _lib.FA_KERNEL_BWD_DKV}
-    evs = {n: [(_event(hip), _event(hip)) for _ in range(a.steps)] for n in kernels}
-    t_start, t_stop = _event(hip), _event(hip)
-    stream = torch.cuda.current_stream(dev).cuda_stream
-
-    torch.cuda.synchronize()
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventRecord(t_start, ctypes.c_void_p(stream))
-    wall0 = time.perf_counter()
-    for i in range(a.steps):
-        for n, kid in kernels.items():
-            lib.fa_set_kernel_timer(kid, evs[n][i][0], evs[n][i][1])
-        step()
-    hip.hipEventRecord(t_stop, ctypes.c_void_p(stream))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    for kid in kernels.values():
-        lib.fa_set_kernel_timer(kid, None, None)
-
-    ms_step = _elapsed(hip, t_start, t_stop) / a.steps
-    kernel_ms = {n: sum(_elapsed(hip, s0, s1) for s0, s1 in evs[n]) / a.steps for n in kernels}
+    t = run_timed(a, step, _attn_kernels(), dev)
+    t["mfma_probe_tflops"] = mfma_probe(dev)
     fwd_flops = 4.0 * B * H * S * S * D / 2.0
-    step_flops = 3.5 * fwd_flops
-    # per kernel, the products its own outputs need (each backward kernel
-    # recomputes S and dP): dq kernel S, dP, dQ; dkv kernel S, dP, dV, dK
-    algo = {"fwd": fwd_flops, "bwd_dq": 1.5 * fwd_flops, "bwd_dkv": 2.0 * fwd_flops}
-    dom = max(kernel_ms, key=kernel_ms.get)
-    achieved = algo[dom] / (kernel_ms[dom] * 1e-3) / 1e12
-    value = step_flops / (ms_step * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                "traffic": _traffic(dom)}
+    shape = {"batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True}
     if a.bias == "dense":
+        workload = ("causal decoder self-attention fwd+bwd with a dense bf16 bias matrix "
+                    "[1, H, S, S] shared by the batch and its fp32 gradient, B8 H12 S4096 D64, "
+                    "scale 1")
+        line = _attention_line(a, METRIC_DENSE, workload, shape, t, fwd_flops)
         # algorithmic bytes per launch: the bf16 tensors each kernel must read
         # and write once, plus one bias element per visible pair (bf16) and,
         # for dkv, one fp32 gradient element per visible pair and batch
+        kernel_ms = t["kernel_ms"]
+        dom = max(kernel_ms, key=kernel_ms.get)
         t_bytes = B * S * H * D * 2
         rows = B * H * S * 4
         pairs = B * H * S * (S + 1) / 2
@@ -531,40 +655,14 @@ def main(argv=None):
                   "bwd_dq": 6 * t_bytes + 2 * rows + pairs * 2,
                   "bwd_dkv": 6 * t_bytes + 2 * rows + pairs * (2 + 4)}
         gbs = abytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1), "peak": PEAK_GBS,
-                    "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None}
-
-    workload = ("causal decoder self-attention fwd+bwd with unidirectional T5 bias "
-                "(32 buckets, max distance 128), B8 H12 S4096 D64, scale 1")
-    if a.bias == "dense":
-        workload = ("causal decoder self-attention fwd+bwd with a dense bf16 bias matrix "
-                    "[1, H, S, S] shared by the batch and its fp32 gradient, B8 H12 S4096 D64, "
-                    "scale 1")
-    line = {
-        "metric": METRIC if a.bias == "t5" else METRIC_DENSE,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": workload,
-            "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
-            "parallelism": "none (one GPU)",
-            "frac_of_peak": round(value / PEAK_TFLOPS, 4),
-            "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
-            "fwd_tflops": round(fwd_flops / (kernel_ms["fwd"] * 1e-3) / 1e12, 2),
-            "host_wall_ms_per_step": round(wall / a.steps * 1e3, 4),
-        },
-        "roofline": roofline,
-        "cpu_baseline": None,
-    }
+        line["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1),
+                            "peak": PEAK_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
+                            "traffic": None}
+    else:
+        workload = ("causal decoder self-attention fwd+bwd with unidirectional T5 bias "
+                    "(32 buckets, max distance 128), B8 H12 S4096 D64, scale 1")
+        line = _attention_line(a, METRIC, workload, shape, t, fwd_flops)
+        line["roofline"]["traffic"] = _traffic(line["roofline"]["kernel"])
     if not a.no_cpu_baseline:
         pairs = [(i % B, (5 * i + 1) % H) for i in range(min(a.cpu_pairs, B * H))]
         dense = None

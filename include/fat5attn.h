@@ -291,6 +291,16 @@ fa_status fa_ce_bwd(const fa_ce_bwd_params *p, hipStream_t stream);
 fa_status fa_t5_buckets(int32_t qlen, int32_t klen, int32_t num_buckets, int32_t max_distance,
                         int32_t bidirectional, int32_t *out, hipStream_t stream);
 
+/* Benchmark hook: the chip's sustained dense bf16 MFMA rate, to set a
+ * kernel's achieved rate beside.  Launches FA_MFMA_PROBE_LANES lanes (8 per
+ * SIMD) whose waves each issue 4 * iters v_mfma_f32_32x32x16_bf16 with no
+ * memory traffic; time the call with events on `stream`.  *flops receives the
+ * call's flop count (2 * 32 * 32 * 16 per MFMA).  sink: device float
+ * [FA_MFMA_PROBE_LANES], overwritten.  FA_ERR_INVALID for iters outside
+ * [1, 1 << 20] or a NULL sink / flops. */
+#define FA_MFMA_PROBE_LANES (2048 * 256)
+fa_status fa_mfma_probe(int32_t iters, float *sink, double *flops, hipStream_t stream);
+
 /* Kernels that fa_set_kernel_timer can bracket. */
 typedef enum {
   FA_KERNEL_FWD = 0,       /* the attention forward kernel                       */

@@ -248,6 +248,15 @@ def test_t5_buckets_checks(lib):
     assert lib.fa_t5_buckets(0, 0, 32, 128, 1, None, None) == _lib.FA_OK
 
 
+def test_mfma_probe_checks(lib):
+    flops = ctypes.c_double()
+    assert lib.fa_mfma_probe(0, 0x1000, ctypes.byref(flops), None) == _lib.FA_ERR_INVALID
+    assert lib.fa_mfma_probe((1 << 20) + 1, 0x1000, ctypes.byref(flops),
+                             None) == _lib.FA_ERR_INVALID
+    assert lib.fa_mfma_probe(10, None, ctypes.byref(flops), None) == _lib.FA_ERR_INVALID
+    assert lib.fa_mfma_probe(10, 0x1000, None, None) == _lib.FA_ERR_INVALID
+
+
 def test_rmsnorm_checks_and_workspace(lib):
     p = _lib.FaRmsnormBwdParams()
     p.f.rows, p.f.dim, p.f.eps = 100, 768, 1e-6
