@@ -19,6 +19,9 @@ Sources (the pages this method is described on):
   kernels also serve ALiBi and RoPE.
 * Blog on DataCollatorWithFlattening and flash_attn_varlen_func: packed
   batches attend only within each example.
+* FAT5 report, note under "Noyau CUDA": FIRE is among the encodings the
+  kernels serve; its definition is taken from the FIRE paper the note cites
+  (``oracle.fire``).
 * FAT5 report, Triton-kernel section and "Torch vs Triton": the fused
   RMSNorm layer and cross-entropy loss with z-loss (``oracle.norm_loss``).
 
@@ -40,6 +43,12 @@ from .attention import (  # noqa: F401
     varlen_attention_fwd,
     varlen_attention_bwd,
     segment_ids,
+)
+from .fire import (  # noqa: F401
+    fire_bias,
+    fire_theta_grad,
+    fire_x,
+    theta_size as fire_theta_size,
 )
 from .norm_loss import (  # noqa: F401
     cross_entropy_bwd,

@@ -41,6 +41,9 @@ Readings taken where the pages are silent:
   adds it to S.  Read here as one [S, S] matrix per (batch, head), given as
   [Bb, H, S, S] with Bb = 1 (shared by the whole batch) or Bb = B; its
   gradient is dS, summed over the batch when Bb = 1.
+* FIRE: the learned bias f_theta(psi(i - j) / psi(max(L, i))), causal
+  attention only; the reading is in ``oracle.fire``.  Its gradient is the
+  flat d(theta), summed over the batch and heads.
 * Causal: key j is visible to query i iff j <= i.
 * Packed batches: a query attends only keys of its own sequence; positions are
   local to the sequence.
@@ -58,6 +61,8 @@ import math
 from typing import Optional
 
 import numpy as np
+
+from .fire import fire_bias, fire_theta_grad
 
 # --------------------------------------------------------------------------
 # Position encodings
@@ -143,14 +148,20 @@ def rope_unrotate(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarr
 
 def bias_matrix(seqlen: int, head: int, *, bias: str, table=None, num_buckets: int = 32,
                 max_distance: int = 128, bidirectional: bool = True,
-                slopes=None, dense=None) -> Optional[np.ndarray]:
+                slopes=None, dense=None, fire=None,
+                fire_hidden: int = 0) -> Optional[np.ndarray]:
     """Additive bias [S, S] (rows = query i, columns = key j) for one head, or
     None when there is no bias.  ``dense`` is the head's own [S, S] matrix
-    (bias "dense")."""
+    (bias "dense"); ``fire`` the flat FIRE parameter vector with
+    ``fire_hidden`` hidden units (bias "fire", see oracle.fire)."""
     if bias == "none":
         return None
     if bias == "dense":
         return np.asarray(dense, dtype=np.float64)
+    if bias == "fire":
+        K = int(fire_hidden)
+        H = (len(fire) - 2 * K - 2) // (K + 1)
+        return fire_bias(seqlen, fire, H, K, head=head)
     i = np.arange(seqlen)[:, None]
     j = np.arange(seqlen)[None, :]
     if bias == "t5":
@@ -162,8 +173,11 @@ def bias_matrix(seqlen: int, head: int, *, bias: str, table=None, num_buckets: i
 
 
 def _scores(qh, kh, head, *, scale, causal, bias, table, num_buckets, max_distance,
-            bidirectional, slopes, rope_base, rope_round=True, dense=None):
+            bidirectional, slopes, rope_base, rope_round=True, dense=None, fire=None,
+            fire_hidden=0):
     S = qh.shape[0]
+    if bias == "fire" and not causal:
+        raise ValueError("FIRE is defined for causal attention (key at or before the query)")
     pos = np.arange(S)
     if rope_base is not None:
         qh = rope_rotate(qh, pos, rope_base)
@@ -173,7 +187,7 @@ def _scores(qh, kh, head, *, scale, causal, bias, table, num_buckets, max_distan
     s = scale * (qh @ kh.T)
     bm = bias_matrix(S, head, bias=bias, table=table, num_buckets=num_buckets,
                      max_distance=max_distance, bidirectional=bidirectional, slopes=slopes,
-                     dense=dense)
+                     dense=dense, fire=fire, fire_hidden=fire_hidden)
     if bm is not None:
         s = s + bm
     if causal:
@@ -195,7 +209,7 @@ def _softmax_rows(s):
 
 def head_fwd(qh, kh, vh, head, *, scale=1.0, causal=False, bias="none", table=None,
              num_buckets=32, max_distance=128, bidirectional=True, slopes=None,
-             rope_base=None, rope_round=True, dense=None):
+             rope_base=None, rope_round=True, dense=None, fire=None, fire_hidden=0):
     """Forward for one head: qh, kh, vh float64 [S, D] -> (O [S, D], LSE [S]).
 
     ``rope_round=False`` skips the bf16 rounding of the rotated q, k: the
@@ -204,17 +218,18 @@ def head_fwd(qh, kh, vh, head, *, scale=1.0, causal=False, bias="none", table=No
     s, _, _ = _scores(qh, kh, head, scale=scale, causal=causal, bias=bias, table=table,
                       num_buckets=num_buckets, max_distance=max_distance,
                       bidirectional=bidirectional, slopes=slopes, rope_base=rope_base,
-                      rope_round=rope_round, dense=dense)
+                      rope_round=rope_round, dense=dense, fire=fire, fire_hidden=fire_hidden)
     P, lse = _softmax_rows(s)
     return P @ vh, lse
 
 
 def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", table=None,
              num_buckets=32, max_distance=128, bidirectional=True, slopes=None,
-             rope_base=None, rope_round=True, dense=None, dlse=None):
+             rope_base=None, rope_round=True, dense=None, fire=None, fire_hidden=0, dlse=None):
     """Backward for one head -> (dq, dk, dv [S, D], bias gradient): the bias
     gradient is dtable_h [num_buckets] for T5, dS [S, S] for a dense bias,
-    None otherwise.
+    this head's part of d(theta) (the flat FIRE vector) for FIRE, None
+    otherwise.
 
     ``dlse`` [S] (optional) is the loss gradient with respect to the returned
     LSE.  LSE_i is the log-sum-exp of row i of S', whose derivative with
@@ -223,7 +238,7 @@ def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", tab
     s, qr, kr = _scores(qh, kh, head, scale=scale, causal=causal, bias=bias, table=table,
                         num_buckets=num_buckets, max_distance=max_distance,
                         bidirectional=bidirectional, slopes=slopes, rope_base=rope_base,
-                        rope_round=rope_round, dense=dense)
+                        rope_round=rope_round, dense=dense, fire=fire, fire_hidden=fire_hidden)
     P, _ = _softmax_rows(s)
     dP = doh @ vh.T
     Drow = (P * dP).sum(axis=1)
@@ -245,6 +260,10 @@ def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", tab
         dtab = np.bincount(b.ravel(), weights=dS.ravel(), minlength=num_buckets)
     if bias == "dense":
         dtab = dS
+    if bias == "fire":
+        K = int(fire_hidden)
+        H = (len(fire) - 2 * K - 2) // (K + 1)
+        dtab = fire_theta_grad(dS, head, fire, H, K)
     return dq, dk, dv, dtab
 
 
@@ -255,7 +274,7 @@ def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", tab
 
 def _kw(kw):
     keys = ("scale", "causal", "bias", "table", "num_buckets", "max_distance",
-            "bidirectional", "slopes", "rope_base", "rope_round")
+            "bidirectional", "slopes", "rope_base", "rope_round", "fire", "fire_hidden")
     return {k: kw[k] for k in keys if k in kw}
 
 
@@ -303,6 +322,8 @@ def attention_bwd(q, k, v, do, pairs=None, dlse=None, **kw):
         dtable = np.zeros((nb, H))
     elif kw.get("bias") == "dense":
         dtable = np.zeros(kw["dense"].shape)
+    elif kw.get("bias") == "fire":
+        dtable = np.zeros(len(kw["fire"]))
     todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in todo:
         a, bb, c, dt = head_bwd(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], h,
@@ -313,6 +334,8 @@ def attention_bwd(q, k, v, do, pairs=None, dlse=None, **kw):
             dtable[:, h] += dt
         elif kw.get("bias") == "dense":
             dtable[b if dtable.shape[0] > 1 else 0, h] += dt
+        elif kw.get("bias") == "fire":
+            dtable += dt
     return dq, dk, dv, dtable
 
 
@@ -357,6 +380,8 @@ def varlen_attention_bwd(q, k, v, do, cu_seqlens, seqs=None, heads=None, dlse=No
     dv = np.full(q.shape, np.nan)
     nb = kw.get("num_buckets", 32)
     dtable = np.zeros((nb, H)) if kw.get("bias") == "t5" else None
+    if kw.get("bias") == "fire":
+        dtable = np.zeros(len(kw["fire"]))
     seqs = range(len(cu) - 1) if seqs is None else seqs
     heads = range(H) if heads is None else heads
     for s in seqs:
@@ -367,6 +392,8 @@ def varlen_attention_bwd(q, k, v, do, cu_seqlens, seqs=None, heads=None, dlse=No
             r = head_bwd(q[a:e, h], k[a:e, h], v[a:e, h], do[a:e, h], h,
                          dlse=None if dlse is None else dlse[h, a:e], **_kw(kw))
             dq[a:e, h], dk[a:e, h], dv[a:e, h] = r[0], r[1], r[2]
-            if dtable is not None:
+            if kw.get("bias") == "fire":
+                dtable += r[3]
+            elif dtable is not None:
                 dtable[:, h] += r[3]
     return dq, dk, dv, dtable

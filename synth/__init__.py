@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     VarlenInputs,
     draw_dense,
     draw_dense_bias,
+    draw_fire_theta,
     draw_rmsnorm,
     draw_cross_entropy,
     draw_varlen,

@@ -10,6 +10,7 @@ Recipe (the same for every consumer):
   those exact bfloat16 values.
 * Then the T5 bias table is drawn as float32 ``normal(0, 0.5)`` of shape
   ``[num_buckets, H]``.
+* FIRE parameters come from their own seeded draw (``draw_fire_theta``).
 """
 from __future__ import annotations
 
@@ -173,3 +174,20 @@ def draw_varlen(seed: int, total: int, H: int, D: int, *, num_buckets: int = 32,
     table = (rng.normal(0.0, 0.5, size=(num_buckets, H)).astype(np.float32)
              if with_table else None)
     return VarlenInputs(lengths, cu, q, k, v, do, table)
+
+
+def draw_fire_theta(seed: int, heads: int, hidden: int = 32, c: float = 0.1,
+                    threshold: float = 512.0) -> np.ndarray:
+    """FIRE parameters as one float32 vector [w1 (K), b1 (K), w2 (H*K), b2 (H),
+    c, L]: w1 ~ N(0, 4), each hidden unit's kink -b1/w1 uniform on
+    (-0.5, 1.5) (so about half of them fall inside the [0, 1] range of the
+    normalised distance), w2 ~ N(0, 1/K), b2 ~ N(0, 0.25), then c and L as
+    given."""
+    rng = np.random.default_rng(seed)
+    K = hidden
+    w1 = 2.0 * rng.standard_normal(K)
+    kink = rng.uniform(-0.5, 1.5, K)
+    b1 = -w1 * kink
+    w2 = rng.standard_normal((heads, K)) / np.sqrt(K)
+    b2 = 0.5 * rng.standard_normal(heads)
+    return np.concatenate([w1, b1, w2.ravel(), b2, [c, threshold]]).astype(np.float32)
