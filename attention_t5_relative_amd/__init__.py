@@ -8,6 +8,8 @@ raises if ``libfat5attn.so`` has not been built (there is no fallback path).
 from .api import (  # noqa: F401
     ALiBi,
     DenseBias,
+    FireBias,
+    fire_theta_size,
     T5Bias,
     alibi_slopes,
     attention,

@@ -32,6 +32,8 @@ FA_BIAS_NONE = 0
 FA_BIAS_T5 = 1
 FA_BIAS_ALIBI = 2
 FA_BIAS_DENSE = 3
+FA_BIAS_FIRE = 4
+FA_FIRE_MAX_HIDDEN = 64
 
 c_i32 = ctypes.c_int32
 c_f32 = ctypes.c_float
@@ -41,7 +43,7 @@ c_ptr = ctypes.c_void_p
 class FaBias(ctypes.Structure):
     _fields_ = [("mode", c_i32), ("num_buckets", c_i32), ("max_distance", c_i32),
                 ("bidirectional", c_i32), ("table", c_ptr), ("slopes", c_ptr),
-                ("dense", c_ptr), ("dense_batch", c_i32), ("reserved2", c_i32)]
+                ("dense", c_ptr), ("dense_batch", c_i32), ("fire_hidden", c_i32)]
 
 
 class FaFwdParams(ctypes.Structure):

@@ -42,7 +42,21 @@ class DenseBias:
     matrix: torch.Tensor
 
 
-BiasSpec = Optional[Union[T5Bias, ALiBi, DenseBias]]
+@dataclass
+class FireBias:
+    """FIRE (causal attention only): theta fp32 [2K + H*K + H + 2] =
+    [w1 (K), b1 (K), w2 (H*K), b2 (H), c, L] with K = hidden; the bias of query
+    i, key j <= i is b2_h + sum_k w2_hk relu(w1_k x + b1_k),
+    x = log(c (i - j) + 1) / log(c max(L, i) + 1)."""
+    theta: torch.Tensor
+    hidden: int = 32
+
+
+def fire_theta_size(heads: int, hidden: int) -> int:
+    return 2 * hidden + heads * hidden + heads + 2
+
+
+BiasSpec = Optional[Union[T5Bias, ALiBi, DenseBias, FireBias]]
 
 
 def alibi_slopes(heads: int, device=None) -> torch.Tensor:
@@ -100,8 +114,14 @@ def _bias_struct(bias: BiasSpec, heads: int, device, batch: Optional[int] = None
         b.mode = _lib.FA_BIAS_DENSE
         b.dense = m.data_ptr()
         b.dense_batch = m.shape[0]
+    elif isinstance(bias, FireBias):
+        _need(bias.theta, "bias.theta", torch.float32, (fire_theta_size(heads, bias.hidden),),
+              device)
+        b.mode = _lib.FA_BIAS_FIRE
+        b.table = bias.theta.data_ptr()
+        b.fire_hidden = int(bias.hidden)
     else:
-        raise TypeError("bias must be None, T5Bias, ALiBi or DenseBias")
+        raise TypeError("bias must be None, T5Bias, ALiBi, DenseBias or FireBias")
     return b
 
 
@@ -111,6 +131,8 @@ def _dbias_shape(bias: BiasSpec, heads: int):
         return (bias.num_buckets, heads)
     if isinstance(bias, DenseBias):
         return tuple(bias.matrix.shape)
+    if isinstance(bias, FireBias):
+        return (fire_theta_size(heads, bias.hidden),)
     return None
 
 
@@ -210,7 +232,8 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, dlse=None, scale=1
            causal=False, bias: BiasSpec = None, rope_base=0.0, workspace=None,
            stream=None) -> None:
     """Dense backward into dq, dk, dv [B,S,H,D] bf16 and the bias gradient
-    ``dtable``: fp32 [nb,H] for T5Bias, fp32 [Bb,H,S,S] for DenseBias.
+    ``dtable``: fp32 [nb,H] for T5Bias, fp32 [Bb,H,S,S] for DenseBias, d(theta)
+    for FireBias.
     ``dlse`` (optional, fp32 [B,H,S]) is the gradient with respect to lse."""
     lib = _lib.load()
     p = _bwd_params(q, k, v, o, lse, dout, dq, dk, dv, dtable, dlse, scale, causal, bias,
@@ -232,15 +255,16 @@ def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, dtable=None, *, dlse=None,
 def fa_varlen_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, max_seqlen, dtable=None, *,
                   dlse=None, scale=1.0, causal=False, bias: BiasSpec = None, rope_base=0.0,
                   workspace=None, stream=None) -> None:
-    """Packed backward into dq, dk, dv [T,H,D] bf16 and dtable [nb,H] fp32;
-    ``dlse`` (optional, fp32 [H,T]) is the gradient with respect to lse."""
+    """Packed backward into dq, dk, dv [T,H,D] bf16 and the bias gradient
+    dtable (fp32 [nb,H] for T5Bias, d(theta) for FireBias); ``dlse``
+    (optional, fp32 [H,T]) is the gradient with respect to lse."""
     lib = _lib.load()
     p = FaVarlenBwdParams()
     p.f = _varlen_params(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, bias, rope_base)
     for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _need(t, name, torch.bfloat16, q.shape, q.device)
     if dtable is not None:
-        _need(dtable, "dtable", torch.float32, (p.f.bias.num_buckets, q.shape[1]), q.device)
+        _need(dtable, "dtable", torch.float32, _dbias_shape(bias, q.shape[1]), q.device)
     if dlse is not None:
         _need(dlse, "dlse", torch.float32, lse.shape, q.device)
     p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
@@ -307,6 +331,8 @@ class _Attention(torch.autograd.Function):
             dtable = torch.empty_like(ctx.bias.table)
         if isinstance(ctx.bias, DenseBias) and ctx.bias.matrix.requires_grad:
             dtable = torch.empty(ctx.bias.matrix.shape, dtype=torch.float32, device=q.device)
+        if isinstance(ctx.bias, FireBias) and ctx.bias.theta.requires_grad:
+            dtable = torch.empty_like(ctx.bias.theta)
         fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, dlse=dlse, scale=ctx.scale,
                causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
         if isinstance(ctx.bias, DenseBias) and dtable is not None:
@@ -316,11 +342,13 @@ class _Attention(torch.autograd.Function):
 
 def attention(q, k, v, *, bias: BiasSpec = None, causal=False, scale=1.0, rope_base=0.0,
               return_lse=False):
-    """Exact attention with optional T5 / ALiBi / dense bias and RoPE; q, k, v
-    [B,S,H,D] bf16."""
+    """Exact attention with optional T5 / ALiBi / FIRE / dense bias and RoPE;
+    q, k, v [B,S,H,D] bf16."""
     table = bias.table if isinstance(bias, T5Bias) else None
     if isinstance(bias, DenseBias):
         table = bias.matrix
+    if isinstance(bias, FireBias):
+        table = bias.theta
     slopes = bias.slopes if isinstance(bias, ALiBi) else None
     o, lse = _Attention.apply(q, k, v, table, slopes, bias, scale, causal, rope_base)
     return (o, lse) if return_lse else o
@@ -348,6 +376,8 @@ class _VarlenAttention(torch.autograd.Function):
         dtable = None
         if isinstance(ctx.bias, T5Bias) and ctx.bias.table.requires_grad:
             dtable = torch.empty_like(ctx.bias.table)
+        if isinstance(ctx.bias, FireBias) and ctx.bias.theta.requires_grad:
+            dtable = torch.empty_like(ctx.bias.theta)
         fa_varlen_bwd(q, k, v, o, lse, do, dq, dk, dv, cu, ctx.max_seqlen, dtable, dlse=dlse,
                       scale=ctx.scale, causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
         return dq, dk, dv, dtable, None, None, None, None, None, None
@@ -357,6 +387,8 @@ def varlen_attention(q, k, v, cu_seqlens, max_seqlen, *, bias: BiasSpec = None, 
                      scale=1.0, rope_base=0.0, return_lse=False):
     """Packed attention; q, k, v [T,H,D] bf16, cu_seqlens int32 [nseq+1]."""
     table = bias.table if isinstance(bias, T5Bias) else None
+    if isinstance(bias, FireBias):
+        table = bias.theta
     o, lse = _VarlenAttention.apply(q, k, v, table, cu_seqlens, max_seqlen, bias, scale, causal,
                                     rope_base)
     return (o, lse) if return_lse else o

@@ -177,9 +177,17 @@ fa_status check_common(int heads, int head_dim, int causal, float scale, float r
         return fail(FA_ERR_UNSUPPORTED, "a dense bias needs seqlen <= %d (got %lld)",
                     fa::kMaxDenseSeqlen, maxlen);
       break;
+    case FA_BIAS_FIRE:
+      if (!bias.table) return fail(FA_ERR_INVALID, "bias.table (FIRE theta) is NULL");
+      if (bias.fire_hidden < 1 || bias.fire_hidden > fa::kFireMaxHidden)
+        return fail(FA_ERR_UNSUPPORTED, "bias.fire_hidden=%d outside [1, %d]", bias.fire_hidden,
+                    fa::kFireMaxHidden);
+      if (causal != 1)
+        return fail(FA_ERR_UNSUPPORTED, "FIRE is defined for causal attention only");
+      return FA_OK;
     default: return fail(FA_ERR_INVALID, "bias.mode=%d is not a fa_bias_mode", bias.mode);
   }
-  if (bias.reserved2 != 0) return fail(FA_ERR_INVALID, "bias.reserved2 must be 0");
+  if (bias.fire_hidden != 0) return fail(FA_ERR_INVALID, "bias.fire_hidden must be 0 unless FIRE");
   return FA_OK;
 }
 
@@ -203,7 +211,8 @@ fa_status check_fwd_impl(const fa_fwd_params *p) {
     if (p->seqlen > fa::kMaxDenseSeqlen)
       return fail(FA_ERR_UNSUPPORTED, "a dense bias needs seqlen <= %d (got %d)",
                   fa::kMaxDenseSeqlen, p->seqlen);
-    if (p->bias.reserved2 != 0) return fail(FA_ERR_INVALID, "bias.reserved2 must be 0");
+    if (p->bias.fire_hidden != 0)
+      return fail(FA_ERR_INVALID, "bias.fire_hidden must be 0 unless FIRE");
     return FA_OK;
   }
   return check_common(p->heads, p->head_dim, p->causal, p->scale, p->rope_base, p->bias,
@@ -256,6 +265,7 @@ fa::Problem make_problem(const fa_fwd_params &f) {
   }
   if (p.bias == FA_BIAS_T5)
     p.t5 = geometry(f.bias.num_buckets, f.bias.max_distance, f.bias.bidirectional);
+  if (p.bias == FA_BIAS_FIRE) p.fire_hidden = f.bias.fire_hidden;
   return p;
 }
 
@@ -276,6 +286,7 @@ fa::Problem make_problem(const fa_varlen_fwd_params &f) {
   p.slopes = f.bias.slopes;
   if (p.bias == FA_BIAS_T5)
     p.t5 = geometry(f.bias.num_buckets, f.bias.max_distance, f.bias.bidirectional);
+  if (p.bias == FA_BIAS_FIRE) p.fire_hidden = f.bias.fire_hidden;
   return p;
 }
 
@@ -299,7 +310,7 @@ size_t rope_table_bytes(const fa::Problem &p) {
 }
 
 struct FwdLayout {
-  size_t krot = 0, rope_cs = 0, prefix = 0, sched = 0, total = 0;
+  size_t krot = 0, rope_cs = 0, prefix = 0, sched = 0, fire_tab = 0, total = 0;
   int nsched = 0;
 };
 
@@ -319,13 +330,14 @@ FwdLayout fwd_layout(const fa::Problem &p) {
     L.prefix = c.take((size_t)fa::sched_prefix_ints(p.nbatch) * 4);
     L.sched = c.take((size_t)L.nsched * 16);
   }
+  if (p.bias == FA_BIAS_FIRE) L.fire_tab = c.take(fa::fire_tab_floats(p.heads) * 4);
   L.total = c.off;
   return L;
 }
 
 struct BwdLayout {
   size_t qrot = 0, krot = 0, rope_cs = 0, delta = 0, part = 0, prefix = 0, sched = 0,
-         dense_ws = 0, total = 0;
+         dense_ws = 0, fire_tab = 0, fire_g = 0, total = 0;
   int nsched = 0;
   bool has_part = false;
   bool has_dense_ws = false;   // per-batch dense bias gradients, summed afterwards
@@ -350,10 +362,15 @@ BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
     L.prefix = c.take((size_t)fa::sched_prefix_ints(p.nbatch) * 4);
     L.sched = c.take((size_t)L.nsched * 16);
   }
-  L.has_part = want_dtable && p.bias == FA_BIAS_T5;
+  L.has_part = want_dtable && (p.bias == FA_BIAS_T5 || p.bias == FA_BIAS_FIRE);
   if (L.has_part) {
-    const int nb = p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp;
+    const int nb = p.bias == FA_BIAS_FIRE ? fa::kFireGradRows
+                                          : (p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp);
     L.part = c.take((size_t)fa::bwd_num_parts(p, L.nsched) * nb * 4);
+  }
+  if (p.bias == FA_BIAS_FIRE) {
+    L.fire_tab = c.take(fa::fire_tab_floats(p.heads) * 4);
+    if (want_dtable) L.fire_g = c.take((size_t)fa::kFireGradRows * p.heads * 4);
   }
   L.has_dense_ws = want_dtable && p.bias == FA_BIAS_DENSE && p.dense_batch == 1 && p.nbatch > 1;
   if (L.has_dense_ws)
@@ -374,8 +391,13 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
     return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 ws == nullptr ? (size_t)0 : ws_bytes);
   if (p.total == 0 || (!p.varlen && (p.nbatch == 0 || p.seqlen == 0))) return FA_OK;
-  fa::FwdBuffers b{q, k, v, o, lse, nullptr};
+  fa::FwdBuffers b{q, k, v, o, lse, nullptr, nullptr};
   hipError_t e;
+  if (p.bias == FA_BIAS_FIRE) {
+    e = fa::launch_fire_setup(p, at<float>(ws, L.fire_tab), s);
+    if (e != hipSuccess) return hip_fail(e, "FIRE segment table");
+    b.fire_tab = at<float>(ws, L.fire_tab);
+  }
   if (p.rope_base > 0.f) {
     e = fa::launch_rope_table(p, at<double2>(ws, L.rope_cs), s);
     if (e == hipSuccess)
@@ -407,10 +429,16 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   hipError_t e;
   const bool t5grad = dtable != nullptr && p.bias == FA_BIAS_T5;
   const bool densegrad = dtable != nullptr && p.bias == FA_BIAS_DENSE;
+  const bool firegrad = dtable != nullptr && p.bias == FA_BIAS_FIRE;
   const int nb = p.bias == FA_BIAS_T5 ? (p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp) : 0;
   if (p.total == 0 || (!p.varlen && (p.nbatch == 0 || p.seqlen == 0))) {
     if (t5grad) {
       e = fa::launch_fill_f32(dtable, (size_t)nb * p.heads, 0.f, s);
+      if (e != hipSuccess) return hip_fail(e, "fill");
+    }
+    if (firegrad) {
+      e = fa::launch_fill_f32(dtable, (size_t)fa::fire_theta_floats(p.heads, p.fire_hidden), 0.f,
+                              s);
       if (e != hipSuccess) return hip_fail(e, "fill");
     }
     if (densegrad) {   // an empty batch contributes nothing to a shared matrix
@@ -434,6 +462,12 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   b.delta = at<float>(ws, L.delta);
   b.part = L.has_part ? at<float>(ws, L.part) : nullptr;
   b.dtable = t5grad ? dtable : nullptr;
+  if (p.bias == FA_BIAS_FIRE) {
+    e = fa::launch_fire_setup(p, at<float>(ws, L.fire_tab), s);
+    if (e != hipSuccess) return hip_fail(e, "FIRE segment table");
+    b.fire_tab = at<float>(ws, L.fire_tab);
+    b.fire_g = firegrad ? at<float>(ws, L.fire_g) : nullptr;
+  }
   b.dbias = densegrad ? dtable : nullptr;
   b.dbias_batch = L.has_dense_ws ? at<float>(ws, L.dense_ws) : nullptr;
   if (densegrad && p.causal && !L.has_dense_ws) {
@@ -466,6 +500,10 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   if (e != hipSuccess) return hip_fail(e, "backward dkv kernel");
   e = fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdReduce, s);
   if (e != hipSuccess) return hip_fail(e, "table-gradient reduction");
+  if (firegrad) {
+    e = fa::launch_fire_grad(p, b.fire_g, dtable, s);
+    if (e != hipSuccess) return hip_fail(e, "FIRE parameter gradient");
+  }
   if (L.has_dense_ws) {
     e = fa::launch_batch_sum(b.dbias_batch, dtable, p.nbatch, p.heads, p.seqlen, p.causal != 0,
                              s);

@@ -45,9 +45,10 @@ struct BwdArgs {
   const float *dlse;       // gradient with respect to lse (lse layout) or nullptr
   uint16_t *dq, *dk, *dv;  // bf16 outputs
   const double2 *rope_cs;   // RoPE: (cos, sin) [seqlen, D/2], or nullptr
+  const float *fire_tab;   // FIRE segment table (fa_internal.h), or nullptr
   float *delta;            // -D_i, same layout as lse
   float *nls;              // -lse_i / scale, same layout (seed of the dkv kernel's S)
-  float *part;             // [nb, nwg] table-gradient partials
+  float *part;             // [nb, nwg] table-gradient partials (FIRE: nb = kFireGradRows)
   const int4 *sched;       // packed batches: {token0, length, head, tile}
   const float *table, *slopes;
   const uint16_t *dense;   // dense bias bf16 [dense_batch, H, S, S]
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
   __shared__ __attribute__((aligned(16))) uint16_t dost[kDoInLds ? BR * D : 8];
   __shared__ float lut_mem[BIAS == kBiasT5 ? 2 * (kMaxDistance + kLutPad) + 1 : 1];
   const float *const lut = lut_mem + (BIAS == kBiasT5 ? a.t5.sat + kLutPad : 0);
+  __shared__ float fire_mem[BIAS == kBiasFire ? kFireLds : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -231,6 +233,13 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
   if constexpr (BIAS == kBiasDense) {
     const size_t mat = (size_t)(a.dense_batch == 1 ? 0 : w.b) * a.heads + h;
     rbias = make_rsrc(a.dense + mat * L * L, (uint32_t)L * (uint32_t)L * 2u);
+  }
+  FireLane fl;
+  if constexpr (BIAS == kBiasFire) {
+    fire_load(a.fire_tab, h, fire_mem, tid, NT);
+    fl.tab = fire_mem;
+    fl.c = a.fire_tab[2];
+    fl.inv = fire_row_inv(fl.c, a.fire_tab[3], myrow);
   }
 
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
@@ -324,10 +333,10 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
       bool fast;
       if constexpr (NKB == 2)
         fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut, slope_l2,
-                                          bconst, bv);
+                                          bconst, bv, fl);
       else
         fast = score_block_T<BIAS, CAUSAL>(sacc[0], j0, wrow0, il, hl, L, c, sat, lut,
-                                           slope_l2, bconst, bv[0]);
+                                           slope_l2, bconst, bv[0], fl);
       const float cc = fast ? c : 1.f;
       const float sub = bconst - lse2;
       // per 16-key group: P o (dP - Dc) as hi + lo fragments and P as bf16,
@@ -424,6 +433,11 @@ constexpr int dkv_wgs() {
   return D == 64 || BIAS == kBiasAlibi || BIAS == kBiasNone ? 2 : 1;
 }
 
+// FIRE in the key-parallel kernel: per query block, each row's normaliser
+// 1 / log2(E_i) (E_i = c max(L, i) + 1), the weight max(L, i) / (E_i ln E_i)
+// of dx/dc and the flag i < L (dx/dL), kFireRowVals floats per row.
+constexpr int kFireRowVals = 3;
+
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool DBIAS>
 __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const BwdArgs a) {
   constexpr int QB = DkvTile<D>::QB;
@@ -437,6 +451,10 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
   __shared__ __attribute__((aligned(16))) float ndls[2][64];
   __shared__ float ubin[4][2];
   extern __shared__ __attribute__((aligned(16))) float dyn[];
+  constexpr bool kFire = BIAS == kBiasFire;
+  __shared__ float fire_mem[kFire ? kFireLds : 1];
+  __shared__ __attribute__((aligned(16))) float fire_rows[kFire ? 2 * kFireRowVals * 64 : 1];
+  __shared__ float fire_acc[kFire && DBIAS ? 4 * kFireGradRows : 1];   // per wave
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -509,6 +527,43 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
   }
   float *const mybins = bins + wave * nbin;
   float *const mytile = tiles + wave * (32 * kTilePitch);
+  FireLane fl;
+  float fire_L = 0.f;
+  if constexpr (kFire) {
+    fire_load(a.fire_tab, h, fire_mem, tid, NT);
+    fl.tab = fire_mem;
+    fl.c = a.fire_tab[2];
+    fire_L = a.fire_tab[3];
+    if constexpr (DBIAS)
+      for (int i = tid; i < 4 * kFireGradRows; i += NT) fire_acc[i] = 0.f;
+  }
+  // FIRE row values of the query block at q0 into buffer buf
+  auto fire_fill_rows = [&](int q0, int buf) {
+    if constexpr (kFire) {
+      if (tid < QB) {
+        const int i = q0 + tid;
+        const float m = fmaxf(fire_L, (float)i);
+        const float E = fmaf(fl.c, m, 1.f);
+        const float lE = __builtin_amdgcn_logf(E);
+        float *rw = fire_rows + buf * (kFireRowVals * 64);
+        rw[tid] = 1.f / lE;
+        rw[64 + tid] = m / (E * lE * kLn2);
+        rw[128 + tid] = (float)i < fire_L ? 1.f : 0.f;
+      }
+    }
+  };
+  // FIRE gradient sums of the segment s_cur (fast lanes keep them in
+  // registers until their segment changes) and the flush into this wave's
+  // LDS sums
+  float fr[kFireTerms] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  int s_cur = -1;
+  float *const my_acc = fire_acc + wave * kFireGradRows;
+  auto fire_flush = [&](int sg, const float (&v)[kFireTerms]) {
+    if constexpr (kFire && DBIAS) {
+#pragma unroll
+      for (int q = 0; q < kFireTerms; ++q) atomicAdd(&my_acc[sg * kFireTerms + q], v[q]);
+    }
+  };
 
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -553,7 +608,10 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
     tro[db][1] = swz_tr_off<D>(lane, 1, db);
   }
 
-  if (qb_first < nqb) fill(qb_first * QB, 0);
+  if (qb_first < nqb) {
+    fill(qb_first * QB, 0);
+    fire_fill_rows(qb_first * QB, 0);
+  }
   wait_vmem_loads();
   __syncthreads();
   // S - lse/scale and dP - D of one 32-row block: each lane holds key myk
@@ -618,7 +676,10 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
   for (int qb = qb_first; qb < nqb; ++qb) {
     const int q0 = qb * QB;
     const int buf = (qb - qb_first) & 1;
-    if (qb + 1 < nqb) fill(q0 + QB, buf ^ 1);
+    if (qb + 1 < nqb) {
+      fill(q0 + QB, buf ^ 1);
+      fire_fill_rows(q0 + QB, buf ^ 1);
+    }
 
     // Every row block takes the same path (products, P, dS, products); only
     // the computation of P branches, so the dK / dV accumulators stay in
@@ -703,7 +764,60 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
       // The fast/slow choice is made once per block, outside the element
       // loops.
       float p[16], ds[16];
-      if (fast) {
+      // FIRE: x of each element (needed again by the gradient), its segment,
+      // and the lane's segment range
+      float fx[kFire ? 16 : 1];
+      int fslo = 0, fshi = 0;
+      if constexpr (kFire) {
+        // element r: row irow0 + 4hl + roff, roff = 8(r/4) + r%4, key myk;
+        // psi argument e = c (row - myk) + 1, at least 1 (masked pairs)
+        const float u0 = fmaf(fl.c, (float)(irow0 + 4 * hl - myk), 1.f);
+        const float *rw = fire_rows + buf * (kFireRowVals * 64) + 32 * rb + 4 * hl;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const f32x4 inv4 = *reinterpret_cast<const f32x4 *>(&rw[8 * qq]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ee = fmaxf(fmaf(fl.c, (float)(8 * qq + e), u0), 1.f);
+            fx[4 * qq + e] = __builtin_amdgcn_logf(ee) * inv4[e];
+          }
+        }
+        // x grows with the row: elements 0 and 15 bound the lane's range
+        fslo = fire_seg(fl.tab, fx[0]);
+        fshi = fire_seg(fl.tab, fx[15]);
+        float fb[16];
+        if (fslo == fshi) {
+          const float A = fl.tab[kFireOffA + fslo], B = fl.tab[kFireOffB + fslo];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) fb[r] = fmaf(B, fx[r], A);
+        } else if (fshi == fslo + 1) {
+          const float tk = fl.tab[kFireOffT + fshi];
+          const float A0 = fl.tab[kFireOffA + fslo], B0 = fl.tab[kFireOffB + fslo];
+          const float A1 = fl.tab[kFireOffA + fshi], B1 = fl.tab[kFireOffB + fshi];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool up = fx[r] >= tk;
+            fb[r] = fmaf(up ? B1 : B0, fx[r], up ? A1 : A0);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int sg = fire_seg(fl.tab, fx[r]);
+            fb[r] = fmaf(fl.tab[kFireOffB + sg], fx[r], fl.tab[kFireOffA + sg]);
+          }
+        }
+        const int rbase = myk - (irow0 + 4 * hl);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * qq + e, roff = 8 * qq + e;
+            const float t = fmaf(sacc[rb][r], c, fb[r]);
+            const bool dead = none | (mask_c & (rbase - roff > 0)) |
+                              (mask_r & (irow0 + 4 * hl + roff >= L)) | (mask_k & (myk >= L));
+            p[r] = __builtin_amdgcn_exp2f(t + (dead ? -INFINITY : 0.f));
+          }
+      } else if (fast) {
         block_p_fast(sacc[rb], bconst, p);
       } else {
         // T5: this lane's distances are rbase - roff, roff in [0, 27]; one
@@ -734,6 +848,52 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) ds[r] = p[r] * pacc[rb][r];
+      if constexpr (DBIAS && kFire) {
+        // the five sums' terms (see fire.hip) of the elements in segment sg
+        // (t_sg <= x < t_sg+1; sg < 0: every element), added to v; masked
+        // pairs carry dS = 0 and a finite x
+        const float *rw = fire_rows + buf * (kFireRowVals * 64) + 32 * rb + 4 * hl;
+        const float u0 = fmaf(fl.c, (float)(irow0 + 4 * hl - myk), 1.f);
+        const float d0 = (float)(irow0 + 4 * hl - myk);
+        auto add_terms = [&](float (&v)[kFireTerms], int sg) {
+          const float tlo = sg < 0 ? -INFINITY : fl.tab[kFireOffT + max(sg, 0)];
+          const float thi = sg < 0 ? INFINITY : fl.tab[kFireOffT + max(sg, 0) + 1];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 inv4 = *reinterpret_cast<const f32x4 *>(&rw[8 * qq]);
+            const f32x4 wc4 = *reinterpret_cast<const f32x4 *>(&rw[64 + 8 * qq]);
+            const f32x4 lf4 = *reinterpret_cast<const f32x4 *>(&rw[128 + 8 * qq]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * qq + e;
+              const float roff = (float)(8 * qq + e);
+              const float ee = fmaxf(fmaf(fl.c, roff, u0), 1.f);
+              const float g = (fx[r] >= tlo && fx[r] < thi) ? ds[r] : 0.f;
+              const float gx = g * fx[r];
+              v[0] += g;
+              v[1] += gx;
+              v[2] = fmaf(g, (d0 + roff) * __builtin_amdgcn_rcpf(ee) * inv4[e], v[2]);
+              v[3] = fmaf(gx, wc4[e], v[3]);
+              v[4] = fmaf(gx, lf4[e], v[4]);
+            }
+          }
+        };
+        if (fslo == fshi) {
+          if (fslo != s_cur) {
+            if (s_cur >= 0) fire_flush(s_cur, fr);
+#pragma unroll
+            for (int q = 0; q < kFireTerms; ++q) fr[q] = 0.f;
+            s_cur = fslo;
+          }
+          add_terms(fr, -1);
+        } else {
+          for (int sg = fslo; sg <= fshi; ++sg) {
+            float v[kFireTerms] = {0.f, 0.f, 0.f, 0.f, 0.f};
+            add_terms(v, sg);
+            fire_flush(sg, v);
+          }
+        }
+      }
       if constexpr (DBIAS && BIAS == kBiasDense) {
         // dL/dB = dS for every pair of the block (0 where masked)
         if (myk < L) {
@@ -827,6 +987,17 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
       buf_store8(rdk, el * 2u, k2);
     }
 
+  if constexpr (DBIAS && kFire) {
+    if (s_cur >= 0) fire_flush(s_cur, fr);
+    __syncthreads();
+    // the four waves' sums in a fixed order, one partial per workgroup
+    for (int i = tid; i < kFireGradRows; i += NT) {
+      float t = 0.f;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) t += fire_acc[w4 * kFireGradRows + i];
+      a.part[(size_t)i * a.nwg + w.part] = t;
+    }
+  }
   if constexpr (DBIAS && BIAS == kBiasT5) {
     // saturated-block sums: reduce over the wave, then fold into the end bins
     float s0 = ub0, s1 = ub1;
@@ -942,7 +1113,7 @@ hipError_t launch_dkv_t(const BwdArgs &a, hipStream_t s) {
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 hipError_t launch_pair(const BwdArgs &a, int phase, bool dbias, hipStream_t s) {
   if (phase == kBwdPre) return launch_dq_t<D, BIAS, CAUSAL, VARLEN>(a, s);
-  if constexpr (BIAS == kBiasT5 || BIAS == kBiasDense) {
+  if constexpr (BIAS == kBiasT5 || BIAS == kBiasDense || BIAS == kBiasFire) {
     if (dbias) return launch_dkv_t<D, BIAS, CAUSAL, VARLEN, true>(a, s);
   }
   return launch_dkv_t<D, BIAS, CAUSAL, VARLEN, false>(a, s);
@@ -954,6 +1125,10 @@ hipError_t launch_b(const BwdArgs &a, int phase, bool causal, bool varlen, bool 
   if constexpr (BIAS == kBiasDense) {   // dense entry points only
     return causal ? launch_pair<D, BIAS, true, false>(a, phase, dbias, s)
                   : launch_pair<D, BIAS, false, false>(a, phase, dbias, s);
+  } else if constexpr (BIAS == kBiasFire) {   // causal only
+    (void)causal;
+    return varlen ? launch_pair<D, BIAS, true, true>(a, phase, dbias, s)
+                  : launch_pair<D, BIAS, true, false>(a, phase, dbias, s);
   } else {
     if (causal)
       return varlen ? launch_pair<D, BIAS, true, true>(a, phase, dbias, s)
@@ -970,6 +1145,7 @@ hipError_t launch_d(const BwdArgs &a, int phase, int bias, bool causal, bool var
     case kBiasT5: return launch_b<D, kBiasT5>(a, phase, causal, varlen, dbias, s);
     case kBiasAlibi: return launch_b<D, kBiasAlibi>(a, phase, causal, varlen, dbias, s);
     case kBiasDense: return launch_b<D, kBiasDense>(a, phase, causal, varlen, dbias, s);
+    case kBiasFire: return launch_b<D, kBiasFire>(a, phase, causal, varlen, dbias, s);
     default: return launch_b<D, kBiasNone>(a, phase, causal, varlen, dbias, s);
   }
 }
@@ -998,6 +1174,7 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.dk = static_cast<uint16_t *>(b.dk);
   a.dv = static_cast<uint16_t *>(b.dv);
   a.rope_cs = b.rope_cs;
+  a.fire_tab = b.fire_tab;
   a.delta = b.delta;
   a.nls = b.delta + (size_t)p.total * p.heads;
   a.part = b.part;
@@ -1011,7 +1188,8 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.seqlen = p.seqlen;
   a.heads = p.heads;
   a.total = p.total;
-  a.nb = p.bias == kBiasT5 ? (p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp) : 0;
+  a.nb = p.bias == kBiasT5 ? (p.t5.bidir ? 2 * p.t5.nbp : p.t5.nbp)
+                           : (p.bias == kBiasFire ? kFireGradRows : 0);
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
   a.t5 = p.t5;
@@ -1028,7 +1206,8 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   if (phase == kBwdReduce) {
     if (b.part == nullptr) return hipSuccess;
     hipLaunchKernelGGL(dbias_reduce_kernel, dim3(a.nb * p.heads), dim3(256), 0, s, a.part,
-                       sched, a.nwg, p.nbatch, p.heads, a.ntile, b.dtable);
+                       sched, a.nwg, p.nbatch, p.heads, a.ntile,
+                       p.bias == kBiasFire ? b.fire_g : b.dtable);
     return hipGetLastError();
   }
   return p.head_dim == 64 ? launch_d<64>(a, phase, p.bias, p.causal, p.varlen, dbias, s)

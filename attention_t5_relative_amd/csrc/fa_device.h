@@ -213,6 +213,99 @@ __device__ __forceinline__ int t5_bucket_dev(int r, const T5Geometry &g) {
 // entries it then reads hold the same saturated value.
 constexpr int kLutPad = 96;
 
+// FIRE (see fa_internal.h and fire.hip): a workgroup's LDS copy of the
+// segment table (the shared part, then its head's A and B), and per lane the
+// constants of its query row.
+struct FireLane {
+  const float *tab = nullptr;   // LDS, kFireLds floats
+  float c = 0.f;                // psi(t) = log(c t + 1)
+  float inv = 0.f;              // 1 / log2(c max(L, i) + 1) for the lane's row i
+};
+
+// Segment of x: the number of kinks t_s <= x, by a branch-free binary search
+// over t_1 .. t_127 (+inf past the last kink).  A NaN x (a masked pair) gives
+// segment 0; the caller discards it.
+__device__ __forceinline__ int fire_seg(const float *tab, float x) {
+  int s = 0;
+#pragma unroll
+  for (int step = kFireTEnd / 2; step >= 1; step >>= 1)
+    s += (x >= tab[kFireOffT + s + step]) ? step : 0;
+  return s;
+}
+
+// Copy the table's shared part and head h's coefficients into LDS (all
+// threads of the workgroup; a barrier must follow before any read).
+__device__ __forceinline__ void fire_load(const float *gtab, int h, float *lds, int tid, int nt) {
+  for (int i = tid; i < kFireLds; i += nt)
+    lds[i] = i < kFireShared ? gtab[i]
+                             : gtab[kFireShared + (size_t)h * kFireHeadStride + (i - kFireShared)];
+}
+
+// 1 / log2(c max(L, i) + 1): the normaliser of row i's distances (log2
+// units, so x = log2(c d + 1) times this).
+__device__ __forceinline__ float fire_row_inv(float c, float Lthr, int i) {
+  return 1.f / __builtin_amdgcn_logf(fmaf(c, fmaxf(Lthr, (float)i), 1.f));
+}
+
+// Scores (log2 units, in place) of one lane's keys in a query-parallel tile
+// of NKB 32-key blocks with the FIRE bias: element (kb, r) is key offset
+// off = 32 kb + 8 (r / 4) + r % 4 past the lane's first key, distance
+// d = -(rbase + off), psi argument e = c d + 1 = u0 - c off.  x is monotone
+// in d, so the segments of the nearest and farthest visible keys (offsets 0
+// and omax) bound every key's: equal, the bias is A + (B inv) log2(e); one
+// kink apart, each key picks its side of the kink; otherwise each key
+// searches.  Masked keys (causal, or off >= lim) become -inf.
+template <int NKB>
+__device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int rbase, int lim,
+                                            bool mask_c, float c, const FireLane &fl) {
+  const float cn = -fl.c;
+  const float u0 = fmaf(cn, (float)rbase, 1.f);
+  const float xn = __builtin_amdgcn_logf(fmaxf(u0, 1.f)) * fl.inv;
+  const float xf = __builtin_amdgcn_logf(fmaxf(fmaf(cn, (float)omax, u0), 1.f)) * fl.inv;
+  const int shi = fire_seg(fl.tab, xn), slo = fire_seg(fl.tab, xf);
+  if (shi == slo) {
+    const float A = fl.tab[kFireOffA + slo], Bi = fl.tab[kFireOffB + slo] * fl.inv;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+        const float l = __builtin_amdgcn_logf(fmaf(cn, (float)off, u0));
+        sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(Bi, l, A));
+      }
+  } else if (shi == slo + 1) {
+    const float tk = fl.tab[kFireOffT + shi];
+    const float A0 = fl.tab[kFireOffA + slo], B0 = fl.tab[kFireOffB + slo];
+    const float A1 = fl.tab[kFireOffA + shi], B1 = fl.tab[kFireOffB + shi];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+        const float x = __builtin_amdgcn_logf(fmaf(cn, (float)off, u0)) * fl.inv;
+        const bool up = x >= tk;
+        sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(up ? B1 : B0, x, up ? A1 : A0));
+      }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+        const float x = __builtin_amdgcn_logf(fmaf(cn, (float)off, u0)) * fl.inv;
+        const int sg = fire_seg(fl.tab, x);
+        sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(fl.tab[kFireOffB + sg], x, fl.tab[kFireOffA + sg]));
+      }
+  }
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+      if ((mask_c && rbase + off > 0) || off >= lim) sacc[kb][r] = -INFINITY;
+    }
+}
+
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -243,7 +336,8 @@ template <int BIAS, bool CAUSAL, bool ALIBI_LINEAR = true>
 __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0, int il, int hl,
                                              int L, float c, int sat, const float *lut,
                                              float slope_l2, float &bconst,
-                                             const uint16_t (&bv)[2][16]) {
+                                             const uint16_t (&bv)[2][16],
+                                             const FireLane &fl = FireLane{}) {
   const int rmin = j0 - (row0 + 31), rmax = j0 + 63 - row0;
   const bool mask_c = CAUSAL && rmax > 0;
   const bool mask_l = j0 + 64 > L;
@@ -272,6 +366,10 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
         const float t = fmaf(sacc[kb][r], c, lb[off]);
         sacc[kb][r] = off >= lim ? -INFINITY : t;
       }
+    return false;
+  }
+  if constexpr (BIAS == kBiasFire) {
+    fire_scores<2>(sacc, 59, rbase, mask_l ? L - jb : 64, mask_c, c, fl);
     return false;
   }
   if constexpr (BIAS == kBiasAlibi && ALIBI_LINEAR) {
@@ -316,7 +414,8 @@ template <int BIAS, bool CAUSAL>
 __device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, int il, int hl,
                                               int L, float c, int sat, const float *lut,
                                               float slope_l2, float &bconst,
-                                              const uint16_t (&bv)[16]) {
+                                              const uint16_t (&bv)[16],
+                                              const FireLane &fl = FireLane{}) {
   const int rmin = jb0 - (row0 + 31), rmax = jb0 + 31 - row0;
   const bool mask_c = CAUSAL && rmax > 0;
   const bool mask_l = jb0 + 32 > L;
@@ -342,6 +441,11 @@ __device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, i
       const float t = fmaf(sacc[r], c, lb[off]);
       sacc[r] = off >= lim ? -INFINITY : t;
     }
+    return false;
+  }
+  if constexpr (BIAS == kBiasFire) {
+    f32x16 (&one)[1] = *reinterpret_cast<f32x16 (*)[1]>(&sacc);
+    fire_scores<1>(one, 27, rbase, mask_l ? L - jb : 32, mask_c, c, fl);
     return false;
   }
   if constexpr (BIAS == kBiasAlibi) {

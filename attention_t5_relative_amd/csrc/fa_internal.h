@@ -26,7 +26,44 @@ struct T5Geometry {
   int32_t thr[kMaxThresholds];
 };
 
-enum BiasKind : int32_t { kBiasNone = 0, kBiasT5 = 1, kBiasAlibi = 2, kBiasDense = 3 };
+enum BiasKind : int32_t {
+  kBiasNone = 0,
+  kBiasT5 = 1,
+  kBiasAlibi = 2,
+  kBiasDense = 3,
+  kBiasFire = 4
+};
+
+// FIRE.  The bias b_h(x) = b2_h + sum_k w2_hk relu(w1_k x + b1_k) of the
+// normalised distance x is piecewise linear in x: on each segment between
+// consecutive kinks -b1_k / w1_k inside (0, 1) the set of active units is
+// fixed and b_h = A_hs + B_hs x.  fire_setup_kernel (fire.hip) writes the
+// segment table, fp32 words:
+//   [0] m (kinks inside (0, 1), int bits), [2] c, [3] L
+//   [kFireOffT + s]    t_s, s = 1 .. kFireTEnd - 1: the kinks t_1 <= .. <= t_m,
+//                      then +inf
+//   per head h at kFireShared + h * kFireHeadStride: A_hs * log2(e) at
+//   [s], B_hs * log2(e) at [66 + s], s = 0 .. m
+// The segment of x (the number of kinks <= x) comes from a branch-free binary
+// search over t_1 .. t_127 (seven steps).
+constexpr int kFireMaxHidden = 64;
+constexpr int kFireSegs = kFireMaxHidden + 1;
+constexpr int kFireOffT = 8;
+constexpr int kFireTEnd = 128;                    // t_s stored for s < kFireTEnd
+constexpr int kFireShared = 144;
+constexpr int kFireHeadStride = 132;
+constexpr int kFireOffA = kFireShared;            // in a workgroup's LDS copy
+constexpr int kFireOffB = kFireShared + 66;
+constexpr int kFireLds = kFireShared + kFireHeadStride;
+constexpr int kFireTerms = 5;                     // gradient sums per (head, segment)
+constexpr int kFireGradRows = kFireTerms * kFireSegs;
+static_assert(kFireOffT + kFireTEnd <= kFireShared, "FIRE table layout");
+__host__ __device__ inline size_t fire_tab_floats(int heads) {
+  return (size_t)kFireShared + (size_t)kFireHeadStride * heads;
+}
+__host__ __device__ inline int fire_theta_floats(int heads, int hidden) {
+  return 2 * hidden + heads * hidden + heads + 2;
+}
 
 // One attention problem, dense or packed, as the kernels see it.
 struct Problem {
@@ -45,6 +82,7 @@ struct Problem {
   const float *slopes;
   const uint16_t *dense;  // bf16 [dense_batch, H, S, S] (kBiasDense)
   int32_t dense_batch;    // 1 (shared by the batch) or nbatch
+  int32_t fire_hidden;    // kBiasFire: hidden units K (table = theta)
   T5Geometry t5;
 };
 
@@ -53,6 +91,7 @@ struct FwdBuffers {
   void *o;
   float *lse;
   const double2 *rope_cs;   // RoPE fp64 (cos, sin) table [seqlen, D/2] or nullptr
+  const float *fire_tab;    // FIRE segment table or nullptr
 };
 
 struct BwdBuffers {
@@ -68,6 +107,8 @@ struct BwdBuffers {
   float *dtable;           // [num_buckets, H] or nullptr
   float *dbias;            // dense bias gradient fp32 [dense_batch, H, S, S] or nullptr
   float *dbias_batch;      // per-batch gradients [B, H, S, S] summed into dbias, or nullptr
+  const float *fire_tab;   // FIRE segment table or nullptr
+  float *fire_g;           // FIRE: reduced gradient sums [kFireGradRows, H] or nullptr
 };
 
 // Launchers (return the first HIP error, hipSuccess otherwise).
@@ -94,6 +135,10 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
 hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
                              hipStream_t s);
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
+// FIRE (fire.hip): the segment table from theta, and d(theta) from the
+// reduced per-(head, segment) gradient sums.
+hipError_t launch_fire_setup(const Problem &p, float *tab, hipStream_t s);
+hipError_t launch_fire_grad(const Problem &p, const float *g, float *dtheta, hipStream_t s);
 // MFMA throughput probe: kMfmaProbeBlocks x kMfmaProbeThreads lanes, each
 // wave 4 chains x iters v_mfma_f32_32x32x16_bf16; sink holds one float per lane.
 constexpr int kMfmaProbeBlocks = 2048;

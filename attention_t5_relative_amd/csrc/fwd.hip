@@ -1,9 +1,9 @@
 // Forward attention for gfx950 (FAT5 report, section "Noyau CUDA", second
 // kernel): per (sequence, head, 128-query tile) one workgroup streams K and V
 // through LDS in 64-key tiles, forms S' = scale * Q K^T + bias on the fly from
-// the per-head table (or ALiBi), keeps a running softmax, accumulates O = P V,
-// and writes O (bf16) and the row logsumexp (fp32).  The score matrix never
-// leaves registers.
+// the per-head table (or ALiBi, or the FIRE segment table), keeps a running
+// softmax, accumulates O = P V, and writes O (bf16) and the row logsumexp
+// (fp32).  The score matrix never leaves registers.
 //
 // Layout of the work inside a workgroup (4 waves, 32 query rows each):
 //   S^T (keys x queries) = K Q^T on 32x32x16 bf16 MFMA, so each lane owns one
@@ -52,6 +52,7 @@ struct FwdArgs {
   const float *table, *slopes;
   const uint16_t *dense;  // dense bias bf16 [dense_batch, H, S, S]
   const double2 *rope_cs;  // RoPE: (cos, sin) [seqlen, D/2], or nullptr
+  const float *fire_tab;   // FIRE segment table (fa_internal.h), or nullptr
   int32_t dense_batch;
   int32_t nbatch, seqlen, heads, total;
   int32_t nq, nwg;
@@ -60,7 +61,8 @@ struct FwdArgs {
 };
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd_kernel(
+__global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense && BIAS != kBiasFire ? 3 : 2)
+void fwd_kernel(
     const FwdArgs a) {
   constexpr int NVF = D / 8;                  // V operand fragments per tile
   // Register budget: at head_dim 64 the K operands of both 32-key blocks are
@@ -79,6 +81,7 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
   __shared__ __attribute__((aligned(16))) uint16_t vs[NBUF][BC * D];
   __shared__ float lut_mem[BIAS == kBiasT5 ? 2 * (kMaxDistance + kLutPad) + 1 : 1];
   const float *const lut = lut_mem + (BIAS == kBiasT5 ? a.t5.sat + kLutPad : 0);
+  __shared__ float fire_mem[BIAS == kBiasFire ? kFireLds : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -151,6 +154,13 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
   }
   float slope_l2 = 0.f;
   if constexpr (BIAS == kBiasAlibi) slope_l2 = -a.slopes[h] * kLog2e;
+  FireLane fl;
+  if constexpr (BIAS == kBiasFire) {
+    fire_load(a.fire_tab, h, fire_mem, tid, NT);
+    fl.tab = fire_mem;
+    fl.c = a.fire_tab[2];
+    fl.inv = fire_row_inv(fl.c, a.fire_tab[3], wrow0 + il);
+  }
   // dense bias: this (batch, head)'s [S, S] matrix
   rsrc_t rbias = make_rsrc(nullptr, 0u);
   if constexpr (BIAS == kBiasDense) {
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(NT, D == 64 && BIAS != kBiasDense ? 3 : 2) void fwd
       // (the linear ALiBi path would not fit the 168 VGPRs of three
       // workgroups per CU at head_dim 64)
       const bool fast = score_tile_T<BIAS, CAUSAL, D == 128>(sacc, j0, wrow0, il, hl, L, c, sat,
-                                                            lut, slope_l2, bconst, bv);
+                                                            lut, slope_l2, bconst, bv, fl);
       // row max: two chains of v_max3 (one instruction per two elements; the
       // empty asm keeps the compiler from rebalancing them into a tree of
       // two-input maxes, which takes half as many instructions again)
@@ -371,6 +381,10 @@ hipError_t launch_b(const FwdArgs &a, int grid, bool causal, bool varlen, hipStr
   if constexpr (BIAS == kBiasDense) {   // dense entry points only
     return causal ? launch_t<D, BIAS, true, false>(a, grid, s)
                   : launch_t<D, BIAS, false, false>(a, grid, s);
+  } else if constexpr (BIAS == kBiasFire) {   // causal only
+    (void)causal;
+    return varlen ? launch_t<D, BIAS, true, true>(a, grid, s)
+                  : launch_t<D, BIAS, true, false>(a, grid, s);
   } else {
     if (causal)
       return varlen ? launch_t<D, BIAS, true, true>(a, grid, s)
@@ -387,6 +401,7 @@ hipError_t launch_d(const FwdArgs &a, int grid, int bias, bool causal, bool varl
     case kBiasT5: return launch_b<D, kBiasT5>(a, grid, causal, varlen, s);
     case kBiasAlibi: return launch_b<D, kBiasAlibi>(a, grid, causal, varlen, s);
     case kBiasDense: return launch_b<D, kBiasDense>(a, grid, causal, varlen, s);
+    case kBiasFire: return launch_b<D, kBiasFire>(a, grid, causal, varlen, s);
     default: return launch_b<D, kBiasNone>(a, grid, causal, varlen, s);
   }
 }
@@ -408,6 +423,7 @@ hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sc
   a.slopes = p.slopes;
   a.dense = p.dense;
   a.rope_cs = b.rope_cs;
+  a.fire_tab = b.fire_tab;
   a.dense_batch = p.dense_batch;
   a.nbatch = p.nbatch;
   a.seqlen = p.seqlen;

@@ -1,7 +1,7 @@
 /*
  * libfat5attn: exact softmax attention with the T5 relative-position bias,
- * ALiBi and RoPE, dense or packed (cu_seqlens), forward and backward, for
- * AMD Instinct MI355X (gfx950).
+ * ALiBi, FIRE and RoPE, dense or packed (cu_seqlens), forward and backward,
+ * for AMD Instinct MI355X (gfx950).
  *
  * What is computed (FAT5 report, section "Noyau CUDA", second kernel): for
  * every (sequence, head) the scores S = scale * Q K^T, then S' = S plus a bias
@@ -80,25 +80,37 @@ typedef enum {
   FA_BIAS_NONE = 0,
   FA_BIAS_T5 = 1,
   FA_BIAS_ALIBI = 2,
-  FA_BIAS_DENSE = 3
+  FA_BIAS_DENSE = 3,
+  FA_BIAS_FIRE = 4
 } fa_bias_mode;
 
 /* Additive score bias.  FAT5 report, "Noyau CUDA": the second kernel is
  * handed the compact bucket tensor T instead of a dense bias matrix; the
  * first kernel was handed the bias matrix B itself (FA_BIAS_DENSE: memory
- * quadratic in the sequence length, dense entry points only). */
+ * quadratic in the sequence length, dense entry points only).
+ *
+ * FA_BIAS_FIRE: the FIRE bias (listed with RoPE and ALiBi in the note under
+ * "Noyau CUDA"; definition from the FIRE paper it cites), causal attention
+ * only.  For query i and key j <= i (positions local to each sequence):
+ *   x = log(c (i - j) + 1) / log(c max(L, i) + 1),
+ *   bias_h = b2_h + sum_k w2_hk relu(w1_k x + b1_k)   (K = fire_hidden units).
+ * `table` points to theta, device fp32
+ *   [w1 (K), b1 (K), w2 (H * K, row h at h * K), b2 (H), c, L]
+ * with c > 0 and L > 0 (trusted: not read on the host).  The backward's
+ * dtable is d(theta) in the same layout, summed over the batch and heads.
+ * K <= 64. */
 typedef struct {
   int32_t mode;            /* fa_bias_mode                                     */
   int32_t num_buckets;     /* T5 only                                          */
   int32_t max_distance;    /* T5 only                                          */
   int32_t bidirectional;   /* T5 only: 1 encoder style, 0 decoder style        */
-  const float *table;      /* T5: device fp32 [num_buckets, H]                 */
+  const float *table;      /* T5: device fp32 [num_buckets, H]; FIRE: theta    */
   const float *slopes;     /* ALiBi: device fp32 [H]                           */
   const void *dense;       /* DENSE: device bf16 [dense_batch, H, S, S], row =
                               query, column = key, added to scale * Q K^T     */
   int32_t dense_batch;     /* DENSE: 1 (one matrix per head, shared by the
                               batch) or B; S <= 16384                         */
-  int32_t reserved2;       /* must be 0                                        */
+  int32_t fire_hidden;     /* FIRE: hidden units K in [1, 64]; else 0          */
 } fa_bias;
 
 /* Dense forward: q, k, v [B, S, H, D] bf16 in; o [B, S, H, D] bf16 and

@@ -53,7 +53,7 @@ def test_status_strings_and_version(lib):
 
 STRUCTS = {
     "fa_bias": (_lib.FaBias, ["mode", "num_buckets", "max_distance", "bidirectional", "table",
-                              "slopes", "dense", "dense_batch", "reserved2"]),
+                              "slopes", "dense", "dense_batch", "fire_hidden"]),
     "fa_fwd_params": (_lib.FaFwdParams, ["batch", "seqlen", "heads", "head_dim", "causal",
                                          "scale", "rope_base", "reserved", "q", "k", "v", "o",
                                          "lse", "bias"]),
@@ -135,7 +135,17 @@ def _dense(**kw):
     ({"bias_mode": _lib.FA_BIAS_ALIBI, "bias_slopes": 0x3000}, _lib.FA_OK),
     ({"bias_mode": _lib.FA_BIAS_NONE, "bias_table": None}, _lib.FA_OK),
     ({"bias_bidirectional": 0, "bias_num_buckets": 31}, _lib.FA_OK),
-    ({"bias_reserved2": 1}, _lib.FA_ERR_INVALID),
+    ({"bias_fire_hidden": 1}, _lib.FA_ERR_INVALID),    # only with FIRE
+    # FIRE: theta in bias.table, causal only, 1..64 hidden units
+    ({"bias_mode": _lib.FA_BIAS_FIRE, "bias_fire_hidden": 32, "causal": 1}, _lib.FA_OK),
+    ({"bias_mode": _lib.FA_BIAS_FIRE, "bias_fire_hidden": 32, "causal": 0},
+     _lib.FA_ERR_UNSUPPORTED),
+    ({"bias_mode": _lib.FA_BIAS_FIRE, "bias_fire_hidden": 0, "causal": 1},
+     _lib.FA_ERR_UNSUPPORTED),
+    ({"bias_mode": _lib.FA_BIAS_FIRE, "bias_fire_hidden": 65, "causal": 1},
+     _lib.FA_ERR_UNSUPPORTED),
+    ({"bias_mode": _lib.FA_BIAS_FIRE, "bias_fire_hidden": 8, "causal": 1, "bias_table": None},
+     _lib.FA_ERR_INVALID),
     ({"bias_mode": _lib.FA_BIAS_DENSE}, _lib.FA_ERR_INVALID),   # dense NULL
     ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense": 0x6000, "bias_dense_batch": 1}, _lib.FA_OK),
     ({"bias_mode": _lib.FA_BIAS_DENSE, "bias_dense": 0x6000, "bias_dense_batch": 2}, _lib.FA_OK),
@@ -222,6 +232,27 @@ def test_workspace_sizes(lib):
     b.dout = b.dq = b.dk = b.dv = 0x4000
     delta = a256(2 * 2 * 100 * 3 * 4)
     assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == 2 * a256(one) + a256(table) + delta
+
+
+def test_fire_workspace(lib):
+    """FIRE: the segment table (144 + 132 H floats) in both workspaces; with
+    d(theta) asked, the per-workgroup partials (325 rows per 128-key tile) and
+    their per-head reduction (325 x H floats)."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    p = _dense(bias_mode=_lib.FA_BIAS_FIRE, bias_fire_hidden=32, causal=1)
+    B, S, H = p.batch, p.seqlen, p.heads
+    tab = a256((144 + 132 * H) * 4)
+    assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == tab
+    b = _lib.FaBwdParams()
+    b.f = p
+    b.dout = b.dq = b.dk = b.dv = 0x4000
+    delta = a256(2 * B * S * H * 4)
+    assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == delta + tab
+    b.dtable = 0x7000
+    parts = B * H * ((S + 127) // 128)
+    assert lib.fa_bwd_workspace_size(ctypes.byref(b)) == (
+        delta + a256(parts * 325 * 4) + tab + a256(325 * H * 4))
 
 
 def test_dense_bias_gradient_workspace(lib):
