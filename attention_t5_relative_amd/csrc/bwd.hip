@@ -152,11 +152,12 @@ __device__ __forceinline__ void rope_unrotate_acc(f32x16 (&acc)[D / 32], const d
 // ---------------------------------------------------------------------------
 // dq kernel
 // ---------------------------------------------------------------------------
-// Workgroups per CU of the dq kernel (the dense bias's per-tile values
-// need more registers than two workgroups leave at head_dim 128).
+// Workgroups per CU of the dq kernel (the dense bias's per-tile values and
+// the FIRE lookups need more registers than two workgroups leave at
+// head_dim 128).
 template <int D, int BIAS>
 constexpr int dq_wgs() {
-  return D == 64 || BIAS != kBiasDense ? 2 : 1;
+  return D == 64 || (BIAS != kBiasDense && BIAS != kBiasFire) ? 2 : 1;
 }
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
@@ -428,8 +429,11 @@ __host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
 // row offsets of the Q/dO operands are computed where they are used, which
 // leaves room for two workgroups per CU without spilling; the T5 (with its
 // table gradient) and dense-bias variants need the registers and run one.
-template <int D, int BIAS>
+// FIRE with its parameter gradient runs one at either head_dim (the five
+// per-segment sums and their per-row weights).
+template <int D, int BIAS, bool DBIAS>
 constexpr int dkv_wgs() {
+  if (BIAS == kBiasFire && DBIAS) return 1;   // the FIRE gradient sums' registers
   return D == 64 || BIAS == kBiasAlibi || BIAS == kBiasNone ? 2 : 1;
 }
 
@@ -439,7 +443,8 @@ constexpr int dkv_wgs() {
 constexpr int kFireRowVals = 3;
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool DBIAS>
-__global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS, DBIAS>())) void bwd_dkv_kernel(
+    const BwdArgs a) {
   constexpr int QB = DkvTile<D>::QB;
   constexpr bool kVInLds = D == 128 && (BIAS == kBiasAlibi || BIAS == kBiasNone);
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kVInLds ? BKV * D : 8];
@@ -773,14 +778,15 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
         // psi argument e = c (row - myk) + 1, at least 1 (masked pairs)
         const float u0 = fmaf(fl.c, (float)(irow0 + 4 * hl - myk), 1.f);
         const float *rw = fire_rows + buf * (kFireRowVals * 64) + 32 * rb + 4 * hl;
+        // (e of row offset 8 qq + i: one fma per four rows, then + c i)
+        const float ce[4] = {0.f, fl.c, 2.f * fl.c, 3.f * fl.c};
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const f32x4 inv4 = *reinterpret_cast<const f32x4 *>(&rw[8 * qq]);
+          const float g = fmaf(fl.c, (float)(8 * qq), u0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ee = fmaxf(fmaf(fl.c, (float)(8 * qq + e), u0), 1.f);
-            fx[4 * qq + e] = __builtin_amdgcn_logf(ee) * inv4[e];
-          }
+          for (int e = 0; e < 4; ++e)
+            fx[4 * qq + e] = __builtin_amdgcn_logf(fmaxf(g + ce[e], 1.f)) * inv4[e];
         }
         // x grows with the row: elements 0 and 15 bound the lane's range
         fslo = fire_seg(fl.tab, fx[0]);
@@ -804,6 +810,7 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
           for (int r = 0; r < 16; ++r) {
             const int sg = fire_seg(fl.tab, fx[r]);
             fb[r] = fmaf(fl.tab[kFireOffB + sg], fx[r], fl.tab[kFireOffA + sg]);
+            __builtin_amdgcn_sched_barrier(0);   // one search at a time
           }
         }
         const int rbase = myk - (irow0 + 4 * hl);
@@ -848,52 +855,6 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) ds[r] = p[r] * pacc[rb][r];
-      if constexpr (DBIAS && kFire) {
-        // the five sums' terms (see fire.hip) of the elements in segment sg
-        // (t_sg <= x < t_sg+1; sg < 0: every element), added to v; masked
-        // pairs carry dS = 0 and a finite x
-        const float *rw = fire_rows + buf * (kFireRowVals * 64) + 32 * rb + 4 * hl;
-        const float u0 = fmaf(fl.c, (float)(irow0 + 4 * hl - myk), 1.f);
-        const float d0 = (float)(irow0 + 4 * hl - myk);
-        auto add_terms = [&](float (&v)[kFireTerms], int sg) {
-          const float tlo = sg < 0 ? -INFINITY : fl.tab[kFireOffT + max(sg, 0)];
-          const float thi = sg < 0 ? INFINITY : fl.tab[kFireOffT + max(sg, 0) + 1];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const f32x4 inv4 = *reinterpret_cast<const f32x4 *>(&rw[8 * qq]);
-            const f32x4 wc4 = *reinterpret_cast<const f32x4 *>(&rw[64 + 8 * qq]);
-            const f32x4 lf4 = *reinterpret_cast<const f32x4 *>(&rw[128 + 8 * qq]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * qq + e;
-              const float roff = (float)(8 * qq + e);
-              const float ee = fmaxf(fmaf(fl.c, roff, u0), 1.f);
-              const float g = (fx[r] >= tlo && fx[r] < thi) ? ds[r] : 0.f;
-              const float gx = g * fx[r];
-              v[0] += g;
-              v[1] += gx;
-              v[2] = fmaf(g, (d0 + roff) * __builtin_amdgcn_rcpf(ee) * inv4[e], v[2]);
-              v[3] = fmaf(gx, wc4[e], v[3]);
-              v[4] = fmaf(gx, lf4[e], v[4]);
-            }
-          }
-        };
-        if (fslo == fshi) {
-          if (fslo != s_cur) {
-            if (s_cur >= 0) fire_flush(s_cur, fr);
-#pragma unroll
-            for (int q = 0; q < kFireTerms; ++q) fr[q] = 0.f;
-            s_cur = fslo;
-          }
-          add_terms(fr, -1);
-        } else {
-          for (int sg = fslo; sg <= fshi; ++sg) {
-            float v[kFireTerms] = {0.f, 0.f, 0.f, 0.f, 0.f};
-            add_terms(v, sg);
-            fire_flush(sg, v);
-          }
-        }
-      }
       if constexpr (DBIAS && BIAS == kBiasDense) {
         // dL/dB = dS for every pair of the block (0 where masked)
         if (myk < L) {
@@ -929,6 +890,57 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
         }
       }
       block_dvdk(buf, rb, p, ds);
+      if constexpr (DBIAS && kFire) {
+        // the five sums' terms (see fire.hip) of the elements in segment sg
+        // (t_sg <= x < t_sg+1; sg < 0: every element), added to v; masked
+        // pairs carry dS = 0 and a finite x
+        const float *rw = fire_rows + buf * (kFireRowVals * 64) + 32 * rb + 4 * hl;
+        const float d0 = (float)(irow0 + 4 * hl - myk);
+        const float u0 = fmaf(fl.c, d0, 1.f);
+        const float ce[4] = {0.f, fl.c, 2.f * fl.c, 3.f * fl.c};
+        const float de[4] = {0.f, 1.f, 2.f, 3.f};
+        auto add_terms = [&](float (&v)[kFireTerms], int sg) {
+          const float tlo = sg < 0 ? -INFINITY : fl.tab[kFireOffT + max(sg, 0)];
+          const float thi = sg < 0 ? INFINITY : fl.tab[kFireOffT + max(sg, 0) + 1];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 inv4 = *reinterpret_cast<const f32x4 *>(&rw[8 * qq]);
+            const f32x4 wc4 = *reinterpret_cast<const f32x4 *>(&rw[64 + 8 * qq]);
+            const f32x4 lf4 = *reinterpret_cast<const f32x4 *>(&rw[128 + 8 * qq]);
+            const float eq = fmaf(fl.c, (float)(8 * qq), u0), dq0 = d0 + (float)(8 * qq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * qq + e;
+              const float ee = fmaxf(eq + ce[e], 1.f);
+              // x again (the same operations as for the score): keeping the
+              // block's 16 values across the products would spill
+              const float x = __builtin_amdgcn_logf(ee) * inv4[e];
+              const float g = (x >= tlo && x < thi) ? ds[r] : 0.f;
+              const float gx = g * x;
+              v[0] += g;
+              v[1] += gx;
+              v[2] = fmaf(g, (dq0 + de[e]) * __builtin_amdgcn_rcpf(ee) * inv4[e], v[2]);
+              v[3] = fmaf(gx, wc4[e], v[3]);
+              v[4] = fmaf(gx, lf4[e], v[4]);
+            }
+          }
+        };
+        if (fslo == fshi) {
+          if (fslo != s_cur) {
+            if (s_cur >= 0) fire_flush(s_cur, fr);
+#pragma unroll
+            for (int q = 0; q < kFireTerms; ++q) fr[q] = 0.f;
+            s_cur = fslo;
+          }
+          add_terms(fr, -1);
+        } else {
+          for (int sg = fslo; sg <= fshi; ++sg) {
+            float v[kFireTerms] = {0.f, 0.f, 0.f, 0.f, 0.f};
+            add_terms(v, sg);
+            fire_flush(sg, v);
+          }
+        }
+      }
       if constexpr (DBIAS && BIAS == kBiasT5) {
         if (!fast) {
           // diagonal il (hl = 0) covers rows below 32 - il, diagonal il - 32

@@ -223,14 +223,15 @@ struct FireLane {
 };
 
 // Segment of x: the number of kinks t_s <= x, by a branch-free binary search
-// over t_1 .. t_127 (+inf past the last kink).  A NaN x (a masked pair) gives
-// segment 0; the caller discards it.
+// over t_1 .. t_127 (+inf past the last kink).  A NaN x (a masked pair; the
+// device code is built without NaN semantics) still yields an index inside
+// the table; the caller discards that element.
 __device__ __forceinline__ int fire_seg(const float *tab, float x) {
   int s = 0;
 #pragma unroll
   for (int step = kFireTEnd / 2; step >= 1; step >>= 1)
     s += (x >= tab[kFireOffT + s + step]) ? step : 0;
-  return s;
+  return min(s, kFireMaxHidden);   // in range whatever a NaN compare gave
 }
 
 // Copy the table's shared part and head h's coefficients into LDS (all
@@ -263,14 +264,22 @@ __device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int r
   const float xn = __builtin_amdgcn_logf(fmaxf(u0, 1.f)) * fl.inv;
   const float xf = __builtin_amdgcn_logf(fmaxf(fmaf(cn, (float)omax, u0), 1.f)) * fl.inv;
   const int shi = fire_seg(fl.tab, xn), slo = fire_seg(fl.tab, xf);
+  // e of key offset 32 kb + 8 q + i: one fma per group of four keys, then
+  // one add of -c i (the offsets as per-key float constants would each be
+  // held in a register)
+  const float ce[4] = {0.f, cn, 2.f * cn, 3.f * cn};
+  auto e_of = [&](int kb, int q, int i, float &g) {
+    if (i == 0) g = fmaf(cn, (float)(32 * kb + 8 * q), u0);
+    return g + ce[i];
+  };
+  float g = 0.f;
   if (shi == slo) {
     const float A = fl.tab[kFireOffA + slo], Bi = fl.tab[kFireOffB + slo] * fl.inv;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-        const float l = __builtin_amdgcn_logf(fmaf(cn, (float)off, u0));
+        const float l = __builtin_amdgcn_logf(e_of(kb, r >> 2, r & 3, g));
         sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(Bi, l, A));
       }
   } else if (shi == slo + 1) {
@@ -281,8 +290,7 @@ __device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int r
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-        const float x = __builtin_amdgcn_logf(fmaf(cn, (float)off, u0)) * fl.inv;
+        const float x = __builtin_amdgcn_logf(e_of(kb, r >> 2, r & 3, g)) * fl.inv;
         const bool up = x >= tk;
         sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(up ? B1 : B0, x, up ? A1 : A0));
       }
@@ -291,10 +299,12 @@ __device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int r
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-        const float x = __builtin_amdgcn_logf(fmaf(cn, (float)off, u0)) * fl.inv;
+        const float x = __builtin_amdgcn_logf(fmaxf(e_of(kb, r >> 2, r & 3, g), 1.f)) * fl.inv;
         const int sg = fire_seg(fl.tab, x);
         sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(fl.tab[kFireOffB + sg], x, fl.tab[kFireOffA + sg]));
+        // one key at a time: searches hoisted side by side would hold their
+        // registers all at once
+        __builtin_amdgcn_sched_barrier(0);
       }
   }
 #pragma unroll

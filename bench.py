@@ -32,8 +32,10 @@ the same way (forward + backward, kernel times by HIP events), each on the
 seeded draw its parity test uses: the bidirectional T5 encoder B16 H12 S1024
 D64 (seed 2); 32768 packed tokens in 55 sequences of lognormal lengths (seed
 4; 12 heads, D64, bidirectional T5); and the long-context causal B2 H16
-S16384 D128 (seed 5) run with ALiBi or with RoPE.  Their cpu_baseline times
-the oracle on a few heads (one head at S16384).
+S16384 D128 (seed 5) run with ALiBi or with RoPE; ``--workload fire`` the
+causal decoder shape and draw with the FIRE bias (32 hidden units, c 0.1,
+L 512) and its parameter gradient.  Their cpu_baseline times the oracle on a
+few heads (one head at S16384 and for FIRE).
 
 Every line reports the mean step over the K timed steps (ms_per_step, from
 which value follows), the median, p10 and p90 of the single steps, and one
@@ -42,7 +44,7 @@ caches.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                     [--bias t5|dense]
-                    [--workload attention|rmsnorm|ce|encoder|varlen|alibi|rope]
+                    [--workload attention|rmsnorm|ce|encoder|varlen|alibi|rope|fire]
 """
 from __future__ import annotations
 
@@ -334,7 +336,9 @@ def norm_loss_cpu_baseline(workload):
                       f"({dt:.2f} s); same algorithmic bytes per row as the GPU value"}
 
 
-OTHER_ATTENTION = {"encoder": "c2", "varlen": "c4", "alibi": "c5a", "rope": "c5b"}
+OTHER_ATTENTION = {"encoder": "c2", "varlen": "c4", "alibi": "c5a", "rope": "c5b", "fire": "c3"}
+# FIRE side line: the causal decoder shape with the FIRE bias in place of T5
+FIRE_HIDDEN, FIRE_C, FIRE_L = 32, 0.1, 512.0
 
 # FlashAttention convention for a fwd+bwd step: the forward's two products
 # count 1.0x, the backward's five 2.5x.  Per kernel the step's 3.5x is split
@@ -444,6 +448,7 @@ def bench_other_attention(a):
 
     H, Dh = c.heads, c.head_dim
     table = slopes = None
+    fire = a.workload == "fire"
     if c.varlen_total:
         inp = synth.draw_varlen(c.seed, c.varlen_total, H, Dh, num_buckets=c.num_buckets)
         lens = inp.lengths
@@ -482,7 +487,15 @@ def bench_other_attention(a):
         Bq, Sq = c.batch, c.seqlen
         rope = c.rope_base or 0.0
         dtable = None
-        if c.bias == "t5":
+        if fire:
+            theta = synth.draw_fire_theta(c.seed, H, FIRE_HIDDEN, c=FIRE_C, threshold=FIRE_L)
+            table = torch.from_numpy(theta).to(dev)
+            bias = fa.FireBias(table, FIRE_HIDDEN)
+            dtable = torch.empty_like(table)
+            workload = (f"causal decoder self-attention fwd+bwd with the FIRE bias (MLP "
+                        f"{FIRE_HIDDEN} hidden units, c {FIRE_C}, L {FIRE_L:g}) and its "
+                        f"parameter gradient, B{Bq} H{H} S{Sq} D{Dh}, scale 1")
+        elif c.bias == "t5":
             table = torch.from_numpy(inp.table).to(dev)
             bias = fa.T5Bias(table, c.num_buckets, c.max_distance, c.bidirectional)
             dtable = torch.empty_like(table)
@@ -517,22 +530,28 @@ def bench_other_attention(a):
 
     t = run_timed(a, step, _attn_kernels(), dev)
     t["mfma_probe_tflops"] = mfma_probe(dev)
-    line = _attention_line(a, f"attention fwd+bwd TFLOP/s, {a.workload} workload ({c.name})",
+    tag = f"{c.name} shape, FIRE bias" if fire else c.name
+    line = _attention_line(a, f"attention fwd+bwd TFLOP/s, {a.workload} workload ({tag})",
                            workload, shape, t, fwd_flops)
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = other_cpu_baseline(c, inp, slopes)
+        line["cpu_baseline"] = other_cpu_baseline(c, inp, slopes,
+                                                  theta if fire else None)
     print(json.dumps(line), flush=True)
     return 0
 
 
-def other_cpu_baseline(c, inp, slopes):
+def other_cpu_baseline(c, inp, slopes, fire_theta=None):
     """The oracle on a bounded sample of one side workload: whole heads
     (dense) or whole sequences of a few heads (packed)."""
     import numpy as np
     import oracle
     kw = dict(scale=c.scale, causal=c.causal, bias=c.bias, num_buckets=c.num_buckets,
               max_distance=c.max_distance, bidirectional=c.bidirectional)
-    if c.bias == "t5":
+    if fire_theta is not None:
+        kw["bias"] = "fire"
+        kw["fire"] = fire_theta.astype(np.float64)
+        kw["fire_hidden"] = FIRE_HIDDEN
+    elif c.bias == "t5":
         kw["table"] = inp.table.astype(np.float64)
     if c.bias == "alibi":
         kw["slopes"] = slopes.astype(np.float64)
@@ -549,7 +568,7 @@ def other_cpu_baseline(c, inp, slopes):
         flops = 3.5 * 4.0 * c.head_dim * float((inp.lengths.astype(np.float64) ** 2).sum())
         return _time_oracle(work, flops * len(heads),
                             f"all {len(inp.lengths)} sequences of heads {heads} of {c.heads}")
-    npairs = 1 if c.seqlen >= 16384 else 48
+    npairs = 1 if c.seqlen >= 16384 or fire_theta is not None else 48
     pairs = [(i % c.batch, (5 * i + 1) % c.heads) for i in range(npairs)]
     work = [lambda: oracle.attention_fwd(f["q"], f["k"], f["v"], pairs=pairs, **kw),
             lambda: oracle.attention_bwd(f["q"], f["k"], f["v"], f["do"], pairs=pairs, **kw)]
