@@ -310,7 +310,7 @@ size_t rope_table_bytes(const fa::Problem &p) {
 }
 
 struct FwdLayout {
-  size_t krot = 0, rope_cs = 0, prefix = 0, sched = 0, fire_tab = 0, total = 0;
+  size_t krot = 0, rope_cs = 0, prefix = 0, sched = 0, fire_tab = 0, fire_dist = 0, total = 0;
   int nsched = 0;
 };
 
@@ -330,14 +330,17 @@ FwdLayout fwd_layout(const fa::Problem &p) {
     L.prefix = c.take((size_t)fa::sched_prefix_ints(p.nbatch) * 4);
     L.sched = c.take((size_t)L.nsched * 16);
   }
-  if (p.bias == FA_BIAS_FIRE) L.fire_tab = c.take(fa::fire_tab_floats(p.heads) * 4);
+  if (p.bias == FA_BIAS_FIRE) {
+    L.fire_tab = c.take(fa::fire_tab_floats(p.heads) * 4);
+    L.fire_dist = c.take(fa::fire_dist_floats(p.seqlen) * 4);
+  }
   L.total = c.off;
   return L;
 }
 
 struct BwdLayout {
   size_t qrot = 0, krot = 0, rope_cs = 0, delta = 0, part = 0, prefix = 0, sched = 0,
-         dense_ws = 0, fire_tab = 0, fire_g = 0, total = 0;
+         dense_ws = 0, fire_tab = 0, fire_dist = 0, fire_g = 0, total = 0;
   int nsched = 0;
   bool has_part = false;
   bool has_dense_ws = false;   // per-batch dense bias gradients, summed afterwards
@@ -370,6 +373,7 @@ BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
   }
   if (p.bias == FA_BIAS_FIRE) {
     L.fire_tab = c.take(fa::fire_tab_floats(p.heads) * 4);
+    L.fire_dist = c.take(fa::fire_dist_floats(p.seqlen) * 4);
     if (want_dtable) L.fire_g = c.take((size_t)fa::kFireGradRows * p.heads * 4);
   }
   L.has_dense_ws = want_dtable && p.bias == FA_BIAS_DENSE && p.dense_batch == 1 && p.nbatch > 1;
@@ -391,12 +395,13 @@ fa_status run_fwd(const fa::Problem &p, const void *q, const void *k, const void
     return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 ws == nullptr ? (size_t)0 : ws_bytes);
   if (p.total == 0 || (!p.varlen && (p.nbatch == 0 || p.seqlen == 0))) return FA_OK;
-  fa::FwdBuffers b{q, k, v, o, lse, nullptr, nullptr};
+  fa::FwdBuffers b{q, k, v, o, lse, nullptr, nullptr, nullptr};
   hipError_t e;
   if (p.bias == FA_BIAS_FIRE) {
-    e = fa::launch_fire_setup(p, at<float>(ws, L.fire_tab), s);
-    if (e != hipSuccess) return hip_fail(e, "FIRE segment table");
+    e = fa::launch_fire_setup(p, at<float>(ws, L.fire_tab), at<float>(ws, L.fire_dist), s);
+    if (e != hipSuccess) return hip_fail(e, "FIRE tables");
     b.fire_tab = at<float>(ws, L.fire_tab);
+    b.fire_dist = at<float>(ws, L.fire_dist);
   }
   if (p.rope_base > 0.f) {
     e = fa::launch_rope_table(p, at<double2>(ws, L.rope_cs), s);
@@ -463,9 +468,10 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   b.part = L.has_part ? at<float>(ws, L.part) : nullptr;
   b.dtable = t5grad ? dtable : nullptr;
   if (p.bias == FA_BIAS_FIRE) {
-    e = fa::launch_fire_setup(p, at<float>(ws, L.fire_tab), s);
-    if (e != hipSuccess) return hip_fail(e, "FIRE segment table");
+    e = fa::launch_fire_setup(p, at<float>(ws, L.fire_tab), at<float>(ws, L.fire_dist), s);
+    if (e != hipSuccess) return hip_fail(e, "FIRE tables");
     b.fire_tab = at<float>(ws, L.fire_tab);
+    b.fire_dist = at<float>(ws, L.fire_dist);
     b.fire_g = firegrad ? at<float>(ws, L.fire_g) : nullptr;
   }
   b.dbias = densegrad ? dtable : nullptr;
@@ -498,6 +504,10 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
   e = timed(FA_KERNEL_BWD_DKV, s,
             [&] { return fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdMain, s); });
   if (e != hipSuccess) return hip_fail(e, "backward dkv kernel");
+  if (firegrad) {
+    e = fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdFire, s);
+    if (e != hipSuccess) return hip_fail(e, "FIRE gradient sums");
+  }
   e = fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdReduce, s);
   if (e != hipSuccess) return hip_fail(e, "table-gradient reduction");
   if (firegrad) {

@@ -46,6 +46,7 @@ struct BwdArgs {
   uint16_t *dq, *dk, *dv;  // bf16 outputs
   const double2 *rope_cs;   // RoPE: (cos, sin) [seqlen, D/2], or nullptr
   const float *fire_tab;   // FIRE segment table (fa_internal.h), or nullptr
+  const float *fire_dist;  // FIRE distance table, or nullptr
   float *delta;            // -D_i, same layout as lse
   float *nls;              // -lse_i / scale, same layout (seed of the dkv kernel's S)
   float *part;             // [nb, nwg] table-gradient partials (FIRE: nb = kFireGradRows)
@@ -238,9 +239,7 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
   FireLane fl;
   if constexpr (BIAS == kBiasFire) {
     fire_load(a.fire_tab, h, fire_mem, tid, NT);
-    fl.tab = fire_mem;
-    fl.c = a.fire_tab[2];
-    fl.inv = fire_row_inv(fl.c, a.fire_tab[3], myrow);
+    fl = fire_lane(a.fire_tab, a.fire_dist, a.seqlen, fire_mem, myrow);
   }
 
   const int kend = CAUSAL ? min(L, q0 + BR) : L;
@@ -334,10 +333,10 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
       bool fast;
       if constexpr (NKB == 2)
         fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut, slope_l2,
-                                          bconst, bv, fl);
+                                          bconst, bv, &fl);
       else
         fast = score_block_T<BIAS, CAUSAL>(sacc[0], j0, wrow0, il, hl, L, c, sat, lut,
-                                           slope_l2, bconst, bv[0], fl);
+                                           slope_l2, bconst, bv[0], &fl);
       const float cc = fast ? c : 1.f;
       const float sub = bconst - lse2;
       // per 16-key group: P o (dP - Dc) as hi + lo fragments and P as bf16,
@@ -401,6 +400,208 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
 }
 
 // ---------------------------------------------------------------------------
+// FIRE parameter gradient: a query-parallel pass after the dq kernel
+// ---------------------------------------------------------------------------
+// The five per-(head, segment) sums of fire.hip need dS with the exact D,
+// which the dq kernel knows only after its sweep.  This pass repeats the
+// dq kernel's S and dP products (no dQ products, no hi/lo splits) with D
+// read back, so each lane owns one query row: the row's weights (1 / log2 E,
+// max(L, i) / (E ln E), [i < L]) are per-lane constants and only three sums
+// per element remain (dS, dS x, dS d / e), weighted per lane when the
+// wave's run in a segment ends.  Along the sweep (keys ascending) a row's x
+// only falls, so a wave passes each segment about once.
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
+  constexpr int KT = D == 64 ? BC : 32;
+  constexpr int NKB = KT / 32;
+  constexpr bool kDoInLds = D == 128;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dost[kDoInLds ? BR * D : 8];
+  __shared__ float fire_mem[kFireLds];
+  __shared__ float fire_acc[4 * kFireGradRows];   // per wave
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, il = lane & 31;
+  const int g = xcd_remap(blockIdx.x, a.nwg);
+  Work w;
+  if (!locate<VARLEN>(a, g, w)) return;
+  const int L = w.L, h = w.h;
+  const int qt = VARLEN ? w.tile : (a.ntile - 1 - w.tile);
+
+  const int HD = a.heads * D;
+  const size_t base = ((size_t)w.tok0 * a.heads + h) * D;
+  const uint32_t nrec = ((uint32_t)(L - 1) * (uint32_t)HD + D) * 2u;
+  const rsrc_t rq = make_rsrc(a.q + base, nrec);
+  const rsrc_t rdo = make_rsrc(a.dout + base, nrec);
+  const int q0 = qt * BR;
+  const int wrow0 = q0 + 32 * wave;
+  const int myrow = wrow0 + il;
+  const bool wave_live = wrow0 < L;
+  const bool row_live = myrow < L;
+
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const uint32_t off = ((uint32_t)myrow * (uint32_t)HD + 16 * s + 8 * hl) * 2u;
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    df[s] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+  }
+  if constexpr (kDoInLds)
+    dma_tile<D, BR, 4>(dma_desc(a.dout + base, nrec), HD, q0, dost, wave, lane);
+  const float lse2 = row_live ? a.lse[w.lse_base + myrow] * kLog2e : 0.f;
+  const float nd = row_live ? a.delta[w.lse_base + myrow] : 0.f;   // -D_i (dlse folded in)
+
+  fire_load(a.fire_tab, h, fire_mem, tid, NT);
+  for (int i = tid; i < 4 * kFireGradRows; i += NT) fire_acc[i] = 0.f;
+  FireLane fl = fire_lane(a.fire_tab, a.fire_dist, a.seqlen, fire_mem, myrow);
+  // the row's weights of dx/dc and dx/dL (see fire.hip)
+  const float fc = a.fire_tab[2], fL = a.fire_tab[3];
+  const float mrow = fmaxf(fL, (float)myrow);
+  const float Erow = fmaf(fc, mrow, 1.f);
+  const float wc = mrow * fl.inv / (Erow * kLn2);
+  const float lf = (float)myrow < fL ? 1.f : 0.f;
+  // Sums of the wave's current segment w_cur, per lane, until the wave's
+  // keys leave it; then each lane weights its row's terms, the wave adds
+  // them up (a fixed butterfly) and lane 0 adds them to the wave's own LDS
+  // sums: no atomics, a fixed order, one flush per segment change.
+  float u0 = 0.f, u1 = 0.f, u2 = 0.f;
+  int w_cur = -1;
+  float *const my_acc = fire_acc + wave * kFireGradRows;
+  auto flush = [&](int sg, float g0, float g1, float g2) {
+    float t[kFireTerms] = {g0, g1, g2 * fl.inv, g1 * wc, g1 * lf};
+#pragma unroll
+    for (int q = 0; q < kFireTerms; ++q)
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) t[q] += __shfl_xor(t[q], off);
+    if (lane == 0)
+#pragma unroll
+      for (int q = 0; q < kFireTerms; ++q) my_acc[sg * kFireTerms + q] += t[q];
+  };
+
+  const int kend = min(L, q0 + BR);
+  const int nkt = (kend + KT - 1) / KT;
+  const i32x4 dk_src = dma_desc(a.k + base, nrec), dv_src = dma_desc(a.v + base, nrec);
+  auto fill = [&](int j0, int buf) {
+    dma_tile<D, KT, 4>(dk_src, HD, j0, ks[buf], wave, lane);
+    dma_tile<D, KT, 4>(dv_src, HD, j0, vs[buf], wave, lane);
+  };
+  int kof[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) kof[s] = swz_off<D>(il, 2 * s + hl);
+  const float c = a.scale_log2;
+
+  wait_vmem_loads();
+  if (nkt > 0) fill(0, 0);
+  wait_vmem_loads();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int j0 = kt * KT;
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) fill(j0 + KT, buf ^ 1);
+    const bool active = wave_live && j0 <= wrow0 + 31;
+    if (active) {
+      f32x16 sacc[NKB], pacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[kb] = f32x16{};
+        pacc[kb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&ks[buf][kof[s] + 32 * kb * D]);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&vs[buf][kof[s] + 32 * kb * D]);
+          bf16x8 dfs;
+          if constexpr (kDoInLds)
+            dfs = *reinterpret_cast<const bf16x8 *>(&dost[kof[s] + 32 * wave * D]);
+          else
+            dfs = df[s];
+          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+          pacc[kb] = mfma32(vf, dfs, pacc[kb]);
+        }
+      }
+      // scores with the bias, every key's x and the lane's segment range
+      constexpr int omax = 32 * NKB - 5;   // the lane's farthest key offset
+      const int rbase = j0 - myrow + 4 * hl;
+      const int jb = j0 + 4 * hl;
+      const bool mask_l = j0 + KT > L;
+      float xs[NKB][16];
+      int shi;
+      fire_scores<NKB, true, true>(sacc, omax, rbase, mask_l ? L - jb : KT, true, c, fl, xs,
+                                   &shi);
+      const int slo = fl.seg;
+      // dS
+      float gs[NKB][16];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - lse2);
+          gs[kb][r] = row_live ? p * (pacc[kb][r] + nd) : 0.f;
+        }
+      // the three sums of the keys in segment sg (t_sg <= x < t_sg+1; sg < 0:
+      // every key); d / e from the distance table (element 3 - e of the four
+      // entries from distance -rbase - 32 kb - 8 q - 3)
+      auto sums = [&](int sg, float &g0, float &g1, float &g2) {
+        const float tlo = sg < 0 ? -INFINITY : fl.tab[kFireOffT + max(sg, 0)];
+        const float thi = sg < 0 ? INFINITY : fl.tab[kFireOffT + max(sg, 0) + 1];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 de = fire_dist4(fl, -rbase - 32 * kb - 8 * q - 3, fl.dist_half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * q + e;
+              const float x = xs[kb][r];
+              const float gv = (x >= tlo && x < thi) ? gs[kb][r] : 0.f;
+              g0 += gv;
+              g1 = fmaf(gv, x, g1);
+              g2 = fmaf(gv, de[3 - e], g2);
+            }
+          }
+      };
+      // the wave's segment range over its lanes' ranges
+      int wlo = slo, whi = shi;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        wlo = min(wlo, __shfl_xor(wlo, off));
+        whi = max(whi, __shfl_xor(whi, off));
+      }
+      if (wlo == whi) {
+        if (wlo != w_cur) {
+          if (w_cur >= 0) flush(w_cur, u0, u1, u2);
+          u0 = u1 = u2 = 0.f;
+          w_cur = wlo;
+        }
+        sums(-1, u0, u1, u2);
+      } else {
+        if (w_cur >= 0) flush(w_cur, u0, u1, u2);
+        u0 = u1 = u2 = 0.f;
+        w_cur = -1;
+        for (int sg = wlo; sg <= whi; ++sg) {
+          float g0 = 0.f, g1 = 0.f, g2 = 0.f;
+          sums(sg, g0, g1, g2);
+          flush(sg, g0, g1, g2);
+        }
+      }
+    }
+    wait_vmem_loads();
+    __syncthreads();
+  }
+  // (wave-uniform: every lane of a wave sees the same w_cur)
+  if (w_cur >= 0) flush(w_cur, u0, u1, u2);
+  __syncthreads();
+  // the four waves' sums in a fixed order, one partial per workgroup
+  for (int i = tid; i < kFireGradRows; i += NT) {
+    float t = 0.f;
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) t += fire_acc[w4 * kFireGradRows + i];
+    a.part[(size_t)i * a.nwg + w.part] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dkv kernel
 // ---------------------------------------------------------------------------
 template <int D>
@@ -429,22 +630,13 @@ __host__ __device__ inline size_t dkv_dyn_bytes(int sat, bool t5, bool dbias) {
 // row offsets of the Q/dO operands are computed where they are used, which
 // leaves room for two workgroups per CU without spilling; the T5 (with its
 // table gradient) and dense-bias variants need the registers and run one.
-// FIRE with its parameter gradient runs one at either head_dim (the five
-// per-segment sums and their per-row weights).
-template <int D, int BIAS, bool DBIAS>
+template <int D, int BIAS>
 constexpr int dkv_wgs() {
-  if (BIAS == kBiasFire && DBIAS) return 1;   // the FIRE gradient sums' registers
   return D == 64 || BIAS == kBiasAlibi || BIAS == kBiasNone ? 2 : 1;
 }
 
-// FIRE in the key-parallel kernel: per query block, each row's normaliser
-// 1 / log2(E_i) (E_i = c max(L, i) + 1), the weight max(L, i) / (E_i ln E_i)
-// of dx/dc and the flag i < L (dx/dL), kFireRowVals floats per row.
-constexpr int kFireRowVals = 3;
-
 template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool DBIAS>
-__global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS, DBIAS>())) void bwd_dkv_kernel(
-    const BwdArgs a) {
+__global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const BwdArgs a) {
   constexpr int QB = DkvTile<D>::QB;
   constexpr bool kVInLds = D == 128 && (BIAS == kBiasAlibi || BIAS == kBiasNone);
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kVInLds ? BKV * D : 8];
@@ -458,8 +650,7 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS, DBIAS>())) void bwd_dkv_kerne
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   constexpr bool kFire = BIAS == kBiasFire;
   __shared__ float fire_mem[kFire ? kFireLds : 1];
-  __shared__ __attribute__((aligned(16))) float fire_rows[kFire ? 2 * kFireRowVals * 64 : 1];
-  __shared__ float fire_acc[kFire && DBIAS ? 4 * kFireGradRows : 1];   // per wave
+  __shared__ __attribute__((aligned(16))) float fire_rows[kFire ? 2 * 64 : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -533,40 +724,22 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS, DBIAS>())) void bwd_dkv_kerne
   float *const mybins = bins + wave * nbin;
   float *const mytile = tiles + wave * (32 * kTilePitch);
   FireLane fl;
-  float fire_L = 0.f;
+  float fire_c = 0.f, fire_L = 0.f;
   if constexpr (kFire) {
     fire_load(a.fire_tab, h, fire_mem, tid, NT);
-    fl.tab = fire_mem;
-    fl.c = a.fire_tab[2];
+    fl = fire_lane(a.fire_tab, a.fire_dist, a.seqlen, fire_mem, 0);
+    fire_c = a.fire_tab[2];
     fire_L = a.fire_tab[3];
-    if constexpr (DBIAS)
-      for (int i = tid; i < 4 * kFireGradRows; i += NT) fire_acc[i] = 0.f;
   }
-  // FIRE row values of the query block at q0 into buffer buf
+  // FIRE: each row's 1 / log2(c max(L, i) + 1) for the query block at q0,
+  // into buffer buf
   auto fire_fill_rows = [&](int q0, int buf) {
     if constexpr (kFire) {
       if (tid < QB) {
         const int i = q0 + tid;
-        const float m = fmaxf(fire_L, (float)i);
-        const float E = fmaf(fl.c, m, 1.f);
-        const float lE = __builtin_amdgcn_logf(E);
-        float *rw = fire_rows + buf * (kFireRowVals * 64);
-        rw[tid] = 1.f / lE;
-        rw[64 + tid] = m / (E * lE * kLn2);
-        rw[128 + tid] = (float)i < fire_L ? 1.f : 0.f;
+        fire_rows[buf * 64 + tid] =
+            1.f / __builtin_amdgcn_logf(fmaf(fire_c, fmaxf(fire_L, (float)i), 1.f));
       }
-    }
-  };
-  // FIRE gradient sums of the segment s_cur (fast lanes keep them in
-  // registers until their segment changes) and the flush into this wave's
-  // LDS sums
-  float fr[kFireTerms] = {0.f, 0.f, 0.f, 0.f, 0.f};
-  int s_cur = -1;
-  float *const my_acc = fire_acc + wave * kFireGradRows;
-  auto fire_flush = [&](int sg, const float (&v)[kFireTerms]) {
-    if constexpr (kFire && DBIAS) {
-#pragma unroll
-      for (int q = 0; q < kFireTerms; ++q) atomicAdd(&my_acc[sg * kFireTerms + q], v[q]);
     }
   };
 
@@ -774,23 +947,21 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS, DBIAS>())) void bwd_dkv_kerne
       float fx[kFire ? 16 : 1];
       int fslo = 0, fshi = 0;
       if constexpr (kFire) {
-        // element r: row irow0 + 4hl + roff, roff = 8(r/4) + r%4, key myk;
-        // psi argument e = c (row - myk) + 1, at least 1 (masked pairs)
-        const float u0 = fmaf(fl.c, (float)(irow0 + 4 * hl - myk), 1.f);
-        const float *rw = fire_rows + buf * (kFireRowVals * 64) + 32 * rb + 4 * hl;
-        // (e of row offset 8 qq + i: one fma per four rows, then + c i)
-        const float ce[4] = {0.f, fl.c, 2.f * fl.c, 3.f * fl.c};
+        // element r: row irow0 + 4hl + roff, roff = 8(r/4) + r%4, key myk,
+        // distance d0 + roff with d0 = irow0 + 4hl - myk; x = psi(d) / log2(E_row)
+        const int d0 = irow0 + 4 * hl - myk;
+        const float *rw = fire_rows + buf * 64 + 32 * rb + 4 * hl;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const f32x4 inv4 = *reinterpret_cast<const f32x4 *>(&rw[8 * qq]);
-          const float g = fmaf(fl.c, (float)(8 * qq), u0);
+          const f32x4 ps = fire_dist4(fl, d0 + 8 * qq);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            fx[4 * qq + e] = __builtin_amdgcn_logf(fmaxf(g + ce[e], 1.f)) * inv4[e];
+          for (int e = 0; e < 4; ++e) fx[4 * qq + e] = ps[e] * inv4[e];
         }
         // x grows with the row: elements 0 and 15 bound the lane's range
-        fslo = fire_seg(fl.tab, fx[0]);
-        fshi = fire_seg(fl.tab, fx[15]);
+        fslo = fire_walk(fl.tab, fx[0], fl.seg);
+        fshi = fire_walk(fl.tab, fx[15], fslo);
+        fl.seg = fshi;
         float fb[16];
         if (fslo == fshi) {
           const float A = fl.tab[kFireOffA + fslo], B = fl.tab[kFireOffB + fslo];
@@ -806,11 +977,16 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS, DBIAS>())) void bwd_dkv_kerne
             fb[r] = fmaf(up ? B1 : B0, fx[r], up ? A1 : A0);
           }
         } else {
+          // the lower segment's line bent at each kink in between (the bias
+          // is continuous; see fire_scores)
+          const float A = fl.tab[kFireOffA + fslo], B = fl.tab[kFireOffB + fslo];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int sg = fire_seg(fl.tab, fx[r]);
-            fb[r] = fmaf(fl.tab[kFireOffB + sg], fx[r], fl.tab[kFireOffA + sg]);
-            __builtin_amdgcn_sched_barrier(0);   // one search at a time
+          for (int r = 0; r < 16; ++r) fb[r] = fmaf(B, fx[r], A);
+          for (int k = fslo + 1; k <= fshi; ++k) {
+            const float tk = fl.tab[kFireOffT + k];
+            const float dB = fl.tab[kFireOffB + k] - fl.tab[kFireOffB + k - 1];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) fb[r] = fmaf(dB, fmaxf(fx[r] - tk, 0.f), fb[r]);
           }
         }
         const int rbase = myk - (irow0 + 4 * hl);
@@ -890,57 +1066,6 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS, DBIAS>())) void bwd_dkv_kerne
         }
       }
       block_dvdk(buf, rb, p, ds);
-      if constexpr (DBIAS && kFire) {
-        // the five sums' terms (see fire.hip) of the elements in segment sg
-        // (t_sg <= x < t_sg+1; sg < 0: every element), added to v; masked
-        // pairs carry dS = 0 and a finite x
-        const float *rw = fire_rows + buf * (kFireRowVals * 64) + 32 * rb + 4 * hl;
-        const float d0 = (float)(irow0 + 4 * hl - myk);
-        const float u0 = fmaf(fl.c, d0, 1.f);
-        const float ce[4] = {0.f, fl.c, 2.f * fl.c, 3.f * fl.c};
-        const float de[4] = {0.f, 1.f, 2.f, 3.f};
-        auto add_terms = [&](float (&v)[kFireTerms], int sg) {
-          const float tlo = sg < 0 ? -INFINITY : fl.tab[kFireOffT + max(sg, 0)];
-          const float thi = sg < 0 ? INFINITY : fl.tab[kFireOffT + max(sg, 0) + 1];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const f32x4 inv4 = *reinterpret_cast<const f32x4 *>(&rw[8 * qq]);
-            const f32x4 wc4 = *reinterpret_cast<const f32x4 *>(&rw[64 + 8 * qq]);
-            const f32x4 lf4 = *reinterpret_cast<const f32x4 *>(&rw[128 + 8 * qq]);
-            const float eq = fmaf(fl.c, (float)(8 * qq), u0), dq0 = d0 + (float)(8 * qq);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * qq + e;
-              const float ee = fmaxf(eq + ce[e], 1.f);
-              // x again (the same operations as for the score): keeping the
-              // block's 16 values across the products would spill
-              const float x = __builtin_amdgcn_logf(ee) * inv4[e];
-              const float g = (x >= tlo && x < thi) ? ds[r] : 0.f;
-              const float gx = g * x;
-              v[0] += g;
-              v[1] += gx;
-              v[2] = fmaf(g, (dq0 + de[e]) * __builtin_amdgcn_rcpf(ee) * inv4[e], v[2]);
-              v[3] = fmaf(gx, wc4[e], v[3]);
-              v[4] = fmaf(gx, lf4[e], v[4]);
-            }
-          }
-        };
-        if (fslo == fshi) {
-          if (fslo != s_cur) {
-            if (s_cur >= 0) fire_flush(s_cur, fr);
-#pragma unroll
-            for (int q = 0; q < kFireTerms; ++q) fr[q] = 0.f;
-            s_cur = fslo;
-          }
-          add_terms(fr, -1);
-        } else {
-          for (int sg = fslo; sg <= fshi; ++sg) {
-            float v[kFireTerms] = {0.f, 0.f, 0.f, 0.f, 0.f};
-            add_terms(v, sg);
-            fire_flush(sg, v);
-          }
-        }
-      }
       if constexpr (DBIAS && BIAS == kBiasT5) {
         if (!fast) {
           // diagonal il (hl = 0) covers rows below 32 - il, diagonal il - 32
@@ -999,17 +1124,6 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS, DBIAS>())) void bwd_dkv_kerne
       buf_store8(rdk, el * 2u, k2);
     }
 
-  if constexpr (DBIAS && kFire) {
-    if (s_cur >= 0) fire_flush(s_cur, fr);
-    __syncthreads();
-    // the four waves' sums in a fixed order, one partial per workgroup
-    for (int i = tid; i < kFireGradRows; i += NT) {
-      float t = 0.f;
-#pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4) t += fire_acc[w4 * kFireGradRows + i];
-      a.part[(size_t)i * a.nwg + w.part] = t;
-    }
-  }
   if constexpr (DBIAS && BIAS == kBiasT5) {
     // saturated-block sums: reduce over the wave, then fold into the end bins
     float s0 = ub0, s1 = ub1;
@@ -1125,8 +1239,14 @@ hipError_t launch_dkv_t(const BwdArgs &a, hipStream_t s) {
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 hipError_t launch_pair(const BwdArgs &a, int phase, bool dbias, hipStream_t s) {
   if (phase == kBwdPre) return launch_dq_t<D, BIAS, CAUSAL, VARLEN>(a, s);
-  if constexpr (BIAS == kBiasT5 || BIAS == kBiasDense || BIAS == kBiasFire) {
+  if constexpr (BIAS == kBiasT5 || BIAS == kBiasDense) {
     if (dbias) return launch_dkv_t<D, BIAS, CAUSAL, VARLEN, true>(a, s);
+  }
+  if constexpr (BIAS == kBiasFire && CAUSAL) {
+    if (phase == kBwdFire) {
+      hipLaunchKernelGGL((bwd_fire_kernel<D, VARLEN>), dim3(a.nwg), dim3(NT), 0, s, a);
+      return hipGetLastError();
+    }
   }
   return launch_dkv_t<D, BIAS, CAUSAL, VARLEN, false>(a, s);
 }
@@ -1187,6 +1307,7 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.dv = static_cast<uint16_t *>(b.dv);
   a.rope_cs = b.rope_cs;
   a.fire_tab = b.fire_tab;
+  a.fire_dist = b.fire_dist;
   a.delta = b.delta;
   a.nls = b.delta + (size_t)p.total * p.heads;
   a.part = b.part;
@@ -1214,7 +1335,8 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
     a.nwg = p.nbatch * p.heads * a.ntile;
   }
   if (a.nwg <= 0) return hipSuccess;
-  const bool dbias = b.part != nullptr || a.dbias != nullptr;
+  const bool dbias = (b.part != nullptr && p.bias != kBiasFire) || a.dbias != nullptr;
+  if (phase == kBwdFire && (p.bias != kBiasFire || b.part == nullptr)) return hipSuccess;
   if (phase == kBwdReduce) {
     if (b.part == nullptr) return hipSuccess;
     hipLaunchKernelGGL(dbias_reduce_kernel, dim3(a.nb * p.heads), dim3(256), 0, s, a.part,

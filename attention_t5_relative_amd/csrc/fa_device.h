@@ -214,24 +214,54 @@ __device__ __forceinline__ int t5_bucket_dev(int r, const T5Geometry &g) {
 constexpr int kLutPad = 96;
 
 // FIRE (see fa_internal.h and fire.hip): a workgroup's LDS copy of the
-// segment table (the shared part, then its head's A and B), and per lane the
-// constants of its query row.
+// segment table (the shared part, then its head's A and B), the distance
+// table, and per lane the constants of its query row and the segment its
+// sweep has reached.
 struct FireLane {
   const float *tab = nullptr;   // LDS, kFireLds floats
+  rsrc_t dist;                  // psi(d) at [kFireDistPad + d], then d / (c d + 1)
+  uint32_t dist_half = 0;       // byte offset of the d / (c d + 1) half
   float c = 0.f;                // psi(t) = log(c t + 1)
   float inv = 0.f;              // 1 / log2(c max(L, i) + 1) for the lane's row i
+  int seg = -1;                 // segment of the last x looked up (-1: none yet)
 };
 
+__device__ __forceinline__ FireLane fire_lane(const float *gtab, const float *dist, int maxlen,
+                                              const float *lds, int row) {
+  FireLane fl;
+  fl.tab = lds;
+  const uint32_t n = (uint32_t)maxlen + 2u * kFireDistPad;
+  fl.dist = make_rsrc(dist, 8u * n);
+  fl.dist_half = 4u * n;
+  fl.c = gtab[2];
+  fl.inv = 1.f / __builtin_amdgcn_logf(fmaf(fl.c, fmaxf(gtab[3], (float)row), 1.f));
+  return fl;
+}
+
+// The four table entries psi(d0) .. psi(d0 + 3) (half = 0) or d / (c d + 1)
+// (half = fl.dist_half), d0 >= -kFireDistPad.
+__device__ __forceinline__ f32x4 fire_dist4(const FireLane &fl, int d0, uint32_t half = 0) {
+  return __builtin_bit_cast(f32x4,
+                            buf_load16(fl.dist, half + 4u * (uint32_t)(kFireDistPad + d0)));
+}
+
 // Segment of x: the number of kinks t_s <= x, by a branch-free binary search
-// over t_1 .. t_127 (+inf past the last kink).  A NaN x (a masked pair; the
-// device code is built without NaN semantics) still yields an index inside
-// the table; the caller discards that element.
+// over t_1 .. t_127 (+inf past the last kink).
 __device__ __forceinline__ int fire_seg(const float *tab, float x) {
   int s = 0;
 #pragma unroll
   for (int step = kFireTEnd / 2; step >= 1; step >>= 1)
     s += (x >= tab[kFireOffT + s + step]) ? step : 0;
-  return min(s, kFireMaxHidden);   // in range whatever a NaN compare gave
+  return min(s, kFireMaxHidden);
+}
+
+// The same, walking from a nearby segment s (x moves little between the
+// tiles of one lane's sweep, so this is a read or two); s < 0 searches.
+__device__ __forceinline__ int fire_walk(const float *tab, float x, int s) {
+  if (s < 0) return fire_seg(tab, x);
+  while (s > 0 && x < tab[kFireOffT + s]) --s;
+  while (s < kFireMaxHidden && x >= tab[kFireOffT + s + 1]) ++s;
+  return s;
 }
 
 // Copy the table's shared part and head h's coefficients into LDS (all
@@ -242,70 +272,136 @@ __device__ __forceinline__ void fire_load(const float *gtab, int h, float *lds, 
                              : gtab[kFireShared + (size_t)h * kFireHeadStride + (i - kFireShared)];
 }
 
-// 1 / log2(c max(L, i) + 1): the normaliser of row i's distances (log2
-// units, so x = log2(c d + 1) times this).
-__device__ __forceinline__ float fire_row_inv(float c, float Lthr, int i) {
-  return 1.f / __builtin_amdgcn_logf(fmaf(c, fmaxf(Lthr, (float)i), 1.f));
-}
-
 // Scores (log2 units, in place) of one lane's keys in a query-parallel tile
 // of NKB 32-key blocks with the FIRE bias: element (kb, r) is key offset
 // off = 32 kb + 8 (r / 4) + r % 4 past the lane's first key, distance
-// d = -(rbase + off), psi argument e = c d + 1 = u0 - c off.  x is monotone
-// in d, so the segments of the nearest and farthest visible keys (offsets 0
-// and omax) bound every key's: equal, the bias is A + (B inv) log2(e); one
-// kink apart, each key picks its side of the kink; otherwise each key
-// searches.  Masked keys (causal, or off >= lim) become -inf.
-template <int NKB>
+// d = -(rbase + off), x = psi(d) inv.  TABLE reads psi from the distance
+// table (one 16-byte load per four keys; the tile's 32 values are held from
+// load to use, which costs registers), otherwise each key takes a log2 (a
+// transcendental, which the exponential of the softmax competes for).
+// x is monotone in d, so the segments of the nearest and farthest keys
+// (offsets 0 and omax) bound every key's: equal, the bias is A + B x; apart,
+// every key adds to the lower segment's line the bend of each kink in
+// between (without the table, a single kink is taken by a select).  Masked keys (causal, or off >= lim)
+// become -inf.  KEEP_X also returns every key's x (0 for keys after the
+// query) and the nearest key's segment (the farthest one's stays in fl.seg).
+template <int NKB, bool TABLE, bool KEEP_X = false>
 __device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int rbase, int lim,
-                                            bool mask_c, float c, const FireLane &fl) {
+                                            bool mask_c, float c, FireLane &fl,
+                                            float (*xkeep)[16] = nullptr, int *seg_hi = nullptr) {
   const float cn = -fl.c;
   const float u0 = fmaf(cn, (float)rbase, 1.f);
-  const float xn = __builtin_amdgcn_logf(fmaxf(u0, 1.f)) * fl.inv;
-  const float xf = __builtin_amdgcn_logf(fmaxf(fmaf(cn, (float)omax, u0), 1.f)) * fl.inv;
-  const int shi = fire_seg(fl.tab, xn), slo = fire_seg(fl.tab, xf);
-  // e of key offset 32 kb + 8 q + i: one fma per group of four keys, then
-  // one add of -c i (the offsets as per-key float constants would each be
-  // held in a register)
+  // without the table: e of key offset 32 kb + 8 q + i is one fma per group
+  // of four keys, then one add of -c i (the offsets as per-key float
+  // constants would each be held in a register); the range ends use the
+  // same operations
   const float ce[4] = {0.f, cn, 2.f * cn, 3.f * cn};
-  auto e_of = [&](int kb, int q, int i, float &g) {
-    if (i == 0) g = fmaf(cn, (float)(32 * kb + 8 * q), u0);
-    return g + ce[i];
-  };
-  float g = 0.f;
-  if (shi == slo) {
-    const float A = fl.tab[kFireOffA + slo], Bi = fl.tab[kFireOffB + slo] * fl.inv;
+  f32x4 ps[TABLE ? NKB : 1][4];
+  float xn, xf;
+  if constexpr (TABLE) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float l = __builtin_amdgcn_logf(e_of(kb, r >> 2, r & 3, g));
-        sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(Bi, l, A));
-      }
-  } else if (shi == slo + 1) {
-    const float tk = fl.tab[kFireOffT + shi];
-    const float A0 = fl.tab[kFireOffA + slo], B0 = fl.tab[kFireOffB + slo];
-    const float A1 = fl.tab[kFireOffA + shi], B1 = fl.tab[kFireOffB + shi];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = __builtin_amdgcn_logf(e_of(kb, r >> 2, r & 3, g)) * fl.inv;
-        const bool up = x >= tk;
-        sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(up ? B1 : B0, x, up ? A1 : A0));
-      }
+      for (int q = 0; q < 4; ++q) ps[kb][q] = fire_dist4(fl, -rbase - 32 * kb - 8 * q - 3);
+    xn = ps[0][0][3] * fl.inv;
+    xf = ps[NKB - 1][3][0] * fl.inv;
   } else {
+    xn = __builtin_amdgcn_logf(fmaxf(u0, 1.f)) * fl.inv;
+    xf = __builtin_amdgcn_logf(fmaxf(fmaf(cn, (float)(omax - 3), u0) + ce[3], 1.f)) * fl.inv;
+  }
+  const int shi = fire_walk(fl.tab, xn, fl.seg);
+  const int slo = fire_walk(fl.tab, xf, shi);
+  fl.seg = slo;
+  if constexpr (KEEP_X) *seg_hi = shi;
+  if constexpr (TABLE) {
+    if (shi == slo) {
+      const float A = fl.tab[kFireOffA + slo], B = fl.tab[kFireOffB + slo];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = __builtin_amdgcn_logf(fmaxf(e_of(kb, r >> 2, r & 3, g), 1.f)) * fl.inv;
-        const int sg = fire_seg(fl.tab, x);
-        sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(fl.tab[kFireOffB + sg], x, fl.tab[kFireOffA + sg]));
-        // one key at a time: searches hoisted side by side would hold their
-        // registers all at once
-        __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < 16; ++r) {
+          const float x = ps[kb][r >> 2][3 - (r & 3)] * fl.inv;
+          if constexpr (KEEP_X) xkeep[kb][r] = x;
+          sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(B, x, A));
+        }
+    } else {
+      // b(x) = A_lo + B_lo x + sum over the kinks t_k above segment lo of
+      // (B_k - B_k-1) max(x - t_k, 0): b is continuous, so each kink only
+      // bends the line
+      const int span = shi - slo;
+      const float A = fl.tab[kFireOffA + slo], B = fl.tab[kFireOffB + slo];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = ps[kb][r >> 2][3 - (r & 3)] * fl.inv;
+          if constexpr (KEEP_X) xkeep[kb][r] = x;
+          sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(B, x, A));
+        }
+      for (int j = 1; j <= span; ++j) {
+        const int k = slo + j;
+        const float tk = fl.tab[kFireOffT + k];
+        const float dB = fl.tab[kFireOffB + k] - fl.tab[kFireOffB + k - 1];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][r] = fmaf(dB, fmaxf(ps[kb][r >> 2][3 - (r & 3)] * fl.inv - tk, 0.f),
+                               sacc[kb][r]);
       }
+    }
+  } else {
+    auto e_of = [&](int kb, int q, int i, float &g) {
+      if (i == 0) g = fmaf(cn, (float)(32 * kb + 8 * q), u0);
+      return g + ce[i];
+    };
+    float g = 0.f;
+    if (shi == slo) {
+      const float A = fl.tab[kFireOffA + slo], Bi = fl.tab[kFireOffB + slo] * fl.inv;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float l = __builtin_amdgcn_logf(e_of(kb, r >> 2, r & 3, g));
+          if constexpr (KEEP_X) xkeep[kb][r] = fmaxf(l, 0.f) * fl.inv;
+          sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(Bi, l, A));
+        }
+    } else if (shi == slo + 1) {
+      const float tk = fl.tab[kFireOffT + shi];
+      const float A0 = fl.tab[kFireOffA + slo], B0 = fl.tab[kFireOffB + slo];
+      const float A1 = fl.tab[kFireOffA + shi], B1 = fl.tab[kFireOffB + shi];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = __builtin_amdgcn_logf(e_of(kb, r >> 2, r & 3, g)) * fl.inv;
+          if constexpr (KEEP_X) xkeep[kb][r] = fmaxf(x, 0.f);
+          const bool up = x >= tk;
+          sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(up ? B1 : B0, x, up ? A1 : A0));
+        }
+    } else {
+      // the kink bends as above, one block of keys at a time holding its x
+      const int span = shi - slo;
+      const float A = fl.tab[kFireOffA + slo], B = fl.tab[kFireOffB + slo];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float xs[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          xs[r] = __builtin_amdgcn_logf(fmaxf(e_of(kb, r >> 2, r & 3, g), 1.f)) * fl.inv;
+          if constexpr (KEEP_X) xkeep[kb][r] = xs[r];
+          sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(B, xs[r], A));
+        }
+        for (int j = 1; j <= span; ++j) {
+          const int k = slo + j;
+          const float tk = fl.tab[kFireOffT + k];
+          const float dB = fl.tab[kFireOffB + k] - fl.tab[kFireOffB + k - 1];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][r] = fmaf(dB, fmaxf(xs[r] - tk, 0.f), sacc[kb][r]);
+        }
+      }
+    }
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -342,12 +438,12 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
 // The causal mask hides keys after the query; keys at or past L are masked.
 // A dense bias arrives as the lane's own values bv (bf16 bits, same order
 // as sacc; see dense_row_load).
-template <int BIAS, bool CAUSAL, bool ALIBI_LINEAR = true>
+template <int BIAS, bool CAUSAL, bool ALIBI_LINEAR = true, bool FIRE_TABLE = false>
 __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0, int il, int hl,
                                              int L, float c, int sat, const float *lut,
                                              float slope_l2, float &bconst,
                                              const uint16_t (&bv)[2][16],
-                                             const FireLane &fl = FireLane{}) {
+                                             FireLane *fl = nullptr) {
   const int rmin = j0 - (row0 + 31), rmax = j0 + 63 - row0;
   const bool mask_c = CAUSAL && rmax > 0;
   const bool mask_l = j0 + 64 > L;
@@ -379,7 +475,8 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
     return false;
   }
   if constexpr (BIAS == kBiasFire) {
-    fire_scores<2>(sacc, 59, rbase, mask_l ? L - jb : 64, mask_c, c, fl);
+    // (the distance table where the registers allow: the forward at 64)
+    fire_scores<2, FIRE_TABLE>(sacc, 59, rbase, mask_l ? L - jb : 64, mask_c, c, *fl);
     return false;
   }
   if constexpr (BIAS == kBiasAlibi && ALIBI_LINEAR) {
@@ -425,7 +522,7 @@ __device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, i
                                               int L, float c, int sat, const float *lut,
                                               float slope_l2, float &bconst,
                                               const uint16_t (&bv)[16],
-                                              const FireLane &fl = FireLane{}) {
+                                              FireLane *fl = nullptr) {
   const int rmin = jb0 - (row0 + 31), rmax = jb0 + 31 - row0;
   const bool mask_c = CAUSAL && rmax > 0;
   const bool mask_l = jb0 + 32 > L;
@@ -455,7 +552,7 @@ __device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, i
   }
   if constexpr (BIAS == kBiasFire) {
     f32x16 (&one)[1] = *reinterpret_cast<f32x16 (*)[1]>(&sacc);
-    fire_scores<1>(one, 27, rbase, mask_l ? L - jb : 32, mask_c, c, fl);
+    fire_scores<1, false>(one, 27, rbase, mask_l ? L - jb : 32, mask_c, c, *fl);
     return false;
   }
   if constexpr (BIAS == kBiasAlibi) {

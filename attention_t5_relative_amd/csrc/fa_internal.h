@@ -58,6 +58,16 @@ constexpr int kFireLds = kFireShared + kFireHeadStride;
 constexpr int kFireTerms = 5;                     // gradient sums per (head, segment)
 constexpr int kFireGradRows = kFireTerms * kFireSegs;
 static_assert(kFireOffT + kFireTEnd <= kFireShared, "FIRE table layout");
+// FIRE distance table (fire_dist_kernel): psi(d) = log2(c d + 1) at
+// [kFireDistPad + d] and d / (c d + 1) at [n + kFireDistPad + d],
+// n = maxlen + 2 kFireDistPad, for 0 <= d < maxlen + kFireDistPad and zero
+// for d < 0: the kernels read a tile's distances, down to -127 (keys after
+// the query near the diagonal) and up to maxlen + 126 (rows past a ragged
+// end), with no range test.
+constexpr int kFireDistPad = 128;
+__host__ __device__ inline size_t fire_dist_floats(int maxlen) {
+  return 2 * ((size_t)maxlen + 2 * kFireDistPad);
+}
 __host__ __device__ inline size_t fire_tab_floats(int heads) {
   return (size_t)kFireShared + (size_t)kFireHeadStride * heads;
 }
@@ -92,6 +102,7 @@ struct FwdBuffers {
   float *lse;
   const double2 *rope_cs;   // RoPE fp64 (cos, sin) table [seqlen, D/2] or nullptr
   const float *fire_tab;    // FIRE segment table or nullptr
+  const float *fire_dist;   // FIRE distance table or nullptr
 };
 
 struct BwdBuffers {
@@ -108,6 +119,7 @@ struct BwdBuffers {
   float *dbias;            // dense bias gradient fp32 [dense_batch, H, S, S] or nullptr
   float *dbias_batch;      // per-batch gradients [B, H, S, S] summed into dbias, or nullptr
   const float *fire_tab;   // FIRE segment table or nullptr
+  const float *fire_dist;  // FIRE distance table or nullptr
   float *fire_g;           // FIRE: reduced gradient sums [kFireGradRows, H] or nullptr
 };
 
@@ -129,7 +141,9 @@ hipError_t launch_rope_rotate(const Problem &p, const double2 *cs, const void *x
                               const void *x1, void *y1, hipStream_t s);
 int bwd_tile();
 int64_t bwd_num_parts(const Problem &p, int nsched);
-enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2 };   // dq, dkv, table reduce
+// dq, dkv, table-gradient reduction, FIRE gradient sums (between dkv and
+// the reduction)
+enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2, kBwdFire = 3 };
 hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
                             int phase, hipStream_t s);
 hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
@@ -137,7 +151,7 @@ hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *o
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
 // FIRE (fire.hip): the segment table from theta, and d(theta) from the
 // reduced per-(head, segment) gradient sums.
-hipError_t launch_fire_setup(const Problem &p, float *tab, hipStream_t s);
+hipError_t launch_fire_setup(const Problem &p, float *tab, float *dist, hipStream_t s);
 hipError_t launch_fire_grad(const Problem &p, const float *g, float *dtheta, hipStream_t s);
 // MFMA throughput probe: kMfmaProbeBlocks x kMfmaProbeThreads lanes, each
 // wave 4 chains x iters v_mfma_f32_32x32x16_bf16; sink holds one float per lane.

@@ -11,11 +11,14 @@
 // A one-input ReLU network is piecewise linear: between consecutive kinks
 // t_k = -b1_k / w1_k the active units are fixed, so b_h = A_hs + B_hs x on
 // segment s.  The attention kernels therefore never evaluate the network:
-// each element costs a log2 (x), a segment lookup and one fma.  This file
-// holds the two small single-workgroup kernels around them:
+// each element costs a table read (x), a segment lookup and one fma.  This
+// file holds the small kernels around them:
 //
 //   fire_setup_kernel  theta -> the segment table (layout in fa_internal.h):
 //                      sorted kinks and A, B per (head, segment);
+//   fire_dist_kernel   psi(d) = log2(c d + 1) and d / (c d + 1) per distance:
+//                      the kernels read x = psi(i - j) / log2(c max(L, i) + 1)
+//                      from it, with no logarithm per element;
 //   fire_grad_kernel   per-(head, segment) gradient sums -> d(theta).
 //
 // Gradient sums (accumulated by the dK/dV kernel over every visible pair of
@@ -36,26 +39,26 @@ namespace {
 
 constexpr int FT = 256;
 
+// theta up to b2 (w1, b1, w2, b2: 2K + HK + H floats) is copied to LDS once;
+// every loop below reads it from there.
+constexpr int kFireMaxHeadsLds = 256;   // heads whose w2 rows fit the LDS copy
+
 // Kinks inside (0, 1), sorted ascending (ties by unit index), into
 // tk[1 .. m] (fp64, LDS); returns m.  All threads of the workgroup call it.
-__device__ int fire_kinks(const float *theta, int K, double *tk) {
+__device__ int fire_kinks(const float *w1, const float *b1, int K, double *tk) {
   const int tid = threadIdx.x;
   bool valid = false;
   double t = 0.0;
-  if (tid < K) {
-    const double w = theta[tid], b = theta[K + tid];
-    if (w != 0.0) {
-      t = -b / w;
-      valid = t > 0.0 && t < 1.0;
-    }
+  if (tid < K && w1[tid] != 0.f) {
+    t = -(double)b1[tid] / (double)w1[tid];
+    valid = t > 0.0 && t < 1.0;
   }
   const int m = __syncthreads_count(valid);
   if (valid) {
     int rank = 0;
     for (int j = 0; j < K; ++j) {
-      const double wj = theta[j], bj = theta[K + j];
-      if (wj == 0.0) continue;
-      const double tj = -bj / wj;
+      if (w1[j] == 0.f) continue;
+      const double tj = -(double)b1[j] / (double)w1[j];
       if (!(tj > 0.0 && tj < 1.0)) continue;
       rank += (tj < t || (tj == t && j < tid)) ? 1 : 0;
     }
@@ -72,26 +75,62 @@ __device__ __forceinline__ double fire_mid(const double *tk, int m, int s) {
   return 0.5 * (lo + hi);
 }
 
+// Shared set-up of both kernels: theta's w1, b1 (and w2 when it fits) in
+// LDS, the sorted kinks, and act[s] = the units active on segment s (bit k).
+struct FireSmem {
+  float w1[kFireMaxHidden], b1[kFireMaxHidden];
+  float w2[kFireMaxHeadsLds * kFireMaxHidden];
+  double tk[kFireSegs + 1];
+  uint64_t act[kFireSegs];
+};
+
+__device__ int fire_prepare(const float *theta, int H, int K, FireSmem &sm) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < K; i += FT) {
+    sm.w1[i] = theta[i];
+    sm.b1[i] = theta[K + i];
+  }
+  if (H <= kFireMaxHeadsLds)
+    for (int i = tid; i < H * K; i += FT) sm.w2[i] = theta[2 * K + i];
+  __syncthreads();
+  const int m = fire_kinks(sm.w1, sm.b1, K, sm.tk);
+  for (int s = tid; s <= m; s += FT) {
+    const double xs = fire_mid(sm.tk, m, s);
+    uint64_t bits = 0;
+    for (int k = 0; k < K; ++k)
+      if ((double)sm.w1[k] * xs + (double)sm.b1[k] > 0.0) bits |= 1ull << k;
+    sm.act[s] = bits;
+  }
+  __syncthreads();
+  return m;
+}
+
+__device__ __forceinline__ float fire_w2(const FireSmem &sm, const float *theta, int H, int K,
+                                         int h, int k) {
+  return H <= kFireMaxHeadsLds ? sm.w2[h * K + k] : theta[2 * K + h * K + k];
+}
+
 __global__ __launch_bounds__(FT) void fire_setup_kernel(const float *theta, int H, int K,
                                                          float *tab) {
-  __shared__ double tk[kFireSegs + 1];
+  __shared__ FireSmem sm;
   const int tid = threadIdx.x;
-  const int m = fire_kinks(theta, K, tk);
+  const int m = fire_prepare(theta, H, K, sm);
   const int n = fire_theta_floats(H, K);
   for (int i = tid; i < kFireTEnd; i += FT)
-    tab[kFireOffT + i] = i == 0 ? -INFINITY : (i <= m ? (float)tk[i] : INFINITY);
+    tab[kFireOffT + i] = i == 0 ? -INFINITY : (i <= m ? (float)sm.tk[i] : INFINITY);
   // A, B (log2 units) per (head, segment)
-  const float *w1 = theta, *b1 = theta + K, *w2 = theta + 2 * K, *b2 = theta + 2 * K + H * K;
+  const float *b2 = theta + 2 * K + H * K;
   for (int i = tid; i < H * kFireSegs; i += FT) {
     const int h = i / kFireSegs, s = i - h * kFireSegs;
     double A = 0.0, B = 0.0;
     if (s <= m) {
-      const double xs = fire_mid(tk, m, s);
       A = b2[h];
+      const uint64_t bits = sm.act[s];
       for (int k = 0; k < K; ++k)
-        if ((double)w1[k] * xs + (double)b1[k] > 0.0) {
-          A += (double)w2[h * K + k] * b1[k];
-          B += (double)w2[h * K + k] * w1[k];
+        if ((bits >> k) & 1) {
+          const double w = fire_w2(sm, theta, H, K, h, k);
+          A += w * sm.b1[k];
+          B += w * sm.w1[k];
         }
     }
     float *ph = tab + kFireShared + (size_t)h * kFireHeadStride;
@@ -109,57 +148,56 @@ __global__ __launch_bounds__(FT) void fire_setup_kernel(const float *theta, int 
 // g: the reduced sums, row (s * kFireTerms + q) of [kFireGradRows, H].
 __global__ __launch_bounds__(FT) void fire_grad_kernel(const float *theta, int H, int K,
                                                         const float *g, float *dtheta) {
-  __shared__ double tk[kFireSegs + 1];
-  __shared__ double xs[kFireSegs];
+  __shared__ FireSmem sm;
   __shared__ double red[2][FT];
   const int tid = threadIdx.x;
-  const int m = fire_kinks(theta, K, tk);
-  for (int s = tid; s <= m; s += FT) xs[s] = fire_mid(tk, m, s);
-  __syncthreads();
-  const float *w1 = theta, *b1 = theta + K, *w2 = theta + 2 * K;
+  const int m = fire_prepare(theta, H, K, sm);
   const int n = fire_theta_floats(H, K);
   const double c = theta[n - 2], L = theta[n - 1];
   auto G = [&](int s, int q, int h) { return (double)g[(size_t)(s * kFireTerms + q) * H + h]; };
-  auto act = [&](int s, int k) { return (double)w1[k] * xs[s] + (double)b1[k] > 0.0; };
-  // dw2 [H, K] and db2 [H]
+  // dw2 [H, K]: b1_k G0 + w1_k G1 over the segments where unit k is active
   for (int i = tid; i < H * K; i += FT) {
     const int h = i / K, k = i - h * K;
     double t = 0.0;
     for (int s = 0; s <= m; ++s)
-      if (act(s, k)) t += (double)b1[k] * G(s, 0, h) + (double)w1[k] * G(s, 1, h);
+      if ((sm.act[s] >> k) & 1) t += (double)sm.b1[k] * G(s, 0, h) + (double)sm.w1[k] * G(s, 1, h);
     dtheta[2 * K + i] = (float)t;
   }
+  // db2 [H]
   for (int h = tid; h < H; h += FT) {
     double t = 0.0;
     for (int s = 0; s <= m; ++s) t += G(s, 0, h);
     dtheta[2 * K + H * K + h] = (float)t;
   }
-  // dw1, db1 [K]
+  // dw1, db1 [K]: sum over heads of w2_hk times the same segment sums
   for (int k = tid; k < K; k += FT) {
     double t1 = 0.0, t0 = 0.0;
     for (int h = 0; h < H; ++h) {
       double s1 = 0.0, s0 = 0.0;
       for (int s = 0; s <= m; ++s)
-        if (act(s, k)) {
+        if ((sm.act[s] >> k) & 1) {
           s1 += G(s, 1, h);
           s0 += G(s, 0, h);
         }
-      t1 += (double)w2[h * K + k] * s1;
-      t0 += (double)w2[h * K + k] * s0;
+      const double w = fire_w2(sm, theta, H, K, h, k);
+      t1 += w * s1;
+      t0 += w * s0;
     }
     dtheta[k] = (float)t1;
     dtheta[K + k] = (float)t0;
   }
-  // dc, dL: per-thread partials over heads, then a fixed-order tree
+  // dc, dL: one (head, segment) pair per thread and step, then a
+  // fixed-order tree
   double pc = 0.0, pl = 0.0;
-  for (int h = tid; h < H; h += FT)
-    for (int s = 0; s <= m; ++s) {
-      double B = 0.0;
-      for (int k = 0; k < K; ++k)
-        if (act(s, k)) B += (double)w2[h * K + k] * w1[k];
-      pc += B * (1.4426950408889634 * G(s, 2, h) - G(s, 3, h));
-      pl += B * G(s, 4, h);
-    }
+  for (int i = tid; i < H * (m + 1); i += FT) {
+    const int h = i / (m + 1), s = i - h * (m + 1);
+    double B = 0.0;
+    const uint64_t bits = sm.act[s];
+    for (int k = 0; k < K; ++k)
+      if ((bits >> k) & 1) B += (double)fire_w2(sm, theta, H, K, h, k) * sm.w1[k];
+    pc += B * (1.4426950408889634 * G(s, 2, h) - G(s, 3, h));
+    pl += B * G(s, 4, h);
+  }
   red[0][tid] = pc;
   red[1][tid] = pl;
   __syncthreads();
@@ -177,11 +215,31 @@ __global__ __launch_bounds__(FT) void fire_grad_kernel(const float *theta, int H
   }
 }
 
+// The distance table (layout in fa_internal.h), in fp64 and rounded once.
+__global__ __launch_bounds__(FT) void fire_dist_kernel(const float *theta, int H, int K,
+                                                        int maxlen, float *dist) {
+  const int n = maxlen + 2 * kFireDistPad;
+  const int idx = blockIdx.x * FT + threadIdx.x;
+  if (idx >= 2 * n) return;
+  const double c = theta[fire_theta_floats(H, K) - 2];
+  const int half = idx >= n ? 1 : 0;
+  const int d = idx - half * n - kFireDistPad;
+  // d past the last distance (rows beyond a ragged end) keeps the formula,
+  // so x stays monotone along a row of keys or a column of rows; d < 0
+  // (keys after the query) reads 0
+  double v = 0.0;
+  if (d >= 0) v = half ? d / fma(c, (double)d, 1.0) : log2(fma(c, (double)d, 1.0));
+  dist[idx] = (float)v;
+}
+
 }  // namespace
 
-hipError_t launch_fire_setup(const Problem &p, float *tab, hipStream_t s) {
+hipError_t launch_fire_setup(const Problem &p, float *tab, float *dist, hipStream_t s) {
   hipLaunchKernelGGL(fire_setup_kernel, dim3(1), dim3(FT), 0, s, p.table, p.heads, p.fire_hidden,
                      tab);
+  const int n = 2 * (p.seqlen + 2 * kFireDistPad);
+  hipLaunchKernelGGL(fire_dist_kernel, dim3((n + FT - 1) / FT), dim3(FT), 0, s, p.table, p.heads,
+                     p.fire_hidden, p.seqlen, dist);
   return hipGetLastError();
 }
 

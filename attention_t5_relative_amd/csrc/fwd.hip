@@ -53,6 +53,7 @@ struct FwdArgs {
   const uint16_t *dense;  // dense bias bf16 [dense_batch, H, S, S]
   const double2 *rope_cs;  // RoPE: (cos, sin) [seqlen, D/2], or nullptr
   const float *fire_tab;   // FIRE segment table (fa_internal.h), or nullptr
+  const float *fire_dist;  // FIRE distance table, or nullptr
   int32_t dense_batch;
   int32_t nbatch, seqlen, heads, total;
   int32_t nq, nwg;
@@ -157,9 +158,7 @@ void fwd_kernel(
   FireLane fl;
   if constexpr (BIAS == kBiasFire) {
     fire_load(a.fire_tab, h, fire_mem, tid, NT);
-    fl.tab = fire_mem;
-    fl.c = a.fire_tab[2];
-    fl.inv = fire_row_inv(fl.c, a.fire_tab[3], wrow0 + il);
+    fl = fire_lane(a.fire_tab, a.fire_dist, a.seqlen, fire_mem, wrow0 + il);
   }
   // dense bias: this (batch, head)'s [S, S] matrix
   rsrc_t rbias = make_rsrc(nullptr, 0u);
@@ -278,8 +277,8 @@ void fwd_kernel(
       float bconst;
       // (the linear ALiBi path would not fit the 168 VGPRs of three
       // workgroups per CU at head_dim 64)
-      const bool fast = score_tile_T<BIAS, CAUSAL, D == 128>(sacc, j0, wrow0, il, hl, L, c, sat,
-                                                            lut, slope_l2, bconst, bv, fl);
+      const bool fast = score_tile_T<BIAS, CAUSAL, D == 128, D == 64>(
+          sacc, j0, wrow0, il, hl, L, c, sat, lut, slope_l2, bconst, bv, &fl);
       // row max: two chains of v_max3 (one instruction per two elements; the
       // empty asm keeps the compiler from rebalancing them into a tree of
       // two-input maxes, which takes half as many instructions again)
@@ -424,6 +423,7 @@ hipError_t launch_fwd_impl(const Problem &p, const FwdBuffers &b, const int4 *sc
   a.dense = p.dense;
   a.rope_cs = b.rope_cs;
   a.fire_tab = b.fire_tab;
+  a.fire_dist = b.fire_dist;
   a.dense_batch = p.dense_batch;
   a.nbatch = p.nbatch;
   a.seqlen = p.seqlen;

@@ -235,14 +235,15 @@ def test_workspace_sizes(lib):
 
 
 def test_fire_workspace(lib):
-    """FIRE: the segment table (144 + 132 H floats) in both workspaces; with
-    d(theta) asked, the per-workgroup partials (325 rows per 128-key tile) and
-    their per-head reduction (325 x H floats)."""
+    """FIRE: the segment table (144 + 132 H floats) and the distance table
+    (2 (S + 256) floats) in both workspaces; with d(theta) asked, the
+    per-workgroup partials (325 rows per 128-key tile) and their per-head
+    reduction (325 x H floats)."""
     def a256(x):
         return (x + 255) // 256 * 256
     p = _dense(bias_mode=_lib.FA_BIAS_FIRE, bias_fire_hidden=32, causal=1)
     B, S, H = p.batch, p.seqlen, p.heads
-    tab = a256((144 + 132 * H) * 4)
+    tab = a256((144 + 132 * H) * 4) + a256(2 * (S + 256) * 4)
     assert lib.fa_fwd_workspace_size(ctypes.byref(p)) == tab
     b = _lib.FaBwdParams()
     b.f = p
