@@ -563,6 +563,7 @@ const char *fa_status_str(fa_status st) {
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "HIP error";
+    default: break;
   }
   return "unknown status";
 }

@@ -73,7 +73,10 @@ typedef enum {
   FA_ERR_INVALID = -1,     /* a NULL pointer, a negative size, a bad enum value */
   FA_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement   */
   FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
-  FA_ERR_HIP = -4          /* a HIP launch failed                            */
+  FA_ERR_HIP = -4,         /* a HIP launch failed                            */
+  FA_STATUS_MAX_ENUM = 0x7fffffff   /* not a status: gives the type the range of
+                                       int32, so any int32 passed as an fa_status
+                                       (fa_status_str) is a valid value        */
 } fa_status;
 
 typedef enum {
