@@ -24,6 +24,9 @@ FA_KERNEL_RMSNORM_FWD = 3
 FA_KERNEL_RMSNORM_BWD = 4
 FA_KERNEL_CE_FWD = 5
 FA_KERNEL_CE_BWD = 6
+FA_KERNEL_BWD_DBIAS_SUM = 7
+FA_KERNEL_BWD_FIRE = 8
+FA_KERNEL_COUNT = 9
 
 FA_BWD_NOALLOC_MAX_BYTES = 16 << 20
 FA_MFMA_PROBE_LANES = 2048 * 256

@@ -340,10 +340,9 @@ FwdLayout fwd_layout(const fa::Problem &p) {
 
 struct BwdLayout {
   size_t qrot = 0, krot = 0, rope_cs = 0, delta = 0, part = 0, prefix = 0, sched = 0,
-         dense_ws = 0, fire_tab = 0, fire_dist = 0, fire_g = 0, total = 0;
+         fire_tab = 0, fire_dist = 0, fire_g = 0, total = 0;
   int nsched = 0;
   bool has_part = false;
-  bool has_dense_ws = false;   // per-batch dense bias gradients, summed afterwards
 };
 
 BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
@@ -376,9 +375,6 @@ BwdLayout bwd_layout(const fa::Problem &p, bool want_dtable) {
     L.fire_dist = c.take(fa::fire_dist_floats(p.seqlen) * 4);
     if (want_dtable) L.fire_g = c.take((size_t)fa::kFireGradRows * p.heads * 4);
   }
-  L.has_dense_ws = want_dtable && p.bias == FA_BIAS_DENSE && p.dense_batch == 1 && p.nbatch > 1;
-  if (L.has_dense_ws)
-    L.dense_ws = c.take((size_t)p.nbatch * p.heads * p.seqlen * p.seqlen * 4);
   L.total = c.off;
   return L;
 }
@@ -474,9 +470,12 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
     b.fire_dist = at<float>(ws, L.fire_dist);
     b.fire_g = firegrad ? at<float>(ws, L.fire_g) : nullptr;
   }
-  b.dbias = densegrad ? dtable : nullptr;
-  b.dbias_batch = L.has_dense_ws ? at<float>(ws, L.dense_ws) : nullptr;
-  if (densegrad && p.causal && !L.has_dense_ws) {
+  // a matrix shared by a batch of several: its gradient is summed over the
+  // batch by a kernel of its own; otherwise the dK/dV kernel writes dS
+  const bool shared_sum = densegrad && p.dense_batch == 1 && p.nbatch > 1;
+  b.dbias = densegrad && !shared_sum ? dtable : nullptr;
+  b.dbias_shared = shared_sum ? dtable : nullptr;
+  if (densegrad && p.causal) {
     // pairs with key > query: the key-parallel kernel skips most of them
     e = fa::launch_zero_upper(dtable, p.dense_batch * p.heads, p.seqlen, s);
     if (e != hipSuccess) return hip_fail(e, "dense bias gradient fill");
@@ -505,7 +504,8 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
             [&] { return fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdMain, s); });
   if (e != hipSuccess) return hip_fail(e, "backward dkv kernel");
   if (firegrad) {
-    e = fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdFire, s);
+    e = timed(FA_KERNEL_BWD_FIRE, s,
+              [&] { return fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdFire, s); });
     if (e != hipSuccess) return hip_fail(e, "FIRE gradient sums");
   }
   e = fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdReduce, s);
@@ -514,10 +514,11 @@ fa_status run_bwd(const fa::Problem &p, const void *q, const void *k, const void
     e = fa::launch_fire_grad(p, b.fire_g, dtable, s);
     if (e != hipSuccess) return hip_fail(e, "FIRE parameter gradient");
   }
-  if (L.has_dense_ws) {
-    e = fa::launch_batch_sum(b.dbias_batch, dtable, p.nbatch, p.heads, p.seqlen, p.causal != 0,
-                             s);
-    if (e != hipSuccess) return hip_fail(e, "dense bias gradient batch sum");
+  if (shared_sum) {
+    e = timed(FA_KERNEL_BWD_DBIAS_SUM, s, [&] {
+      return fa::launch_bwd_phase(p, b, sched, L.nsched, fa::kBwdDenseSum, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "dense bias gradient over the batch");
   }
   return FA_OK;
 }

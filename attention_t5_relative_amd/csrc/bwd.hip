@@ -53,7 +53,8 @@ struct BwdArgs {
   const int4 *sched;       // packed batches: {token0, length, head, tile}
   const float *table, *slopes;
   const uint16_t *dense;   // dense bias bf16 [dense_batch, H, S, S]
-  float *dbias;            // dense bias gradient fp32, one [S, S] per (batch, head)
+  float *dbias;            // dense bias gradient fp32, one [S, S] per (batch, head) (the
+                           // summing kernel: one per head)
   int32_t dense_batch;
   int32_t nbatch, seqlen, heads, total;
   int32_t ntile;           // dense: tiles of 128 per sequence
@@ -1180,6 +1181,220 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
 }
 
 // ---------------------------------------------------------------------------
+// Dense bias shared by the batch: its gradient summed over the batch
+// ---------------------------------------------------------------------------
+// dL/dB[h] = sum over b of dS[b, h] for a bias matrix [1, H, S, S].  One
+// workgroup per (head, 128 x 128 output tile), lanes on keys as in the dkv
+// kernel (wave w: keys 32 w .. 32 w + 31 of the tile, all 128 rows); the
+// tile's sums stay in registers while the batch is the loop.  For batch b
+// the tile's Q and dO rows (LDS) and the lane's K and V rows (registers)
+// give S and dP, seeded with -lse/scale and -D; P takes the bias (read once,
+// kept packed two per register) and dS = P (dP - D) is added in batch
+// order.  After the last batch each sum is stored once: no workspace, no
+// second pass over per-batch gradients, and one fixed order of the sum.
+// The next batch's tiles are requested while the current one is worked on
+// (two LDS buffers, two register sets; the loop is unrolled by two so each
+// set is addressed statically).  head_dim 64 takes tiles of 128 rows and
+// fits 256 registers (two workgroups per CU); head_dim 128, whose K/V sets
+// are twice as large, takes tiles of 64 rows and a little more than 256
+// registers (one workgroup, one wave per SIMD, per CU: the unrolled blocks
+// give the scheduler independent MFMA and exponential work to overlap).
+// Causal: only tiles with a visible pair are launched (the lower triangle
+// of 128 x 128 super tiles, each cut into 128 / RT row tiles).
+template <int D>
+constexpr int dbias_sum_rows() { return D == 64 ? 128 : 64; }
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dbias_sum_kernel(const BwdArgs a) {
+  constexpr int RT = dbias_sum_rows<D>();   // query rows per workgroup
+  constexpr int NB = RT / 32;               // 32-row blocks
+  constexpr int M = BKV / RT;               // row tiles per 128-row super tile
+  constexpr int NP = RT / 64;               // 64-float pieces of -lse/scale (and of -D)
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][RT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dos[2][RT * D];
+  __shared__ __attribute__((aligned(16))) float nlss[2][RT];
+  __shared__ __attribute__((aligned(16))) float ndls[2][RT];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, il = lane & 31;
+  const int L = a.seqlen, B = a.nbatch, nt = a.ntile;
+  // logical id -> (head, super tile (R, kt), row tile within it); causal:
+  // kt <= R, t = R (R + 1) / 2 + kt
+  const int per_head = (CAUSAL ? nt * (nt + 1) / 2 : nt * nt) * M;
+  const int g = xcd_remap(blockIdx.x, a.nwg);
+  const int h = g / per_head;
+  const int tl = g - h * per_head;
+  const int t = tl / M, sub = tl - (tl / M) * M;
+  int R, kt;
+  if constexpr (CAUSAL) {
+    R = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+    while (R > 0 && R * (R + 1) / 2 > t) --R;
+    while ((R + 1) * (R + 2) / 2 <= t) ++R;
+    kt = t - R * (R + 1) / 2;
+  } else {
+    R = t / nt;
+    kt = t - R * nt;
+  }
+  const int row0 = R * BKV + sub * RT;
+  const int kw0 = kt * BKV + 32 * wave;
+  const int myk = kw0 + il;
+
+  const int HD = a.heads * D;
+  const uint32_t nrec = ((uint32_t)(L - 1) * (uint32_t)HD + D) * 2u;
+  auto seq_base = [&](int b) { return ((size_t)b * L * a.heads + h) * D; };
+  auto row_base = [&](int b) { return ((size_t)b * a.heads + h) * L; };
+  const rsrc_t rbias = make_rsrc(a.dense + (size_t)h * L * L, (uint32_t)L * (uint32_t)L * 2u);
+
+  const int aw = swz<D>(il);
+  const int abase = il * D + 8 * (hl ^ (aw & 1));
+  auto aoff = [&](int j, int s) { return j * 32 * D + abase + 16 * (s ^ (aw >> 1)); };
+  const float c = a.scale_log2;
+  // keys of this wave that see no row of the tile (or lie past the end):
+  // its products are skipped, its sums stay 0
+  const bool none = kw0 >= L || row0 >= L || (CAUSAL && kw0 > row0 + RT - 1);
+  // no pair of the wave's part of the tile is masked
+  const bool full = (!CAUSAL || kw0 + 31 <= row0) && row0 + RT <= L && kw0 + 32 <= L;
+
+  auto fill = [&](int b, int buf) {
+    dma_tile<D, RT, 4>(dma_desc(a.q + seq_base(b), nrec), HD, row0, qs[buf], wave, lane);
+    dma_tile<D, RT, 4>(dma_desc(a.dout + seq_base(b), nrec), HD, row0, dos[buf], wave, lane);
+    if (wave < 2 * NP) {
+      const int which = wave / NP, piece = wave - which * NP;
+      dma4(dma_desc((which ? a.delta : a.nls) + row_base(b), (uint32_t)L * 4u),
+           (uint32_t)(row0 + 64 * piece + lane) * 4u, (which ? ndls[buf] : nlss[buf]) + 64 * piece);
+    }
+  };
+  auto load_kv = [&](int b, bf16x8 (&kf)[D / 16], bf16x8 (&vf)[D / 16]) {
+    const rsrc_t rk = make_rsrc(a.k + seq_base(b), nrec);
+    const rsrc_t rv = make_rsrc(a.v + seq_base(b), nrec);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const uint32_t off = ((uint32_t)myk * (uint32_t)HD + 16 * s + 8 * hl) * 2u;
+      kf[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+      vf[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+    }
+  };
+
+  // lane element r of block j: key myk, row row0 + 4 hl + roff(j, r)
+  const uint32_t voff = (uint32_t)(row0 + 4 * hl) * (uint32_t)L + (uint32_t)myk;
+  auto roff = [&](int j, int r) { return 32 * j + 8 * (r >> 2) + (r & 3); };
+  // the first batch's tiles, then the bias, then one wait for both
+  bf16x8 kfa[D / 16], vfa[D / 16], kfb[D / 16], vfb[D / 16];
+  if (B > 0) {
+    fill(0, 0);
+    load_kv(0, kfa, vfa);
+  }
+  float dsum[NB * 16];
+#pragma unroll
+  for (int r = 0; r < NB * 16; ++r) dsum[r] = 0.f;
+
+  // Offsets of the rows roff(j, r) walk from row to row (+1 row within a
+  // group of four, +5 to the next), each step hidden from the compiler so
+  // it does not turn them into one scalar constant per row, all alive
+  // across the batch loop.
+  auto next_row = [&](uint32_t &o, int r, uint32_t row_bytes) {
+    o += ((r & 3) == 3 ? 5u : 1u) * row_bytes;
+    asm volatile("" : "+v"(o));
+  };
+  // The bias, two rows per register (bf16 bits).  Masked pairs (key after
+  // the query, row or key past the end) hold -inf instead, so P is 0 there
+  // with no test in the batch loop.
+  uint32_t bpk[NB * 8];
+  {
+    uint16_t raw[NB * 16];
+    uint32_t o = voff * 2u;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        raw[16 * j + r] = buf_load_u16(rbias, o);
+        next_row(o, r, (uint32_t)L * 2u);
+      }
+    // every load (the first batch's too) is in flight before the first use
+    wait_vmem_loads();
+    const int rkey = myk - (row0 + 4 * hl);   // key - first row of the lane
+    const int rlim = L - (row0 + 4 * hl);     // rows past the end: roff >= rlim
+    const bool part = !full;
+    const bool kout = myk >= L;
+    // branch-free: the masks are per element, not per wave
+    auto bits = [&](int j, int r) -> uint32_t {
+      const bool dead = part & ((CAUSAL & (rkey > roff(j, r))) | (roff(j, r) >= rlim) | kout);
+      return dead ? 0xff80u : (uint32_t)raw[16 * j + r];
+    };
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r2 = 0; r2 < 8; ++r2)
+        bpk[8 * j + r2] = bits(j, 2 * r2) | (bits(j, 2 * r2 + 1) << 16);
+  }
+
+  // one batch: S and dP block by block, dS into the sums
+  auto step = [&](int buf, const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16]) {
+    if (none) return;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&ndls[buf][32 * j + 8 * qq + 4 * hl]);
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&nlss[buf][32 * j + 8 * qq + 4 * hl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pacc[4 * qq + e] = d4[e];
+          sacc[4 * qq + e] = l4[e];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        sacc = mfma32(*reinterpret_cast<const bf16x8 *>(&qs[buf][aoff(j, s)]), kf[s], sacc);
+        pacc = mfma32(*reinterpret_cast<const bf16x8 *>(&dos[buf][aoff(j, s)]), vf[s], pacc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t w = bpk[8 * j + (r >> 1)];
+        const float bias = __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
+        const float p = __builtin_amdgcn_exp2f(fmaf(bias, kLog2e, sacc[r] * c));
+        dsum[16 * j + r] = fmaf(p, pacc[r], dsum[16 * j + r]);
+      }
+    }
+  };
+
+  wait_vmem_loads();
+  __syncthreads();
+  for (int b = 0; b < B; b += 2) {
+    // even batch: buffer 0, registers a; prefetch into buffer 1 / b
+    if (b + 1 < B) {
+      fill(b + 1, 1);
+      load_kv(b + 1, kfb, vfb);
+    }
+    step(0, kfa, vfa);
+    wait_vmem_loads();
+    __syncthreads();
+    if (b + 1 >= B) break;
+    // odd batch: buffer 1, registers b; prefetch into buffer 0 / a
+    if (b + 2 < B) {
+      fill(b + 2, 0);
+      load_kv(b + 2, kfa, vfa);
+    }
+    step(1, kfb, vfb);
+    wait_vmem_loads();
+    __syncthreads();
+  }
+  const rsrc_t rdbias = make_rsrc(a.dbias + (size_t)h * L * L, (uint32_t)L * (uint32_t)L * 4u);
+  if (myk < L) {
+    uint32_t o = voff * 4u;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        buf_store_f32(rdbias, o, dsum[16 * j + r]);
+        next_row(o, r, (uint32_t)L * 4u);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Table-gradient reduction
 // ---------------------------------------------------------------------------
 // dtable[b, h] = sum of the partials of head h, one workgroup per (b, h):
@@ -1316,7 +1531,7 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   a.slopes = p.slopes;
   a.dense = p.dense;
   a.dense_batch = p.dense_batch;
-  a.dbias = b.dbias_batch ? b.dbias_batch : b.dbias;
+  a.dbias = b.dbias;
   a.nbatch = p.nbatch;
   a.seqlen = p.seqlen;
   a.heads = p.heads;
@@ -1337,6 +1552,19 @@ hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *s
   if (a.nwg <= 0) return hipSuccess;
   const bool dbias = (b.part != nullptr && p.bias != kBiasFire) || a.dbias != nullptr;
   if (phase == kBwdFire && (p.bias != kBiasFire || b.part == nullptr)) return hipSuccess;
+  if (phase == kBwdDenseSum) {
+    if (b.dbias_shared == nullptr) return hipSuccess;
+    a.dbias = b.dbias_shared;
+    const int nt = a.ntile;
+    const int m = BKV / (p.head_dim == 64 ? dbias_sum_rows<64>() : dbias_sum_rows<128>());
+    a.nwg = p.heads * (p.causal ? nt * (nt + 1) / 2 : nt * nt) * m;
+    auto kern = p.head_dim == 64 ? (p.causal ? bwd_dbias_sum_kernel<64, true>
+                                             : bwd_dbias_sum_kernel<64, false>)
+                                 : (p.causal ? bwd_dbias_sum_kernel<128, true>
+                                             : bwd_dbias_sum_kernel<128, false>);
+    hipLaunchKernelGGL(kern, dim3(a.nwg), dim3(NT), 0, s, a);
+    return hipGetLastError();
+  }
   if (phase == kBwdReduce) {
     if (b.part == nullptr) return hipSuccess;
     hipLaunchKernelGGL(dbias_reduce_kernel, dim3(a.nb * p.heads), dim3(256), 0, s, a.part,

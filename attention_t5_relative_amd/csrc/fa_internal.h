@@ -116,8 +116,8 @@ struct BwdBuffers {
   float *delta;            // fp32, two lse-layout arrays: -D, then -lse / scale
   float *part;             // fp32 [num_buckets, parts] (T5 table gradient) or nullptr
   float *dtable;           // [num_buckets, H] or nullptr
-  float *dbias;            // dense bias gradient fp32 [dense_batch, H, S, S] or nullptr
-  float *dbias_batch;      // per-batch gradients [B, H, S, S] summed into dbias, or nullptr
+  float *dbias;            // dense bias gradient fp32 [B, H, S, S] written per batch, or nullptr
+  float *dbias_shared;     // dense bias gradient fp32 [1, H, S, S] summed over B > 1, or nullptr
   const float *fire_tab;   // FIRE segment table or nullptr
   const float *fire_dist;  // FIRE distance table or nullptr
   float *fire_g;           // FIRE: reduced gradient sums [kFireGradRows, H] or nullptr
@@ -142,8 +142,8 @@ hipError_t launch_rope_rotate(const Problem &p, const double2 *cs, const void *x
 int bwd_tile();
 int64_t bwd_num_parts(const Problem &p, int nsched);
 // dq, dkv, table-gradient reduction, FIRE gradient sums (between dkv and
-// the reduction)
-enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2, kBwdFire = 3 };
+// the reduction), the batch sum of a shared dense bias's gradient
+enum BwdPhase { kBwdPre = 0, kBwdMain = 1, kBwdReduce = 2, kBwdFire = 3, kBwdDenseSum = 4 };
 hipError_t launch_bwd_phase(const Problem &p, const BwdBuffers &b, const int4 *sched, int nsched,
                             int phase, hipStream_t s);
 hipError_t launch_t5_buckets(const T5Geometry &g, int qlen, int klen, int32_t *out,
@@ -158,10 +158,8 @@ hipError_t launch_fire_grad(const Problem &p, const float *g, float *dtheta, hip
 constexpr int kMfmaProbeBlocks = 2048;
 constexpr int kMfmaProbeThreads = 256;
 hipError_t launch_mfma_probe(float *sink, int iters, hipStream_t s);
-// Dense bias gradient helpers: zero the pairs with key > query of `count`
-// [S, S] matrices (causal: the backward never visits most of them), and sum
-// `nbatch` [H, S, S] slabs into one (pairs with key > query set to 0 when
-// causal, without reading them).
+// Dense bias gradient helper: zero the pairs with key > query of `count`
+// [S, S] matrices (causal: the backward never visits most of them).
 hipError_t launch_zero_upper(float *m, int count, int S, hipStream_t s);
 
 // RMSNorm and cross-entropy (norm_loss.hip).  rmsnorm_bwd's dw partials are
@@ -181,8 +179,7 @@ hipError_t launch_ce_fwd(const void *z, const int32_t *labels, float *loss, floa
 hipError_t launch_ce_bwd(const void *z, const int32_t *labels, const float *lse,
                          const float *dloss, void *dz, int rows, int vocab, float z_loss,
                          int ignore, hipStream_t s);
-hipError_t launch_batch_sum(const float *src, float *dst, int nbatch, int heads, int S,
-                            bool causal, hipStream_t s);
+
 
 
 }  // namespace fa

@@ -322,31 +322,4 @@ hipError_t launch_zero_upper(float *m, int count, int S, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One workgroup per row (h, i) of the output: dst[h, i, :] = sum over b of
-// src[b, h, i, :] in batch order; columns past the row are 0 when causal.
-__global__ __launch_bounds__(256) void batch_sum_kernel(const float *src, float *dst, int nbatch,
-                                                        int heads, int S, int causal) {
-  const size_t row = blockIdx.x;                 // h * S + i
-  const int i = (int)(row % (size_t)S);
-  const size_t slab = (size_t)heads * S * S;
-  const int jend = causal ? i + 1 : S;
-  float *d = dst + row * (size_t)S;
-  const float *a = src + row * (size_t)S;
-  for (int j = (int)threadIdx.x; j < S; j += 256) {
-    float t = 0.f;
-    if (j < jend)
-      for (int b = 0; b < nbatch; ++b) t += a[b * slab + j];
-    d[j] = t;
-  }
-}
-
-hipError_t launch_batch_sum(const float *src, float *dst, int nbatch, int heads, int S,
-                            bool causal, hipStream_t s) {
-  const size_t rows = (size_t)heads * S;
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(batch_sum_kernel, dim3((unsigned)rows), dim3(256), 0, s, src, dst, nbatch,
-                     heads, S, (int)causal);
-  return hipGetLastError();
-}
-
 }  // namespace fa

@@ -18,9 +18,10 @@ the fp64 NumPy oracle on a bounded sample of the same workload on the host.
 
 ``--bias dense`` runs the same step with the report's first-kernel semantics
 instead: a dense bf16 bias matrix [1, H, S, S] shared by the batch, and its
-fp32 gradient.  Its line is bound by HBM traffic (the matrix is read by all
-three kernels and its gradient written per batch, then summed), so
-"roofline" there counts algorithmic bytes.
+fp32 gradient, summed over the batch by a fourth kernel (timed beside the
+three, outside the convention's shares).  Its roofline is the same MFMA one;
+config.hbm_unique gives each kernel's least HBM bytes (every tensor and the
+shared matrix once) and that rate, which stays far below 8 TB/s.
 
 ``--workload rmsnorm`` and ``--workload ce`` time the report's two other fused
 kernels (RMSNorm, cross-entropy with z-loss) forward + backward on the same
@@ -285,7 +286,7 @@ def bench_norm_loss(a):
 
     t = run_timed(a, step, kernels, dev)
     ms_step, kernel_ms = t["ms_step"], t["kernel_ms"]
-    dom = max(kernel_ms, key=kernel_ms.get)
+    dom = max((n for n in kernel_ms if n in CONVENTION), key=kernel_ms.get)
     gbs = abytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
     value = step_bytes / (ms_step * 1e-3) / 1e9
     line = {
@@ -345,8 +346,11 @@ FIRE_HIDDEN, FIRE_C, FIRE_L = 32, 0.1, 512.0
 # so each product counts once: fwd S, PV = 1.0; dkv S, dP, dV, dK = 2.0; dq
 # dQ = 0.5.  OWN_PRODUCTS credits each kernel with every product its outputs
 # need (the dq kernel recomputes S and dP too): shown beside, never in value.
+# The dense-bias batch sum and the FIRE gradient pass recompute S and dP
+# (1.0x) for outputs the convention does not count: they have no share, so
+# they are timed and listed but never the roofline's kernel.
 CONVENTION = {"fwd": 1.0, "bwd_dq": 0.5, "bwd_dkv": 2.0}
-OWN_PRODUCTS = {"fwd": 1.0, "bwd_dq": 1.5, "bwd_dkv": 2.0}
+OWN_PRODUCTS = {"fwd": 1.0, "bwd_dq": 1.5, "bwd_dkv": 2.0, "bwd_dbias_sum": 1.0, "bwd_fire": 1.0}
 
 
 def _oracle_threads():
@@ -410,7 +414,8 @@ def _attention_line(a, metric, workload, shape, t, fwd_flops, traffic=None):
         "config": dict({"workload": workload, "parallelism": "none (one GPU)",
                         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
                         "kernel_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
-                        "kernel_tflops_convention": {n: tf(CONVENTION[n], n) for n in kernel_ms},
+                        "kernel_tflops_convention": {n: tf(CONVENTION[n], n) for n in kernel_ms
+                                                     if n in CONVENTION},
                         "kernel_tflops_own_products": {n: tf(OWN_PRODUCTS[n], n)
                                                        for n in kernel_ms},
                         "step_ms": t["step_ms"],
@@ -422,10 +427,12 @@ def _attention_line(a, metric, workload, shape, t, fwd_flops, traffic=None):
     }
 
 
-def _attn_kernels():
+def _attn_kernels(extra=()):
     from attention_t5_relative_amd import _lib
-    return {"fwd": _lib.FA_KERNEL_FWD, "bwd_dq": _lib.FA_KERNEL_BWD_DQ,
-            "bwd_dkv": _lib.FA_KERNEL_BWD_DKV}
+    ids = {"fwd": _lib.FA_KERNEL_FWD, "bwd_dq": _lib.FA_KERNEL_BWD_DQ,
+           "bwd_dkv": _lib.FA_KERNEL_BWD_DKV, "bwd_dbias_sum": _lib.FA_KERNEL_BWD_DBIAS_SUM,
+           "bwd_fire": _lib.FA_KERNEL_BWD_FIRE}
+    return {n: ids[n] for n in ("fwd", "bwd_dq", "bwd_dkv") + tuple(extra)}
 
 
 def bench_other_attention(a):
@@ -528,7 +535,7 @@ def bench_other_attention(a):
                       bias=bias, rope_base=rope, workspace=wsb)
         shape = {"batch": Bq, "heads": H, "seq_len": Sq, "head_dim": Dh, "causal": c.causal}
 
-    t = run_timed(a, step, _attn_kernels(), dev)
+    t = run_timed(a, step, _attn_kernels(("bwd_fire",) if fire else ()), dev)
     t["mfma_probe_tflops"] = mfma_probe(dev)
     tag = f"{c.name} shape, FIRE bias" if fire else c.name
     line = _attention_line(a, f"attention fwd+bwd TFLOP/s, {a.workload} workload ({tag})",
@@ -653,7 +660,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
-    t = run_timed(a, step, _attn_kernels(), dev)
+    t = run_timed(a, step, _attn_kernels(("bwd_dbias_sum",) if a.bias == "dense" else ()), dev)
     t["mfma_probe_tflops"] = mfma_probe(dev)
     fwd_flops = 4.0 * B * H * S * S * D / 2.0
     shape = {"batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True}
@@ -662,21 +669,23 @@ def main(argv=None):
                     "[1, H, S, S] shared by the batch and its fp32 gradient, B8 H12 S4096 D64, "
                     "scale 1")
         line = _attention_line(a, METRIC_DENSE, workload, shape, t, fwd_flops)
-        # algorithmic bytes per launch: the bf16 tensors each kernel must read
-        # and write once, plus one bias element per visible pair (bf16) and,
-        # for dkv, one fp32 gradient element per visible pair and batch
+        # HBM side of each kernel: the bytes it must move at least (each bf16
+        # tensor, the per-row LSE / D and the shared matrix [1, H, S, S]
+        # read or written once; the batch sum writes the fp32 gradient of the
+        # visible pairs once), and that over its time
         kernel_ms = t["kernel_ms"]
-        dom = max(kernel_ms, key=kernel_ms.get)
         t_bytes = B * S * H * D * 2
         rows = B * H * S * 4
-        pairs = B * H * S * (S + 1) / 2
-        abytes = {"fwd": 4 * t_bytes + rows + pairs * 2,
-                  "bwd_dq": 6 * t_bytes + 2 * rows + pairs * 2,
-                  "bwd_dkv": 6 * t_bytes + 2 * rows + pairs * (2 + 4)}
-        gbs = abytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
-        line["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1),
-                            "peak": PEAK_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
-                            "traffic": None}
+        vis = H * S * (S + 1) / 2
+        ubytes = {"fwd": 4 * t_bytes + rows + vis * 2,
+                  "bwd_dq": 6 * t_bytes + 2 * rows + vis * 2,
+                  "bwd_dkv": 6 * t_bytes + 2 * rows + vis * 2,
+                  "bwd_dbias_sum": 4 * t_bytes + 2 * rows + vis * (2 + 4)}
+        line["config"]["hbm_unique"] = {
+            n: {"bytes": int(ubytes[n]),
+                "gbs": round(ubytes[n] / (kernel_ms[n] * 1e-3) / 1e9, 1),
+                "frac": round(ubytes[n] / (kernel_ms[n] * 1e-3) / 1e9 / PEAK_GBS, 4)}
+            for n in kernel_ms}
     else:
         workload = ("causal decoder self-attention fwd+bwd with unidirectional T5 bias "
                     "(32 buckets, max distance 128), B8 H12 S4096 D64, scale 1")

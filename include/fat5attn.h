@@ -144,8 +144,9 @@ typedef struct {
  * it): T5, fp32 [num_buckets, H], the sum over the batch and over every
  * visible (query, key) pair in bucket b of dL/dS'; DENSE, fp32
  * [dense_batch, H, S, S], dL/dS' itself (0 for masked pairs), summed over
- * the batch when dense_batch is 1 (that case needs B*H*S*S*4 bytes of
- * workspace when B > 1); other modes ignore it. */
+ * the batch in batch order when dense_batch is 1 (no workspace: a kernel of
+ * its own sums each element in registers); FIRE, d(theta) (see fa_bias);
+ * other modes ignore it. */
 typedef struct {
   fa_fwd_params f;
   const void *dout;
@@ -325,7 +326,10 @@ typedef enum {
   FA_KERNEL_RMSNORM_BWD = 4, /* dx and the dw partials (not their final sum)     */
   FA_KERNEL_CE_FWD = 5,
   FA_KERNEL_CE_BWD = 6,
-  FA_KERNEL_COUNT = 7
+  FA_KERNEL_BWD_DBIAS_SUM = 7, /* backward, a dense bias shared by the batch:
+                                  its gradient summed over the batch       */
+  FA_KERNEL_BWD_FIRE = 8,  /* backward, FIRE: the parameter-gradient sums    */
+  FA_KERNEL_COUNT = 9
 } fa_kernel;
 
 /* Benchmark hook.  While set, every launch of `kernel` is bracketed by

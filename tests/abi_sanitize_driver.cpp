@@ -127,9 +127,13 @@ static void dense_checks() {
   b.f = p;
   b.dout = b.dq = b.dk = b.dv = P(0x3000);
   b.dtable = static_cast<float *>(P(0x4000));
-  EXPECT(fa_bwd_workspace_size(&b) >= (size_t)4 * 2 * 1024 * 1024 * 4);
-  EXPECT(fa_bwd_noalloc(&b, nullptr) == FA_ERR_UNSUPPORTED);   // beyond the static scratch
+  EXPECT(fa_bwd_workspace_size(&b) > 0);   // -D and -lse/scale: no per-batch gradients
   EXPECT(fa_bwd(&b, nullptr, 0, nullptr) == FA_ERR_WORKSPACE);
+  p = dense(2, 16384, 16, 128);   // RoPE copies beyond the static scratch
+  p.rope_base = 10000.f;
+  b.f = p;
+  EXPECT(fa_bwd_workspace_size(&b) > FA_BWD_NOALLOC_MAX_BYTES);
+  EXPECT(fa_bwd_noalloc(&b, nullptr) == FA_ERR_UNSUPPORTED);
   b.dk = nullptr;
   EXPECT(fa_check_bwd(&b) == FA_ERR_INVALID);
   EXPECT(fa_bwd(&b, nullptr, 0, nullptr) == FA_ERR_INVALID);
