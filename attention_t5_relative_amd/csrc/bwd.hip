@@ -864,13 +864,13 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
     // the computation of P branches, so the dK / dV accumulators stay in
     // place.  A block with no visible pair runs fully masked (P = 0).
     f32x16 sacc[QB / 32], pacc[QB / 32];
-#pragma unroll
-    for (int rb = 0; rb < QB / 32; ++rb) block_sdp(buf, rb, sacc[rb], pacc[rb]);
 
     // When every row block of the iteration is unmasked with a constant
-    // bias, all of them go through one straight-line path (no branch between
-    // the blocks, so the compiler can overlap one block's products with the
-    // next block's exponentials); otherwise each block branches on its own.
+    // bias (decided from positions alone), all of them go through one
+    // straight-line path from the S and dP products on (no branch between
+    // the blocks, so the scheduler can overlap one block's products with
+    // the next block's exponentials); otherwise each block branches on its
+    // own.
     bool all_fast = BIAS == kBiasT5;
     float bcv[QB / 32];
     int ulov[QB / 32];
@@ -891,6 +891,8 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
     }
     if (all_fast) {
 #pragma unroll
+      for (int rb = 0; rb < QB / 32; ++rb) block_sdp(buf, rb, sacc[rb], pacc[rb]);
+#pragma unroll
       for (int rb = 0; rb < QB / 32; ++rb) {
         float p[16], ds[16];
         block_p_fast(sacc[rb], bcv[rb], p);
@@ -905,6 +907,9 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
         }
         block_dvdk(buf, rb, p, ds);
       }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < QB / 32; ++rb) block_sdp(buf, rb, sacc[rb], pacc[rb]);
     }
 #pragma unroll
     for (int rb = 0; rb < QB / 32; ++rb) {
