@@ -153,3 +153,27 @@ def test_dense_bias_full_size_sampled_head():
     assert_grad(out["dk"][:, :, h], dk[:, :, h], "dK[:,:,3]")
     assert_grad(out["dv"][:, :, h], dv[:, :, h], "dV[:,:,3]")
     assert_dbias(out["dbias"][0, h], dbias[0, h], "dbias[0,3]")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_dense_bias_shared_gradient_deterministic(D):
+    """The batch sum of a shared matrix's gradient runs in one fixed order:
+    two backward calls give the same bits."""
+    B, S, H = 4, 300, 2
+    inp = synth.draw_dense(900 + D, B, S, H, D, with_table=False)
+    dense = synth.draw_dense_bias(901 + D, 1, H, S)
+    q, k, v, do = (bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    bias = fa.DenseBias(bf16_tensor(dense))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    fa.fa_fwd(q, k, v, o, lse, scale=0.125, causal=True, bias=bias)
+    runs = []
+    for _ in range(2):
+        g = [torch.empty_like(q) for _ in range(3)]
+        db = torch.full(dense.shape, float("nan"), device="cuda")
+        fa.fa_bwd(q, k, v, o, lse, do, *g, db, scale=0.125, causal=True, bias=bias)
+        runs.append(g + [db])
+    torch.cuda.synchronize()
+    assert torch.isfinite(runs[0][3]).all()
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)

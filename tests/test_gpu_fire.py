@@ -205,3 +205,57 @@ def test_fire_autograd_and_rope():
     assert_o(to_f64(o), ro, "FIRE+RoPE O")
     assert_grad(to_f64(q.grad), rq, "FIRE+RoPE dQ")
     _check_theta(to_f64(th.grad), rth, H, K, "FIRE+RoPE")
+
+
+def test_fire_full_length_batch_one():
+    """The FIRE workload's length, heads and parameters (S 4096, H 12, D 64,
+    32 hidden units, c 0.1, L 512, the same seeded draws) at batch 1: O, LSE,
+    dQ, dK and dV of two heads, and d(theta), which sums over every head,
+    against the oracle on all twelve pairs.  The kernels' grid differs from
+    the batch-8 launch only in its size."""
+    _need_gpu()
+    c = synth.config_by_name("c3")
+    B, S, H, D, K = 1, c.seqlen, c.heads, c.head_dim, 32
+    inp = synth.draw_dense(c.seed, B, S, H, D, with_table=False)
+    theta = synth.draw_fire_theta(c.seed, H, K, c=0.1, threshold=512.0)
+    t = {n: bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do")}
+    th = torch.from_numpy(theta).cuda()
+    bias = fa.FireBias(th, K)
+    o = nan_like(t["q"])
+    lse = torch.full((B, H, S), float("nan"), device="cuda")
+    fa.fa_fwd(t["q"], t["k"], t["v"], o, lse, scale=c.scale, causal=True, bias=bias)
+    dq, dk, dv = nan_like(t["q"]), nan_like(t["q"]), nan_like(t["q"])
+    dth = torch.full_like(th, float("nan"))
+    fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], dq, dk, dv, dth, scale=c.scale,
+              causal=True, bias=bias)
+    torch.cuda.synchronize()
+    out = {k_: to_f64(v_) for k_, v_ in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
+    for name, arr in out.items():
+        assert np.isfinite(arr).all(), f"{name}: elements not written or not finite"
+    kw = dict(scale=c.scale, causal=True, bias="fire", fire=theta.astype(np.float64),
+              fire_hidden=K)
+    f = {n: inp.f64(n) for n in ("q", "k", "v", "do")}
+    checked = (3, 10)
+
+    def one(h):
+        pair = [(0, h)]
+        res = {}
+        if h in checked:
+            O, LSE = oracle.attention_fwd(f["q"], f["k"], f["v"], pairs=pair, **kw)
+            res.update(o=O[0, :, h], lse=LSE[0, h])
+        rq, rk, rv, rth = oracle.attention_bwd(f["q"], f["k"], f["v"], f["do"], pairs=pair, **kw)
+        res.update(dq=rq[0, :, h], dk=rk[0, :, h], dv=rv[0, :, h], dth=rth)
+        return res
+
+    res = pmap(one, range(H), workers=12)
+    for h in checked:
+        r = res[h]
+        tag = f"FIRE S{S} h{h}"
+        assert_o(out["o"][0, :, h], r["o"], tag + " O")
+        assert_lse(out["lse"][0, h], r["lse"], tag + " LSE")
+        assert_grad(out["dq"][0, :, h], r["dq"], tag + " dQ")
+        assert_grad(out["dk"][0, :, h], r["dk"], tag + " dK")
+        assert_grad(out["dv"][0, :, h], r["dv"], tag + " dV")
+    te = _check_theta(to_f64(dth), np.sum([r["dth"] for r in res], axis=0), H, K,
+                      f"FIRE S{S}")
+    log_margin(f"fire_full_length_b1", **{"dtheta_" + k_: v_ for k_, v_ in te.items()})
