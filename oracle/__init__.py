@@ -38,6 +38,7 @@ from .attention import (  # noqa: F401
     rope_unrotate,
     bf16_round_exact,
     bias_matrix,
+    head_sampled,
     attention_fwd,
     attention_bwd,
     varlen_attention_fwd,

@@ -267,6 +267,55 @@ def head_bwd(qh, kh, vh, doh, head, *, scale=1.0, causal=False, bias="none", tab
     return dq, dk, dv, dtab
 
 
+def head_sampled(qh, kh, vh, doh, head, rows, keys, *, scale=1.0, causal=False, bias="none",
+                 table=None, num_buckets=32, max_distance=128, bidirectional=True,
+                 slopes=None):
+    """Selected outputs of one head, for sequences whose S x S score matrix
+    is too large to hold: O, LSE and dQ at the query rows ``rows``, dK and
+    dV at the keys ``keys``.  The definitions are those of head_fwd and
+    head_bwd, evaluated on whole rows of S' only: a selected row needs its
+    own row; a selected key j needs every row that sees it (rows j .. S-1
+    under a causal mask, all rows otherwise), each with its own D_i.  T5,
+    ALiBi or no bias, no RoPE.
+
+    Returns (O [len(rows), D], LSE [len(rows)], dQ [len(rows), D],
+    dK [len(keys), D], dV [len(keys), D])."""
+    S = qh.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    j = np.arange(S)[None, :]
+
+    def score_rows(ii):
+        s = scale * (qh[ii] @ kh.T)
+        rel = j - ii[:, None]
+        if bias == "t5":
+            s = s + np.asarray(table, dtype=np.float64)[
+                t5_bucket(rel, num_buckets, max_distance, bidirectional), head]
+        elif bias == "alibi":
+            s = s - float(slopes[head]) * np.abs(rel).astype(np.float64)
+        elif bias != "none":
+            raise ValueError(bias)
+        if causal:
+            s = np.where(rel > 0, -np.inf, s)
+        return s
+
+    def grads(ii):
+        P, lse = _softmax_rows(score_rows(ii))
+        dP = doh[ii] @ vh.T
+        Drow = (P * dP).sum(axis=1)
+        return P, lse, P * (dP - Drow[:, None])
+
+    P, lse, dS = grads(rows)
+    O = P @ vh
+    dq = scale * (dS @ kh)
+    first = int(keys.min()) if (causal and keys.size) else 0
+    seen = np.arange(first, S)
+    Pk, _, dSk = grads(seen)
+    dk = scale * (dSk[:, keys].T @ qh[seen])
+    dv = Pk[:, keys].T @ doh[seen]
+    return O, lse, dq, dk, dv
+
+
 # --------------------------------------------------------------------------
 # Dense batches [B, S, H, D]
 # --------------------------------------------------------------------------

@@ -565,3 +565,28 @@ def test_varlen_lengths_recipe():
         L = synth.draw_varlen_lengths(np.random.default_rng(seed), 32768)
         assert L.sum() == 32768 and L.min() >= 16 and L.max() <= 4096
         assert len(L) == nseq and int((L ** 2).sum()) == ssq
+
+
+@pytest.mark.parametrize("bias,causal,bidi", [("t5", True, False), ("t5", False, True),
+                                              ("alibi", True, True), ("none", False, True)])
+def test_sampled_rows_and_keys_equal_the_whole_head(bias, causal, bidi):
+    # the row-by-row form for long sequences against the materialised head:
+    # the same definitions on fewer rows, so the results agree to rounding
+    from oracle.attention import head_bwd, head_fwd, head_sampled
+    rng = np.random.default_rng(17)
+    S, D, h = 70, 8, 1
+    q, k, v, do = (rng.standard_normal((S, D)) for _ in range(4))
+    table = rng.standard_normal((32, 2))
+    slopes = np.array([0.5, 0.125])
+    kw = dict(scale=0.7, causal=causal, bias=bias, table=table, num_buckets=32,
+              max_distance=20, bidirectional=bidi, slopes=slopes)
+    O, lse = head_fwd(q, k, v, h, **kw)
+    dq, dk, dv, _ = head_bwd(q, k, v, do, h, **kw)
+    rows = [0, 1, 33, 68, 69]
+    keys = [40, 55, 69] if causal else [0, 21, 69]
+    o_r, l_r, dq_r, dk_k, dv_k = oracle.head_sampled(q, k, v, do, h, rows, keys, **kw)
+    np.testing.assert_allclose(o_r, O[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_r, lse[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq_r, dq[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk_k, dk[keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv_k, dv[keys], rtol=0, atol=1e-12)
