@@ -1014,8 +1014,20 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
         // in the table
         const int rbase = myk - (irow0 + 4 * hl);
         const float *const lb = lut + min(max(rbase - 27, -sat - kLutPad), sat + kLutPad - 27);
+        // a T5 block with no row or key past the end (the band near the
+        // diagonal: the causal mask is in the table) needs no mask at all
+        const bool t5_plain = BIAS == kBiasT5 && !none && !mask_r && !mask_k;
+        if (t5_plain) {
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              p[4 * qq + e] =
+                  __builtin_amdgcn_exp2f(fmaf(sacc[rb][4 * qq + e], c, lb[27 - 8 * qq - e]));
+        }
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
+          if (t5_plain) break;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * qq + e;
