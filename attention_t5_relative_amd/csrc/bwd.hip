@@ -1025,6 +1025,15 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
               p[4 * qq + e] =
                   __builtin_amdgcn_exp2f(fmaf(sacc[rb][4 * qq + e], c, lb[27 - 8 * qq - e]));
         }
+        // Without T5 (whose causal mask is in its table) element r, at row
+        // offset roff, is masked iff roff < lo_lim (a key after the query:
+        // rbase - roff > 0) or roff >= hi_lim (a row past the end); a block
+        // with no visible pair or a key past the end masks everything.  Two
+        // compares per element against per-lane limits; the T5 variants keep
+        // the direct form, which their register allocation prefers.
+        int lo_lim = (BIAS != kBiasT5 && mask_c) ? rbase : -1;
+        const int hi_lim = mask_r ? L - (irow0 + 4 * hl) : 32;
+        if (none || (mask_k && myk >= L)) lo_lim = 32;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           if (t5_plain) break;
@@ -1038,8 +1047,10 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
             if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
             if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bkv[r]), kLog2e, t);
             // non-short-circuit operators keep this straight-line code
-            const bool dead = none | (BIAS != kBiasT5 && mask_c & (rr > 0)) |
-                              (mask_r & (irow0 + 4 * hl + roff >= L)) | (mask_k & (myk >= L));
+            const bool dead = BIAS == kBiasT5
+                                  ? none | (mask_r & (irow0 + 4 * hl + roff >= L)) |
+                                        (mask_k & (myk >= L))
+                                  : (roff < lo_lim) | (roff >= hi_lim);
             // the mask as an additive -inf (exp2(-inf) = 0): a select
             // between the whole argument and -inf would be turned into a
             // branch around the table read
