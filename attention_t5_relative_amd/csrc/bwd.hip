@@ -162,7 +162,10 @@ constexpr int dq_wgs() {
   return D == 64 || (BIAS != kBiasDense && BIAS != kBiasFire) ? 2 : 1;
 }
 
-template <int D, int BIAS, bool CAUSAL, bool VARLEN>
+// WHOLE (dense batches with T5 at head_dim 64): the sequence length is a
+// multiple of the 64-key tile, so the per-element length test of tiles near
+// the diagonal drops out.
+template <int D, int BIAS, bool CAUSAL, bool VARLEN, bool WHOLE = false>
 __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const BwdArgs a) {
   // K and V tiles, swizzled (see swz): K is read both row-wise
   // (S^T = K Q^T) and transposed (dQ^T = K^T dS^T), V row-wise.  At
@@ -333,7 +336,8 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
       float bconst;
       bool fast;
       if constexpr (NKB == 2)
-        fast = score_tile_T<BIAS, CAUSAL>(sacc, j0, wrow0, il, hl, L, c, sat, lut, slope_l2,
+        fast = score_tile_T<BIAS, CAUSAL, true, false, WHOLE>(sacc, j0, wrow0, il, hl, L, c, sat,
+                                                              lut, slope_l2,
                                           bconst, bv, &fl);
       else
         fast = score_block_T<BIAS, CAUSAL>(sacc[0], j0, wrow0, il, hl, L, c, sat, lut,
@@ -1461,6 +1465,13 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *part, co
 
 template <int D, int BIAS, bool CAUSAL, bool VARLEN>
 hipError_t launch_dq_t(const BwdArgs &a, hipStream_t s) {
+  if constexpr (BIAS == kBiasT5 && !VARLEN && D == 64) {
+    if (a.seqlen % 64 == 0) {
+      hipLaunchKernelGGL((bwd_dq_kernel<D, BIAS, CAUSAL, false, true>), dim3(a.nwg), dim3(NT), 0,
+                         s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((bwd_dq_kernel<D, BIAS, CAUSAL, VARLEN>), dim3(a.nwg), dim3(NT), 0, s, a);
   return hipGetLastError();
 }

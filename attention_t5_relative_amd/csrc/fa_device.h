@@ -438,7 +438,10 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
 // The causal mask hides keys after the query; keys at or past L are masked.
 // A dense bias arrives as the lane's own values bv (bf16 bits, same order
 // as sacc; see dense_row_load).
-template <int BIAS, bool CAUSAL, bool ALIBI_LINEAR = true, bool FIRE_TABLE = false>
+// WHOLE: the sequence length is a multiple of 64, so no tile reaches past
+// its end and the length test drops out at compile time.
+template <int BIAS, bool CAUSAL, bool ALIBI_LINEAR = true, bool FIRE_TABLE = false,
+          bool WHOLE = false>
 __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0, int il, int hl,
                                              int L, float c, int sat, const float *lut,
                                              float slope_l2, float &bconst,
@@ -446,7 +449,7 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
                                              FireLane *fl = nullptr) {
   const int rmin = j0 - (row0 + 31), rmax = j0 + 63 - row0;
   const bool mask_c = CAUSAL && rmax > 0;
-  const bool mask_l = j0 + 64 > L;
+  const bool mask_l = !WHOLE && j0 + 64 > L;
   bool uniform = (BIAS == kBiasNone);
   bconst = 0.f;
   if constexpr (BIAS == kBiasT5) {
