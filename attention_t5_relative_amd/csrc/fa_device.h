@@ -500,6 +500,11 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
       return false;
     }
   }
+  // one per-lane limit for both masks: offset off is a key after the query
+  // (rbase + off > 0) or past the end (jb + off >= L) iff off >= lim
+  int lim = 64;
+  if (mask_c) lim = min(lim, 1 - rbase);
+  if (mask_l) lim = min(lim, L - jb);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -509,9 +514,7 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
       float t = sacc[kb][r] * c;
       if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
       if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bv[kb][r]), kLog2e, t);
-      if (mask_c && rr > 0) t = -INFINITY;
-      if (mask_l && jb + off >= L) t = -INFINITY;
-      sacc[kb][r] = t;
+      sacc[kb][r] = off >= lim ? -INFINITY : t;
       // keep the bias-table reads from being hoisted all at once
       if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
@@ -573,6 +576,10 @@ __device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, i
       return false;
     }
   }
+  // one per-lane limit for both masks, as in score_tile_T
+  int lim = 32;
+  if (mask_c) lim = min(lim, 1 - rbase);
+  if (mask_l) lim = min(lim, L - jb);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int off = 8 * (r >> 2) + (r & 3);
@@ -580,9 +587,7 @@ __device__ __forceinline__ bool score_block_T(f32x16 &sacc, int jb0, int row0, i
     float t = sacc[r] * c;
     if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
     if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bv[r]), kLog2e, t);
-    if (mask_c && rr > 0) t = -INFINITY;
-    if (mask_l && jb + off >= L) t = -INFINITY;
-    sacc[r] = t;
+    sacc[r] = off >= lim ? -INFINITY : t;
   }
   return false;
 }
