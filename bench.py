@@ -286,7 +286,7 @@ def bench_norm_loss(a):
 
     t = run_timed(a, step, kernels, dev)
     ms_step, kernel_ms = t["ms_step"], t["kernel_ms"]
-    dom = max((n for n in kernel_ms if n in CONVENTION), key=kernel_ms.get)
+    dom = dominant(kernel_ms)
     gbs = abytes[dom] / (kernel_ms[dom] * 1e-3) / 1e9
     value = step_bytes / (ms_step * 1e-3) / 1e9
     line = {
@@ -353,6 +353,14 @@ CONVENTION = {"fwd": 1.0, "bwd_dq": 0.5, "bwd_dkv": 2.0}
 OWN_PRODUCTS = {"fwd": 1.0, "bwd_dq": 1.5, "bwd_dkv": 2.0, "bwd_dbias_sum": 1.0, "bwd_fire": 1.0}
 
 
+def dominant(kernel_ms, shares=None):
+    """The slowest timed kernel; with ``shares``, the slowest of those that
+    have a share of the step's flop count (the others are timed and listed
+    only)."""
+    names = [n for n in kernel_ms if shares is None or n in shares]
+    return max(names, key=kernel_ms.get)
+
+
 def _oracle_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -393,7 +401,7 @@ def _host_info(threads):
 def _attention_line(a, metric, workload, shape, t, fwd_flops, traffic=None):
     """The JSON line of an attention fwd+bwd step from run_timed's result."""
     ms_step, kernel_ms = t["ms_step"], t["kernel_ms"]
-    dom = max(kernel_ms, key=kernel_ms.get)
+    dom = dominant(kernel_ms, CONVENTION)
 
     def tf(share, n):
         return round(share * fwd_flops / (kernel_ms[n] * 1e-3) / 1e12, 2)
