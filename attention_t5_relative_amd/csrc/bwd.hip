@@ -1000,14 +1000,18 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
           }
         }
         const int rbase = myk - (irow0 + 4 * hl);
+        // masked iff roff < lo_lim (key after the query) or roff >= hi_lim
+        // (row past the end), as in the generic path below
+        int lo_lim = mask_c ? rbase : -1;
+        const int hi_lim = mask_r ? L - (irow0 + 4 * hl) : 32;
+        if (none || (mask_k && myk >= L)) lo_lim = 32;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * qq + e, roff = 8 * qq + e;
             const float t = fmaf(sacc[rb][r], c, fb[r]);
-            const bool dead = none | (mask_c & (rbase - roff > 0)) |
-                              (mask_r & (irow0 + 4 * hl + roff >= L)) | (mask_k & (myk >= L));
+            const bool dead = (roff < lo_lim) | (roff >= hi_lim);
             p[r] = __builtin_amdgcn_exp2f(t + (dead ? -INFINITY : 0.f));
           }
       } else if (fast) {

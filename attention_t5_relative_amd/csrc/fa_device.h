@@ -403,12 +403,15 @@ __device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int r
       }
     }
   }
+  // one per-lane limit: a key after the query (rbase + off > 0) or past
+  // the end (off >= lim)
+  const int lim2 = mask_c ? min(lim, 1 - rbase) : lim;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-      if ((mask_c && rbase + off > 0) || off >= lim) sacc[kb][r] = -INFINITY;
+      if (off >= lim2) sacc[kb][r] = -INFINITY;
     }
 }
 
