@@ -8,7 +8,10 @@ v_readlane_b32 restoring a spilled descriptor) and a buffer load that reads
 it.  Every such copy must therefore be issued right after `s_nop 4` or a
 longer one.  This test disassembles every gfx950 code object in
 libfat5attn.so and checks that, and that no kernel spills to scratch (a
-spill would also mean the kernel runs far below its design occupancy)."""
+spill would also mean the kernel runs far below its design occupancy): no
+VGPR spill and no private segment.  SGPRs the compiler parks in spare VGPR
+lanes (v_writelane / v_readlane, no memory) are allowed, up to a few per
+kernel."""
 import os
 import re
 import shutil
@@ -89,11 +92,14 @@ def test_no_kernel_uses_scratch(code_objects):
     for obj in code_objects:
         notes = subprocess.run([readelf, "--notes", str(obj)], capture_output=True, text=True,
                                check=True).stdout
-        spills = re.findall(r"\.(?:s|v)gpr_spill_count:\s+(\d+)", notes)
-        kernels += len(spills)
-        if not spills:   # a code object holding device data only (the static scratch)
+        vspills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", notes)
+        sspills = re.findall(r"\.sgpr_spill_count:\s+(\d+)", notes)
+        kernels += len(vspills)
+        if not vspills:   # a code object holding device data only (the static scratch)
             continue
-        assert all(int(n) == 0 for n in spills), f"{obj.name}: spill counts {set(spills)}"
+        assert all(int(n) == 0 for n in vspills), f"{obj.name}: VGPR spills {set(vspills)}"
+        # SGPR spills go to VGPR lanes while the private segment stays empty
+        assert all(int(n) <= 8 for n in sspills), f"{obj.name}: SGPR spills {set(sspills)}"
         priv = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", notes)
         assert all(int(n) == 0 for n in priv), f"{obj.name}: private segment {set(priv)}"
     assert kernels > 0, "no kernel metadata found"
