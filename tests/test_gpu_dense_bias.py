@@ -61,6 +61,7 @@ CASES = [
     (1, 129, 2, 128, True, 1, 0.2, None),
     (3, 100, 1, 64, False, 1, 1.0, None),
     (1, 160, 2, 64, True, 1, 0.3, 10000.0),   # with RoPE
+    (2, 150, 2, 64, True, 1, 0.3, 10000.0),   # RoPE and the batch sum of a shared matrix
     # the batch-sum kernel at head_dim 128 (64-row tiles, two per 128-row
     # super tile; a ragged last one), odd and even batch counts
     (3, 200, 2, 128, True, 1, 0.125, None),
