@@ -469,18 +469,16 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
   const float lf = (float)myrow < fL ? 1.f : 0.f;
   // Sums of the wave's current segment w_cur, per lane, until the wave's
   // keys leave it; then each lane weights its row's terms, the wave adds
-  // them up (a fixed butterfly) and lane 0 adds them to the wave's own LDS
-  // sums: no atomics, a fixed order, one flush per segment change.
+  // them up (DPP moves in a fixed order) and lane 63 adds them to the
+  // wave's own LDS sums: no atomics, one flush per segment change.
   float u0 = 0.f, u1 = 0.f, u2 = 0.f;
   int w_cur = -1;
   float *const my_acc = fire_acc + wave * kFireGradRows;
   auto flush = [&](int sg, float g0, float g1, float g2) {
     float t[kFireTerms] = {g0, g1, g2 * fl.inv, g1 * wc, g1 * lf};
 #pragma unroll
-    for (int q = 0; q < kFireTerms; ++q)
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) t[q] += __shfl_xor(t[q], off);
-    if (lane == 0)
+    for (int q = 0; q < kFireTerms; ++q) t[q] = wave_sum_lane63(t[q]);
+    if (lane == 63)
 #pragma unroll
       for (int q = 0; q < kFireTerms; ++q) my_acc[sg * kFireTerms + q] += t[q];
   };

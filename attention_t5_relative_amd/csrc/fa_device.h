@@ -145,6 +145,27 @@ __device__ __forceinline__ float half_sum(float x) {
   return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
 }
 
+// Sum over the 64 lanes of a wave, complete in lane 63 (the other lanes hold
+// partial sums), by DPP moves within the VALU: pairs and quads by quad
+// permutes, rows of 16 by two rotations, then row 0's sum broadcast into row
+// 1 and row 2's into row 3, and row 1's (rows 0 + 1) into row 3.  A fixed
+// order: the result does not depend on timing.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  // lanes outside ROW_MASK take 0 (the `old` operand)
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                   CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_lane63(float x) {
+  x = dpp_add<0xb1, 0xf>(x);    // quad_perm [1, 0, 3, 2]
+  x = dpp_add<0x4e, 0xf>(x);    // quad_perm [2, 3, 0, 1]
+  x = dpp_add<0x124, 0xf>(x);   // row_ror 4
+  x = dpp_add<0x128, 0xf>(x);   // row_ror 8: every lane holds its row's sum
+  x = dpp_add<0x142, 0xa>(x);   // row_bcast 15: rows 1 and 3 add rows 0 and 2
+  x = dpp_add<0x143, 0xc>(x);   // row_bcast 31: rows 2 and 3 add lane 31 (rows 0 + 1)
+  return x;
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8),
 // each XCD with its own L2.  This remap gives every XCD a contiguous range of
 // logical ids, so the query tiles of one (sequence, head) - which stream the
