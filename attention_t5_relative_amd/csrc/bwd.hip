@@ -566,11 +566,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
       };
       // the wave's segment range over its lanes' ranges
       int wlo = slo, whi = shi;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        wlo = min(wlo, __shfl_xor(wlo, off));
-        whi = max(whi, __shfl_xor(whi, off));
-      }
+      wave_min_max(wlo, whi);
       if (wlo == whi) {
         if (wlo != w_cur) {
           if (w_cur >= 0) flush(w_cur, u0, u1, u2);

@@ -166,6 +166,26 @@ __device__ __forceinline__ float wave_sum_lane63(float x) {
   return x;
 }
 
+// Minimum and maximum over the 64 lanes of a wave, returned in every lane:
+// the same DPP pattern as wave_sum_lane63 (lanes outside a row mask take the
+// identity), then lane 63 read back as a scalar.  The wave must be fully
+// active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_min_max(int &lo, int &hi) {
+  lo = min(lo, __builtin_amdgcn_update_dpp(0x7fffffff, lo, CTRL, ROW_MASK, 0xf, false));
+  hi = max(hi, __builtin_amdgcn_update_dpp(-0x7fffffff - 1, hi, CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ void wave_min_max(int &lo, int &hi) {
+  dpp_min_max<0xb1, 0xf>(lo, hi);
+  dpp_min_max<0x4e, 0xf>(lo, hi);
+  dpp_min_max<0x124, 0xf>(lo, hi);
+  dpp_min_max<0x128, 0xf>(lo, hi);
+  dpp_min_max<0x142, 0xa>(lo, hi);
+  dpp_min_max<0x143, 0xc>(lo, hi);
+  lo = __builtin_amdgcn_readlane(lo, 63);
+  hi = __builtin_amdgcn_readlane(hi, 63);
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8),
 // each XCD with its own L2.  This remap gives every XCD a contiguous range of
 // logical ids, so the query tiles of one (sequence, head) - which stream the
