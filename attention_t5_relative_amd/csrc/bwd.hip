@@ -88,9 +88,9 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int g, Work &w) {
     int pair;
     tile_order<4>(g, a.nbatch * a.heads, a.ntile, pair, w.tile);   // 2 workgroups per CU
     w.part = pair * a.ntile + w.tile;
-    const int b = pair / a.heads;
+    int b;
+    pair_bh(pair, a.nbatch, a.heads, a.dense != nullptr && a.dense_batch == 1, b, w.h);
     w.b = b;
-    w.h = pair - b * a.heads;
     w.tok0 = b * a.seqlen;
     w.L = a.seqlen;
     w.lse_base = ((size_t)b * a.heads + w.h) * a.seqlen;

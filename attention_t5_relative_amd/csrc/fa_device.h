@@ -228,6 +228,22 @@ __device__ __forceinline__ void tile_order(int g, int npairs, int ntile, int &pa
   }
 }
 
+// (batch, head) of a dense grid's pair.  Pairs run in order on each XCD
+// (tile_order), so with a dense bias matrix shared by the batch the pairs of
+// one head are numbered together (head-major): the tiles running at once on
+// an XCD then read the same bias rows, which the XCD's L2 serves after the
+// first read.  Otherwise batch-major.
+__device__ __forceinline__ void pair_bh(int pair, int nbatch, int heads, bool head_major, int &b,
+                                        int &h) {
+  if (head_major) {
+    h = pair / nbatch;
+    b = pair - h * nbatch;
+  } else {
+    b = pair / heads;
+    h = pair - b * heads;
+  }
+}
+
 // T5 bucket of relative position r (key - query) from the integer thresholds.
 __device__ __forceinline__ int t5_bucket_dev(int r, const T5Geometry &g) {
   int off = 0, n;

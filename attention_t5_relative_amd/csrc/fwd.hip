@@ -101,8 +101,7 @@ void fwd_kernel(
     int pair, rank;
     tile_order<6>(g, a.nbatch * a.heads, a.nq, pair, rank);   // 3 workgroups per CU
     qt = a.nq - 1 - rank;                     // longest causal rows first
-    bidx = pair / a.heads;
-    h = pair - bidx * a.heads;
+    pair_bh(pair, a.nbatch, a.heads, BIAS == kBiasDense && a.dense_batch == 1, bidx, h);
     tok0 = bidx * a.seqlen;
     L = a.seqlen;
   }
