@@ -74,11 +74,11 @@ def _varlen_cases(n=12, seed=20262):
     return out
 
 
-def _bias(kind, H, table, nb, md, bidi):
+def _bias(kind, H, table, nb, md, bidi, slope_mult=1.0):
     if kind == "t5":
         return fa.T5Bias(torch.from_numpy(table).cuda(), nb, md, bidi), None
     if kind == "alibi":
-        s = synth.alibi_slope_values(H)
+        s = (synth.alibi_slope_values(H) * slope_mult).astype(np.float32)
         return fa.ALiBi(torch.from_numpy(s).cuda()), s.astype(np.float64)
     return None, None
 
@@ -93,8 +93,48 @@ def _dense_id(c):
 def test_random_dense_problem(case):
     B, S, H, D, causal, kind, nb, md, bidi, rope, scale = case
     inp = synth.draw_dense(5000 + S * 7 + H, B, S, H, D, num_buckets=nb)
+    _check_dense(inp, case)
+
+
+class _Scaled:
+    """Inputs with q and k multiplied by 2^a (exact in bf16) and the T5 table
+    by tmul: a softmax peaked far beyond the N(0, 1) draws."""
+
+    def __init__(self, inp, a, tmul):
+        f = 2.0 ** a
+        for n in ("q", "k"):
+            setattr(self, n, synth.bf16_round(synth.bf16_bits_to_f32(getattr(inp, n)) * f))
+        self.v, self.do = inp.v, inp.do
+        self.table = None if inp.table is None else (inp.table * tmul).astype(np.float32)
+
+    def f64(self, name):
+        return synth.bf16_bits_to_f32(getattr(self, name)).astype(np.float64)
+
+
+PEAKED = [
+    # B, S, H, D, causal, bias, nb, md, bidirectional, rope, scale, log2 of the q/k factor,
+    # table factor, ALiBi slope factor
+    (1, 300, 2, 64, True, "t5", 32, 128, False, None, 1.0, 2, 8.0, 1.0),
+    (2, 257, 2, 128, False, "t5", 32, 128, True, None, 128 ** -0.5, 2, 4.0, 1.0),
+    (1, 320, 3, 128, True, "alibi", 32, 128, False, None, 128 ** -0.5, 1, 1.0, 16.0),
+    (1, 200, 2, 64, False, "none", 32, 128, False, 10000.0, 0.125, 2, 1.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", PEAKED, ids=lambda c: f"{c[5]}-d{c[3]}-a{c[11]}")
+def test_peaked_softmax(case):
+    """Scores a few hundred log2 units apart (q, k amplified, large table
+    values or slopes): nearly one-hot rows, exercising the running-max
+    rescale, exponent underflow and the backward's exact D."""
+    B, S, H, D, causal, kind, nb, md, bidi, rope, scale, a, tmul, smul = case
+    base = synth.draw_dense(6100 + S, B, S, H, D, num_buckets=nb)
+    _check_dense(_Scaled(base, a, tmul), case[:11], slope_mult=smul)
+
+
+def _check_dense(inp, case, slope_mult=1.0):
+    B, S, H, D, causal, kind, nb, md, bidi, rope, scale = case
     q, k, v, do = (bf16_tensor(getattr(inp, n)) for n in ("q", "k", "v", "do"))
-    bias, slopes = _bias(kind, H, inp.table, nb, md, bidi)
+    bias, slopes = _bias(kind, H, inp.table, nb, md, bidi, slope_mult)
     o = nan_like(q)
     lse = torch.full((B, H, S), float("nan"), device="cuda")
     fa.fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, bias=bias, rope_base=rope or 0.0)
