@@ -196,8 +196,6 @@ __global__ __launch_bounds__(NT, (dq_wgs<D, BIAS>())) void bwd_dq_kernel(const B
   const size_t base = ((size_t)w.tok0 * a.heads + h) * D;
   const uint32_t nrec = ((uint32_t)(L - 1) * (uint32_t)HD + D) * 2u;
   const rsrc_t rq = make_rsrc(a.q + base, nrec);
-  const rsrc_t rk = make_rsrc(a.k + base, nrec);
-  const rsrc_t rv = make_rsrc(a.v + base, nrec);
   const rsrc_t rdo = make_rsrc(a.dout + base, nrec);
   const rsrc_t ro = make_rsrc(a.o + base, nrec);
 
@@ -669,10 +667,8 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
   const int HD = a.heads * D;
   const size_t base = ((size_t)w.tok0 * a.heads + h) * D;
   const uint32_t nrec = ((uint32_t)(L - 1) * (uint32_t)HD + D) * 2u;
-  const rsrc_t rq = make_rsrc(a.q + base, nrec);
   const rsrc_t rk = make_rsrc(a.k + base, nrec);
   const rsrc_t rv = make_rsrc(a.v + base, nrec);
-  const rsrc_t rdo = make_rsrc(a.dout + base, nrec);
 
   // this wave's 32 keys as the B operand of S = Q K^T and dP = dO V^T
   bf16x8 kf[D / 16], vf[kVInLds ? 1 : D / 16];
@@ -1349,7 +1345,8 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 1) void bwd_dbias_sum_kernel(cons
     const bool kout = myk >= L;
     // branch-free: the masks are per element, not per wave
     auto bits = [&](int j, int r) -> uint32_t {
-      const bool dead = part & ((CAUSAL & (rkey > roff(j, r))) | (roff(j, r) >= rlim) | kout);
+      const int dead = (int)part & ((int)(CAUSAL && rkey > roff(j, r)) |
+                                    (int)(roff(j, r) >= rlim) | (int)kout);
       return dead ? 0xff80u : (uint32_t)raw[16 * j + r];
     };
 #pragma unroll
