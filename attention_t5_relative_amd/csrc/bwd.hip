@@ -562,6 +562,25 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
             }
           }
       };
+      // the three sums of the keys at or above kink t_sg (x >= t_sg)
+      auto sums_from = [&](int sg, float &g0, float &g1, float &g2) {
+        const float tlo = fl.tab[kFireOffT + sg];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 de = fire_dist4(fl, -rbase - 32 * kb - 8 * q - 3, fl.dist_half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * q + e;
+              const float x = xs[kb][r];
+              const float gv = x >= tlo ? gs[kb][r] : 0.f;
+              g0 += gv;
+              g1 = fmaf(gv, x, g1);
+              g2 = fmaf(gv, de[3 - e], g2);
+            }
+          }
+      };
       // the wave's segment range over its lanes' ranges
       int wlo = slo, whi = shi;
       wave_min_max(wlo, whi);
@@ -576,10 +595,17 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
         if (w_cur >= 0) flush(w_cur, u0, u1, u2);
         u0 = u1 = u2 = 0.f;
         w_cur = -1;
-        for (int sg = wlo; sg <= whi; ++sg) {
-          float g0 = 0.f, g1 = 0.f, g2 = 0.f;
-          sums(sg, g0, g1, g2);
-          flush(sg, g0, g1, g2);
+        // from the top segment down, the sums over x >= t_sg (one compare
+        // per key); a segment's own sums are the differences of consecutive
+        // ones (x falls along a lane's keys, so every key lies in [wlo, whi])
+        float h0 = 0.f, h1 = 0.f, h2 = 0.f;
+        for (int sg = whi; sg >= wlo; --sg) {
+          float c0 = 0.f, c1 = 0.f, c2 = 0.f;
+          sums_from(sg, c0, c1, c2);
+          flush(sg, c0 - h0, c1 - h1, c2 - h2);
+          h0 = c0;
+          h1 = c1;
+          h2 = c2;
         }
       }
     }
