@@ -29,6 +29,8 @@
 // gradients miss the accuracy gate.  P enters the dV product the same way:
 // with bf16 P alone, dV's elementwise-normalised error reached 1.94e-2 on the
 // causal S = 4096 workload, against a gate of 2e-2.
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -540,12 +542,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
           const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - lse2);
           gs[kb][r] = row_live ? p * (pacc[kb][r] + nd) : 0.f;
         }
-      // the three sums of the keys in segment sg (t_sg <= x < t_sg+1; sg < 0:
-      // every key); d / e from the distance table (element 3 - e of the four
-      // entries from distance -rbase - 32 kb - 8 q - 3)
-      auto sums = [&](int sg, float &g0, float &g1, float &g2) {
-        const float tlo = sg < 0 ? -INFINITY : fl.tab[kFireOffT + max(sg, 0)];
-        const float thi = sg < 0 ? INFINITY : fl.tab[kFireOffT + max(sg, 0) + 1];
+      // the three sums of the keys at or above kink t_sg (x >= t_sg; ALL:
+      // every key, with no compare); d / e from the distance table (element
+      // 3 - e of the four entries from distance -rbase - 32 kb - 8 q - 3)
+      auto sums_from = [&](auto all, int sg, float &g0, float &g1, float &g2) {
+        constexpr bool ALL = decltype(all)::value;
+        const float tlo = ALL ? -INFINITY : fl.tab[kFireOffT + sg];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -555,26 +557,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * q + e;
               const float x = xs[kb][r];
-              const float gv = (x >= tlo && x < thi) ? gs[kb][r] : 0.f;
-              g0 += gv;
-              g1 = fmaf(gv, x, g1);
-              g2 = fmaf(gv, de[3 - e], g2);
-            }
-          }
-      };
-      // the three sums of the keys at or above kink t_sg (x >= t_sg)
-      auto sums_from = [&](int sg, float &g0, float &g1, float &g2) {
-        const float tlo = fl.tab[kFireOffT + sg];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 de = fire_dist4(fl, -rbase - 32 * kb - 8 * q - 3, fl.dist_half);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * q + e;
-              const float x = xs[kb][r];
-              const float gv = x >= tlo ? gs[kb][r] : 0.f;
+              const float gv = (ALL || x >= tlo) ? gs[kb][r] : 0.f;
               g0 += gv;
               g1 = fmaf(gv, x, g1);
               g2 = fmaf(gv, de[3 - e], g2);
@@ -590,7 +573,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
           u0 = u1 = u2 = 0.f;
           w_cur = wlo;
         }
-        sums(-1, u0, u1, u2);
+        sums_from(std::true_type{}, 0, u0, u1, u2);
       } else {
         if (w_cur >= 0) flush(w_cur, u0, u1, u2);
         u0 = u1 = u2 = 0.f;
@@ -601,7 +584,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
         float h0 = 0.f, h1 = 0.f, h2 = 0.f;
         for (int sg = whi; sg >= wlo; --sg) {
           float c0 = 0.f, c1 = 0.f, c2 = 0.f;
-          sums_from(sg, c0, c1, c2);
+          sums_from(std::false_type{}, sg, c0, c1, c2);
           flush(sg, c0 - h0, c1 - h1, c2 - h2);
           h0 = c0;
           h1 = c1;
