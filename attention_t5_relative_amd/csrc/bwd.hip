@@ -530,7 +530,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_fire_kernel(const BwdArgs a) {
       const bool mask_l = j0 + KT > L;
       float xs[NKB][16];
       int shi;
-      fire_scores<NKB, true, true>(sacc, omax, rbase, mask_l ? L - jb : KT, true, c, fl, xs,
+      // (the causal mask reaches this tile when its last key follows the
+      // wave's first row)
+      fire_scores<NKB, true, true>(sacc, omax, rbase, mask_l ? L - jb : KT, j0 + KT - 1 > wrow0,
+                                   c, fl, xs,
                                    &shi);
       const int slo = fl.seg;
       // dS
@@ -1004,15 +1007,20 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
         int lo_lim = mask_c ? rbase : -1;
         const int hi_lim = mask_r ? L - (irow0 + 4 * hl) : 32;
         if (none || (mask_k && myk >= L)) lo_lim = 32;
+        if (!none && !mask_c && !mask_r && !mask_k) {
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
+          for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[rb][r], c, fb[r]));
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * qq + e, roff = 8 * qq + e;
-            const float t = fmaf(sacc[rb][r], c, fb[r]);
-            const bool dead = (roff < lo_lim) | (roff >= hi_lim);
-            p[r] = __builtin_amdgcn_exp2f(t + (dead ? -INFINITY : 0.f));
-          }
+          for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * qq + e, roff = 8 * qq + e;
+              const float t = fmaf(sacc[rb][r], c, fb[r]);
+              const bool dead = (roff < lo_lim) | (roff >= hi_lim);
+              p[r] = __builtin_amdgcn_exp2f(t + (dead ? -INFINITY : 0.f));
+            }
+        }
       } else if (fast) {
         block_p_fast(sacc[rb], bconst, p);
       } else {

@@ -461,15 +461,19 @@ __device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int r
     }
   }
   // one per-lane limit: a key after the query (rbase + off > 0) or past
-  // the end (off >= lim)
-  const int lim2 = mask_c ? min(lim, 1 - rbase) : lim;
+  // the end (off >= lim); a tile with neither mask skips the compares
+  // (mask_c is per tile, and lim is below the tile width on every lane or
+  // on none)
+  if (mask_c || lim < 32 * NKB) {
+    const int lim2 = mask_c ? min(lim, 1 - rbase) : lim;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-      if (off >= lim2) sacc[kb][r] = -INFINITY;
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+        if (off >= lim2) sacc[kb][r] = -INFINITY;
+      }
+  }
 }
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
