@@ -565,10 +565,12 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
     }
   }
   // one per-lane limit for both masks: offset off is a key after the query
-  // (rbase + off > 0) or past the end (jb + off >= L) iff off >= lim
+  // (rbase + off > 0) or past the end (jb + off >= L) iff off >= lim; a
+  // tile with neither mask skips the compares
   int lim = 64;
   if (mask_c) lim = min(lim, 1 - rbase);
   if (mask_l) lim = min(lim, L - jb);
+  const bool masked = mask_c || mask_l;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -578,10 +580,17 @@ __device__ __forceinline__ bool score_tile_T(f32x16 (&sacc)[2], int j0, int row0
       float t = sacc[kb][r] * c;
       if constexpr (BIAS == kBiasAlibi) t = fmaf(fabsf((float)rr), slope_l2, t);
       if constexpr (BIAS == kBiasDense) t = fmaf(bf16_bits(bv[kb][r]), kLog2e, t);
-      sacc[kb][r] = off >= lim ? -INFINITY : t;
+      sacc[kb][r] = t;
       // keep the bias-table reads from being hoisted all at once
       if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) sacc[kb][r] = -INFINITY;
+  }
   return false;
 }
 
