@@ -1040,6 +1040,14 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
               p[4 * qq + e] =
                   __builtin_amdgcn_exp2f(fmaf(sacc[rb][4 * qq + e], c, lb[27 - 8 * qq - e]));
         }
+        // a dense-bias block (head_dim 64) with no mask: no compares
+        const bool dense_plain =
+            BIAS == kBiasDense && D == 64 && !none && !mask_c && !mask_r && !mask_k;
+        if (dense_plain) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            p[r] = __builtin_amdgcn_exp2f(fmaf(bf16_bits(bkv[r]), kLog2e, sacc[rb][r] * c));
+        }
         // Without T5 (whose causal mask is in its table) element r, at row
         // offset roff, is masked iff roff < lo_lim (a key after the query:
         // rbase - roff > 0) or roff >= hi_lim (a row past the end); a block
@@ -1051,7 +1059,7 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
         if (none || (mask_k && myk >= L)) lo_lim = 32;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          if (t5_plain) break;
+          if (t5_plain || dense_plain) break;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * qq + e;
