@@ -373,13 +373,21 @@ __device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int r
   if constexpr (TABLE) {
     if (shi == slo) {
       const float A = fl.tab[kFireOffA + slo], B = fl.tab[kFireOffB + slo];
+      // without KEEP_X the lane's normaliser folds into the slope: one FMA
+      // per key for the bias
+      const float Bi = B * fl.inv;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = ps[kb][r >> 2][3 - (r & 3)] * fl.inv;
-          if constexpr (KEEP_X) xkeep[kb][r] = x;
-          sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(B, x, A));
+          const float psd = ps[kb][r >> 2][3 - (r & 3)];
+          if constexpr (KEEP_X) {
+            const float x = psd * fl.inv;
+            xkeep[kb][r] = x;
+            sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(B, x, A));
+          } else {
+            sacc[kb][r] = fmaf(sacc[kb][r], c, fmaf(Bi, psd, A));
+          }
         }
     } else {
       // b(x) = A_lo + B_lo x + sum over the kinks t_k above segment lo of
