@@ -971,9 +971,12 @@ __global__ __launch_bounds__(NT, (dkv_wgs<D, BIAS>())) void bwd_dkv_kernel(const
           for (int e = 0; e < 4; ++e) fx[4 * qq + e] = ps[e] * inv4[e];
         }
         // x grows with the row: elements 0 and 15 bound the lane's range
-        fslo = fire_walk(fl.tab, fx[0], fl.seg);
-        fshi = fire_walk(fl.tab, fx[15], fslo);
+        float blo = fl.seg_lo, bhi = fl.seg_hi;
+        fslo = fire_walk_cached(fl.tab, fx[0], fl.seg, blo, bhi);
+        fshi = fire_walk_cached(fl.tab, fx[15], fslo, blo, bhi);
         fl.seg = fshi;
+        fl.seg_lo = blo;
+        fl.seg_hi = bhi;
         float fb[16];
         if (fslo == fshi) {
           const float A = fl.tab[kFireOffA + fslo], B = fl.tab[kFireOffB + fslo];

@@ -281,6 +281,7 @@ struct FireLane {
   float c = 0.f;                // psi(t) = log(c t + 1)
   float inv = 0.f;              // 1 / log2(c max(L, i) + 1) for the lane's row i
   int seg = -1;                 // segment of the last x looked up (-1: none yet)
+  float seg_lo = 0.f, seg_hi = 0.f;   // its bounds t_seg, t_seg+1 (valid when seg >= 0)
 };
 
 __device__ __forceinline__ FireLane fire_lane(const float *gtab, const float *dist, int maxlen,
@@ -318,6 +319,18 @@ __device__ __forceinline__ int fire_walk(const float *tab, float x, int s) {
   if (s < 0) return fire_seg(tab, x);
   while (s > 0 && x < tab[kFireOffT + s]) --s;
   while (s < kFireMaxHidden && x >= tab[kFireOffT + s + 1]) ++s;
+  return s;
+}
+
+// The same with segment s's bounds [lo, hi) held in registers: while x
+// stays inside (most tiles) no table read waits; otherwise the walk, and lo,
+// hi become the bounds of the segment found.
+__device__ __forceinline__ int fire_walk_cached(const float *tab, float x, int s, float &lo,
+                                                float &hi) {
+  if (s >= 0 && x >= lo && x < hi) return s;
+  s = fire_walk(tab, x, s);
+  lo = tab[kFireOffT + s];
+  hi = tab[kFireOffT + s + 1];
   return s;
 }
 
@@ -366,9 +379,12 @@ __device__ __forceinline__ void fire_scores(f32x16 (&sacc)[NKB], int omax, int r
     xn = __builtin_amdgcn_logf(fmaxf(u0, 1.f)) * fl.inv;
     xf = __builtin_amdgcn_logf(fmaxf(fmaf(cn, (float)(omax - 3), u0) + ce[3], 1.f)) * fl.inv;
   }
-  const int shi = fire_walk(fl.tab, xn, fl.seg);
-  const int slo = fire_walk(fl.tab, xf, shi);
+  float lo = fl.seg_lo, hi = fl.seg_hi;
+  const int shi = fire_walk_cached(fl.tab, xn, fl.seg, lo, hi);
+  const int slo = fire_walk_cached(fl.tab, xf, shi, lo, hi);
   fl.seg = slo;
+  fl.seg_lo = lo;
+  fl.seg_hi = hi;
   if constexpr (KEEP_X) *seg_hi = shi;
   if constexpr (TABLE) {
     if (shi == slo) {
