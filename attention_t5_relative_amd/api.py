@@ -4,7 +4,8 @@ Torch is plumbing here: it owns device memory and supplies the current HIP
 stream.  Each function checks dtypes/shapes, fills the C params struct with
 ``data_ptr()`` values and calls the library; every step of the attention path
 runs in the HIP kernels.  ``attention`` / ``varlen_attention`` wrap the pair
-of calls in a ``torch.autograd.Function``.
+of calls as torch custom ops with autograd (torch.compile traces them as
+single nodes).
 """
 from __future__ import annotations
 
@@ -309,88 +310,205 @@ def _output_grads(do, dlse, o):
     return do, dlse
 
 
-class _Attention(torch.autograd.Function):
-    @staticmethod
-    def forward(ctx, q, k, v, table, slopes, bias, scale, causal, rope_base):
-        B, S, H, D = q.shape
-        o = torch.empty_like(q)
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-        fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, bias=bias, rope_base=rope_base)
-        ctx.save_for_backward(q, k, v, o, lse)
-        ctx.bias, ctx.scale, ctx.causal, ctx.rope_base = bias, scale, causal, rope_base
-        ctx.set_materialize_grads(False)
-        return o, lse
+# The attention pair as torch custom ops (torch.library), so that
+# torch.compile traces a call as one opaque node (no graph break) and
+# autograd reaches the backward kernels.  The bias travels as its tensor plus
+# plain scalars: kind 0 none, 1 T5, 2 ALiBi, 3 dense matrix, 4 FIRE.
+_NO_BIAS, _T5, _ALIBI, _DENSE, _FIRE = 0, 1, 2, 3, 4
 
-    @staticmethod
-    def backward(ctx, do, dlse):
-        q, k, v, o, lse = ctx.saved_tensors
-        do, dlse = _output_grads(do, dlse, o)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        dtable = None
-        if isinstance(ctx.bias, T5Bias) and ctx.bias.table.requires_grad:
-            dtable = torch.empty_like(ctx.bias.table)
-        if isinstance(ctx.bias, DenseBias) and ctx.bias.matrix.requires_grad:
-            dtable = torch.empty(ctx.bias.matrix.shape, dtype=torch.float32, device=q.device)
-        if isinstance(ctx.bias, FireBias) and ctx.bias.theta.requires_grad:
-            dtable = torch.empty_like(ctx.bias.theta)
-        fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dtable, dlse=dlse, scale=ctx.scale,
-               causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
-        if isinstance(ctx.bias, DenseBias) and dtable is not None:
-            dtable = dtable.to(ctx.bias.matrix.dtype)   # a leaf's gradient keeps its dtype
-        return dq, dk, dv, dtable, None, None, None, None, None
+
+def _bias_fields(bias: BiasSpec):
+    """(kind, tensor, num_buckets, max_distance, bidirectional, hidden)."""
+    if isinstance(bias, T5Bias):
+        return _T5, bias.table, bias.num_buckets, bias.max_distance, bool(bias.bidirectional), 0
+    if isinstance(bias, ALiBi):
+        return _ALIBI, bias.slopes, 0, 0, False, 0
+    if isinstance(bias, DenseBias):
+        return _DENSE, bias.matrix, 0, 0, False, 0
+    if isinstance(bias, FireBias):
+        return _FIRE, bias.theta, 0, 0, False, bias.hidden
+    if bias is None:
+        return _NO_BIAS, None, 0, 0, False, 0
+    raise TypeError(f"unsupported bias {type(bias).__name__}")
+
+
+def _bias_spec(kind, t, nb, md, bidi, hidden) -> BiasSpec:
+    if kind == _T5:
+        return T5Bias(t, nb, md, bidi)
+    if kind == _ALIBI:
+        return ALiBi(t)
+    if kind == _DENSE:
+        return DenseBias(t)
+    if kind == _FIRE:
+        return FireBias(t, hidden)
+    return None
+
+
+def _dbias_like(kind, t, device):
+    """The bias-gradient buffer the kernels write (fp32), or an empty tensor
+    when the bias has none."""
+    if kind in (_T5, _FIRE):
+        return torch.empty(t.shape, dtype=torch.float32, device=device)
+    if kind == _DENSE:
+        return torch.empty(t.shape, dtype=torch.float32, device=device)
+    return torch.empty(0, dtype=torch.float32, device=device)
+
+
+@torch.library.custom_op("fat5attn::attention_fwd", mutates_args=(), device_types="cuda")
+def _attention_fwd_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      bias_t: Optional[torch.Tensor], kind: int, nb: int, md: int, bidi: bool,
+                      hidden: int, scale: float, causal: bool,
+                      rope_base: float) -> tuple[torch.Tensor, torch.Tensor]:
+    B, S, H, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale=scale, causal=causal,
+           bias=_bias_spec(kind, bias_t, nb, md, bidi, hidden), rope_base=rope_base)
+    return o, lse
+
+
+@_attention_fwd_op.register_fake
+def _(q, k, v, bias_t, kind, nb, md, bidi, hidden, scale, causal, rope_base):
+    B, S, H, D = q.shape
+    return torch.empty_like(q), q.new_empty((B, H, S), dtype=torch.float32)
+
+
+@torch.library.custom_op("fat5attn::attention_bwd", mutates_args=(), device_types="cuda")
+def _attention_bwd_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                      lse: torch.Tensor, do: torch.Tensor, dlse: Optional[torch.Tensor],
+                      bias_t: Optional[torch.Tensor], kind: int, nb: int, md: int, bidi: bool,
+                      hidden: int, scale: float, causal: bool, rope_base: float,
+                      want_dbias: bool) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor,
+                                                 torch.Tensor]:
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias = (_dbias_like(kind, bias_t, q.device) if want_dbias
+             else torch.empty(0, dtype=torch.float32, device=q.device))
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dbias if dbias.numel() else None, dlse=dlse,
+           scale=scale, causal=causal, bias=_bias_spec(kind, bias_t, nb, md, bidi, hidden),
+           rope_base=rope_base)
+    return dq, dk, dv, dbias
+
+
+@_attention_bwd_op.register_fake
+def _(q, k, v, o, lse, do, dlse, bias_t, kind, nb, md, bidi, hidden, scale, causal, rope_base,
+      want_dbias):
+    dbias = (_dbias_like(kind, bias_t, q.device) if want_dbias
+             else q.new_empty((0,), dtype=torch.float32))
+    return torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), dbias
+
+
+def _attention_setup(ctx, inputs, output):
+    q, k, v, bias_t, kind, nb, md, bidi, hidden, scale, causal, rope_base = inputs
+    o, lse = output
+    ctx.save_for_backward(q, k, v, o, lse, bias_t)
+    ctx.cfg = (kind, nb, md, bidi, hidden, scale, causal, rope_base)
+
+
+def _attention_backward(ctx, do, dlse):
+    q, k, v, o, lse, bias_t = ctx.saved_tensors
+    kind = ctx.cfg[0]
+    want = bool(ctx.needs_input_grad[3]) and kind in (_T5, _DENSE, _FIRE)
+    do, dlse = _output_grads(do, dlse, o)
+    dq, dk, dv, dbias = _attention_bwd_op(q, k, v, o, lse, do, dlse, bias_t, *ctx.cfg, want)
+    if not want:
+        dbias = None
+    elif kind == _DENSE:
+        dbias = dbias.to(bias_t.dtype)   # a leaf's gradient keeps its dtype
+    return dq, dk, dv, dbias, None, None, None, None, None, None, None, None
+
+
+_attention_fwd_op.register_autograd(_attention_backward, setup_context=_attention_setup)
 
 
 def attention(q, k, v, *, bias: BiasSpec = None, causal=False, scale=1.0, rope_base=0.0,
               return_lse=False):
     """Exact attention with optional T5 / ALiBi / FIRE / dense bias and RoPE;
-    q, k, v [B,S,H,D] bf16."""
-    table = bias.table if isinstance(bias, T5Bias) else None
-    if isinstance(bias, DenseBias):
-        table = bias.matrix
-    if isinstance(bias, FireBias):
-        table = bias.theta
-    slopes = bias.slopes if isinstance(bias, ALiBi) else None
-    o, lse = _Attention.apply(q, k, v, table, slopes, bias, scale, causal, rope_base)
+    q, k, v [B,S,H,D] bf16.  Differentiable in q, k, v and the bias tensor
+    (T5 table, dense matrix, FIRE theta), and traceable by torch.compile."""
+    kind, t, nb, md, bidi, hidden = _bias_fields(bias)
+    o, lse = _attention_fwd_op(q, k, v, t, kind, nb, md, bidi, hidden, float(scale),
+                               bool(causal), float(rope_base))
     return (o, lse) if return_lse else o
 
 
-class _VarlenAttention(torch.autograd.Function):
-    @staticmethod
-    def forward(ctx, q, k, v, table, cu_seqlens, max_seqlen, bias, scale, causal, rope_base):
-        T, H, D = q.shape
-        o = torch.empty_like(q)
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-        fa_varlen_fwd(q, k, v, o, lse, cu_seqlens, max_seqlen, scale=scale, causal=causal,
-                      bias=bias, rope_base=rope_base)
-        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
-        ctx.max_seqlen, ctx.bias, ctx.scale = max_seqlen, bias, scale
-        ctx.causal, ctx.rope_base = causal, rope_base
-        ctx.set_materialize_grads(False)
-        return o, lse
+@torch.library.custom_op("fat5attn::varlen_attention_fwd", mutates_args=(), device_types="cuda")
+def _varlen_fwd_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                   max_seqlen: int, bias_t: Optional[torch.Tensor], kind: int, nb: int, md: int,
+                   bidi: bool, hidden: int, scale: float, causal: bool,
+                   rope_base: float) -> tuple[torch.Tensor, torch.Tensor]:
+    T, H, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    fa_varlen_fwd(q, k, v, o, lse, cu_seqlens, max_seqlen, scale=scale, causal=causal,
+                  bias=_bias_spec(kind, bias_t, nb, md, bidi, hidden), rope_base=rope_base)
+    return o, lse
 
-    @staticmethod
-    def backward(ctx, do, dlse):
-        q, k, v, o, lse, cu = ctx.saved_tensors
-        do, dlse = _output_grads(do, dlse, o)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        dtable = None
-        if isinstance(ctx.bias, T5Bias) and ctx.bias.table.requires_grad:
-            dtable = torch.empty_like(ctx.bias.table)
-        if isinstance(ctx.bias, FireBias) and ctx.bias.theta.requires_grad:
-            dtable = torch.empty_like(ctx.bias.theta)
-        fa_varlen_bwd(q, k, v, o, lse, do, dq, dk, dv, cu, ctx.max_seqlen, dtable, dlse=dlse,
-                      scale=ctx.scale, causal=ctx.causal, bias=ctx.bias, rope_base=ctx.rope_base)
-        return dq, dk, dv, dtable, None, None, None, None, None, None
+
+@_varlen_fwd_op.register_fake
+def _(q, k, v, cu_seqlens, max_seqlen, bias_t, kind, nb, md, bidi, hidden, scale, causal,
+      rope_base):
+    T, H, D = q.shape
+    return torch.empty_like(q), q.new_empty((H, T), dtype=torch.float32)
+
+
+@torch.library.custom_op("fat5attn::varlen_attention_bwd", mutates_args=(), device_types="cuda")
+def _varlen_bwd_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                   lse: torch.Tensor, do: torch.Tensor, dlse: Optional[torch.Tensor],
+                   cu_seqlens: torch.Tensor, max_seqlen: int, bias_t: Optional[torch.Tensor],
+                   kind: int, nb: int, md: int, bidi: bool, hidden: int, scale: float,
+                   causal: bool, rope_base: float,
+                   want_dbias: bool) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor,
+                                              torch.Tensor]:
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias = (_dbias_like(kind, bias_t, q.device) if want_dbias
+             else torch.empty(0, dtype=torch.float32, device=q.device))
+    fa_varlen_bwd(q, k, v, o, lse, do, dq, dk, dv, cu_seqlens, max_seqlen,
+                  dbias if dbias.numel() else None, dlse=dlse, scale=scale, causal=causal,
+                  bias=_bias_spec(kind, bias_t, nb, md, bidi, hidden), rope_base=rope_base)
+    return dq, dk, dv, dbias
+
+
+@_varlen_bwd_op.register_fake
+def _(q, k, v, o, lse, do, dlse, cu_seqlens, max_seqlen, bias_t, kind, nb, md, bidi, hidden,
+      scale, causal, rope_base, want_dbias):
+    dbias = (_dbias_like(kind, bias_t, q.device) if want_dbias
+             else q.new_empty((0,), dtype=torch.float32))
+    return torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), dbias
+
+
+def _varlen_setup(ctx, inputs, output):
+    (q, k, v, cu_seqlens, max_seqlen, bias_t, kind, nb, md, bidi, hidden, scale, causal,
+     rope_base) = inputs
+    o, lse = output
+    ctx.save_for_backward(q, k, v, o, lse, cu_seqlens, bias_t)
+    ctx.max_seqlen = max_seqlen
+    ctx.cfg = (kind, nb, md, bidi, hidden, scale, causal, rope_base)
+
+
+def _varlen_backward(ctx, do, dlse):
+    q, k, v, o, lse, cu, bias_t = ctx.saved_tensors
+    kind = ctx.cfg[0]
+    want = bool(ctx.needs_input_grad[5]) and kind in (_T5, _FIRE)
+    do, dlse = _output_grads(do, dlse, o)
+    dq, dk, dv, dbias = _varlen_bwd_op(q, k, v, o, lse, do, dlse, cu, ctx.max_seqlen, bias_t,
+                                       *ctx.cfg, want)
+    return (dq, dk, dv, None, None, dbias if want else None, None, None, None, None, None,
+            None, None, None)
+
+
+_varlen_fwd_op.register_autograd(_varlen_backward, setup_context=_varlen_setup)
 
 
 def varlen_attention(q, k, v, cu_seqlens, max_seqlen, *, bias: BiasSpec = None, causal=False,
                      scale=1.0, rope_base=0.0, return_lse=False):
-    """Packed attention; q, k, v [T,H,D] bf16, cu_seqlens int32 [nseq+1]."""
-    table = bias.table if isinstance(bias, T5Bias) else None
-    if isinstance(bias, FireBias):
-        table = bias.theta
-    o, lse = _VarlenAttention.apply(q, k, v, table, cu_seqlens, max_seqlen, bias, scale, causal,
-                                    rope_base)
+    """Packed attention; q, k, v [T,H,D] bf16, cu_seqlens int32 [nseq+1].
+    Differentiable in q, k, v and the T5 table or FIRE theta, and traceable
+    by torch.compile."""
+    if isinstance(bias, DenseBias):
+        raise ValueError("a dense bias matrix is for the dense entry points")
+    kind, t, nb, md, bidi, hidden = _bias_fields(bias)
+    o, lse = _varlen_fwd_op(q, k, v, cu_seqlens, int(max_seqlen), t, kind, nb, md, bidi, hidden,
+                            float(scale), bool(causal), float(rope_base))
     return (o, lse) if return_lse else o
 
 
