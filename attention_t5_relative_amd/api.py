@@ -588,49 +588,102 @@ def fa_ce_bwd(logits, labels, lse, dloss, dlogits, *, z_loss=0.0, ignore_index=-
     check(lib.fa_ce_bwd(ctypes.byref(p), _stream(logits.device, stream)), "fa_ce_bwd")
 
 
-class _RMSNorm(torch.autograd.Function):
-    @staticmethod
-    def forward(ctx, x, w, eps):
-        y = torch.empty_like(x)
-        rstd = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
-        fa_rmsnorm_fwd(x, w, y, rstd, eps=eps)
-        ctx.save_for_backward(x, w, rstd)
-        ctx.eps = eps
-        return y
+# RMSNorm and cross-entropy as torch custom ops with autograd as well.
+@torch.library.custom_op("fat5attn::rms_norm_fwd", mutates_args=(), device_types="cuda")
+def _rmsnorm_fwd_op(x: torch.Tensor, w: torch.Tensor,
+                    eps: float) -> tuple[torch.Tensor, torch.Tensor]:
+    y = torch.empty_like(x)
+    rstd = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    fa_rmsnorm_fwd(x, w, y, rstd, eps=eps)
+    return y, rstd
 
-    @staticmethod
-    def backward(ctx, dy):
-        x, w, rstd = ctx.saved_tensors
-        dx = torch.empty_like(x)
-        dw = torch.empty(w.shape, dtype=torch.float32, device=w.device) if w.requires_grad else None
-        fa_rmsnorm_bwd(x, w, rstd, dy.contiguous(), dx, dw, eps=ctx.eps)
-        return dx, (None if dw is None else dw.to(w.dtype)), None
+
+@_rmsnorm_fwd_op.register_fake
+def _(x, w, eps):
+    return torch.empty_like(x), x.new_empty((x.shape[0],), dtype=torch.float32)
+
+
+@torch.library.custom_op("fat5attn::rms_norm_bwd", mutates_args=(), device_types="cuda")
+def _rmsnorm_bwd_op(x: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor, dy: torch.Tensor,
+                    eps: float, want_dw: bool) -> tuple[torch.Tensor, torch.Tensor]:
+    dx = torch.empty_like(x)
+    dw = torch.empty(w.shape if want_dw else (0,), dtype=torch.float32, device=w.device)
+    fa_rmsnorm_bwd(x, w, rstd, dy, dx, dw if want_dw else None, eps=eps)
+    return dx, dw
+
+
+@_rmsnorm_bwd_op.register_fake
+def _(x, w, rstd, dy, eps, want_dw):
+    return torch.empty_like(x), w.new_empty(w.shape if want_dw else (0,), dtype=torch.float32)
+
+
+def _rmsnorm_setup(ctx, inputs, output):
+    x, w, eps = inputs
+    ctx.save_for_backward(x, w, output[1])
+    ctx.eps = eps
+
+
+def _rmsnorm_backward(ctx, dy, drstd):
+    x, w, rstd = ctx.saved_tensors
+    want = bool(ctx.needs_input_grad[1])
+    dx, dw = _rmsnorm_bwd_op(x, w, rstd, dy.contiguous(), ctx.eps, want)
+    return dx, (dw.to(w.dtype) if want else None), None
+
+
+_rmsnorm_fwd_op.register_autograd(_rmsnorm_backward, setup_context=_rmsnorm_setup)
 
 
 def rms_norm(x, w, eps=1e-6):
     """RMSNorm over the last dimension of bf16 x (any leading shape), weight w [dim]."""
     shape = x.shape
-    return _RMSNorm.apply(x.reshape(-1, shape[-1]).contiguous(), w, eps).reshape(shape)
+    y, _ = _rmsnorm_fwd_op(x.reshape(-1, shape[-1]).contiguous(), w, float(eps))
+    return y.reshape(shape)
 
 
-class _CrossEntropy(torch.autograd.Function):
-    @staticmethod
-    def forward(ctx, logits, labels, z_loss, ignore_index):
-        rows = logits.shape[0]
-        loss = torch.empty(rows, dtype=torch.float32, device=logits.device)
-        lse = torch.empty_like(loss)
-        fa_ce_fwd(logits, labels, loss, lse, z_loss=z_loss, ignore_index=ignore_index)
-        ctx.save_for_backward(logits, labels, lse)
-        ctx.z_loss, ctx.ignore_index = z_loss, ignore_index
-        return loss
+@torch.library.custom_op("fat5attn::cross_entropy_fwd", mutates_args=(), device_types="cuda")
+def _ce_fwd_op(logits: torch.Tensor, labels: torch.Tensor, z_loss: float,
+               ignore_index: int) -> tuple[torch.Tensor, torch.Tensor]:
+    rows = logits.shape[0]
+    loss = torch.empty(rows, dtype=torch.float32, device=logits.device)
+    lse = torch.empty_like(loss)
+    fa_ce_fwd(logits, labels, loss, lse, z_loss=z_loss, ignore_index=ignore_index)
+    return loss, lse
 
-    @staticmethod
-    def backward(ctx, dloss):
-        logits, labels, lse = ctx.saved_tensors
-        dlogits = torch.empty_like(logits)
-        fa_ce_bwd(logits, labels, lse, dloss.contiguous().float(), dlogits, z_loss=ctx.z_loss,
-                  ignore_index=ctx.ignore_index)
-        return dlogits, None, None, None
+
+@_ce_fwd_op.register_fake
+def _(logits, labels, z_loss, ignore_index):
+    rows = logits.shape[0]
+    return (logits.new_empty((rows,), dtype=torch.float32),
+            logits.new_empty((rows,), dtype=torch.float32))
+
+
+@torch.library.custom_op("fat5attn::cross_entropy_bwd", mutates_args=(), device_types="cuda")
+def _ce_bwd_op(logits: torch.Tensor, labels: torch.Tensor, lse: torch.Tensor,
+               dloss: torch.Tensor, z_loss: float, ignore_index: int) -> torch.Tensor:
+    dlogits = torch.empty_like(logits)
+    fa_ce_bwd(logits, labels, lse, dloss, dlogits, z_loss=z_loss, ignore_index=ignore_index)
+    return dlogits
+
+
+@_ce_bwd_op.register_fake
+def _(logits, labels, lse, dloss, z_loss, ignore_index):
+    return torch.empty_like(logits)
+
+
+def _ce_setup(ctx, inputs, output):
+    logits, labels, z_loss, ignore_index = inputs
+    ctx.save_for_backward(logits, labels, output[1])
+    ctx.z_loss, ctx.ignore_index = z_loss, ignore_index
+
+
+def _ce_backward(ctx, dloss, dlse):
+    logits, labels, lse = ctx.saved_tensors
+    dlogits = _ce_bwd_op(logits, labels, lse, dloss.contiguous().float(), ctx.z_loss,
+                         ctx.ignore_index)
+    return dlogits, None, None, None
+
+
+_ce_fwd_op.register_autograd(_ce_backward, setup_context=_ce_setup)
 
 
 def cross_entropy(logits, labels, *, z_loss=0.0, ignore_index=-100):
@@ -638,5 +691,6 @@ def cross_entropy(logits, labels, *, z_loss=0.0, ignore_index=-100):
     labels [rows]: fp32 [rows], 0 for ignored rows.  Any reduction over the
     rows (a mean over the non-ignored ones, a sum) is the caller's, as in the
     C ABI: the kernels compute per-row losses and their gradients."""
-    return _CrossEntropy.apply(logits.contiguous(), labels.to(torch.int32).contiguous(),
-                               float(z_loss), int(ignore_index))
+    loss, _ = _ce_fwd_op(logits.contiguous(), labels.to(torch.int32).contiguous(),
+                         float(z_loss), int(ignore_index))
+    return loss

@@ -45,3 +45,18 @@ def test_dense_bias_refused_by_packed_entry():
     with pytest.raises(ValueError):
         fa.varlen_attention(q, q, q, torch.zeros(2, dtype=torch.int32), 10,
                             bias=fa.DenseBias(_meta(1, 1, 10, 10)))
+
+
+def test_norm_and_loss_ops_fake_shapes():
+    x = _meta(64, 768)
+    w = _meta(768)
+    y, rstd = torch.ops.fat5attn.rms_norm_fwd(x, w, 1e-6)
+    assert y.shape == x.shape and rstd.shape == (64,) and rstd.dtype == torch.float32
+    dx, dw = torch.ops.fat5attn.rms_norm_bwd(x, w, rstd, y, 1e-6, True)
+    assert dx.shape == x.shape and dw.shape == (768,) and dw.dtype == torch.float32
+    logits = _meta(64, 1000)
+    labels = torch.empty(64, dtype=torch.int32, device="meta")
+    loss, lse = torch.ops.fat5attn.cross_entropy_fwd(logits, labels, 1e-4, -100)
+    assert loss.shape == lse.shape == (64,) and loss.dtype == torch.float32
+    dl = torch.ops.fat5attn.cross_entropy_bwd(logits, labels, lse, loss, 1e-4, -100)
+    assert dl.shape == logits.shape and dl.dtype == torch.bfloat16

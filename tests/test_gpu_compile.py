@@ -68,3 +68,27 @@ def test_compiled_packed_fire_equals_eager():
         runs.append([loss.detach()] + [x.grad for x in (q, k, v, th)])
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+def test_compiled_norm_and_loss_equal_eager():
+    g = torch.Generator("cuda").manual_seed(5)
+    x0 = torch.randn(256, 768, device="cuda", generator=g).to(torch.bfloat16)
+    w0 = (1 + 0.25 * torch.randn(768, device="cuda", generator=g)).to(torch.bfloat16)
+    proj = (torch.randn(768, 1000, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    labels = torch.randint(0, 1000, (256,), device="cuda", generator=g)
+    labels[::7] = -100
+
+    def loss_fn(x, w):
+        h = fa.rms_norm(x, w)
+        rows = fa.cross_entropy(h @ proj, labels, z_loss=1e-4)
+        return rows.sum() / (labels != -100).sum()
+
+    runs = []
+    for fn in (loss_fn, torch.compile(loss_fn, fullgraph=True, backend="aot_eager")):
+        x, w = x0.clone().requires_grad_(), w0.clone().requires_grad_()
+        loss = fn(x, w)
+        loss.backward()
+        torch.cuda.synchronize()
+        runs.append([loss.detach(), x.grad, w.grad])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
