@@ -45,21 +45,24 @@ constexpr int kFireMaxHeadsLds = 256;   // heads whose w2 rows fit the LDS copy
 
 // Kinks inside (0, 1), sorted ascending (ties by unit index), into
 // tk[1 .. m] (fp64, LDS); returns m.  All threads of the workgroup call it.
-__device__ int fire_kinks(const float *w1, const float *b1, int K, double *tk) {
+// Each unit's kink is divided out once into tv (LDS; units without a kink
+// in (0, 1) hold 2), then ranked against the others.
+__device__ int fire_kinks(const float *w1, const float *b1, int K, double *tk, double *tv) {
   const int tid = threadIdx.x;
   bool valid = false;
   double t = 0.0;
-  if (tid < K && w1[tid] != 0.f) {
-    t = -(double)b1[tid] / (double)w1[tid];
-    valid = t > 0.0 && t < 1.0;
+  if (tid < K) {
+    if (w1[tid] != 0.f) {
+      t = -(double)b1[tid] / (double)w1[tid];
+      valid = t > 0.0 && t < 1.0;
+    }
+    tv[tid] = valid ? t : 2.0;
   }
   const int m = __syncthreads_count(valid);
   if (valid) {
     int rank = 0;
     for (int j = 0; j < K; ++j) {
-      if (w1[j] == 0.f) continue;
-      const double tj = -(double)b1[j] / (double)w1[j];
-      if (!(tj > 0.0 && tj < 1.0)) continue;
+      const double tj = tv[j];
       rank += (tj < t || (tj == t && j < tid)) ? 1 : 0;
     }
     tk[rank + 1] = t;
@@ -81,6 +84,7 @@ struct FireSmem {
   float w1[kFireMaxHidden], b1[kFireMaxHidden];
   float w2[kFireMaxHeadsLds * kFireMaxHidden];
   double tk[kFireSegs + 1];
+  double tv[kFireMaxHidden];
   uint64_t act[kFireSegs];
 };
 
@@ -93,7 +97,7 @@ __device__ int fire_prepare(const float *theta, int H, int K, FireSmem &sm) {
   if (H <= kFireMaxHeadsLds)
     for (int i = tid; i < H * K; i += FT) sm.w2[i] = theta[2 * K + i];
   __syncthreads();
-  const int m = fire_kinks(sm.w1, sm.b1, K, sm.tk);
+  const int m = fire_kinks(sm.w1, sm.b1, K, sm.tk, sm.tv);
   for (int s = tid; s <= m; s += FT) {
     const double xs = fire_mid(sm.tk, m, s);
     uint64_t bits = 0;
