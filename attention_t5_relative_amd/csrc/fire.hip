@@ -173,23 +173,39 @@ __global__ __launch_bounds__(FT) void fire_grad_kernel(const float *theta, int H
     for (int s = 0; s <= m; ++s) t += G(s, 0, h);
     dtheta[2 * K + H * K + h] = (float)t;
   }
-  // dw1, db1 [K]: sum over heads of w2_hk times the same segment sums
+  // dw1, db1 [K]: sum over heads of w2_hk times the same segment sums.
+  // Thread (g, k), g < NG = FT / K, takes the heads h = g (mod NG); the NG
+  // partials of each unit are then added in g order (a fixed order).
+  const int NG = FT / K;
+  {
+    const int k = tid % K, grp = tid / K;
+    double t1 = 0.0, t0 = 0.0;
+    if (grp < NG)
+      for (int h = grp; h < H; h += NG) {
+        double s1 = 0.0, s0 = 0.0;
+        for (int s = 0; s <= m; ++s)
+          if ((sm.act[s] >> k) & 1) {
+            s1 += G(s, 1, h);
+            s0 += G(s, 0, h);
+          }
+        const double w = fire_w2(sm, theta, H, K, h, k);
+        t1 += w * s1;
+        t0 += w * s0;
+      }
+    red[0][tid] = t1;
+    red[1][tid] = t0;
+  }
+  __syncthreads();
   for (int k = tid; k < K; k += FT) {
     double t1 = 0.0, t0 = 0.0;
-    for (int h = 0; h < H; ++h) {
-      double s1 = 0.0, s0 = 0.0;
-      for (int s = 0; s <= m; ++s)
-        if ((sm.act[s] >> k) & 1) {
-          s1 += G(s, 1, h);
-          s0 += G(s, 0, h);
-        }
-      const double w = fire_w2(sm, theta, H, K, h, k);
-      t1 += w * s1;
-      t0 += w * s0;
+    for (int grp = 0; grp < NG; ++grp) {
+      t1 += red[0][grp * K + k];
+      t0 += red[1][grp * K + k];
     }
     dtheta[k] = (float)t1;
     dtheta[K + k] = (float)t0;
   }
+  __syncthreads();   // red is reused below
   // dc, dL: one (head, segment) pair per thread and step, then a
   // fixed-order tree
   double pc = 0.0, pl = 0.0;
